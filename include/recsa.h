@@ -1,0 +1,187 @@
+/*
+ * recsa.h -- C ABI of librecsa.so, the MI355X (gfx950) hot path of RecSA,
+ * "Recursive Sparse Attention: Million-Token Length Extrapolation at
+ * Logarithmic Cost" (arXiv 2611.07232).
+ *
+ * The pages (picx.dev summary, "Methodology") define the operation:
+ *   - Tree Construction, Eq. 1: per layer and KV head, level 0 holds the
+ *     exact token keys/values; C = 16 consecutive entries of a level form a
+ *     parent whose key comes from a pooler and whose value is the mean of the
+ *     children's values.
+ *   - Pooler Distillation, Eq. 5: the pooler that makes a node key from its C
+ *     children keys (one pooler per layer, shared by all levels: abstract).
+ *   - Hierarchical Selection, Eq. 3: top-down, each level >= 1 keeps the
+ *     current node plus the k-1 highest-scoring other candidates; the kept
+ *     nodes' children form the next candidate list.
+ *   - Key Theoretical Insight: each entry's RoPE position is its index in its
+ *     level's candidate list, so every distance stays below C*k.
+ *   - Unified Softmax, Eq. 4: one softmax over the exact level-0 candidates
+ *     and the summaries of the unselected candidates of every level >= 1.
+ *
+ * Conventions shared by every call
+ *   - All tensors are device memory owned by the caller.  The library never
+ *     allocates, frees or synchronises; every call is ordered on `stream`
+ *     (a hipStream_t passed as void*; NULL = the legacy default stream) and
+ *     may be captured into a HIP graph.
+ *   - Storage dtype (tree, q, k_new, v_new) is RECSA_F32 (float) or
+ *     RECSA_BF16 (bfloat16 bits in uint16).  Arithmetic is float32; outputs
+ *     are float32.
+ *   - Query head h belongs to KV head h / (Hq / Hkv).  One selection is made
+ *     per (query, KV head) and shared by its Hq/Hkv query heads.
+ *   - q and the level-0 keys are given before RoPE: positions are assigned
+ *     at query time from the candidate lists.
+ *   - Logit of query head h and an entry at list position p (p = C*r + c) of
+ *     a list whose last position is p_q = C*r_q + c_q:
+ *         s = (q~ . k~) / sqrt(d),
+ *         q~ = rnd(R(C*(r_q - r) + c_q) q_h),  k~ = rnd(R(c) K_entry),
+ *     R = rotate-half RoPE (pairs (j, j+d/2), angle phi * theta^(-2j/d)),
+ *     evaluated in float32 as (x*c - y*s, x*s + y*c) without fused
+ *     multiply-add; rnd rounds to the storage dtype (nearest even).  In exact
+ *     arithmetic this is q . R(p - p_q) K, RoPE at candidate-local positions.
+ *   - Importance at a scored level (the pages leave it open) is the mean over
+ *     the G query heads of the softmax of s over the non-current candidates;
+ *     ties go to the smaller node index.
+ *   - Return value: RECSA_OK or a negative status.  Arguments are validated
+ *     before anything is launched; on an error nothing is launched.
+ *     RECSA_E_HIP reports a failed launch (hipGetLastError).
+ */
+#ifndef RECSA_H
+#define RECSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RECSA_OK 0
+#define RECSA_E_INVALID (-1)     /* null pointer, bad shape, range error      */
+#define RECSA_E_UNSUPPORTED (-2) /* C != 16, d not 64/128, k*C > 4096, dtype  */
+#define RECSA_E_WORKSPACE (-3)   /* workspace smaller than required           */
+#define RECSA_E_HIP (-4)         /* HIP launch error                          */
+
+#define RECSA_F32 0
+#define RECSA_BF16 1
+
+#define RECSA_MAX_LEVELS 8
+
+/* One layer's KV tree.
+ * K[l], V[l]: level l rows, layout [B][Hkv][recsa_level_rows(L_cap, C, l)][d]
+ *   in the storage dtype; level 0 is the ordinary KV cache (pre-RoPE keys).
+ *   Only complete nodes are ever written: node i of level l covers tokens
+ *   [i*C^l, (i+1)*C^l).
+ * n_levels: levels allocated, >= recsa_levels_needed(L_cap, C, k) (so the
+ *   list of the top level has at most k nodes for every position < L_cap);
+ *   more levels do not change any result.
+ * rope: float32 table [C*k][d/2][2] of (cos, sin), filled by recsa_init_rope.
+ */
+typedef struct recsa_tree {
+  int32_t dtype;
+  int32_t B;
+  int32_t Hkv;
+  int32_t d;
+  int32_t C;
+  int32_t k;
+  int32_t n_levels;
+  int32_t reserved;
+  int64_t L_cap;
+  void* K[RECSA_MAX_LEVELS];
+  void* V[RECSA_MAX_LEVELS];
+  const float* rope;
+} recsa_tree;
+
+/* The pooler of Eq. 5, float32 device arrays, one per layer:
+ *   mu = mean_c x_c;  sigma = sqrt(mean_{c,j} (x_cj - mu_j)^2 + eps);
+ *   rho = sqrt(mean_j mu_j^2 + eps);
+ *   alpha = softmax_c(tau * w.(x_c - mu) / sigma);  p = sum_c alpha_c x_c;
+ *   m = W2 SiLU(W1 [mu/rho ; (p - mu)/sigma] + b1);
+ *   K = mu + g (p - mu) + sigma m.
+ * w: [d]; W1: [hidden][2d] row-major; b1: [hidden]; W2: [d][hidden].
+ * hidden must be a multiple of 16 and at most 256. */
+typedef struct recsa_pooler {
+  int32_t d;
+  int32_t hidden;
+  float tau;
+  float g;
+  float eps;
+  int32_t reserved;
+  const float* w;
+  const float* W1;
+  const float* b1;
+  const float* W2;
+} recsa_pooler;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* recsa_status_string(int status);
+
+/* Rows allocated at `level` for capacity L_cap: floor(L_cap / C^level). */
+int64_t recsa_level_rows(int64_t L_cap, int32_t C, int32_t level);
+
+/* Smallest level count whose top list [0 .. floor(t / C^(n-1))] has at most
+ * k nodes for every t < L_cap (the walk starts there; Eq. 3 first line). */
+int32_t recsa_levels_needed(int64_t L_cap, int32_t C, int32_t k);
+
+/* Fill the RoPE table `table` [n_pos][d/2][2] (device, float32) with
+ * cos/sin(phi * theta^(-2j/d)), evaluated in double and rounded once.
+ * n_pos must be C*k for use in a recsa_tree. */
+int recsa_init_rope(float* table, int32_t d, int32_t n_pos, double theta, void* stream);
+
+/* Workspace bytes recsa_select and recsa_attn_* need for n_queries = B*T
+ * queries with Hq query heads (logits of every scored candidate, selection
+ * bitmaps and attention partials).  0 on invalid arguments. */
+size_t recsa_workspace_bytes(const recsa_tree* tree, int32_t Hq, int64_t n_queries);
+
+/* Tree Construction (Eq. 1, Eq. 5): (re)compute every complete node, at every
+ * level >= 1, whose last token lies in [tok_begin, tok_end).  Level-0 rows
+ * [0, tok_end) must already be written.  Nodes are computed level by level,
+ * each from the stored (rounded) children.  0 <= tok_begin <= tok_end <= L_cap. */
+int recsa_build_tree(const recsa_tree* tree, const recsa_pooler* pooler,
+                     int64_t tok_begin, int64_t tok_end, void* stream);
+
+/* Decode append: for each sequence b write k_new/v_new [B][Hkv][d] as level-0
+ * row t = pos_dev[b] (device int64 [B]) and complete every node whose last
+ * token is t (levels l with (t+1) mod C^l == 0).  Precondition (device side,
+ * not checked): 0 <= t < L_cap and rows [0, t) are in the tree. */
+int recsa_append_decode(const recsa_tree* tree, const recsa_pooler* pooler,
+                        const void* k_new, const void* v_new,
+                        const int64_t* pos_dev, void* stream);
+
+/* Hierarchical Selection (Eq. 3) for T queries per sequence.
+ * q: [B][T][Hq][d] storage dtype; pos_dev: [B][T] device int64, each query's
+ *   token position t (the query attends over tokens [0, t]; row t and every
+ *   complete node over [0, t) must be in the tree).
+ * sel_idx: [B][T][Hkv][n_levels-1][k] int32: slot l-1 holds S^(l) in ascending
+ *   node order (the current node last), -1 padded.
+ * sel_cnt: [B][T][Hkv][n_levels-1] int32 = |S^(l)|.
+ * importance_or_null: optional [B][T][Hkv][n_levels-1][C*k] float32; entry p
+ *   is the importance of the candidate at list position p (0 where unscored).
+ * ws: workspace of at least recsa_workspace_bytes(tree, Hq, B*T) bytes; it
+ *   keeps the logits that recsa_attn_* reuse for the unselected summaries, so
+ *   pass the same ws, untouched, to the attention call of the same queries. */
+int recsa_select(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
+                 const int64_t* pos_dev, int32_t* sel_idx, int32_t* sel_cnt,
+                 float* importance_or_null, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Unified Softmax (Eq. 4) for one decode query per sequence: q [B][Hq][d],
+ * pos_dev [B], the selection and ws of recsa_select (T = 1); out [B][Hq][d]
+ * float32.  The launch shape depends only on the tree's static sizes. */
+int recsa_attn_decode(const recsa_tree* tree, const void* q, int32_t Hq,
+                      const int64_t* pos_dev, const int32_t* sel_idx,
+                      const int32_t* sel_cnt, float* out, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Unified Softmax (Eq. 4) for T queries per sequence (a causal prefill
+ * chunk): q [B][T][Hq][d], pos_dev [B][T], selection and ws of recsa_select;
+ * out [B][T][Hq][d] float32. */
+int recsa_attn_prefill(const recsa_tree* tree, const void* q, int32_t Hq,
+                       int32_t T, const int64_t* pos_dev,
+                       const int32_t* sel_idx, const int32_t* sel_cnt,
+                       float* out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RECSA_H */

@@ -1,0 +1,154 @@
+// C ABI of librecsa: argument validation, then stream-ordered launches.
+// Nothing is launched when validation fails; no call allocates, frees or
+// synchronises, so every call can be captured into a HIP graph.
+#include <math.h>
+
+#include "recsa_common.hpp"
+#include "recsa_kernels.hpp"
+
+using namespace recsa;
+
+namespace {
+
+bool tree_ok(const recsa_tree* t, int* why) {
+  *why = RECSA_E_INVALID;
+  if (!t) return false;
+  if (t->B < 1 || t->Hkv < 1 || t->L_cap < 1 || t->k < 1 || t->n_levels < 1 ||
+      t->n_levels > RECSA_MAX_LEVELS)
+    return false;
+  if (t->dtype != RECSA_F32 && t->dtype != RECSA_BF16) { *why = RECSA_E_UNSUPPORTED; return false; }
+  if (t->C != kC || (t->d != 64 && t->d != 128) || t->k > 256 ||
+      static_cast<int64_t>(t->C) * t->k > kMaxCK) {
+    *why = RECSA_E_UNSUPPORTED;
+    return false;
+  }
+  if (t->L_cap > (int64_t{1} << 40)) return false;
+  if (t->n_levels < recsa_levels_needed(t->L_cap, t->C, t->k)) return false;
+  if (!t->rope) return false;
+  for (int l = 0; l < t->n_levels; ++l) {
+    if (level_rows_host(t->L_cap, l) > 0 && (!t->K[l] || !t->V[l])) return false;
+  }
+  return true;
+}
+
+bool pooler_ok(const recsa_pooler* p, const recsa_tree* t) {
+  if (!p) return false;
+  if (p->d != t->d || p->hidden < 16 || p->hidden > 256 || p->hidden % 16 != 0) return false;
+  if (!p->w || !p->W1 || !p->b1 || !p->W2) return false;
+  if (!isfinite(p->tau) || !isfinite(p->g) || !isfinite(p->eps) || p->eps < 0.f) return false;
+  return true;
+}
+
+bool heads_ok(const recsa_tree* t, int32_t Hq) {
+  if (Hq < 1 || Hq % t->Hkv != 0) return false;
+  const int G = Hq / t->Hkv;
+  return G == 1 || G == 2 || G == 4 || G == 8;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RECSA_OK : RECSA_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* recsa_status_string(int status) {
+  switch (status) {
+    case RECSA_OK: return "ok";
+    case RECSA_E_INVALID: return "invalid argument";
+    case RECSA_E_UNSUPPORTED: return "unsupported configuration";
+    case RECSA_E_WORKSPACE: return "workspace too small";
+    case RECSA_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int64_t recsa_level_rows(int64_t L_cap, int32_t C, int32_t level) {
+  if (L_cap < 0 || C < 2 || level < 0) return 0;
+  int64_t r = L_cap;
+  for (int l = 0; l < level && r > 0; ++l) r /= C;
+  return r;
+}
+
+int32_t recsa_levels_needed(int64_t L_cap, int32_t C, int32_t k) {
+  if (L_cap < 1 || C < 2 || k < 1) return 0;
+  const int64_t t_max = L_cap - 1;
+  int32_t D = 1;
+  int64_t span = 1;
+  while (t_max / span + 1 > k) {
+    span *= C;
+    ++D;
+  }
+  return D;
+}
+
+int recsa_init_rope(float* table, int32_t d, int32_t n_pos, double theta, void* stream) {
+  if (!table || d < 2 || d % 2 != 0 || n_pos < 1 || !(theta > 1.0)) return RECSA_E_INVALID;
+  return hip_status(launch_rope_table(table, d, n_pos, theta, static_cast<hipStream_t>(stream)));
+}
+
+size_t recsa_workspace_bytes(const recsa_tree* tree, int32_t Hq, int64_t n_queries) {
+  int why;
+  if (!tree_ok(tree, &why) || !heads_ok(tree, Hq) || n_queries < 1) return 0;
+  return static_cast<size_t>(ws_layout(*tree, Hq, n_queries).total);
+}
+
+int recsa_build_tree(const recsa_tree* tree, const recsa_pooler* pooler, int64_t tok_begin,
+                     int64_t tok_end, void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!pooler_ok(pooler, tree)) return RECSA_E_INVALID;
+  if (tok_begin < 0 || tok_end < tok_begin || tok_end > tree->L_cap) return RECSA_E_INVALID;
+  if (tok_end == tok_begin) return RECSA_OK;
+  return hip_status(launch_build(*tree, *pooler, tok_begin, tok_end, static_cast<hipStream_t>(stream)));
+}
+
+int recsa_append_decode(const recsa_tree* tree, const recsa_pooler* pooler, const void* k_new,
+                        const void* v_new, const int64_t* pos_dev, void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!pooler_ok(pooler, tree) || !k_new || !v_new || !pos_dev) return RECSA_E_INVALID;
+  return hip_status(launch_append(*tree, *pooler, k_new, v_new, pos_dev, static_cast<hipStream_t>(stream)));
+}
+
+int recsa_select(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T, const int64_t* pos_dev,
+                 int32_t* sel_idx, int32_t* sel_cnt, float* importance_or_null, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
+  if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !ws) return RECSA_E_INVALID;
+  if (static_cast<int64_t>(tree->B) * T > 0x7FFFFFFF / tree->Hkv) return RECSA_E_INVALID;
+  const WsLayout w = ws_layout(*tree, Hq, static_cast<int64_t>(tree->B) * T);
+  if (ws_bytes < static_cast<size_t>(w.total)) return RECSA_E_WORKSPACE;
+  if (tree->n_levels < 2) return RECSA_OK;      // a single level: nothing to select
+  return hip_status(launch_select(*tree, q, Hq, T, pos_dev, sel_idx, sel_cnt, importance_or_null,
+                                  ws, w, static_cast<hipStream_t>(stream)));
+}
+
+static int attn_common(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
+                       const int64_t* pos_dev, const int32_t* sel_idx, const int32_t* sel_cnt,
+                       float* out, void* ws, size_t ws_bytes, bool decode, void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
+  if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !out || !ws) return RECSA_E_INVALID;
+  if (static_cast<int64_t>(tree->B) * T > 0x7FFFFFFF / tree->Hkv) return RECSA_E_INVALID;
+  const WsLayout w = ws_layout(*tree, Hq, static_cast<int64_t>(tree->B) * T);
+  if (ws_bytes < static_cast<size_t>(w.total)) return RECSA_E_WORKSPACE;
+  return hip_status(launch_attn(*tree, q, Hq, T, pos_dev, sel_idx, sel_cnt, out, ws, w, decode,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int recsa_attn_decode(const recsa_tree* tree, const void* q, int32_t Hq, const int64_t* pos_dev,
+                      const int32_t* sel_idx, const int32_t* sel_cnt, float* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return attn_common(tree, q, Hq, 1, pos_dev, sel_idx, sel_cnt, out, ws, ws_bytes, true, stream);
+}
+
+int recsa_attn_prefill(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
+                       const int64_t* pos_dev, const int32_t* sel_idx, const int32_t* sel_cnt,
+                       float* out, void* ws, size_t ws_bytes, void* stream) {
+  return attn_common(tree, q, Hq, T, pos_dev, sel_idx, sel_cnt, out, ws, ws_bytes, false, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+// Device helpers shared by the RecSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "recsa.h"
+
+namespace recsa {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;        // 4 waves per workgroup
+constexpr int kC = 16;             // branching factor (picx.dev Tree Construction)
+constexpr int kMaxCK = 4096;       // longest candidate list, C*k
+constexpr int kMaxG = 8;           // query heads per KV head
+constexpr int kChunk = 256;        // list positions per attention/score chunk
+
+// ---------------------------------------------------------------- storage
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even float32 -> bfloat16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <int DT>
+struct Stor;
+
+template <>
+struct Stor<RECSA_F32> {
+  using T = float;
+  static __device__ __forceinline__ float load(const T* p) { return *p; }
+  static __device__ __forceinline__ void store(T* p, float v) { *p = v; }
+  static __device__ __forceinline__ float round(float v) { return v; }
+};
+
+template <>
+struct Stor<RECSA_BF16> {
+  using T = uint16_t;
+  static __device__ __forceinline__ float load(const T* p) { return bf16_bits_to_f32(*p); }
+  static __device__ __forceinline__ void store(T* p, float v) { *p = f32_to_bf16_bits(v); }
+  static __device__ __forceinline__ float round(float v) {
+    return bf16_bits_to_f32(f32_to_bf16_bits(v));
+  }
+};
+
+// Load n consecutive storage elements (n = 2, 4 or 8) as floats.
+template <int DT, int N>
+__device__ __forceinline__ void load_vec(const typename Stor<DT>::T* p, float* out) {
+  if constexpr (DT == RECSA_BF16) {
+    if constexpr (N == 8) {
+      uint4 u = *reinterpret_cast<const uint4*>(p);
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(w[i] << 16);
+        out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else if constexpr (N == 4) {
+      uint2 u = *reinterpret_cast<const uint2*>(p);
+      out[0] = __uint_as_float(u.x << 16);
+      out[1] = __uint_as_float(u.x & 0xFFFF0000u);
+      out[2] = __uint_as_float(u.y << 16);
+      out[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    } else {
+      static_assert(N == 2, "vector width");
+      uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+      out[0] = __uint_as_float(u << 16);
+      out[1] = __uint_as_float(u & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      if constexpr (N >= 4) {
+        float4 v = *reinterpret_cast<const float4*>(p + i);
+        out[i] = v.x;
+        out[i + 1] = v.y;
+        out[i + 2] = v.z;
+        out[i + 3] = v.w;
+      }
+    }
+    if constexpr (N == 2) {
+      float2 v = *reinterpret_cast<const float2*>(p);
+      out[0] = v.x;
+      out[1] = v.y;
+    }
+  }
+}
+
+// ------------------------------------------------------------------- RoPE
+// Rotate-half pair (x, y) by the angle whose (cos, sin) = (c, s):
+// (x*c - y*s, x*s + y*c), each product and sum rounded to float32 separately
+// (no fused multiply-add), so that the rounded operand is reproducible.
+__device__ __forceinline__ void rope_pair(float x, float y, float c, float s,
+                                          float& xo, float& yo) {
+#pragma clang fp contract(off)
+  const float xc = x * c;
+  const float ys = y * s;
+  const float xs = x * s;
+  const float yc = y * c;
+  xo = xc - ys;
+  yo = xs + yc;
+}
+
+// ------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a 256-thread block; `red` is LDS of >= 4 ints.
+// Returns the exclusive prefix and writes the block total to *total.
+__device__ __forceinline__ int block_excl_scan(int v, int* red, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x >> 6;
+  int inc = wave_incl_scan(v);
+  if (lane == kWave - 1) red[wid] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kBlock / kWave; ++w) {
+    int x = red[w];
+    off += (w < wid) ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + inc - v;
+}
+
+// --------------------------------------------------------- list geometry
+// Per (query, KV head, level l) view of the candidate list A^(l) of Eq. 3:
+// A^(l) is the concatenation, in ascending node order, of the children of the
+// selected nodes of level l+1, clipped at the current node a_l; at the top
+// level it is [0 .. a_top].  Position p = C*r + c holds node C*S[r] + c.
+struct ListView {
+  int len;              // |A^(l)|
+  int64_t cur;          // current node a_l
+  const int32_t* up;    // S^(l+1) (ascending), nullptr at the top level
+  __device__ __forceinline__ int64_t node(int p) const {
+    return up ? static_cast<int64_t>(kC) * up[p / kC] + (p % kC) : static_cast<int64_t>(p);
+  }
+};
+
+// Build the list view of level l.  sel/cnt point at this (query, head)'s
+// selection arrays ([n_sel][k] and [n_sel]); top = n_levels - 1.
+__device__ __forceinline__ ListView list_view(int64_t t, int l, int top, int k,
+                                              const int32_t* sel, const int32_t* cnt) {
+  ListView v;
+  v.cur = t >> (4 * l);
+  if (l >= top) {
+    v.len = static_cast<int>(v.cur) + 1;
+    v.up = nullptr;
+  } else {
+    const int c_up = cnt[l];                    // |S^(l+1)| sits in slot l
+    v.len = kC * (c_up - 1) + static_cast<int>(v.cur % kC) + 1;
+    v.up = sel + static_cast<int64_t>(l) * k;
+  }
+  return v;
+}
+
+}  // namespace recsa

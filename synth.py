@@ -82,12 +82,13 @@ def generator(device, *parts) -> torch.Generator:
 
 
 def normal(shape, device, *parts, std=1.0):
-    """N(0, std^2) float32 tensor from a generator seeded by ``parts``."""
-    g = generator(device, *parts)
-    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    """N(0, std^2) float32 tensor from a CPU generator seeded by ``parts``,
+    moved to ``device`` (so every device sees the same numbers)."""
+    g = generator("cpu", *parts)
+    x = torch.randn(shape, generator=g, dtype=torch.float32)
     if std != 1.0:
         x.mul_(std)
-    return x
+    return x.to(device)
 
 
 def to_storage(x: torch.Tensor, dtype: str) -> torch.Tensor:

@@ -1,0 +1,121 @@
+"""Host-side checks of librecsa.so that need no GPU: every symbol declared in
+include/recsa.h is exported, the layout helpers are right, and argument
+validation rejects bad calls with the documented status before launching."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_kv_amd import recsa as R
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "recsa.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(recsa_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("recsa_build_tree", "recsa_append_decode", "recsa_select",
+              "recsa_attn_decode", "recsa_attn_prefill"):
+        assert n in names
+    assert set(names) == set(R.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(R.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_layout_helpers():
+    assert R.recsa_level_rows(524288, 16, 0) == 524288
+    assert R.recsa_level_rows(524288, 16, 2) == 2048
+    assert R.recsa_level_rows(100, 16, 2) == 0
+    assert R.recsa_levels_needed(4096, 16, 16) == 3          # tiny workload: 3 levels
+    assert R.recsa_levels_needed(524288 + 4096, 16, 256) == 4
+    assert R.recsa_levels_needed(1048577, 16, 256) == 5
+    assert R.recsa_levels_needed(256, 16, 256) == 1
+    assert R.recsa_status_string(R.RECSA_E_WORKSPACE) == "workspace too small"
+    assert R.recsa_status_string(12345) == "unknown status"
+
+
+def _tree(**over):
+    t = R.TreeC()
+    t.dtype, t.B, t.Hkv, t.d, t.C, t.k = R.RECSA_BF16, 1, 8, 128, 16, 256
+    t.L_cap, t.n_levels = 528384, 4
+    for lvl in range(4):
+        t.K[lvl] = 0x1000 * (lvl + 1)       # never dereferenced: validation fails first
+        t.V[lvl] = 0x2000 * (lvl + 1)
+    t.rope = 0x3000
+    for k, v in over.items():
+        setattr(t, k, v)
+    return t
+
+
+def _pooler(**over):
+    p = R.PoolerC()
+    p.d, p.hidden, p.tau, p.g, p.eps = 128, 128, 1.0, 0.5, 1e-6
+    p.w = p.W1 = p.b1 = p.W2 = 0x4000
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(C=8), R.RECSA_E_UNSUPPORTED),
+    (dict(d=96), R.RECSA_E_UNSUPPORTED),
+    (dict(k=512), R.RECSA_E_UNSUPPORTED),
+    (dict(dtype=7), R.RECSA_E_UNSUPPORTED),
+    (dict(n_levels=3), R.RECSA_E_INVALID),      # top list would exceed k
+    (dict(n_levels=9), R.RECSA_E_INVALID),
+    (dict(B=0), R.RECSA_E_INVALID),
+    (dict(rope=None), R.RECSA_E_INVALID),
+])
+def test_tree_validation(over, status):
+    L = R.lib()
+    t = _tree(**over)
+    p = _pooler()
+    assert L.recsa_build_tree(ctypes.byref(t), ctypes.byref(p), 0, 16, None) == status
+
+
+def test_call_validation_without_launch():
+    L = R.lib()
+    t, p = _tree(), _pooler()
+    b = ctypes.byref
+    assert L.recsa_build_tree(None, b(p), 0, 16, None) == R.RECSA_E_INVALID
+    assert L.recsa_build_tree(b(t), b(p), 0, t.L_cap + 1, None) == R.RECSA_E_INVALID
+    assert L.recsa_build_tree(b(t), b(p), 10, 5, None) == R.RECSA_E_INVALID
+    assert L.recsa_build_tree(b(t), b(p), 7, 7, None) == R.RECSA_OK          # empty range
+    assert L.recsa_build_tree(b(t), b(_pooler(d=64)), 0, 16, None) == R.RECSA_E_INVALID
+    assert L.recsa_build_tree(b(t), b(_pooler(hidden=100)), 0, 16, None) == R.RECSA_E_INVALID
+    assert L.recsa_build_tree(b(t), b(_pooler(eps=-1.0)), 0, 16, None) == R.RECSA_E_INVALID
+    assert L.recsa_append_decode(b(t), b(p), None, 0x10, 0x10, None) == R.RECSA_E_INVALID
+    ws_need = L.recsa_workspace_bytes(b(t), 32, 1)
+    assert ws_need > 0
+    assert L.recsa_workspace_bytes(b(t), 30, 1) == 0                        # Hq % Hkv
+    args = (b(t), 0x10, 32, 1, 0x10, 0x10, 0x10, None, 0x10)
+    assert L.recsa_select(*args, ws_need - 1, None) == R.RECSA_E_WORKSPACE
+    assert L.recsa_select(b(t), 0x10, 24, 1, 0x10, 0x10, 0x10, None, 0x10, ws_need, None) \
+        == R.RECSA_E_UNSUPPORTED                                            # G = 3
+    assert L.recsa_select(b(t), None, 32, 1, 0x10, 0x10, 0x10, None, 0x10, ws_need, None) \
+        == R.RECSA_E_INVALID
+    assert L.recsa_attn_decode(b(t), 0x10, 32, 0x10, 0x10, 0x10, None, 0x10, ws_need, None) \
+        == R.RECSA_E_INVALID
+    assert L.recsa_attn_prefill(b(t), 0x10, 32, 0, 0x10, 0x10, 0x10, 0x10, 0x10, ws_need, None) \
+        == R.RECSA_E_INVALID
+    assert L.recsa_init_rope(None, 128, 4096, 1e6, None) == R.RECSA_E_INVALID
+    assert L.recsa_init_rope(0x10, 127, 4096, 1e6, None) == R.RECSA_E_INVALID
+
+
+def test_workspace_grows_with_queries():
+    L = R.lib()
+    t = _tree()
+    a = L.recsa_workspace_bytes(ctypes.byref(t), 32, 1)
+    b = L.recsa_workspace_bytes(ctypes.byref(t), 32, 4096)
+    # logits of 3 selection levels x 4 heads x 4096 positions per (query, head)
+    assert b - a == 4095 * 8 * (3 * 4 * 4096 * 4 + 3 * 128 * 4)

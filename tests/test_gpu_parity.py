@@ -1,0 +1,265 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Bars: tree nodes within one storage ulp of the oracle (float32: 1e-5
+relative); selections equal, except near-ties where the oracle's importances
+of the swapped pair differ by less than 1e-5 relative (more only where a key
+row itself differs by a storage-rounding flip); outputs within 1e-5 (float32)
+or 2e-3 (bfloat16) max relative error.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import recsa_oracle as O
+from tests import parity as PY
+
+pytestmark = pytest.mark.gpu
+
+R = pytest.importorskip("long_context_kv_amd.recsa")
+DEV = "cuda"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    R.lib()
+
+
+def _setup(B, Hkv, d, L_tokens, L_cap, k, dtype, seed, hidden=None):
+    """Seeded level-0 rows [B, Hkv, L_cap, d] (first L_tokens filled), pooler."""
+    wl = synth.Workload("t", B, Hkv, Hkv * 4, d, dtype, L_tokens, 16, k, seed)
+    K, V = synth.kv_rows(wl, DEV, n_rows=L_cap)
+    pdict = synth.pooler_params(d, hidden or d, DEV, seed)
+    tree = R.Tree.allocate(B, Hkv, d, L_cap, k=k, dtype=dtype, device=DEV, level0=(K, V))
+    pool = R.Pooler.from_dict(pdict, DEV)
+    return wl, tree, pool, pdict
+
+
+def _oracle_tree(tree, pdict, b, j, n_tokens, n_levels=None):
+    K0 = PY.to64(tree.K[0][b, j, :n_tokens])
+    V0 = PY.to64(tree.V[0][b, j, :n_tokens])
+    D = n_levels or tree.n_levels
+    return O.build_tree(K0, V0, 16, D, PY.oracle_pooler(pdict), tree.dtype)
+
+
+# ---------------------------------------------------------------------------
+
+def test_rope_table_matches_oracle():
+    _need_gpu()
+    for d, n in ((64, 256), (128, 4096)):
+        t = torch.empty((n, d // 2, 2), dtype=torch.float32, device=DEV)
+        R.recsa_init_rope(t, d, n, 1e6)
+        torch.cuda.synchronize()
+        cos, sin = O.rope_table(d, n, 1e6)
+        g = t.cpu().numpy()
+        diff = np.maximum(np.abs(g[..., 0] - cos), np.abs(g[..., 1] - sin))
+        assert diff.max() <= 2.0 ** -24, diff.max()
+        assert (diff > 0).mean() < 1e-4
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("f32", 128), ("bf16", 64)])
+def test_build_tree_matches_oracle(dtype, d):
+    _need_gpu()
+    L = 16 ** 3 * 2 + 37                     # ragged tail: incomplete nodes stay unbuilt
+    wl, tree, pool, pdict = _setup(1, 2, d, L, L, 16, dtype, 11)
+    R.recsa_build_tree(tree, pool, 0, L)
+    torch.cuda.synchronize()
+    for j in range(2):
+        K, V = _oracle_tree(tree, pdict, 0, j, L)
+        for lvl in range(1, tree.n_levels):
+            gk, gv = PY.to64(tree.K[lvl][0, j]), PY.to64(tree.V[lvl][0, j])
+            n = K[lvl].shape[0]
+            assert n == gk.shape[0] == L // 16 ** lvl
+            if dtype == "f32":
+                assert np.allclose(gk, K[lvl], rtol=1e-5, atol=1e-6), lvl
+                assert np.allclose(gv, V[lvl], rtol=1e-5, atol=1e-7), lvl
+            else:
+                # one ulp of the rounded result plus float32 error relative to
+                # the row's scale (cancellation can make a key tiny); above
+                # level 1 each side reads its own rounded children, so a child
+                # flip (half a ulp of the children's scale, averaged over 16)
+                # may also carry through
+                scale = np.abs(K[lvl]).max(axis=1, keepdims=True)
+                tight = PY.ulp_bf16(K[lvl]) + 4e-6 * scale
+                bound = tight + (lvl - 1) * 2.0 ** -9 * scale
+                dk = np.abs(gk - K[lvl])
+                assert np.all(dk <= bound), (lvl, float((dk / bound).max()))
+                assert (dk > tight).mean() < 1e-2, (lvl, (dk > tight).mean())
+                # level 1 reads identical inputs on both sides: flips are rare
+                assert (dk > 0).mean() < (2e-3 if lvl == 1 else 5e-2), (lvl, (dk > 0).mean())
+                dv = np.abs(gv - V[lvl]) / PY.ulp_bf16(V[lvl])
+                assert dv.max() <= 1.0 and (dv > 0).mean() < 1e-3, lvl
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_append_equals_build(dtype, d):
+    """Appending tokens one at a time (completing nodes on the fly) gives
+    exactly the tree a single build gives."""
+    _need_gpu()
+    L0, n_app = 4096 - 40, 300
+    L_cap = L0 + n_app
+    wl, tree, pool, pdict = _setup(2, 2, d, L_cap, L_cap, 16, dtype, 12)
+    ref = R.Tree.allocate(2, 2, d, L_cap, k=16, dtype=dtype, device=DEV,
+                          level0=(tree.K[0].clone(), tree.V[0].clone()))
+    R.recsa_build_tree(ref, pool, 0, L_cap)
+    # the appending tree starts from a build of [0, L0) and fresh rows after
+    newk, newv = tree.K[0][:, :, L0:].clone(), tree.V[0][:, :, L0:].clone()
+    tree.K[0][:, :, L0:] = 0
+    tree.V[0][:, :, L0:] = 0
+    R.recsa_build_tree(tree, pool, 0, L0)
+    for i in range(n_app):
+        pos = torch.full((2,), L0 + i, dtype=torch.int64, device=DEV)
+        R.recsa_append_decode(tree, pool, newk[:, :, i].contiguous(), newv[:, :, i].contiguous(), pos)
+    torch.cuda.synchronize()
+    for lvl in range(tree.n_levels):
+        assert torch.equal(tree.K[lvl], ref.K[lvl]), lvl
+        assert torch.equal(tree.V[lvl], ref.V[lvl]), lvl
+
+
+def _run_select_attn(tree, q, Hq, pos, decode):
+    B, T = pos.shape
+    nq = B * T
+    ws = R.workspace(tree, Hq, nq)
+    sel, cnt, imp = tree.selection_buffers(nq, with_importance=True)
+    R.recsa_select(tree, q, Hq, T, pos, sel, cnt, imp, ws)
+    out = torch.empty((B, T, Hq, tree.d), dtype=torch.float32, device=DEV)
+    if decode:
+        assert T == 1
+        R.recsa_attn_decode(tree, q, Hq, pos, sel, cnt, out, ws)
+    else:
+        R.recsa_attn_prefill(tree, q, Hq, T, pos, sel, cnt, out, ws)
+    torch.cuda.synchronize()
+    return (sel.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel, tree.k),
+            cnt.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel),
+            imp.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel, -1),
+            out.cpu().numpy().astype(np.float64))
+
+
+def _check_queries(tree, pdict, q, pos, sel, cnt, imp, out, heads, tie_rel, out_tol,
+                   trees=None, max_swaps=0):
+    """Walk every (b, query, head in `heads`) in the oracle and compare."""
+    B, T = pos.shape
+    G = q.shape[2] // tree.Hkv
+    cos, sin = O.rope_table(tree.d, tree.C * tree.k, 1e6)
+    rep = PY.WalkReport()
+    qn = PY.to64(q)
+    trees = trees if trees is not None else {}
+    for b in range(B):
+        for j in heads:
+            if (b, j) not in trees:
+                n_tok = int(pos[b].max()) + 1
+                trees[(b, j)] = _oracle_tree(tree, pdict, b, j, n_tok)
+            K, V = trees[(b, j)]
+            gk = {lvl: PY.to64(tree.K[lvl][b, j, :K[lvl].shape[0]]) for lvl in range(1, len(K))}
+            differs = lambda lvl, node: not np.array_equal(gk[lvl][node], K[lvl][node])
+            for ti in range(T):
+                t = int(pos[b, ti])
+                D = O.n_levels_for(t, 16, tree.k)
+                Kt = [K[0][: t + 1]] + [K[lvl][: (t + 1) // 16 ** lvl] for lvl in range(1, len(K))]
+                Vt = [V[0][: t + 1]] + [V[lvl][: (t + 1) // 16 ** lvl] for lvl in range(1, len(V))]
+                Kt, Vt = Kt[: max(D, 1)], Vt[: max(D, 1)]
+                o_ref, tr = O.decode_reference(qn[b, ti, j * G:(j + 1) * G], t, Kt, Vt, 16,
+                                               tree.k, cos, sin, tree.dtype)
+                ok = PY.compare_walk(tr, sel[b, ti, j], cnt[b, ti, j], imp[b, ti, j], rep,
+                                     tie_rel, differs, 2e-2)
+                # levels above the oracle's top are fully selected prefixes
+                for lvl in range(D, tree.n_levels):
+                    a = t >> (4 * lvl)
+                    assert cnt[b, ti, j, lvl - 1] == a + 1
+                    assert np.array_equal(sel[b, ti, j, lvl - 1, : a + 1], np.arange(a + 1))
+                if ok:
+                    err = PY.out_rel_err(out[b, ti, j * G:(j + 1) * G], o_ref)
+                    rep.max_out_rel = max(rep.max_out_rel, err)
+                    assert err <= out_tol, (b, t, j, err)
+    assert rep.swapped <= max_swaps, rep.notes
+    return rep
+
+
+def test_tiny_fp32_decode_queries():
+    """Tiny workload: 1 KV head, 4 query heads, d=64, fp32, L=4096, k=16 (3
+    levels); 8 queries at the last positions, through the T-query path and
+    each through the decode path (split + combine)."""
+    _need_gpu()
+    wl = synth.WORKLOADS["tiny"]
+    K, V = synth.kv_rows(wl, DEV)
+    pdict = synth.pooler_params(wl.d, wl.d, DEV, wl.seed)
+    tree = R.Tree.allocate(1, 1, wl.d, wl.L, k=wl.k, dtype="f32", device=DEV, level0=(K, V))
+    assert tree.n_levels == 3
+    pool = R.Pooler.from_dict(pdict, DEV)
+    R.recsa_build_tree(tree, pool, 0, wl.L)
+    q = synth.decode_queries(wl, DEV)                       # [1, 8, 4, 64]
+    pos = torch.arange(wl.L - 8, wl.L, device=DEV).view(1, 8)
+    sel, cnt, imp, out = _run_select_attn(tree, q, wl.Hq, pos, decode=False)
+    trees = {}
+    rep = _check_queries(tree, pdict, q, pos.cpu(), sel, cnt, imp, out, [0], 1e-5, 1e-5, trees)
+    assert rep.matched == 8 and rep.max_imp_rel < 1e-4, rep
+    for i in range(8):
+        qi = q[:, i:i + 1].contiguous()
+        pi = pos[:, i:i + 1].contiguous()
+        s2, c2, m2, o2 = _run_select_attn(tree, qi, wl.Hq, pi, decode=True)
+        assert np.array_equal(s2[0, 0], sel[0, i]) and np.array_equal(c2[0, 0], cnt[0, i])
+        assert np.allclose(o2[0, 0], out[0, i], rtol=0, atol=1e-6 * np.abs(out[0, i]).max())
+
+
+def test_edge_positions_fp32():
+    """Queries at every kind of position in one call: the first token, dense
+    short contexts (t < C*k), exact powers of 16, node boundaries and a
+    ragged end; T-query path and decode path."""
+    _need_gpu()
+    L = 5000
+    wl, tree, pool, pdict = _setup(1, 1, 64, L, L, 16, "f32", 13)
+    R.recsa_build_tree(tree, pool, 0, L)
+    ts = [0, 1, 2, 15, 16, 17, 255, 256, 257, 300, 4095, 4096, 4097, 4111, 4112, 4999]
+    pos = torch.tensor([ts], dtype=torch.int64, device=DEV)
+    q = synth.to_storage(synth.normal((1, len(ts), 4, 64), DEV, 13, 99), "f32")
+    sel, cnt, imp, out = _run_select_attn(tree, q, 4, pos, decode=False)
+    rep = _check_queries(tree, pdict, q, pos.cpu(), sel, cnt, imp, out, [0], 1e-5, 1e-5)
+    assert rep.matched == len(ts)
+    for i in (0, 5, 12, 15):
+        s2, c2, m2, o2 = _run_select_attn(tree, q[:, i:i + 1].contiguous(),
+                                          4, pos[:, i:i + 1].contiguous(), decode=True)
+        assert np.allclose(o2[0, 0], out[0, i], rtol=0, atol=1e-6 * np.abs(out[0, i]).max())
+
+
+def test_qwen_shape_bf16_decode_64k():
+    """8 KV heads, 32 query heads, d=128, bf16, k=256 at L=65536: append the
+    decode token at t=L, select, attend (decode path); every head vs oracle."""
+    _need_gpu()
+    L = 65536
+    L_cap = L + 64
+    wl, tree, pool, pdict = _setup(1, 8, 128, L + 1, L_cap, 256, "bf16", 14)
+    newk = tree.K[0][:, :, L].clone()
+    newv = tree.V[0][:, :, L].clone()
+    R.recsa_build_tree(tree, pool, 0, L)
+    pos1 = torch.tensor([L], dtype=torch.int64, device=DEV)
+    R.recsa_append_decode(tree, pool, newk.contiguous(), newv.contiguous(), pos1)
+    q = synth.to_storage(synth.normal((1, 1, 32, 128), DEV, 14, 98), "bf16")
+    sel, cnt, imp, out = _run_select_attn(tree, q, 32, pos1.view(1, 1), decode=True)
+    rep = _check_queries(tree, pdict, q, pos1.view(1, 1).cpu(), sel, cnt, imp, out,
+                         range(8), 1e-5, 2e-3, max_swaps=1)
+    assert rep.matched >= 7, rep
+
+
+def test_prefill_chunk_bf16_causal():
+    """A 512-query prefill chunk appended at [L0, L0+512): incremental build,
+    T-query selection and attention; sampled queries vs oracle on two KV heads,
+    and the last query's decode path equals its prefill result."""
+    _need_gpu()
+    L0, T = 20000, 512
+    L_cap = L0 + T
+    wl, tree, pool, pdict = _setup(1, 4, 128, L_cap, L_cap, 256, "bf16", 15)
+    R.recsa_build_tree(tree, pool, 0, L0)
+    R.recsa_build_tree(tree, pool, L0, L0 + T)               # the chunk's nodes
+    q = synth.to_storage(synth.normal((1, T, 16, 128), DEV, 15, 97), "bf16")
+    pos = torch.arange(L0, L0 + T, device=DEV).view(1, T)
+    sel, cnt, imp, out = _run_select_attn(tree, q, 16, pos, decode=False)
+    idx = list(range(0, T, 37)) + [T - 1]
+    rep = _check_queries(tree, pdict, q[:, idx], pos[:, idx].cpu(), sel[:, idx], cnt[:, idx],
+                         imp[:, idx], out[:, idx], [0, 3], 1e-5, 2e-3, max_swaps=1)
+    assert rep.matched >= 2 * len(idx) - 1
+    s2, c2, m2, o2 = _run_select_attn(tree, q[:, T - 1:].contiguous(), 16,
+                                      pos[:, T - 1:].contiguous(), decode=True)
+    assert np.array_equal(s2[0, 0], sel[0, T - 1]) and np.array_equal(c2[0, 0], cnt[0, T - 1])
+    assert np.allclose(o2[0, 0], out[0, T - 1], rtol=0, atol=1e-5 * np.abs(out[0, T - 1]).max())
