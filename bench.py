@@ -1,0 +1,385 @@
+"""RecSA hot-path benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 524k] [--no-cpu-baseline]
+
+Workload (default "524k"): one Qwen3-4B-shaped attention layer (8 KV heads,
+32 query heads, head dim 128, bf16, C=16, k=256) holding L=524288 tokens of
+seeded synthetic K/V (N(0,1), 16 planted needle keys per KV head).  One step
+is the whole hot path once:
+  prefill: a 4096-query causal chunk at [L, L+4096) -- incremental tree
+           build of the chunk's nodes, T-query selection, attention;
+  decode : one token at t = L+4096 -- append, selection, attention, replayed
+           as one HIP graph with a launch shape independent of L.
+Inputs are resident in HBM before timing.  W untimed steps, then K timed
+steps between two device synchronisations; HIP events on the stream the
+kernels run on split each step into its prefill and decode parts.
+
+Printed: one JSON line.  `value` is the decode latency per token in
+microseconds (lower is better); prefill tokens/s, the full-tree build and
+per-call splits ride along.  `roofline` is for the dominant decode kernel
+measured in a separate instrumented pass; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload (rank 0, one thread).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ROW_BYTES = 256                # one bf16 row of d=128
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def list_sizes(t, C, k, n_levels):
+    """Data-free candidate-list sizes of the walk for a query at t (Eq. 3):
+    returns {level: |A|} for levels n_levels-1 .. 0."""
+    sizes = {}
+    top = n_levels - 1
+    n = (t >> (4 * top)) + 1
+    sizes[top] = n
+    for lvl in range(top - 1, -1, -1):
+        kept = min(k, sizes[lvl + 1])
+        sizes[lvl] = C * (kept - 1) + ((t >> (4 * lvl)) % C) + 1
+    return sizes
+
+
+def decode_rows(t, C, k, n_levels):
+    """Rows one decode query must read per KV head: scored keys at every
+    scored level, level-0 keys, and the value of every entry of E."""
+    s = list_sizes(t, C, k, n_levels)
+    scored = sum(s[lvl] - 1 for lvl in range(1, n_levels) if s[lvl] > k)
+    summaries = sum(s[lvl] - k for lvl in range(1, n_levels) if s[lvl] > k)
+    n_e = s[0] + summaries
+    return dict(scored_keys=scored, level0_keys=s[0], entries=n_e,
+                rows=scored + s[0] + n_e, sizes=s)
+
+
+def build_bytes(L, Hkv, n_levels, tb=0):
+    total = 0
+    for lvl in range(1, n_levels):
+        n = (L >> (4 * lvl)) - (tb >> (4 * lvl))
+        total += n * Hkv * (2 * 16 + 2) * ROW_BYTES
+    return total
+
+
+class Work:
+    """Device-resident state of one benchmark workload (see module doc)."""
+
+
+def setup_workload(name="524k", dev="cuda"):
+    """Build the inputs of a workload in HBM and return the step closures.
+
+    Level-0 K/V of L tokens plus the prefill chunk's rows and the decode
+    token's row, the tree (levels >= 1 still empty), pooler, queries,
+    positions, selection buffers, workspaces and outputs."""
+    import torch
+
+    import synth
+    from long_context_kv_amd import recsa as R
+
+    R.lib()                                     # fail loudly without the library
+    wl = synth.WORKLOADS[name]
+    w = Work()
+    w.R, w.wl = R, wl
+    L, T, B, Hkv, Hq, d = wl.L, max(wl.prefill_T, 1), wl.B, wl.Hkv, wl.Hq, wl.d
+    t_dec = L + wl.prefill_T
+    L_cap = t_dec + 64
+    w.L, w.T, w.t_dec = L, T, t_dec
+    log(f"workload {wl.name}: B={B} Hkv={Hkv} Hq={Hq} d={d} {wl.dtype} L={L} T={wl.prefill_T}")
+    t0 = time.time()
+    K0, V0 = synth.kv_rows(wl, dev, n_rows=L_cap)
+    w.q_dec = synth.decode_queries(wl, dev)                        # [B, 1, Hq, d]
+    w.needles = synth.plant_needles(wl, K0[:, :, :L], w.q_dec)
+    w.pdict = synth.pooler_params(d, d, dev, wl.seed)
+    w.pool = R.Pooler.from_dict(w.pdict, dev)
+    w.tree = R.Tree.allocate(B, Hkv, d, L_cap, k=wl.k, dtype=wl.dtype, device=dev,
+                             level0=(K0, V0), theta=wl.theta)
+    tree = w.tree
+    ck, cv, w.q_pre = synth.new_rows(wl, dev, T, "chunk")
+    tree.K[0][:, :, L:L + T] = ck
+    tree.V[0][:, :, L:L + T] = cv
+    w.k_new = tree.K[0][:, :, t_dec].clone().contiguous()
+    w.v_new = tree.V[0][:, :, t_dec].clone().contiguous()
+    w.pos_pre = torch.arange(L, L + T, device=dev).view(1, T).expand(B, T).contiguous()
+    w.pos_dec = torch.full((B,), t_dec, dtype=torch.int64, device=dev)
+    w.ws_pre = R.workspace(tree, Hq, B * T)
+    w.ws_dec = R.workspace(tree, Hq, B)
+    w.sel_pre, w.cnt_pre, _ = tree.selection_buffers(B * T)
+    w.sel_dec, w.cnt_dec, _ = tree.selection_buffers(B)
+    w.out_pre = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    w.out_dec = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+
+    def prefill():
+        R.recsa_build_tree(tree, w.pool, L, L + T)
+        R.recsa_select(tree, w.q_pre, Hq, T, w.pos_pre, w.sel_pre, w.cnt_pre, None, w.ws_pre)
+        R.recsa_attn_prefill(tree, w.q_pre, Hq, T, w.pos_pre, w.sel_pre, w.cnt_pre, w.out_pre,
+                             w.ws_pre)
+
+    def decode():
+        R.recsa_decode(tree, w.pool, w.k_new, w.v_new, w.q_dec, Hq, w.pos_dec, w.sel_dec,
+                       w.cnt_dec, w.out_dec, w.ws_dec)
+
+    def decode_split():
+        R.recsa_append_decode(tree, w.pool, w.k_new, w.v_new, w.pos_dec)
+        R.recsa_select(tree, w.q_dec, Hq, 1, w.pos_dec.view(B, 1), w.sel_dec, w.cnt_dec, None,
+                       w.ws_dec)
+        R.recsa_attn_decode(tree, w.q_dec, Hq, w.pos_dec, w.sel_dec, w.cnt_dec, w.out_dec,
+                            w.ws_dec)
+
+    def build_full():
+        R.recsa_build_tree(tree, w.pool, 0, L)
+
+    w.prefill, w.decode, w.decode_split, w.build_full = prefill, decode, decode_split, build_full
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s; tree levels={tree.n_levels}")
+    return w
+
+
+def capture_decode(w, fn=None):
+    """Capture a decode step as one HIP graph (its launch shape is fixed)."""
+    import torch
+    fn = fn or w.decode
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="524k")
+    ap.add_argument("--decode-reps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = setup_workload(args.workload)
+    wl, tree, pool, R = w.wl, w.tree, w.pool, w.R
+    L, T, B, Hkv, Hq, d = w.L, w.T, wl.B, wl.Hkv, wl.Hq, wl.d
+    t_dec = w.t_dec
+    prefill, decode = w.prefill, w.decode
+    k_new, v_new, pos_dec, q_dec, q_pre = w.k_new, w.v_new, w.pos_dec, w.q_dec, w.q_pre
+    pos_pre, ws_pre, ws_dec = w.pos_pre, w.ws_pre, w.ws_dec
+    sel_pre, cnt_pre, sel_dec, cnt_dec = w.sel_pre, w.cnt_pre, w.sel_dec, w.cnt_dec
+    out_pre, out_dec, pdict = w.out_pre, w.out_dec, w.pdict
+
+    # ------------------------------------------------------ full tree build
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    build_ms = []
+    for _ in range(3):
+        a, b = ev(), ev()
+        a.record()
+        w.build_full()
+        b.record()
+        torch.cuda.synchronize()
+        build_ms.append(a.elapsed_time(b))
+    build_s = sorted(build_ms)[1] / 1e3
+    bb = build_bytes(L, Hkv, tree.n_levels) * B
+    log(f"full build over {L} tokens: {build_s * 1e3:.3f} ms, {bb / build_s / 1e9:.0f} GB/s")
+
+    graph = capture_decode(w)
+
+    for _ in range(args.warmup):
+        prefill()
+        graph.replay()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    evs = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for e0, e1, e2 in evs:
+        e0.record()
+        prefill()
+        e1.record()
+        graph.replay()
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    pre_ms = [a.elapsed_time(b) for a, b, _ in evs]
+    dec_ms = [b.elapsed_time(c) for _, b, c in evs]
+    log(f"timed {args.steps} steps in {wall:.3f}s")
+
+    # decode alone, many replays (latency distribution)
+    reps = [(ev(), ev()) for _ in range(args.decode_reps)]
+    for a, b in reps:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    dec_rep_us = sorted(a.elapsed_time(b) * 1e3 for a, b in reps)
+
+    # the same decode step as three calls (append, select, attention)
+    graph_split = capture_decode(w, w.decode_split)
+    reps2 = [(ev(), ev()) for _ in range(50)]
+    for a, b in reps2:
+        a.record()
+        graph_split.replay()
+        b.record()
+    torch.cuda.synchronize()
+    split_rep_us = sorted(a.elapsed_time(b) * 1e3 for a, b in reps2)
+    # restore the fused step's outputs for anything read later
+    graph.replay()
+    torch.cuda.synchronize()
+
+    # ------------------------------------------- instrumented per-call pass
+    def timed(fn, n=20):
+        xs = []
+        for _ in range(n):
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            xs.append((a, b))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in xs)
+        return ts[len(ts) // 2]
+    split = {
+        "decode_fused_us": timed(lambda: R.recsa_decode(tree, pool, k_new, v_new, q_dec, Hq, pos_dec,
+                                                        sel_dec, cnt_dec, out_dec, ws_dec)),
+        "decode_append_us": timed(lambda: R.recsa_append_decode(tree, pool, k_new, v_new, pos_dec)),
+        "decode_select_us": timed(lambda: R.recsa_select(tree, q_dec, Hq, 1, pos_dec.view(B, 1),
+                                                         sel_dec, cnt_dec, None, ws_dec)),
+        "decode_attn_us": timed(lambda: R.recsa_attn_decode(tree, q_dec, Hq, pos_dec, sel_dec,
+                                                            cnt_dec, out_dec, ws_dec)),
+        "prefill_build_us": timed(lambda: R.recsa_build_tree(tree, pool, L, L + T), 5),
+        "prefill_select_us": timed(lambda: R.recsa_select(tree, q_pre, Hq, T, pos_pre, sel_pre,
+                                                          cnt_pre, None, ws_pre), 5),
+        "prefill_attn_us": timed(lambda: R.recsa_attn_prefill(tree, q_pre, Hq, T, pos_pre, sel_pre,
+                                                              cnt_pre, out_pre, ws_pre), 5),
+    }
+    log("split " + json.dumps({k_: round(v, 1) for k_, v in split.items()}))
+
+    # ------------------------------------------------------------- numbers
+    dr = decode_rows(t_dec, 16, wl.k, tree.n_levels)
+    dec_bytes = dr["rows"] * ROW_BYTES * Hkv * B
+    dec_us = float(np.mean(dec_ms)) * 1e3
+    pre_s = float(np.mean(pre_ms)) / 1e3
+    fused_gbs = dec_bytes / (split["decode_fused_us"] * 1e-6) / 1e9
+    roof = {
+        "kernel": "decode_fused_kernel (recsa_decode: append + select + attention), "
+                  "decode at t=%d" % t_dec,
+        "bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(fused_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+        "algorithmic_bytes_per_launch": dec_bytes,
+        "avg_launch_us": round(split["decode_fused_us"], 2),
+    }
+    step_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
+
+    result = {
+        "metric": "RecSA decode µs/token & prefill tok/s at 524K; % HBM / MFMA peak",
+        "value": round(dec_us, 2),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: 1 layer, {Hkv} KV heads, {Hq} query heads, d={d}, "
+                               f"{wl.dtype}, L={L}, C=16, k={wl.k}; decode B={B} at t={t_dec}; "
+                               f"prefill chunk T={T} at [{L},{L + T})",
+                   "seq_len": L, "global_batch": B, "prefill_T": T},
+        "decode_us_per_token": round(dec_us, 2),
+        "decode_us_median_replay": round(dec_rep_us[len(dec_rep_us) // 2], 2),
+        "decode_us_p10_p90": [round(dec_rep_us[len(dec_rep_us) // 10], 2),
+                              round(dec_rep_us[(9 * len(dec_rep_us)) // 10], 2)],
+        "decode_split_calls_us_median": round(split_rep_us[len(split_rep_us) // 2], 2),
+        "decode_algorithmic_MB": round(dec_bytes / 1e6, 2),
+        "decode_step_GBs": round(step_gbs, 1),
+        "decode_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "prefill_tok_s": round(B * T / pre_s, 1),
+        "prefill_ms_per_chunk": round(pre_s * 1e3, 3),
+        "build_full_ms": round(build_s * 1e3, 3),
+        "build_full_GBs": round(bb / build_s / 1e9, 1),
+        "build_full_hbm_frac": round(bb / build_s / 1e9 / HBM_PEAK_GBS, 4),
+        "split_us": {k_: round(v, 1) for k_, v in split.items()},
+        "roofline": roof,
+        "cache_state": "decode replays after a prefill chunk; levels >= 1 (~134 MB) fit the 256 MB MALL",
+    }
+
+    # ------------------------------------------------------- CPU baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T):
+    """The CPU oracle, one thread, on a bounded sample: KV head 0 of sequence
+    0 (its tree built once, untimed), one decode query and 8 prefill queries
+    timed; decode scaled x Hkv*B heads to microseconds per token."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import recsa_oracle as O
+    from tests import parity as PY
+
+    t0 = time.time()
+    with threadpool_limits(limits=1):
+        K0 = PY.to64(tree.K[0][0, 0, :t_dec + 1])
+        V0 = PY.to64(tree.V[0][0, 0, :t_dec + 1])
+        P = PY.oracle_pooler(pdict)
+        Kt, Vt = O.build_tree(K0, V0, 16, tree.n_levels, P, wl.dtype)
+        cos, sin = O.rope_table(wl.d, 16 * wl.k, wl.theta)
+        tb = time.time() - t0
+        G = wl.Hq // wl.Hkv
+        qd = PY.to64(q_dec[0, 0, :G])
+        t1 = time.time()
+        O.decode_reference(qd, t_dec, Kt, Vt, 16, wl.k, cos, sin, wl.dtype)
+        dec_s = time.time() - t1
+        qp = PY.to64(q_pre[0, :, :G])
+        idx = np.linspace(0, T - 1, 8).astype(int)
+        t2 = time.time()
+        for i in idx:
+            t = L + int(i)
+            Ktt = [Kt[0][: t + 1]] + [Kt[lv][: (t + 1) >> (4 * lv)] for lv in range(1, len(Kt))]
+            Vtt = [Vt[0][: t + 1]] + [Vt[lv][: (t + 1) >> (4 * lv)] for lv in range(1, len(Vt))]
+            O.decode_reference(qp[i], t, Ktt, Vtt, 16, wl.k, cos, sin, wl.dtype)
+        pre_s = (time.time() - t2) / len(idx)
+    heads = wl.Hkv * wl.B
+    log(f"cpu baseline: tree {tb:.1f}s (untimed), decode/head {dec_s:.3f}s, "
+        f"prefill query/head {pre_s:.3f}s")
+    return {
+        "value": round(dec_s * heads * 1e6, 1), "unit": "us/token", "cores": 1, "kind": "oracle",
+        "sample": (f"KV head 0 of {heads}: oracle tree over {t_dec + 1} tokens built once "
+                   f"(untimed, {tb:.1f}s), one decode walk+softmax timed and scaled x{heads}; "
+                   f"8 prefill queries timed"),
+        "prefill_tok_s": round(1.0 / (pre_s * heads), 3),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -26,8 +26,9 @@
  *   - Storage dtype (tree, q, k_new, v_new) is RECSA_F32 (float) or
  *     RECSA_BF16 (bfloat16 bits in uint16).  Arithmetic is float32; outputs
  *     are float32.
- *   - Query head h belongs to KV head h / (Hq / Hkv).  One selection is made
- *     per (query, KV head) and shared by its Hq/Hkv query heads.
+ *   - Query head h belongs to KV head h / (Hq / Hkv), with Hq / Hkv in
+ *     {1, 2, 4} (other ratios return RECSA_E_UNSUPPORTED).  One selection is
+ *     made per (query, KV head) and shared by its Hq/Hkv query heads.
  *   - q and the level-0 keys are given before RoPE: positions are assigned
  *     at query time from the candidate lists.
  *   - Logit of query head h and an entry at list position p (p = C*r + c) of
@@ -179,6 +180,22 @@ int recsa_attn_prefill(const recsa_tree* tree, const void* q, int32_t Hq,
                        int32_t T, const int64_t* pos_dev,
                        const int32_t* sel_idx, const int32_t* sel_cnt,
                        float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step in a single launch: recsa_append_decode, recsa_select (T = 1)
+ * and recsa_attn_decode with the same arguments and results, for when the
+ * caller wants the lowest latency.  The (sequence, KV head) pairs are each
+ * served by a group of workgroups that must all be resident at once; the
+ * call returns RECSA_E_UNSUPPORTED when B*Hkv groups cannot be.
+ * ws: recsa_workspace_bytes(tree, Hq, B) bytes whose control block (the last
+ * B*Hkv*2112 bytes: 528 32-bit words per (sequence, KV head)) is zero before
+ * the first call -- a zero-filled workspace satisfies this -- and is left
+ * zero by every call.  Should a group ever wait longer than its bounded
+ * spin, word 1 of its block is set to nonzero and its output is NaN.  Calls
+ * sharing one ws must not overlap. */
+int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler,
+                 const void* k_new, const void* v_new, const void* q, int32_t Hq,
+                 const int64_t* pos_dev, int32_t* sel_idx, int32_t* sel_cnt,
+                 float* out, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,250 @@
+// One decode step -- append, hierarchical selection (picx.dev Hierarchical
+// Selection, Eq. 3) and the unified softmax (Unified Softmax, Eq. 4) -- in
+// one persistent launch.
+//
+// Grid (W, Hkv, B), 512 threads per workgroup.  The W workgroups of one
+// (sequence, KV head) cooperate:
+//   WG 0 appends token t (row t, and every node whose last token is t: those
+//   are current nodes of this query, never read by it);
+//   for each level from the top down that must be scored: the W workgroups
+//   score interleaved groups of the candidate list into the workspace, meet
+//   at a barrier, and then every workgroup runs the same exact top-(k-1) on
+//   all the logits, keeping S and the kept-position bitmap in its own LDS
+//   (WG 0 also writes them out), so no second barrier is needed;
+//   all W then accumulate interleaved entry groups (token t's row comes from
+//   k_new/v_new), publish a partial softmax state, and WG 0 waits for them
+//   and merges them into the output.
+// Barrier: each workgroup raises its own arrival flag with an atomic exchange
+// (one 64-byte line per flag, so arrivals do not contend) and polls the
+// group's flags with a
+// bounded spin; if the bound is hit (workgroups of a group not co-resident)
+// the error word is set and the output is poisoned with NaN.  The host only
+// launches this kernel when the grid fits on the device with room to spare.
+#include <algorithm>
+
+#include "recsa_common.hpp"
+#include "recsa_device.hpp"
+#include "recsa_kernels.hpp"
+#include "recsa_pool.hpp"
+
+namespace recsa {
+
+constexpr int kFusedThreads = 512;
+constexpr uint32_t kSpinLimit = 1u << 19;
+
+// Every wave drains its own memory operations, so after the workgroup
+// barrier all of the workgroup's stores have reached its L2; one thread
+// releases them to the device (one L2 write-back per workgroup), raises this
+// workgroup's flag to `gen`, waits for every flag of the group with relaxed
+// loads, and acquires once (one L2 invalidation per workgroup).
+__device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uint32_t gen,
+                                              uint32_t* err, uint32_t* s_fail) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // an atomic read-modify-write is performed where every XCD sees it (a
+    // plain store could stay in this XCD's L2)
+    __hip_atomic_exchange(flags + 16 * w, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t spins = 0;
+    for (int i = 0; i < W; ++i) {
+      while (__hip_atomic_load(flags + 16 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) break;
+      }
+      if (spins > kSpinLimit) {
+        atomicOr(err, 1u);
+        *s_fail = 1u;
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+template <int DT, int D, int G>
+__global__ void __launch_bounds__(kFusedThreads)
+    decode_fused_kernel(recsa_tree tr, recsa_pooler P, const void* k_new, const void* v_new,
+                        const void* q, int Hq, const int64_t* pos, int32_t* sel, int32_t* cnt,
+                        float* out, float* ws_logits, float* part, uint32_t* ctl_words, int W,
+                        int n_sel, int CK) {
+  using T = typename Stor<DT>::T;
+  constexpr int NT = kFusedThreads;
+  constexpr int NW = NT / kWave;
+  constexpr int kMaxSel = RECSA_MAX_LEVELS - 1;
+  __shared__ int32_t s_sel[kMaxSel * 256];          // S^(l) of every level, this group
+  __shared__ int32_t s_cnt[kMaxSel + 1];
+  __shared__ uint32_t s_bm[kMaxSel * (kMaxCK / 32)];
+  __shared__ uint32_t s_fail;
+  __shared__ float qs[G * D];
+  __shared__ union Smem {
+    TopkSmem tk;
+    AttnSmem<D, G, NT> at;
+    PoolSmem<DT, D, 1> pl;
+  } sm;
+  const int w = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
+  const int k = tr.k;
+  const int top = tr.n_levels - 1;
+  const int bm_words = (CK + 31) / 32;
+  const int64_t slot = static_cast<int64_t>(b) * tr.Hkv + j;    // one query per sequence
+  const int64_t t = pos[b];
+  int32_t* sel_q = sel + slot * n_sel * k;
+  int32_t* cnt_q = cnt + slot * n_sel;
+  float* lg_slot = ws_logits + slot * n_sel * static_cast<int64_t>(G) * CK;
+  uint32_t* ctl = ctl_words + slot * kCtlWords;
+  uint32_t* err = ctl + 1;
+  uint32_t* flags = ctl + 16;
+  const T* k_t = static_cast<const T*>(k_new) + slot * D;
+  const T* v_t = static_cast<const T*>(v_new) + slot * D;
+  if (tid == 0) s_fail = 0u;
+  load_query_rows<DT, D, G, NT>(q, static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G, qs);
+
+  // ---- append (WG 0)
+  if (w == 0) {
+    T* kd = static_cast<T*>(tr.K[0]) + (slot * tr.L_cap + t) * D;
+    T* vd = static_cast<T*>(tr.V[0]) + (slot * tr.L_cap + t) * D;
+    for (int i = tid; i < D; i += NT) {
+      kd[i] = k_t[i];
+      vd[i] = v_t[i];
+    }
+    int64_t span = 1;
+    for (int l = 1; l < tr.n_levels; ++l) {
+      span *= kC;
+      if ((t + 1) % span != 0) break;
+      __threadfence();
+      __syncthreads();
+      const int64_t node = (t + 1) / span - 1;
+      const int64_t rows_up = level_rows_dev(tr.L_cap, l - 1);
+      const int64_t rows = level_rows_dev(tr.L_cap, l);
+      pool_tile<DT, D, 1, NT>(static_cast<const T*>(tr.K[l - 1]) + (slot * rows_up + node * kC) * D,
+                              static_cast<const T*>(tr.V[l - 1]) + (slot * rows_up + node * kC) * D,
+                              static_cast<T*>(tr.K[l]) + (slot * rows + node) * D,
+                              static_cast<T*>(tr.V[l]) + (slot * rows + node) * D, 1, P, sm.pl);
+      __syncthreads();
+    }
+    if (top >= 1) {                    // the top list [0 .. a_top] is fully selected
+      const ListView lt = list_view(t, top, top, k, sel_q, cnt_q);
+      wg_take_all<NT>(lt, k, sel_q + static_cast<int64_t>(top - 1) * k, cnt_q + (top - 1), nullptr, CK);
+    }
+  }
+  __syncthreads();
+
+  // ---- selection, top level down (S^(l) kept in LDS by every workgroup)
+  uint32_t gen = 0;
+  for (int l = top - 1; l >= 1; --l) {
+    const ListView lv = list_view(t, l, top, k, s_sel, s_cnt);
+    int32_t* ls = s_sel + (l - 1) * 256;
+    if (lv.len <= k) {
+      wg_take_all<NT>(lv, k, ls, s_cnt + (l - 1), nullptr, CK);
+    } else {
+      const int n = lv.len - 1;
+      const int ng = (n + kC - 1) / kC;
+      const int64_t rows_l = level_rows_dev(tr.L_cap, l);
+      const int p_q = lv.len - 1;
+      float* out_l = lg_slot + static_cast<int64_t>(l - 1) * G * CK;
+      for (int gi = w + W * wid; gi < ng; gi += W * NW) {
+        const int p0 = gi * kC;
+        rotate_query<DT, D, G>(qs, sm.at.qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
+        wave_sync();
+        const int nvalid = min(kC, n - p0);
+        const T* rows = static_cast<const T*>(tr.K[l]) + (slot * rows_l + lv.node(p0)) * D;
+        float lg[G];
+        group_logits<DT, D, G>(rows, 0, nvalid, sm.at.qt[wid], tr.rope, lg);
+        const int c = lane >> 2, s = lane & 3;
+        if (c < nvalid) {
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            if ((g & 3) == s) out_l[static_cast<int64_t>(g) * CK + p0 + c] = lg[g];
+        }
+        wave_sync();
+      }
+      group_barrier(flags, w, W, ++gen, err, &s_fail);
+      wg_topk<G, NT>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1), s_bm + (l - 1) * bm_words,
+                     nullptr, sm.tk);
+    }
+    __syncthreads();
+    if (w == 0) {                      // API outputs
+      for (int i = tid; i < k; i += NT) sel_q[static_cast<int64_t>(l - 1) * k + i] = ls[i];
+      if (tid == 0) cnt_q[l - 1] = s_cnt[l - 1];
+    }
+  }
+
+  // ---- unified softmax over this workgroup's interleaved entry groups
+  const EntryGroups eg = entry_groups(t, tr, n_sel, s_sel, s_cnt);
+  attn_groups<DT, D, G, NT>(tr, t, slot, s_sel, s_cnt, eg, w, W, qs, lg_slot, s_bm, CK, k_t, v_t,
+                            sm.at);
+  float* pp = part + (slot * kPartSlots + w) * static_cast<int64_t>(G) * (D + 2);
+  for (int e = tid; e < G * D; e += NT) pp[(e / D) * (D + 2) + 2 + e % D] = sm.at.wacc[0][e / D][e % D];
+  if (tid < G) {
+    pp[tid * (D + 2)] = sm.at.res_m[tid];
+    pp[tid * (D + 2) + 1] = sm.at.res_l[tid];
+  }
+  // ---- WG 0 waits for every partial and merges them
+  if (w != 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_exchange(flags + 16 * w, gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  group_barrier(flags, w, W, gen + 1, err, &s_fail);
+  float* o = out + (static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G) * D;
+  merge_partials<D, G, NT>(part + slot * kPartSlots * static_cast<int64_t>(G) * (D + 2), W, o);
+  __syncthreads();
+  if (s_fail || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
+  }
+  // every other workgroup has raised its final flag, so none reads them again
+  if (tid < W) __hip_atomic_exchange(flags + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Largest W such that B*Hkv*W workgroups are resident at once (0: none fit).
+template <int DT, int D, int G>
+static int fused_width(const recsa_tree& tr) {
+  static int cached_dev = -1, cached_per_cu = 0, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != cached_dev) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fused_kernel<DT, D, G>,
+                                                     kFusedThreads, 0) != hipSuccess)
+      return 0;
+    cached_dev = dev;
+    cached_cus = cus;
+    cached_per_cu = per_cu;
+  }
+  // keep a quarter of the device spare so a group never waits on a
+  // workgroup that cannot be placed
+  const int64_t capacity = static_cast<int64_t>(cached_cus) * cached_per_cu * 3 / 4;
+  const int64_t groups = static_cast<int64_t>(tr.B) * tr.Hkv;
+  return static_cast<int>(std::min<int64_t>(kFusedMaxW, capacity / groups));
+}
+
+template <int DT, int D, int G>
+static hipError_t fused_impl(const recsa_tree& tr, const recsa_pooler& P, const void* k_new,
+                             const void* v_new, const void* q, int Hq, const int64_t* pos,
+                             int32_t* sel, int32_t* cnt, float* out, void* ws, const WsLayout& w,
+                             hipStream_t s) {
+  const int W = fused_width<DT, D, G>(tr);
+  if (W < 1) return hipErrorLaunchOutOfResources;
+  char* base = static_cast<char*>(ws);
+  decode_fused_kernel<DT, D, G><<<dim3(W, tr.Hkv, tr.B), kFusedThreads, 0, s>>>(
+      tr, P, k_new, v_new, q, Hq, pos, sel, cnt, out, reinterpret_cast<float*>(base + w.logits_off),
+      reinterpret_cast<float*>(base + w.part_off), reinterpret_cast<uint32_t*>(base + w.ctl_off), W,
+      w.n_sel, w.CK);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fused(const recsa_tree& tr, const recsa_pooler& P, const void* k_new,
+                               const void* v_new, const void* q, int Hq, const int64_t* pos,
+                               int32_t* sel, int32_t* cnt, float* out, void* ws, const WsLayout& w,
+                               hipStream_t s) {
+  RECSA_DISPATCH(fused_impl, tr, P, k_new, v_new, q, Hq, pos, sel, cnt, out, ws, w, s);
+}
+
+}  // namespace recsa

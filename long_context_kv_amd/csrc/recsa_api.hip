@@ -39,10 +39,12 @@ bool pooler_ok(const recsa_pooler* p, const recsa_tree* t) {
   return true;
 }
 
+// Query heads per KV head: 1, 2 or 4.  (8 is switched off: its fused-decode
+// variant runs out of registers and its one GPU run stalled.)
 bool heads_ok(const recsa_tree* t, int32_t Hq) {
   if (Hq < 1 || Hq % t->Hkv != 0) return false;
   const int G = Hq / t->Hkv;
-  return G == 1 || G == 2 || G == 4 || G == 8;
+  return G == 1 || G == 2 || G == 4;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RECSA_OK : RECSA_E_HIP; }
@@ -149,6 +151,24 @@ int recsa_attn_prefill(const recsa_tree* tree, const void* q, int32_t Hq, int32_
                        const int64_t* pos_dev, const int32_t* sel_idx, const int32_t* sel_cnt,
                        float* out, void* ws, size_t ws_bytes, void* stream) {
   return attn_common(tree, q, Hq, T, pos_dev, sel_idx, sel_cnt, out, ws, ws_bytes, false, stream);
+}
+
+int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler, const void* k_new,
+                 const void* v_new, const void* q, int32_t Hq, const int64_t* pos_dev,
+                 int32_t* sel_idx, int32_t* sel_cnt, float* out, void* ws, size_t ws_bytes,
+                 void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!pooler_ok(pooler, tree)) return RECSA_E_INVALID;
+  if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
+  if (!k_new || !v_new || !q || !pos_dev || !sel_idx || !sel_cnt || !out || !ws)
+    return RECSA_E_INVALID;
+  const WsLayout w = ws_layout(*tree, Hq, tree->B);
+  if (ws_bytes < static_cast<size_t>(w.total)) return RECSA_E_WORKSPACE;
+  const hipError_t e = launch_decode_fused(*tree, *pooler, k_new, v_new, q, Hq, pos_dev, sel_idx,
+                                           sel_cnt, out, ws, w, static_cast<hipStream_t>(stream));
+  if (e == hipErrorLaunchOutOfResources) return RECSA_E_UNSUPPORTED;
+  return hip_status(e);
 }
 
 }  // extern "C"

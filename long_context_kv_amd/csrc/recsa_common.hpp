@@ -15,6 +15,11 @@ constexpr int kMaxCK = 4096;       // longest candidate list, C*k
 constexpr int kMaxG = 8;           // query heads per KV head
 constexpr int kChunk = 256;        // list positions per attention/score chunk
 
+// Rows allocated at a level: floor(L_cap / 16^level).
+__host__ __device__ __forceinline__ int64_t level_rows_dev(int64_t L_cap, int level) {
+  return L_cap >> (4 * level);
+}
+
 // ---------------------------------------------------------------- storage
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -165,11 +170,14 @@ struct ListView {
 
 // Build the list view of level l.  sel/cnt point at this (query, head)'s
 // selection arrays ([n_sel][k] and [n_sel]); top = n_levels - 1.
+// When the level above holds the full prefix [0 .. a_{l+1}] with at most k
+// nodes (always true at and above the top), it is fully selected and A^(l)
+// is the full prefix [0 .. a_l]: no stored selection is read.
 __device__ __forceinline__ ListView list_view(int64_t t, int l, int top, int k,
                                               const int32_t* sel, const int32_t* cnt) {
   ListView v;
   v.cur = t >> (4 * l);
-  if (l >= top) {
+  if (l >= top || (t >> (4 * (l + 1))) + 1 <= k) {
     v.len = static_cast<int>(v.cur) + 1;
     v.up = nullptr;
   } else {

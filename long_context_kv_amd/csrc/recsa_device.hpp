@@ -1,0 +1,677 @@
+// Device building blocks shared by the selection / attention kernels:
+// candidate-group logits with split candidate-local RoPE, query rotation,
+// block reductions for any block size, the workgroup top-(k-1) selection and
+// the per-group barrier used by the fused decode kernel.
+#pragma once
+
+#include "recsa_common.hpp"
+
+namespace recsa {
+
+// ------------------------------------------------------------------------
+// Logits of the 16 rows of one list group against G rotated query heads.
+// Lane = (row c = lane/4, quarter s = lane%4); each lane rotates 2*E pairs of
+// its row by the in-group offset c (the key half of the split RoPE), rounds
+// them to the storage dtype and dots them with the group's rotated query
+// (LDS, float).  The four quarter lanes of a row are summed, so every lane of
+// row c ends with the G logits of that row.  Only rows in [row_lo, nvalid)
+// are read; the others give 0.
+template <int DT, int D, int G>
+__device__ __forceinline__ void group_logits(const typename Stor<DT>::T* __restrict__ rows,
+                                             int row_lo, int nvalid, const float* qt,
+                                             const float* __restrict__ rope, float* lg) {
+  constexpr int E = D / 16, QD = D / 4, H2 = D / 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane >> 2, s = lane & 3;
+  float acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.f;
+  if (c >= row_lo && c < nvalid) {
+    const typename Stor<DT>::T* row = rows + static_cast<int64_t>(c) * D;
+    // raw storage words stay packed until used (bf16: 2 values per word)
+    constexpr int WPC = DT == RECSA_BF16 ? E / 2 : E;      // 32-bit words per chunk
+    uint32_t xr[2][WPC], yr[2][WPC];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int base = hh * QD + s * E;
+      const uint32_t* px = reinterpret_cast<const uint32_t*>(row + base);
+      const uint32_t* py = reinterpret_cast<const uint32_t*>(row + H2 + base);
+#pragma unroll
+      for (int i = 0; i < WPC; i += 4) {
+        if constexpr (WPC % 4 == 0) {
+          const uint4 a = *reinterpret_cast<const uint4*>(px + i);
+          const uint4 b = *reinterpret_cast<const uint4*>(py + i);
+          xr[hh][i] = a.x; xr[hh][i + 1] = a.y; xr[hh][i + 2] = a.z; xr[hh][i + 3] = a.w;
+          yr[hh][i] = b.x; yr[hh][i + 1] = b.y; yr[hh][i + 2] = b.z; yr[hh][i + 3] = b.w;
+        }
+      }
+      if constexpr (WPC % 4 != 0) {
+#pragma unroll
+        for (int i = 0; i < WPC; ++i) {
+          xr[hh][i] = px[i];
+          yr[hh][i] = py[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      // keep the two halves' LDS reads from being hoisted together
+      __builtin_amdgcn_sched_barrier(0);
+      const int base = hh * QD + s * E;
+      const float* rp = rope + (c * H2 + base) * 2;
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        float x, y;
+        if constexpr (DT == RECSA_BF16) {
+          const uint32_t wx = xr[hh][m / 2], wy = yr[hh][m / 2];
+          x = __uint_as_float((m & 1) ? (wx & 0xFFFF0000u) : (wx << 16));
+          y = __uint_as_float((m & 1) ? (wy & 0xFFFF0000u) : (wy << 16));
+        } else {
+          x = __uint_as_float(xr[hh][m]);
+          y = __uint_as_float(yr[hh][m]);
+        }
+        float xo, yo;
+        rope_pair(x, y, rp[2 * m], rp[2 * m + 1], xo, yo);
+        xo = Stor<DT>::round(xo);
+        yo = Stor<DT>::round(yo);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          acc[g] += qt[g * D + base + m] * xo + qt[g * D + H2 + base + m] * yo;
+      }
+    }
+  }
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float v = acc[g];
+    v += __shfl_xor(v, 1, kWave);
+    v += __shfl_xor(v, 2, kWave);
+    lg[g] = v * scale;
+  }
+}
+
+// Rotate the G query heads by phi and round (one wave): qt = rnd(R(phi) q),
+// the query half of the split RoPE.
+template <int DT, int D, int G>
+__device__ __forceinline__ void rotate_query(const float* qs, float* qt, int phi,
+                                             const float* __restrict__ rope) {
+  constexpr int H2 = D / 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int idx = lane; idx < G * H2; idx += kWave) {
+    const int g = idx / H2, j = idx % H2;
+    const float* rp = rope + (static_cast<int64_t>(phi) * H2 + j) * 2;
+    float xo, yo;
+    rope_pair(qs[g * D + j], qs[g * D + j + H2], rp[0], rp[1], xo, yo);
+    qt[g * D + j] = Stor<DT>::round(xo);
+    qt[g * D + j + H2] = Stor<DT>::round(yo);
+  }
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int DT, int D, int G, int NT>
+__device__ __forceinline__ void load_query_rows(const void* q, int64_t row0, float* qs) {
+  using T = typename Stor<DT>::T;
+  const T* src = static_cast<const T*>(q) + row0 * D;
+  for (int i = threadIdx.x; i < G * D; i += NT) qs[i] = Stor<DT>::load(src + i);
+}
+
+// ------------------------------------------------------------ reductions
+// Block-wide reductions / scans for NT threads; `red` is LDS of NT/64 slots.
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  constexpr int NW = NT / kWave;
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  constexpr int NW = NT / kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) r += red[w];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
+  return v;
+}
+
+// Exclusive prefix sum over NT threads in thread order; total in *total.
+template <int NT>
+__device__ __forceinline__ int block_scan_excl(int v, int* red, int* total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == kWave - 1) red[wid] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = red[w];
+    off += (w < wid) ? x : 0;
+    tot += x;
+  }
+  *total = tot;
+  return off + inc - v;
+}
+
+// --------------------------------------------------------------- top-k
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+
+struct TopkSmem {
+  int hist[kHistBins];
+  float redg[kMaxG][16];
+  float redf[16];
+  int redi[16];
+  uint32_t redu[2][16];
+  int s_bin, s_need, s_full;
+};
+
+// Selection at one scored level for one (query, KV head), by the whole
+// workgroup (NT threads; thread i owns list positions [i*PPT, (i+1)*PPT)).
+//   lgs    : logits [G][CK] of the n = |A|-1 non-current candidates
+//   imp    : optional importance output [CK]
+// Writes S^(l) (k-1 kept candidates in ascending order, then the current
+// node), |S| = k, and the bitmap of kept list positions.
+// Importance I_p = (1/G) sum_g softmax_p(s_g) is ranked through its float
+// bits (I >= 0, so the bits order like the values); the (k-1)-th largest is
+// found by 11-bit radix passes starting at the highest bit where the keys
+// differ, and ties at the threshold go to the lower list position (= the
+// lower node index, the list being in ascending node order).
+template <int G, int NT>
+__device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
+                        int32_t* out_sel, int32_t* out_cnt, uint32_t* bm, float* imp,
+                        TopkSmem& sm) {
+  constexpr int PPT = kMaxCK / NT;
+  const int tid = threadIdx.x;
+  const int p0 = tid * PPT;
+  constexpr int NW = NT / kWave;
+  const int lane = tid & (kWave - 1), wid = tid >> 6;
+  float e[G][PPT];
+  float I[PPT];
+  // ---- all logits first (one memory round trip), then per-head max and
+  // normaliser with one block exchange for all heads
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float* src = lgs + static_cast<int64_t>(g) * CK + p0;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) e[g][i] = (p0 + i < n) ? src[i] : -INFINITY;
+  }
+  float M[G], Z[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) m = fmaxf(m, e[g][i]);
+    M[g] = wave_max(m);
+  }
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) sm.redg[g][wid] = M[g];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float m = sm.redg[g][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, sm.redg[g][w]);
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      e[g][i] = (p0 + i < n) ? __expf(e[g][i] - m) : 0.f;
+      z += e[g][i];
+    }
+    Z[g] = wave_sum(z);
+  }
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) sm.redg[g][wid] = Z[g];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float z = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) z += sm.redg[g][w];
+    const float inv = 1.0f / z;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) e[g][i] *= inv;
+  }
+  uint32_t key[PPT];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) s += e[g][i];
+    I[i] = s * (1.0f / G);
+    key[i] = __float_as_uint(I[i]);
+    if (p0 + i < n) {
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+  }
+  if (imp) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+      if (p0 + i < CK) imp[p0 + i] = (p0 + i < n) ? I[i] : 0.f;
+  }
+  const int need0 = k - 1;
+  uint32_t prefix = 0, pmask = 0;
+  int need = need0;
+  bool whole_bin = false;
+  if (need0 > 0) {
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) {
+      sm.redu[0][tid >> 6] = kmin;
+      sm.redu[1][tid >> 6] = kmax;
+    }
+    __syncthreads();
+    kmin = sm.redu[0][0];
+    kmax = sm.redu[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      kmin = min(kmin, sm.redu[0][w]);
+      kmax = max(kmax, sm.redu[1][w]);
+    }
+    int hb = (kmin == kmax) ? -1 : 31 - __clz(kmin ^ kmax);   // highest differing bit
+    pmask = (hb >= 31) ? 0u : ~((2u << hb) - 1u);             // bits above hb (all when hb<0)
+    if (hb < 0) pmask = 0xFFFFFFFFu;
+    prefix = kmin & pmask;
+#pragma unroll 1
+    while (hb >= 0) {
+      const int lo = max(hb - (kHistBits - 1), 0);
+      const int nb = hb - lo + 1;
+      const uint32_t dmask = (1u << nb) - 1u;
+      for (int b = tid; b < (1 << nb); b += NT) sm.hist[b] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < PPT; ++i)
+        if (p0 + i < n && (key[i] & pmask) == prefix) atomicAdd(&sm.hist[(key[i] >> lo) & dmask], 1);
+      __syncthreads();
+      // suffix counts over bins: thread t owns bins [t*BPT, (t+1)*BPT)
+      const int nbins = 1 << nb;
+      const int bpt = (nbins + NT - 1) / NT;
+      const int b0 = tid * bpt;
+      int local = 0;
+      for (int b = b0; b < min(b0 + bpt, nbins); ++b) local += sm.hist[b];
+      // reverse exclusive scan: count in bins above my range
+      int tot;
+      const int below = block_scan_excl<NT>(local, sm.redi, &tot);
+      int above = tot - below - local;
+      for (int b = min(b0 + bpt, nbins) - 1; b >= b0; --b) {
+        const int h = sm.hist[b];
+        if (above < need && need <= above + h) {
+          sm.s_bin = b;
+          sm.s_need = need - above;
+          sm.s_full = (need - above) == h;
+        }
+        above += h;
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(sm.s_bin) << lo;
+      pmask |= dmask << lo;
+      need = sm.s_need;
+      whole_bin = sm.s_full != 0;
+      __syncthreads();
+      if (whole_bin) break;
+      hb = lo - 1;
+    }
+  }
+  // ---- keep: truncated key above the threshold prefix, or equal to it and
+  // (whole bin kept, or among the first `need` equal ones by position)
+  int n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) n_eq += (p0 + i < n && (key[i] & pmask) == prefix) ? 1 : 0;
+  int tot;
+  int eq_rank = block_scan_excl<NT>(n_eq, sm.redi, &tot);
+  bool take[PPT];
+  int n_take = 0;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const bool valid = need0 > 0 && p0 + i < n;
+    const uint32_t kt = key[i] & pmask;
+    const bool eq = valid && kt == prefix;
+    take[i] = valid && (kt > prefix || (eq && (whole_bin || eq_rank < need)));
+    eq_rank += eq ? 1 : 0;
+    n_take += take[i] ? 1 : 0;
+  }
+  int slot = block_scan_excl<NT>(n_take, sm.redi, &tot);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    if (take[i]) {
+      out_sel[slot++] = static_cast<int32_t>(lv.node(p0 + i));
+      bits |= 1u << ((p0 + i) & 31);
+    }
+  }
+  // PPT consecutive positions per thread: 32/PPT threads share one word
+  constexpr int LPW = 32 / PPT;
+#pragma unroll
+  for (int o = 1; o < LPW; o <<= 1) bits |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), o, kWave));
+  if ((tid % LPW) == 0 && p0 < CK) bm[p0 / 32] = bits;
+  if (tid == 0) {
+    out_sel[k - 1] = static_cast<int32_t>(lv.cur);
+    *out_cnt = k;
+  }
+}
+
+// Fill the selection of a level whose list has at most k candidates (all kept).
+template <int NT>
+__device__ __forceinline__ void wg_take_all(const ListView& lv, int k, int32_t* out_sel,
+                                            int32_t* out_cnt, float* imp, int CK) {
+  for (int p = threadIdx.x; p < k; p += NT)
+    out_sel[p] = p < lv.len ? static_cast<int32_t>(lv.node(p)) : -1;
+  if (threadIdx.x == 0) *out_cnt = lv.len;
+  if (imp)
+    for (int p = threadIdx.x; p < CK; p += NT) imp[p] = 0.f;
+}
+
+// ------------------------------------------------------------ attention
+// Per-query bookkeeping of the entry set E (Eq. 4) as 16-position groups:
+// level 0 contributes every candidate (exact tokens, logits computed here);
+// a scored level l >= 1 contributes its non-current candidates, of which the
+// selected ones are masked out (their logits come from the workspace).
+// Every access uses a compile-time index (unrolled loops) so the arrays stay
+// in registers.
+struct EntryGroups {
+  int first[RECSA_MAX_LEVELS + 1];   // first group of each level; first[n_sel] = total
+  int tot;
+  __device__ __forceinline__ int total() const { return tot; }
+  // level of group gi and the group's index within its level
+  __device__ __forceinline__ void locate(int gi, int& level, int& local) const {
+    level = 0;
+    int base = 0;
+#pragma unroll
+    for (int l = 1; l < RECSA_MAX_LEVELS; ++l) {
+      if (gi >= first[l] && first[l] < tot) {
+        level = l;
+        base = first[l];
+      }
+    }
+    local = gi - base;
+  }
+};
+
+__device__ __forceinline__ EntryGroups entry_groups(int64_t t, const recsa_tree& tr, int n_sel,
+                                                    const int32_t* sel, const int32_t* cnt) {
+  EntryGroups eg;
+  const int top = tr.n_levels - 1;
+  int acc = 0;
+#pragma unroll
+  for (int l = 0; l < RECSA_MAX_LEVELS; ++l) {
+    eg.first[l] = acc;
+    if (l < n_sel) {
+      const ListView lv = list_view(t, l, top, tr.k, sel, cnt);
+      int n = 0;
+      if (l == 0) n = lv.len;
+      else if (lv.len > tr.k) n = lv.len - 1;
+      acc += (n + kC - 1) / kC;
+    }
+  }
+  eg.first[RECSA_MAX_LEVELS] = acc;
+  eg.tot = acc;
+  return eg;
+}
+
+template <int D, int G, int NT>
+struct AttnSmem {
+  float qt[NT / kWave][G * D];
+  float pw[NT / kWave][G][kC];
+  float wm[NT / kWave][G];
+  float wl[NT / kWave][G];
+  float wacc[NT / kWave][G][D];
+  float res_m[G], res_l[G];      // merged state; the merged sum is in wacc[0]
+};
+
+// Softmax state of a set of entries: running max m, normaliser l, sum acc.
+template <int G, int DPL>
+struct SoftState {
+  float m[G], l[G], acc[G][DPL];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) acc[g][u] = 0.f;
+    }
+  }
+};
+
+// Process entry groups g_lo, g_lo + g_step, ... of one (query, KV head) with
+// the whole workgroup (its waves take every NW-th of those; no block barrier
+// inside the loop), then merge the waves: on return sm.wm[0], sm.wl[0], sm.wacc[0] hold
+// the workgroup's softmax state (valid after the trailing __syncthreads).
+// Value rows of a group are issued before its logits are computed.  If
+// k_t/v_t are given they replace the tree rows of token t (decode append).
+template <int DT, int D, int G, int NT>
+__device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, const int32_t* sel,
+                            const int32_t* cnt, const EntryGroups& eg, int g_lo, int g_step,
+                            const float* qs, const float* __restrict__ lg_slot,
+                            const uint32_t* __restrict__ bm_slot, int CK,
+                            const typename Stor<DT>::T* k_t, const typename Stor<DT>::T* v_t,
+                            AttnSmem<D, G, NT>& sm) {
+  using T = typename Stor<DT>::T;
+  constexpr int DPL = D / kWave;
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  const int c = lane >> 2, s = lane & 3;
+  const int top = tr.n_levels - 1;
+  SoftState<G, DPL> st;
+  st.init();
+  const int g_hi = eg.total();
+#pragma unroll 1
+  for (int gi = g_lo + wid * g_step; gi < g_hi; gi += NW * g_step) {
+    int level, local;
+    eg.locate(gi, level, local);
+    const int p0 = local * kC;
+    const ListView lv = list_view(t, level, top, tr.k, sel, cnt);
+    const int n_pos = level == 0 ? lv.len : lv.len - 1;
+    const int nvalid = min(kC, n_pos - p0);
+    const int64_t rows_l = level_rows_dev(tr.L_cap, level);
+    const int64_t node0 = lv.node(p0);
+    // token t (the query itself) is the last level-0 position
+    const int ovr = (level == 0 && k_t) ? static_cast<int>(lv.len - 1 - p0) : -1;
+    // ---- value rows (lanes own dims), issued first, kept as raw words
+    constexpr int VW = DT == RECSA_BF16 ? (DPL + 1) / 2 : DPL;   // words per lane per row
+    const T* vrows = static_cast<const T*>(tr.V[level]) + (seq_head * rows_l + node0) * D + lane * DPL;
+    uint32_t vraw[kC][VW];
+#pragma unroll
+    for (int r = 0; r < kC; ++r) {
+      const T* vr = (r == ovr) ? v_t + lane * DPL : vrows + static_cast<int64_t>(r) * D;
+      if (r < nvalid) {
+        if constexpr (DT == RECSA_BF16 && DPL == 2) {
+          vraw[r][0] = *reinterpret_cast<const uint32_t*>(vr);
+        } else if constexpr (DT == RECSA_BF16) {
+          vraw[r][0] = static_cast<uint32_t>(*vr) << 16;
+        } else {
+#pragma unroll
+          for (int u = 0; u < DPL; ++u) vraw[r][u] = __float_as_uint(vr[u]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < VW; ++u) vraw[r][u] = 0u;
+      }
+    }
+    // ---- logits of the 16 rows (lane layout: row c, quarter s)
+    float lgv[G];
+    if (level == 0) {
+      const int p_q = lv.len - 1;
+      rotate_query<DT, D, G>(qs, sm.qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
+      wave_sync();
+      const T* krows = static_cast<const T*>(tr.K[0]) + (seq_head * rows_l + node0) * D;
+      if (ovr >= 0 && ovr < kC) {
+        // rows before t from the tree, row t from k_t: score in two calls
+        float a[G], b[G];
+        group_logits<DT, D, G>(krows, 0, ovr, sm.qt[wid], tr.rope, a);
+        // only row ovr is read from this base, i.e. exactly k_t
+        group_logits<DT, D, G>(k_t - static_cast<int64_t>(ovr) * D, ovr, ovr + 1, sm.qt[wid],
+                               tr.rope, b);
+#pragma unroll
+        for (int g = 0; g < G; ++g) lgv[g] = (c == ovr) ? b[g] : a[g];
+      } else {
+        group_logits<DT, D, G>(krows, 0, nvalid, sm.qt[wid], tr.rope, lgv);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) if (c >= nvalid) lgv[g] = -INFINITY;
+    } else {
+      const uint32_t word = bm_slot[(level - 1) * ((CK + 31) / 32) + (p0 >> 5)];
+      const bool ent = c < nvalid && !((word >> ((p0 & 31) + c)) & 1u);
+      const float* src = lg_slot + static_cast<int64_t>(level - 1) * G * CK + p0 + c;
+#pragma unroll
+      for (int g = 0; g < G; ++g) lgv[g] = ent ? src[static_cast<int64_t>(g) * CK] : -INFINITY;
+    }
+    // ---- online softmax update (rows are replicated over the 4 quarter lanes)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mx = wave_max(lgv[g]);
+      const float mnew = fmaxf(st.m[g], mx);
+      if (mnew == -INFINITY) {
+        if (s == 0) sm.pw[wid][g][c] = 0.f;
+        continue;
+      }
+      const float pr = (lgv[g] == -INFINITY) ? 0.f : __expf(lgv[g] - mnew);
+      const float rs = wave_sum(s == 0 ? pr : 0.f);
+      const float sc = (st.m[g] == -INFINITY) ? 0.f : __expf(st.m[g] - mnew);
+      st.l[g] = st.l[g] * sc + rs;
+      st.m[g] = mnew;
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) st.acc[g][u] *= sc;
+      if (s == 0) sm.pw[wid][g][c] = pr;
+    }
+    wave_sync();
+#pragma unroll
+    for (int r = 0; r < kC; ++r) {
+      float v[DPL];
+      if constexpr (DT == RECSA_BF16 && DPL == 2) {
+        v[0] = __uint_as_float(vraw[r][0] << 16);
+        v[1] = __uint_as_float(vraw[r][0] & 0xFFFF0000u);
+      } else if constexpr (DT == RECSA_BF16) {
+        v[0] = __uint_as_float(vraw[r][0]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < DPL; ++u) v[u] = __uint_as_float(vraw[r][u]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float w = sm.pw[wid][g][r];
+#pragma unroll
+        for (int u = 0; u < DPL; ++u) st.acc[g][u] += w * v[u];
+      }
+    }
+    wave_sync();
+  }
+  // ---- merge the waves
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (lane == 0) {
+      sm.wm[wid][g] = st.m[g];
+      sm.wl[wid][g] = st.l[g];
+    }
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) sm.wacc[wid][g][lane * DPL + u] = st.acc[g][u];
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.wm[w][g]);
+    float l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        if (sm.wm[w][g] != -INFINITY) l += __expf(sm.wm[w][g] - M) * sm.wl[w][g];
+    }
+    sm.res_m[g] = M;
+    sm.res_l[g] = l;
+  }
+  // each (g, d) is read and then overwritten by exactly one thread
+  for (int e = threadIdx.x; e < G * D; e += NT) {
+    const int g = e / D, dd = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.wm[w][g]);
+    float a = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm.wm[w][g];
+        if (mw != -INFINITY) a += __expf(mw - M) * sm.wacc[w][g][dd];
+      }
+    }
+    sm.wacc[0][g][dd] = a;
+  }
+  __syncthreads();
+}
+
+// Merge n_split partial softmax states [n_split][G][D+2] = (m, l, acc[D])
+// into out [G][D].  Threads own (g, d) pairs and walk the splits with
+// several loads in flight.
+template <int D, int G, int NT>
+__device__ __forceinline__ void merge_partials(const float* __restrict__ pp, int n_split,
+                                               float* __restrict__ o) {
+  const int stride = G * (D + 2);
+  for (int e = threadIdx.x; e < G * D; e += NT) {
+    const int g = e / D, dd = e % D;
+    float M = -INFINITY, a = 0.f, l = 0.f;
+    for (int s0 = 0; s0 < n_split; s0 += 8) {
+      float ms[8], ls[8], as[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = s0 + i < n_split;
+        const float* q = pp + (s0 + i) * stride + g * (D + 2);
+        ms[i] = ok ? q[0] : -INFINITY;
+        ls[i] = ok ? q[1] : 0.f;
+        as[i] = ok ? q[2 + dd] : 0.f;
+      }
+      float mb = M;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mb = fmaxf(mb, ms[i]);
+      if (mb == -INFINITY) continue;
+      const float sc = (M == -INFINITY) ? 0.f : __expf(M - mb);
+      a *= sc;
+      l *= sc;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float f = (ms[i] == -INFINITY) ? 0.f : __expf(ms[i] - mb);
+        a += f * as[i];
+        l += f * ls[i];
+      }
+      M = mb;
+    }
+    o[e] = a / l;
+  }
+}
+
+}  // namespace recsa

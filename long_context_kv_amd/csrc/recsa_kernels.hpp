@@ -8,23 +8,28 @@
 
 namespace recsa {
 
-__host__ __device__ __forceinline__ int64_t level_rows_dev(int64_t L_cap, int level) {
-  return L_cap >> (4 * level);   // floor(L_cap / 16^level)
-}
 inline int64_t level_rows_host(int64_t L_cap, int level) { return L_cap >> (4 * level); }
 
-// Workspace layout, per (query, KV head) "slot":
-//   logits  [n_sel][G][C*k] float   (scored candidates' logits)
-//   bitmap  [n_sel][C*k/32] uint32   (selected list positions)
-// followed by the decode attention partials
-//   part    [B][Hkv][n_split][G][d+2] float   (m, l, acc[d])
+// Workspace layout (bytes, 256-aligned regions):
+//   logits  [n_queries*Hkv][n_sel][G][C*k] float   scored candidates' logits
+//   bitmap  [n_queries*Hkv][n_sel][C*k/32] uint32  kept list positions
+//   part    [B*Hkv][kPartSlots][G][d+2] float      decode attention partials
+//   ctl     [B*Hkv][kCtlWords] uint32              fused-decode control block:
+//           word 1 = error word, words 16 + 16*w = arrival flag of workgroup w
+// The ctl words must be zero before the first recsa_decode call; every call
+// leaves them zero (except the error word, see recsa.h).
+constexpr int kDecodeSplits = 64;    // attention workgroups per (query, KV head), decode
+constexpr int kFusedMaxW = 32;       // workgroups per (sequence, KV head), fused decode
+constexpr int kPartSlots = kDecodeSplits > kFusedMaxW ? kDecodeSplits : kFusedMaxW;
+constexpr int kCtlWords = 16 + 16 * kFusedMaxW;   // one 64-byte line per flag
+
 struct WsLayout {
   int n_sel, G, CK, d, n_split;
-  int64_t slot_floats;        // logits floats per slot
-  int64_t slot_words;         // bitmap words per slot
   int64_t n_slots;            // n_queries * Hkv
-  int64_t logits_off, bitmap_off, part_off, total;   // bytes
+  int64_t logits_off, bitmap_off, part_off, ctl_off, total;   // bytes
 };
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~static_cast<int64_t>(255); }
 
 inline WsLayout ws_layout(const recsa_tree& tr, int Hq, int64_t n_queries) {
   WsLayout w;
@@ -32,17 +37,16 @@ inline WsLayout ws_layout(const recsa_tree& tr, int Hq, int64_t n_queries) {
   w.G = Hq / tr.Hkv;
   w.CK = tr.C * tr.k;
   w.d = tr.d;
-  const int chunks_per_level = (w.CK + 255) / 256;
-  w.n_split = w.n_sel * chunks_per_level;     // levels 0 .. n_levels-2
-  w.slot_floats = static_cast<int64_t>(w.n_sel) * w.G * w.CK;
-  w.slot_words = static_cast<int64_t>(w.n_sel) * ((w.CK + 31) / 32);
+  w.n_split = kDecodeSplits;
   w.n_slots = n_queries * tr.Hkv;
+  const int64_t slot_floats = static_cast<int64_t>(w.n_sel) * w.G * w.CK;
+  const int64_t slot_words = static_cast<int64_t>(w.n_sel) * ((w.CK + 31) / 32);
+  const int64_t heads = static_cast<int64_t>(tr.B) * tr.Hkv;
   w.logits_off = 0;
-  w.bitmap_off = w.logits_off + w.n_slots * w.slot_floats * 4;
-  w.part_off = w.bitmap_off + w.n_slots * w.slot_words * 4;
-  w.part_off = (w.part_off + 255) & ~static_cast<int64_t>(255);
-  const int64_t part = static_cast<int64_t>(tr.B) * tr.Hkv * w.n_split * w.G * (w.d + 2) * 4;
-  w.total = w.part_off + part;
+  w.bitmap_off = align256(w.logits_off + w.n_slots * slot_floats * 4);
+  w.part_off = align256(w.bitmap_off + w.n_slots * slot_words * 4);
+  w.ctl_off = align256(w.part_off + heads * kPartSlots * w.G * (w.d + 2) * 4);
+  w.total = w.ctl_off + heads * kCtlWords * 4;   // the control words end the workspace
   return w;
 }
 
@@ -54,8 +58,35 @@ hipError_t launch_append(const recsa_tree& tr, const recsa_pooler& P, const void
 hipError_t launch_select(const recsa_tree& tr, const void* q, int Hq, int T, const int64_t* pos,
                          int32_t* sel, int32_t* cnt, float* imp, void* ws, const WsLayout& w,
                          hipStream_t s);
+hipError_t launch_decode_fused(const recsa_tree& tr, const recsa_pooler& P, const void* k_new,
+                               const void* v_new, const void* q, int Hq, const int64_t* pos,
+                               int32_t* sel, int32_t* cnt, float* out, void* ws, const WsLayout& w,
+                               hipStream_t s);
 hipError_t launch_attn(const recsa_tree& tr, const void* q, int Hq, int T, const int64_t* pos,
                        const int32_t* sel, const int32_t* cnt, float* out, void* ws,
                        const WsLayout& w, bool decode, hipStream_t s);
+
+#define RECSA_DISPATCH(FN, ...)                                                     \
+  do {                                                                              \
+    const int G = Hq / tr.Hkv;                                                      \
+    if (tr.dtype == RECSA_BF16 && tr.d == 128) {                                    \
+      if (G == 4) return FN<RECSA_BF16, 128, 4>(__VA_ARGS__);                       \
+      if (G == 1) return FN<RECSA_BF16, 128, 1>(__VA_ARGS__);                       \
+      if (G == 2) return FN<RECSA_BF16, 128, 2>(__VA_ARGS__);                       \
+    } else if (tr.dtype == RECSA_BF16 && tr.d == 64) {                              \
+      if (G == 4) return FN<RECSA_BF16, 64, 4>(__VA_ARGS__);                        \
+      if (G == 1) return FN<RECSA_BF16, 64, 1>(__VA_ARGS__);                        \
+      if (G == 2) return FN<RECSA_BF16, 64, 2>(__VA_ARGS__);                        \
+    } else if (tr.dtype == RECSA_F32 && tr.d == 128) {                              \
+      if (G == 4) return FN<RECSA_F32, 128, 4>(__VA_ARGS__);                        \
+      if (G == 1) return FN<RECSA_F32, 128, 1>(__VA_ARGS__);                        \
+      if (G == 2) return FN<RECSA_F32, 128, 2>(__VA_ARGS__);                        \
+    } else if (tr.dtype == RECSA_F32 && tr.d == 64) {                               \
+      if (G == 4) return FN<RECSA_F32, 64, 4>(__VA_ARGS__);                         \
+      if (G == 1) return FN<RECSA_F32, 64, 1>(__VA_ARGS__);                         \
+      if (G == 2) return FN<RECSA_F32, 64, 2>(__VA_ARGS__);                         \
+    }                                                                               \
+    return hipErrorInvalidValue;                                                    \
+  } while (0)
 
 }  // namespace recsa

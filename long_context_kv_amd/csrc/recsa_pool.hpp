@@ -1,0 +1,207 @@
+// Pooling of C=16 children into one tree node (picx.dev Tree Construction,
+// Eq. 1 for values; Pooler Distillation, Eq. 5 for keys), for a tile of
+// NODES consecutive nodes and a workgroup of NT threads.  Arithmetic is
+// float32; the node is rounded once to the storage dtype when stored.
+#pragma once
+
+#include "recsa_common.hpp"
+
+namespace recsa {
+
+// ---------------------------------------------------------- pooling tile
+// One workgroup pools NODES consecutive nodes of one (sequence, KV head).
+// Phase 1 (one wave per node): children statistics, alpha, p, value mean.
+// Phase 2/3 (all threads): the pooler MLP for the tile, weights streamed
+// from L2 once per tile.  Phase 4: K = mu + g (p - mu) + sigma m.
+template <int DT, int D, int NODES>
+struct PoolSmem {
+  float feat[NODES][2 * D];
+  float hid[NODES][256];
+  float m[NODES][D];
+};
+
+template <int DT, int D, int NODES, int NT>
+__device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child K rows
+                          const typename Stor<DT>::T* __restrict__ vc,  // child V rows
+                          typename Stor<DT>::T* __restrict__ ko,        // node K rows
+                          typename Stor<DT>::T* __restrict__ vo,        // node V rows
+                          int n_valid, const recsa_pooler& P,
+                          PoolSmem<DT, D, NODES>& sm) {
+  using T = typename Stor<DT>::T;
+  constexpr int DPL = D / kWave;                 // dims per lane (1 or 2)
+  constexpr int NWAVES = NT / kWave;
+  constexpr int NPW = (NODES + NWAVES - 1) / NWAVES;   // nodes per wave
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x >> 6;
+  const int i0 = lane * DPL;
+
+  float mu_r[NPW][DPL], p_r[NPW][DPL], sig_r[NPW];
+
+  // ---- phase 1
+#pragma unroll
+  for (int nw = 0; nw < NPW; ++nw) {
+    const int n = wid * NPW + nw;
+    sig_r[nw] = 0.f;
+    if (n >= NODES || n >= n_valid) continue;
+    float x[kC][DPL];
+    float vs[DPL];
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) vs[u] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      const T* kr = kc + (static_cast<int64_t>(n) * kC + c) * D + i0;
+      const T* vr = vc + (static_cast<int64_t>(n) * kC + c) * D + i0;
+      float tmp[2];
+      if constexpr (DPL == 2) {
+        load_vec<DT, 2>(kr, x[c]);
+        load_vec<DT, 2>(vr, tmp);
+        vs[0] += tmp[0];
+        vs[1] += tmp[1];
+      } else {
+        x[c][0] = Stor<DT>::load(kr);
+        vs[0] += Stor<DT>::load(vr);
+      }
+    }
+    // value mean (Eq. 1)
+#pragma unroll
+    for (int u = 0; u < DPL; ++u)
+      Stor<DT>::store(vo + static_cast<int64_t>(n) * D + i0 + u, vs[u] * (1.0f / kC));
+    // mu, sigma, rho
+    float mu[DPL];
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < kC; ++c) s += x[c][u];
+      mu[u] = s * (1.0f / kC);
+    }
+    float sq = 0.f, mq = 0.f;
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) {
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        const float dv = x[c][u] - mu[u];
+        sq += dv * dv;
+      }
+      mq += mu[u] * mu[u];
+    }
+    sq = wave_sum(sq);
+    mq = wave_sum(mq);
+    const float sigma = sqrtf(sq / static_cast<float>(kC * D) + P.eps);
+    const float rho = sqrtf(mq / static_cast<float>(D) + P.eps);
+    // alpha_c = softmax_c(tau * w.(x_c - mu) / sigma)
+    float w[DPL];
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) w[u] = P.w[i0 + u];
+    float a[kC];
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      float s = 0.f;
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) s += w[u] * (x[c][u] - mu[u]);
+      a[c] = s;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+      for (int c = 0; c < kC; ++c) a[c] += __shfl_xor(a[c], o, kWave);
+    }
+    const float scale = P.tau / sigma;
+    float amax = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      a[c] *= scale;
+      amax = fmaxf(amax, a[c]);
+    }
+    float asum = 0.f;
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      a[c] = __expf(a[c] - amax);
+      asum += a[c];
+    }
+    const float inv = 1.0f / asum;
+    float p[DPL];
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < kC; ++c) s += a[c] * x[c][u];
+      p[u] = s * inv;
+    }
+    const float inv_rho = 1.0f / rho, inv_sig = 1.0f / sigma;
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) {
+      sm.feat[n][i0 + u] = mu[u] * inv_rho;
+      sm.feat[n][D + i0 + u] = (p[u] - mu[u]) * inv_sig;
+      mu_r[nw][u] = mu[u];
+      p_r[nw][u] = p[u];
+    }
+    sig_r[nw] = sigma;
+  }
+  __syncthreads();
+
+  // ---- phase 2: hid = SiLU(W1 feat + b1)
+  constexpr int NPG = NODES < 8 ? NODES : 8;     // nodes per thread
+  constexpr int NGRP = NODES / NPG;
+  const int H = P.hidden;
+  for (int item = threadIdx.x; item < NGRP * H; item += NT) {
+    const int i = item % H;
+    const int g0 = (item / H) * NPG;
+    float acc[NPG];
+#pragma unroll
+    for (int q = 0; q < NPG; ++q) acc[q] = 0.f;
+    const float4* wr = reinterpret_cast<const float4*>(P.W1 + static_cast<int64_t>(i) * 2 * D);
+#pragma unroll 4
+    for (int k4 = 0; k4 < (2 * D) / 4; ++k4) {
+      const float4 wv = wr[k4];
+#pragma unroll
+      for (int q = 0; q < NPG; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(&sm.feat[g0 + q][4 * k4]);
+        acc[q] += wv.x * f.x + wv.y * f.y + wv.z * f.z + wv.w * f.w;
+      }
+    }
+    const float b = P.b1[i];
+#pragma unroll
+    for (int q = 0; q < NPG; ++q) {
+      const float z = acc[q] + b;
+      sm.hid[g0 + q][i] = z / (1.0f + __expf(-z));
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: m = W2 hid
+  for (int item = threadIdx.x; item < NGRP * D; item += NT) {
+    const int j = item % D;
+    const int g0 = (item / D) * NPG;
+    float acc[NPG];
+#pragma unroll
+    for (int q = 0; q < NPG; ++q) acc[q] = 0.f;
+    const float4* wr = reinterpret_cast<const float4*>(P.W2 + static_cast<int64_t>(j) * H);
+    for (int k4 = 0; k4 < H / 4; ++k4) {
+      const float4 wv = wr[k4];
+#pragma unroll
+      for (int q = 0; q < NPG; ++q) {
+        const float4 h = *reinterpret_cast<const float4*>(&sm.hid[g0 + q][4 * k4]);
+        acc[q] += wv.x * h.x + wv.y * h.y + wv.z * h.z + wv.w * h.w;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NPG; ++q) sm.m[g0 + q][j] = acc[q];
+  }
+  __syncthreads();
+
+  // ---- phase 4: K = mu + g (p - mu) + sigma m
+#pragma unroll
+  for (int nw = 0; nw < NPW; ++nw) {
+    const int n = wid * NPW + nw;
+    if (n >= NODES || n >= n_valid) continue;
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) {
+      const float kv = mu_r[nw][u] + P.g * (p_r[nw][u] - mu_r[nw][u]) +
+                       sig_r[nw] * sm.m[n][i0 + u];
+      Stor<DT>::store(ko + static_cast<int64_t>(n) * D + i0 + u, kv);
+    }
+  }
+}
+
+}  // namespace recsa

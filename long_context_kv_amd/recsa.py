@@ -30,7 +30,7 @@ EXPORTS = (
     "recsa_status_string", "recsa_level_rows", "recsa_levels_needed",
     "recsa_init_rope", "recsa_workspace_bytes", "recsa_build_tree",
     "recsa_append_decode", "recsa_select", "recsa_attn_decode",
-    "recsa_attn_prefill",
+    "recsa_attn_prefill", "recsa_decode",
 )
 
 
@@ -86,6 +86,7 @@ def lib():
             "recsa_select": (ctypes.c_int, [T, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "recsa_attn_decode": (ctypes.c_int, [T, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "recsa_attn_prefill": (ctypes.c_int, [T, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "recsa_decode": (ctypes.c_int, [T, P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -275,9 +276,38 @@ def recsa_attn_prefill(tree, q, Hq: int, T: int, pos_dev, sel_idx, sel_cnt, out,
         _ptr(out), _ptr(ws), nb, _stream(stream)))
 
 
+def recsa_decode(tree, pooler, k_new, v_new, q, Hq: int, pos_dev, sel_idx, sel_cnt, out, ws,
+                 ws_bytes: int | None = None, stream=None):
+    tc, pc = _tc(tree), _pc(pooler)
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("recsa_decode", lib().recsa_decode(
+        ctypes.byref(tc), ctypes.byref(pc), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, _ptr(pos_dev),
+        _ptr(sel_idx), _ptr(sel_cnt), _ptr(out), _ptr(ws), nb, _stream(stream)))
+
+
 def workspace(tree, Hq: int, n_queries: int):
-    """Allocate a workspace tensor of the size recsa_workspace_bytes reports."""
+    """Allocate a zero-filled workspace of the size recsa_workspace_bytes
+    reports (zero control words, as recsa_decode requires on first use)."""
     nb = recsa_workspace_bytes(tree, Hq, n_queries)
     if nb == 0:
         raise RecsaError("recsa_workspace_bytes", RECSA_E_INVALID, "invalid arguments")
-    return torch.empty(nb, dtype=torch.uint8, device=tree.rope.device)
+    return torch.zeros(nb, dtype=torch.uint8, device=tree.rope.device)
+
+
+CTL_WORDS = 16 + 16 * 32      # per (sequence, KV head): see recsa_decode in recsa.h
+
+
+def decode_error_words(ws, tree, Hq: int):
+    """Error words of the fused-decode control blocks, one per (sequence, KV
+    head); nonzero means that group gave up waiting (its output is NaN)."""
+    nb = recsa_workspace_bytes(tree, Hq, tree.B)
+    n = tree.B * tree.Hkv
+    ctl = ws[nb - 4 * CTL_WORDS * n: nb].view(torch.int32).view(n, CTL_WORDS)
+    return ctl[:, 1]
+
+
+def decode_control_words(ws, tree, Hq: int):
+    """The whole fused-decode control block [B*Hkv, CTL_WORDS] (int32)."""
+    nb = recsa_workspace_bytes(tree, Hq, tree.B)
+    n = tree.B * tree.Hkv
+    return ws[nb - 4 * CTL_WORDS * n: nb].view(torch.int32).view(n, CTL_WORDS)

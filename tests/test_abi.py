@@ -102,6 +102,10 @@ def test_call_validation_without_launch():
     assert L.recsa_select(*args, ws_need - 1, None) == R.RECSA_E_WORKSPACE
     assert L.recsa_select(b(t), 0x10, 24, 1, 0x10, 0x10, 0x10, None, 0x10, ws_need, None) \
         == R.RECSA_E_UNSUPPORTED                                            # G = 3
+    assert L.recsa_select(b(t), 0x10, 64, 1, 0x10, 0x10, 0x10, None, 0x10, ws_need, None) \
+        == R.RECSA_E_UNSUPPORTED                                            # G = 8: off
+    assert L.recsa_decode(b(t), b(p), 0x10, 0x10, 0x10, 64, 0x10, 0x10, 0x10, 0x10, 0x10,
+                          ws_need, None) == R.RECSA_E_UNSUPPORTED
     assert L.recsa_select(b(t), None, 32, 1, 0x10, 0x10, 0x10, None, 0x10, ws_need, None) \
         == R.RECSA_E_INVALID
     assert L.recsa_attn_decode(b(t), 0x10, 32, 0x10, 0x10, 0x10, None, 0x10, ws_need, None) \

@@ -162,7 +162,8 @@ def _check_queries(tree, pdict, q, pos, sel, cnt, imp, out, heads, tie_rel, out_
                 Kt, Vt = Kt[: max(D, 1)], Vt[: max(D, 1)]
                 o_ref, tr = O.decode_reference(qn[b, ti, j * G:(j + 1) * G], t, Kt, Vt, 16,
                                                tree.k, cos, sin, tree.dtype)
-                ok = PY.compare_walk(tr, sel[b, ti, j], cnt[b, ti, j], imp[b, ti, j], rep,
+                ok = PY.compare_walk(tr, sel[b, ti, j], cnt[b, ti, j],
+                                     None if imp is None else imp[b, ti, j], rep,
                                      tie_rel, differs, 2e-2)
                 # levels above the oracle's top are fully selected prefixes
                 for lvl in range(D, tree.n_levels):
@@ -263,3 +264,75 @@ def test_prefill_chunk_bf16_causal():
                                       pos[:, T - 1:].contiguous(), decode=True)
     assert np.array_equal(s2[0, 0], sel[0, T - 1]) and np.array_equal(c2[0, 0], cnt[0, T - 1])
     assert np.allclose(o2[0, 0], out[0, T - 1], rtol=0, atol=1e-5 * np.abs(out[0, T - 1]).max())
+
+
+def _fused_step(tree, pool, k_new, v_new, q, Hq, pos, ws=None):
+    B = tree.B
+    ws = ws if ws is not None else R.workspace(tree, Hq, B)
+    sel, cnt, _ = tree.selection_buffers(B)
+    out = torch.empty((B, Hq, tree.d), dtype=torch.float32, device=DEV)
+    R.recsa_decode(tree, pool, k_new, v_new, q, Hq, pos, sel, cnt, out, ws)
+    return sel, cnt, out, ws
+
+
+@pytest.mark.parametrize("dtype,d,Hkv,G,B", [("bf16", 128, 8, 4, 1), ("f32", 64, 2, 4, 2),
+                                             ("bf16", 128, 4, 2, 3)])
+def test_fused_decode_matches_separate_calls(dtype, d, Hkv, G, B):
+    """recsa_decode (append + select + attend in one launch) gives the same
+    selection and output as recsa_append_decode + recsa_select +
+    recsa_attn_decode, over consecutive steps that complete level-1 and
+    level-2 nodes, and leaves its control words clear."""
+    _need_gpu()
+    L0, steps = 65536 - 3, 5                     # t = 65533 .. 65537 crosses 65536
+    L_cap = L0 + 64
+    Hq = Hkv * G
+    wl, tree, pool, pdict = _setup(B, Hkv, d, L_cap, L_cap, 256, dtype, 21)
+    ref = R.Tree.allocate(B, Hkv, d, L_cap, k=256, dtype=dtype, device=DEV,
+                          level0=(tree.K[0].clone(), tree.V[0].clone()))
+    rows_k = tree.K[0][:, :, L0:L0 + steps].clone()
+    rows_v = tree.V[0][:, :, L0:L0 + steps].clone()
+    R.recsa_build_tree(tree, pool, 0, L0)
+    R.recsa_build_tree(ref, pool, 0, L0)
+    ws = R.workspace(tree, Hq, B)
+    ws_ref = R.workspace(ref, Hq, B)
+    for i in range(steps):
+        t = L0 + i
+        pos = torch.full((B,), t, dtype=torch.int64, device=DEV)
+        q = synth.to_storage(synth.normal((B, 1, Hq, d), DEV, 21, 500 + i), dtype)
+        kn, vn = rows_k[:, :, i].contiguous(), rows_v[:, :, i].contiguous()
+        sel, cnt, out, ws = _fused_step(tree, pool, kn, vn, q, Hq, pos, ws)
+        R.recsa_append_decode(ref, pool, kn, vn, pos)
+        s2, c2, m2, o2 = _run_select_attn(ref, q, Hq, pos.view(B, 1), decode=True)
+        torch.cuda.synchronize()
+        assert torch.equal(R.decode_error_words(ws, tree, Hq), torch.zeros_like(R.decode_error_words(ws, tree, Hq)))
+        assert np.array_equal(sel.cpu().numpy().reshape(s2.shape), s2), t
+        assert np.array_equal(cnt.cpu().numpy().reshape(c2.shape), c2), t
+        o = out.cpu().numpy().astype(np.float64).reshape(o2.shape)
+        assert np.allclose(o, o2, rtol=0, atol=1e-5 * np.abs(o2).max()), t
+    for lvl in range(tree.n_levels):
+        assert torch.equal(tree.K[lvl], ref.K[lvl]) and torch.equal(tree.V[lvl], ref.V[lvl]), lvl
+    # control block: every arrival flag back at zero, no error word set
+    assert torch.count_nonzero(R.decode_control_words(ws, tree, Hq).cpu()) == 0
+
+
+def test_fused_decode_vs_oracle_bf16():
+    """The fused decode step at the Qwen shape (8/32/128, bf16, k=256) on a
+    64K-token cache: every KV head's selection and output vs the oracle."""
+    _need_gpu()
+    L = 65536 + 15                              # t + 1 = 65552: completes a level-1 node
+    L_cap = L + 64
+    wl, tree, pool, pdict = _setup(1, 8, 128, L + 1, L_cap, 256, "bf16", 22)
+    kn, vn = tree.K[0][:, :, L].clone().contiguous(), tree.V[0][:, :, L].clone().contiguous()
+    R.recsa_build_tree(tree, pool, 0, L)
+    pos = torch.tensor([L], dtype=torch.int64, device=DEV)
+    q = synth.to_storage(synth.normal((1, 1, 32, 128), DEV, 22, 98), "bf16")
+    sel, cnt, out, ws = _fused_step(tree, pool, kn, vn, q, 32, pos)
+    torch.cuda.synchronize()
+    B, n_sel, k = 1, tree.n_sel, tree.k
+    s = sel.cpu().numpy().reshape(B, 1, 8, n_sel, k)
+    c = cnt.cpu().numpy().reshape(B, 1, 8, n_sel)
+    imp = np.zeros((B, 1, 8, n_sel, 16 * k))
+    o = out.cpu().numpy().astype(np.float64).reshape(B, 1, 32, 128)
+    rep = _check_queries(tree, pdict, q, pos.view(1, 1).cpu(), s, c, None, o, range(8),
+                         1e-5, 2e-3, max_swaps=1)
+    assert rep.matched >= 7, rep
