@@ -28,6 +28,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
+    # run LLVM's machine-code verifier on every function: a backend that emits
+    # invalid code (e.g. reads an undefined condition register) fails the build
+    "-mllvm", "-verify-machineinstrs",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

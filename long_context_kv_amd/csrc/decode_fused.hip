@@ -46,13 +46,18 @@ __device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uin
     // an atomic read-modify-write is performed where every XCD sees it (a
     // plain store could stay in this XCD's L2)
     __hip_atomic_exchange(flags + 16 * w, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every poll reads all W flags at once (one memory round trip)
     uint32_t spins = 0;
-    for (int i = 0; i < W; ++i) {
-      while (__hip_atomic_load(flags + 16 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) break;
+    while (true) {
+      uint32_t lo = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < kFusedMaxW; ++i) {
+        if (i < W)
+          lo = min(lo, __hip_atomic_load(flags + 16 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       }
-      if (spins > kSpinLimit) {
+      if (lo >= gen) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
         atomicOr(err, 1u);
         *s_fail = 1u;
         break;
@@ -146,12 +151,14 @@ __global__ void __launch_bounds__(kFusedThreads)
       float* out_l = lg_slot + static_cast<int64_t>(l - 1) * G * CK;
       for (int gi = w + W * wid; gi < ng; gi += W * NW) {
         const int p0 = gi * kC;
-        rotate_query<DT, D, G>(qs, sm.at.qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
-        wave_sync();
         const int nvalid = min(kC, n - p0);
         const T* rows = static_cast<const T*>(tr.K[l]) + (slot * rows_l + lv.node(p0)) * D;
+        KRows<DT, D> kr;                 // key rows in flight during the rotation
+        group_load_k<DT, D>(rows, 0, nvalid, kr);
+        rotate_query<DT, D, G>(qs, sm.at.qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
+        wave_sync();
         float lg[G];
-        group_logits<DT, D, G>(rows, 0, nvalid, sm.at.qt[wid], tr.rope, lg);
+        group_logits_from<DT, D, G>(kr, 0, nvalid, sm.at.qt[wid], tr.rope, lg);
         const int c = lane >> 2, s = lane & 3;
         if (c < nvalid) {
 #pragma unroll

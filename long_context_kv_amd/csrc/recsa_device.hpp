@@ -10,16 +10,61 @@ namespace recsa {
 
 // ------------------------------------------------------------------------
 // Logits of the 16 rows of one list group against G rotated query heads.
-// Lane = (row c = lane/4, quarter s = lane%4); each lane rotates 2*E pairs of
-// its row by the in-group offset c (the key half of the split RoPE), rounds
-// them to the storage dtype and dots them with the group's rotated query
-// (LDS, float).  The four quarter lanes of a row are summed, so every lane of
-// row c ends with the G logits of that row.  Only rows in [row_lo, nvalid)
-// are read; the others give 0.
+// Lane = (row c = lane/4, quarter s = lane%4); each lane holds 2*E pairs of
+// its row (as raw storage words), rotates them by the in-group offset c (the
+// key half of the split RoPE), rounds them to the storage dtype and dots them
+// with the group's rotated query (LDS, float).  The four quarter lanes of a
+// row are summed, so every lane of row c ends with the G logits of that row.
+// Only rows in [row_lo, nvalid) are read; the others give 0.  Loading and
+// computing are separate steps so a caller can issue the loads early.
+template <int DT, int D>
+struct KRows {
+  static constexpr int E = D / 16;
+  static constexpr int WPC = DT == RECSA_BF16 ? E / 2 : E;   // 32-bit words per chunk
+  uint32_t xr[2][WPC], yr[2][WPC];
+};
+
+template <int DT, int D>
+__device__ __forceinline__ void group_load_k(const typename Stor<DT>::T* __restrict__ rows,
+                                             int row_lo, int nvalid, KRows<DT, D>& kr) {
+  constexpr int E = D / 16, QD = D / 4, H2 = D / 2, WPC = KRows<DT, D>::WPC;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane >> 2, s = lane & 3;
+  if (c >= row_lo && c < nvalid) {
+    const typename Stor<DT>::T* row = rows + static_cast<int64_t>(c) * D;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int base = hh * QD + s * E;
+      const uint32_t* px = reinterpret_cast<const uint32_t*>(row + base);
+      const uint32_t* py = reinterpret_cast<const uint32_t*>(row + H2 + base);
+      if constexpr (WPC % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < WPC; i += 4) {
+          const uint4 a = *reinterpret_cast<const uint4*>(px + i);
+          const uint4 b = *reinterpret_cast<const uint4*>(py + i);
+          kr.xr[hh][i] = a.x; kr.xr[hh][i + 1] = a.y; kr.xr[hh][i + 2] = a.z; kr.xr[hh][i + 3] = a.w;
+          kr.yr[hh][i] = b.x; kr.yr[hh][i + 1] = b.y; kr.yr[hh][i + 2] = b.z; kr.yr[hh][i + 3] = b.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < WPC; ++i) {
+          kr.xr[hh][i] = px[i];
+          kr.yr[hh][i] = py[i];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < WPC; ++i) kr.xr[hh][i] = kr.yr[hh][i] = 0u;
+  }
+}
+
 template <int DT, int D, int G>
-__device__ __forceinline__ void group_logits(const typename Stor<DT>::T* __restrict__ rows,
-                                             int row_lo, int nvalid, const float* qt,
-                                             const float* __restrict__ rope, float* lg) {
+__device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int row_lo, int nvalid,
+                                                  const float* qt, const float* __restrict__ rope,
+                                                  float* lg) {
   constexpr int E = D / 16, QD = D / 4, H2 = D / 2;
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane >> 2, s = lane & 3;
@@ -27,32 +72,6 @@ __device__ __forceinline__ void group_logits(const typename Stor<DT>::T* __restr
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = 0.f;
   if (c >= row_lo && c < nvalid) {
-    const typename Stor<DT>::T* row = rows + static_cast<int64_t>(c) * D;
-    // raw storage words stay packed until used (bf16: 2 values per word)
-    constexpr int WPC = DT == RECSA_BF16 ? E / 2 : E;      // 32-bit words per chunk
-    uint32_t xr[2][WPC], yr[2][WPC];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int base = hh * QD + s * E;
-      const uint32_t* px = reinterpret_cast<const uint32_t*>(row + base);
-      const uint32_t* py = reinterpret_cast<const uint32_t*>(row + H2 + base);
-#pragma unroll
-      for (int i = 0; i < WPC; i += 4) {
-        if constexpr (WPC % 4 == 0) {
-          const uint4 a = *reinterpret_cast<const uint4*>(px + i);
-          const uint4 b = *reinterpret_cast<const uint4*>(py + i);
-          xr[hh][i] = a.x; xr[hh][i + 1] = a.y; xr[hh][i + 2] = a.z; xr[hh][i + 3] = a.w;
-          yr[hh][i] = b.x; yr[hh][i + 1] = b.y; yr[hh][i + 2] = b.z; yr[hh][i + 3] = b.w;
-        }
-      }
-      if constexpr (WPC % 4 != 0) {
-#pragma unroll
-        for (int i = 0; i < WPC; ++i) {
-          xr[hh][i] = px[i];
-          yr[hh][i] = py[i];
-        }
-      }
-    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       // keep the two halves' LDS reads from being hoisted together
@@ -63,12 +82,12 @@ __device__ __forceinline__ void group_logits(const typename Stor<DT>::T* __restr
       for (int m = 0; m < E; ++m) {
         float x, y;
         if constexpr (DT == RECSA_BF16) {
-          const uint32_t wx = xr[hh][m / 2], wy = yr[hh][m / 2];
+          const uint32_t wx = kr.xr[hh][m / 2], wy = kr.yr[hh][m / 2];
           x = __uint_as_float((m & 1) ? (wx & 0xFFFF0000u) : (wx << 16));
           y = __uint_as_float((m & 1) ? (wy & 0xFFFF0000u) : (wy << 16));
         } else {
-          x = __uint_as_float(xr[hh][m]);
-          y = __uint_as_float(yr[hh][m]);
+          x = __uint_as_float(kr.xr[hh][m]);
+          y = __uint_as_float(kr.yr[hh][m]);
         }
         float xo, yo;
         rope_pair(x, y, rp[2 * m], rp[2 * m + 1], xo, yo);
@@ -88,6 +107,15 @@ __device__ __forceinline__ void group_logits(const typename Stor<DT>::T* __restr
     v += __shfl_xor(v, 2, kWave);
     lg[g] = v * scale;
   }
+}
+
+template <int DT, int D, int G>
+__device__ __forceinline__ void group_logits(const typename Stor<DT>::T* __restrict__ rows,
+                                             int row_lo, int nvalid, const float* qt,
+                                             const float* __restrict__ rope, float* lg) {
+  KRows<DT, D> kr;
+  group_load_k<DT, D>(rows, row_lo, nvalid, kr);
+  group_logits_from<DT, D, G>(kr, row_lo, nvalid, qt, rope, lg);
 }
 
 // Rotate the G query heads by phi and round (one wave): qt = rnd(R(phi) q),
@@ -183,8 +211,14 @@ __device__ __forceinline__ int block_scan_excl(int v, int* red, int* total) {
 constexpr int kHistBits = 11;
 constexpr int kHistBins = 1 << kHistBits;
 
+constexpr int kSmallBin = 64;
+
 struct TopkSmem {
   int hist[kHistBins];
+  uint32_t small_key[kSmallBin];
+  int small_pos[kSmallBin];
+  uint32_t small_take[kMaxCK / 32];
+  int s_nsmall;
   float redg[kMaxG][16];
   float redf[16];
   int redi[16];
@@ -216,11 +250,20 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   float I[PPT];
   // ---- all logits first (one memory round trip), then per-head max and
   // normaliser with one block exchange for all heads
+  // (each thread's PPT positions are contiguous and 16-byte aligned; the
+  // logits row holds CK floats, so the vector loads stay inside it)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const float* src = lgs + static_cast<int64_t>(g) * CK + p0;
+    if (p0 < n) {
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) e[g][i] = (p0 + i < n) ? src[i] : -INFINITY;
+      for (int i = 0; i < PPT; i += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + i);
+        e[g][i] = v.x; e[g][i + 1] = v.y; e[g][i + 2] = v.z; e[g][i + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) if (p0 + i >= n) e[g][i] = -INFINITY;
   }
   float M[G], Z[G];
 #pragma unroll
@@ -286,7 +329,7 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   const int need0 = k - 1;
   uint32_t prefix = 0, pmask = 0;
   int need = need0;
-  bool whole_bin = false;
+  bool whole_bin = false, small = false;
   if (need0 > 0) {
     kmin = wave_min_u32(kmin);
     kmax = wave_max_u32(kmax);
@@ -303,9 +346,12 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       kmin = min(kmin, sm.redu[0][w]);
       kmax = max(kmax, sm.redu[1][w]);
     }
-    int hb = (kmin == kmax) ? -1 : 31 - __clz(kmin ^ kmax);   // highest differing bit
-    pmask = (hb >= 31) ? 0u : ~((2u << hb) - 1u);             // bits above hb (all when hb<0)
-    if (hb < 0) pmask = 0xFFFFFFFFu;
+    // highest differing bit (-1 when all keys are equal) and the mask of the
+    // bits above it, which every key shares; the 64-bit shift keeps every
+    // count in [0, 32] defined
+    const uint32_t diff = kmin ^ kmax;
+    int hb = diff ? 31 - __clz(diff) : -1;
+    pmask = static_cast<uint32_t>(0xFFFFFFFFull << (hb + 1));
     prefix = kmin & pmask;
 #pragma unroll 1
     while (hb >= 0) {
@@ -342,38 +388,84 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       pmask |= dmask << lo;
       need = sm.s_need;
       whole_bin = sm.s_full != 0;
+      const int in_bin = sm.hist[sm.s_bin];
       __syncthreads();
       if (whole_bin) break;
+      if (lo > 0 && in_bin <= kSmallBin) {
+        // few keys left in the boundary bin: rank them exactly (key
+        // descending, then list position ascending) in one wave
+        if (tid == 0) sm.s_nsmall = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+          if (p0 + i < n && (key[i] & pmask) == prefix) {
+            const int at = atomicAdd(&sm.s_nsmall, 1);
+            sm.small_key[at] = key[i];
+            sm.small_pos[at] = p0 + i;
+          }
+        }
+        for (int wd = tid; wd < kMaxCK / 32; wd += NT) sm.small_take[wd] = 0u;
+        __syncthreads();
+        if (tid < kWave) {
+          const int m = sm.s_nsmall;
+          if (tid < m) {
+            const uint32_t ki = sm.small_key[tid];
+            const int pi = sm.small_pos[tid];
+            int rank = 0;
+            for (int q2 = 0; q2 < m; ++q2) {
+              const uint32_t kq = sm.small_key[q2];
+              rank += (kq > ki || (kq == ki && sm.small_pos[q2] < pi)) ? 1 : 0;
+            }
+            if (rank < need) atomicOr(&sm.small_take[pi >> 5], 1u << (pi & 31));
+          }
+        }
+        __syncthreads();
+        small = true;
+        break;
+      }
       hb = lo - 1;
     }
   }
   // ---- keep: truncated key above the threshold prefix, or equal to it and
-  // (whole bin kept, or among the first `need` equal ones by position)
-  int n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < PPT; ++i) n_eq += (p0 + i < n && (key[i] & pmask) == prefix) ? 1 : 0;
-  int tot;
-  int eq_rank = block_scan_excl<NT>(n_eq, sm.redi, &tot);
-  bool take[PPT];
-  int n_take = 0;
+  // (whole bin kept, ranked in by the small-bin pass, or among the first
+  // `need` equal ones by position).  Per-thread flags are bit masks over the
+  // PPT positions (bit i = position p0 + i).
+  static_assert(PPT < 32 && 32 % PPT == 0, "positions per thread");
+  uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
     const bool valid = need0 > 0 && p0 + i < n;
     const uint32_t kt = key[i] & pmask;
-    const bool eq = valid && kt == prefix;
-    take[i] = valid && (kt > prefix || (eq && (whole_bin || eq_rank < need)));
-    eq_rank += eq ? 1 : 0;
-    n_take += take[i] ? 1 : 0;
+    gtm |= (valid && kt > prefix) ? (1u << i) : 0u;
+    eqm |= (valid && kt == prefix) ? (1u << i) : 0u;
   }
-  int slot = block_scan_excl<NT>(n_take, sm.redi, &tot);
-  uint32_t bits = 0;
+  int tot;
+  const int eq_rank = block_scan_excl<NT>(__popc(eqm), sm.redi, &tot);
+  uint32_t inm;
+  if (small) {
+    inm = (sm.small_take[p0 >> 5] >> (p0 & 31)) & eqm;
+  } else if (whole_bin) {
+    inm = eqm;
+  } else {
+    inm = 0u;
+    int room = need - eq_rank;          // equal keys still wanted, in position order
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    if (take[i]) {
-      out_sel[slot++] = static_cast<int32_t>(lv.node(p0 + i));
-      bits |= 1u << ((p0 + i) & 31);
+    for (int i = 0; i < PPT; ++i) {
+      const bool e = ((eqm >> i) & 1u) != 0u;
+      inm |= (e && room > 0) ? (1u << i) : 0u;
+      room -= e ? 1 : 0;
     }
   }
+  const uint32_t takem = gtm | inm;
+  int slot = block_scan_excl<NT>(__popc(takem), sm.redi, &tot);
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    if ((takem >> i) & 1u) {
+      if (slot < k - 1) out_sel[slot] = static_cast<int32_t>(lv.node(p0 + i));
+      ++slot;
+    }
+  }
+  uint32_t bits = takem << (p0 & 31);
   // PPT consecutive positions per thread: 32/PPT threads share one word
   constexpr int LPW = 32 / PPT;
 #pragma unroll
@@ -527,20 +619,23 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
     float lgv[G];
     if (level == 0) {
       const int p_q = lv.len - 1;
+      const T* krows = static_cast<const T*>(tr.K[0]) + (seq_head * rows_l + node0) * D;
+      const bool split = ovr >= 0 && ovr < kC;
+      // key rows first (in flight during the rotation), then the query turn
+      KRows<DT, D> ka, kb;
+      group_load_k<DT, D>(krows, 0, split ? ovr : nvalid, ka);
+      // only row ovr is read from this base, i.e. exactly k_t
+      if (split) group_load_k<DT, D>(k_t - static_cast<int64_t>(ovr) * D, ovr, ovr + 1, kb);
       rotate_query<DT, D, G>(qs, sm.qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
       wave_sync();
-      const T* krows = static_cast<const T*>(tr.K[0]) + (seq_head * rows_l + node0) * D;
-      if (ovr >= 0 && ovr < kC) {
-        // rows before t from the tree, row t from k_t: score in two calls
+      if (split) {
         float a[G], b[G];
-        group_logits<DT, D, G>(krows, 0, ovr, sm.qt[wid], tr.rope, a);
-        // only row ovr is read from this base, i.e. exactly k_t
-        group_logits<DT, D, G>(k_t - static_cast<int64_t>(ovr) * D, ovr, ovr + 1, sm.qt[wid],
-                               tr.rope, b);
+        group_logits_from<DT, D, G>(ka, 0, ovr, sm.qt[wid], tr.rope, a);
+        group_logits_from<DT, D, G>(kb, ovr, ovr + 1, sm.qt[wid], tr.rope, b);
 #pragma unroll
         for (int g = 0; g < G; ++g) lgv[g] = (c == ovr) ? b[g] : a[g];
       } else {
-        group_logits<DT, D, G>(krows, 0, nvalid, sm.qt[wid], tr.rope, lgv);
+        group_logits_from<DT, D, G>(ka, 0, nvalid, sm.qt[wid], tr.rope, lgv);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) if (c >= nvalid) lgv[g] = -INFINITY;

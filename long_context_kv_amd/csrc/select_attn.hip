@@ -62,13 +62,15 @@ __global__ void __launch_bounds__(kBlock)
   const int p0 = pbase + wid * kC;                  // this wave's group
   if (p0 >= n_others) return;                        // no block barrier below
   const int p_q = lv.len - 1;
-  rotate_query<DT, D, G>(qs, qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
-  wave_sync();
   const int nvalid = min(kC, n_others - p0);
   const int64_t rows_l = level_rows_dev(tr.L_cap, level);
   const T_* rows = static_cast<const T_*>(tr.K[level]) + (qc.seq_head * rows_l + lv.node(p0)) * D;
+  KRows<DT, D> kr;                       // key rows in flight during the rotation
+  group_load_k<DT, D>(rows, 0, nvalid, kr);
+  rotate_query<DT, D, G>(qs, qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
+  wave_sync();
   float lg[G];
-  group_logits<DT, D, G>(rows, 0, nvalid, qt[wid], tr.rope, lg);
+  group_logits_from<DT, D, G>(kr, 0, nvalid, qt[wid], tr.rope, lg);
   float* out = ws_logits + (qc.slot * n_sel + (level - 1)) * static_cast<int64_t>(G) * CK;
   const int c = lane >> 2, s = lane & 3;
   if (c < nvalid) {
