@@ -359,13 +359,13 @@ def cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T):
         Kt, Vt = O.build_tree(K0, V0, 16, tree.n_levels, P, wl.dtype)
         build_s = time.time() - t0
         cos, sin = O.rope_table(wl.d, 16 * wl.k, wl.theta)
-        qd = PY.to64(q_dec[0])                               # [Hq, d]
+        qd = PY.to64(q_dec[0, 0])                            # [Hq, d]
         t1 = time.time()
         for j in range(wl.Hkv):
             O.decode_reference(qd[j * G:(j + 1) * G], t_dec, Kt, Vt, 16, wl.k, cos, sin, wl.dtype)
         dec_s = (time.time() - t1) / wl.Hkv
         qp = PY.to64(q_pre[0, :, :G])
-        idx = np.linspace(0, T - 1, 256).astype(int)
+        idx = np.linspace(0, T - 1, 512).astype(int)
         t2 = time.time()
         for i in idx:
             t = L + int(i)
@@ -379,7 +379,7 @@ def cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T):
     return {
         "value": round(dec_s * heads * 1e6, 1), "unit": "us/token", "cores": 1, "kind": "oracle",
         "sample": (f"KV head 0 of {heads}, one thread: oracle tree build over {t_dec + 1} tokens, "
-                   f"8 decode walks+softmaxes at t={t_dec} and 256 evenly spaced queries of the "
+                   f"8 decode walks+softmaxes at t={t_dec} and 512 evenly spaced queries of the "
                    f"{T}-query prefill chunk, each scaled x{heads} heads ({total:.1f}s of CPU work)"),
         "prefill_tok_s": round(1.0 / (pre_s * heads), 3),
         "build_full_ms": round(build_s * heads * 1e3, 1),
