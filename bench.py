@@ -67,10 +67,13 @@ def decode_rows(t, C, k, n_levels):
 
 
 def build_bytes(L, Hkv, n_levels, tb=0):
-    total = 0
+    """Bytes a build over tokens [tb, L) must move per sequence: the rotated
+    copy of each level-0 key row (read K, write Kr), and per node its 16
+    children's K and V rows read plus its K, V and Kr rows written."""
+    total = (L - tb) * Hkv * 2 * ROW_BYTES
     for lvl in range(1, n_levels):
         n = (L >> (4 * lvl)) - (tb >> (4 * lvl))
-        total += n * Hkv * (2 * 16 + 2) * ROW_BYTES
+        total += n * Hkv * (2 * 16 + 3) * ROW_BYTES
     return total
 
 

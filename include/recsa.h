@@ -72,6 +72,12 @@ extern "C" {
  *   in the storage dtype; level 0 is the ordinary KV cache (pre-RoPE keys).
  *   Only complete nodes are ever written: node i of level l covers tokens
  *   [i*C^l, (i+1)*C^l).
+ * Kr[l]: the same layout; row i holds the key half of the split RoPE,
+ *   rnd(R(i mod C) K[l][i]) (see the logit below), which depends on the row
+ *   alone.  The library writes it for every row it writes (nodes built or
+ *   appended, the appended token) and, in recsa_build_tree, for the level-0
+ *   rows of the given token range; selection and attention read keys only
+ *   from Kr.  The caller allocates it like K.
  * n_levels: levels allocated, >= recsa_levels_needed(L_cap, C, k) (so the
  *   list of the top level has at most k nodes for every position < L_cap);
  *   more levels do not change any result.
@@ -89,6 +95,7 @@ typedef struct recsa_tree {
   int64_t L_cap;
   void* K[RECSA_MAX_LEVELS];
   void* V[RECSA_MAX_LEVELS];
+  void* Kr[RECSA_MAX_LEVELS];
   const float* rope;
 } recsa_tree;
 
@@ -133,16 +140,18 @@ int recsa_init_rope(float* table, int32_t d, int32_t n_pos, double theta, void* 
  * bitmaps and attention partials).  0 on invalid arguments. */
 size_t recsa_workspace_bytes(const recsa_tree* tree, int32_t Hq, int64_t n_queries);
 
-/* Tree Construction (Eq. 1, Eq. 5): (re)compute every complete node, at every
- * level >= 1, whose last token lies in [tok_begin, tok_end).  Level-0 rows
- * [0, tok_end) must already be written.  Nodes are computed level by level,
- * each from the stored (rounded) children.  0 <= tok_begin <= tok_end <= L_cap. */
+/* Tree Construction (Eq. 1, Eq. 5): write the rotated keys Kr[0] of the
+ * level-0 rows [tok_begin, tok_end), then (re)compute every complete node, at
+ * every level >= 1, whose last token lies in [tok_begin, tok_end), with its
+ * rotated key.  Level-0 rows [0, tok_end) must already be written.  Nodes are
+ * computed level by level, each from the stored (rounded) children.
+ * 0 <= tok_begin <= tok_end <= L_cap. */
 int recsa_build_tree(const recsa_tree* tree, const recsa_pooler* pooler,
                      int64_t tok_begin, int64_t tok_end, void* stream);
 
 /* Decode append: for each sequence b write k_new/v_new [B][Hkv][d] as level-0
- * row t = pos_dev[b] (device int64 [B]) and complete every node whose last
- * token is t (levels l with (t+1) mod C^l == 0).  Precondition (device side,
+ * row t = pos_dev[b] (device int64 [B]), with its rotated key, and complete
+ * every node whose last token is t (levels l with (t+1) mod C^l == 0).  Precondition (device side,
  * not checked): 0 <= t < L_cap and rows [0, t) are in the tree. */
 int recsa_append_decode(const recsa_tree* tree, const recsa_pooler* pooler,
                         const void* k_new, const void* v_new,

@@ -45,7 +45,24 @@ __global__ void __launch_bounds__(kBlock) build_level_kernel(recsa_tree tr, recs
   const T* vc = static_cast<const T*>(tr.V[level - 1]) + (head * rows_up + first * kC) * D;
   T* ko = static_cast<T*>(tr.K[level]) + (head * rows + first) * D;
   T* vo = static_cast<T*>(tr.V[level]) + (head * rows + first) * D;
-  pool_tile<DT, D, NODES, kBlock>(kc, vc, ko, vo, n_valid, P, sm);
+  T* kro = static_cast<T*>(tr.Kr[level]) + (head * rows + first) * D;
+  pool_tile<DT, D, NODES, kBlock>(kc, vc, ko, vo, kro, static_cast<int>(first % kC), tr.rope,
+                                  n_valid, P, sm);
+}
+
+// Rotated keys Kr[0] of the level-0 rows [tb, te): one row per wave, one
+// pair per lane (D/2 <= 64), 4 rows per workgroup.
+template <int DT, int D>
+__global__ void __launch_bounds__(kBlock) rotate_level0_kernel(recsa_tree tr, int64_t tb,
+                                                               int64_t te) {
+  using T = typename Stor<DT>::T;
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const int64_t t = tb + static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + wid;
+  if (t >= te) return;
+  const int64_t head = static_cast<int64_t>(blockIdx.z) * tr.Hkv + blockIdx.y;
+  const int64_t off = (head * tr.L_cap + t) * D;
+  rotate_key_row<DT, D>(static_cast<const T*>(tr.K[0]) + off, static_cast<T*>(tr.Kr[0]) + off,
+                        static_cast<int>(t % kC), tr.rope, lane, kWave);
 }
 
 // Decode append: write row t, then complete each node whose last token is t.
@@ -67,6 +84,8 @@ __global__ void __launch_bounds__(kBlock) append_kernel(recsa_tree tr, recsa_poo
       kd[i] = ks[i];
       vd[i] = vs[i];
     }
+    rotate_key_row<DT, D>(ks, static_cast<T*>(tr.Kr[0]) + (head * tr.L_cap + t) * D,
+                          static_cast<int>(t % kC), tr.rope, threadIdx.x, kBlock);
   }
   int64_t span = 1;
   for (int l = 1; l < tr.n_levels; ++l) {
@@ -81,7 +100,9 @@ __global__ void __launch_bounds__(kBlock) append_kernel(recsa_tree tr, recsa_poo
     const T* vc = static_cast<const T*>(tr.V[l - 1]) + (head * rows_up + node * kC) * D;
     T* ko = static_cast<T*>(tr.K[l]) + (head * rows + node) * D;
     T* vo = static_cast<T*>(tr.V[l]) + (head * rows + node) * D;
-    pool_tile<DT, D, 1, kBlock>(kc, vc, ko, vo, 1, P, sm);
+    T* kro = static_cast<T*>(tr.Kr[l]) + (head * rows + node) * D;
+    pool_tile<DT, D, 1, kBlock>(kc, vc, ko, vo, kro, static_cast<int>(node % kC), tr.rope, 1, P,
+                                sm);
     __syncthreads();
   }
 }
@@ -97,6 +118,13 @@ hipError_t launch_rope_table(float* table, int d, int n_pos, double theta, hipSt
 template <int DT, int D>
 static hipError_t build_impl(const recsa_tree& tr, const recsa_pooler& P, int64_t tb, int64_t te,
                              hipStream_t s) {
+  {
+    constexpr int RPB = kBlock / kWave;
+    dim3 grid(static_cast<unsigned>((te - tb + RPB - 1) / RPB), tr.Hkv, tr.B);
+    rotate_level0_kernel<DT, D><<<grid, kBlock, 0, s>>>(tr, tb, te);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   int64_t span = 1;
   for (int l = 1; l < tr.n_levels; ++l) {
     span *= kC;

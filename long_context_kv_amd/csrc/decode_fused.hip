@@ -114,6 +114,8 @@ __global__ void __launch_bounds__(kFusedThreads)
       kd[i] = k_t[i];
       vd[i] = v_t[i];
     }
+    rotate_key_row<DT, D>(k_t, static_cast<T*>(tr.Kr[0]) + (slot * tr.L_cap + t) * D,
+                          static_cast<int>(t % kC), tr.rope, tid, NT);
     int64_t span = 1;
     for (int l = 1; l < tr.n_levels; ++l) {
       span *= kC;
@@ -126,7 +128,9 @@ __global__ void __launch_bounds__(kFusedThreads)
       pool_tile<DT, D, 1, NT>(static_cast<const T*>(tr.K[l - 1]) + (slot * rows_up + node * kC) * D,
                               static_cast<const T*>(tr.V[l - 1]) + (slot * rows_up + node * kC) * D,
                               static_cast<T*>(tr.K[l]) + (slot * rows + node) * D,
-                              static_cast<T*>(tr.V[l]) + (slot * rows + node) * D, 1, P, sm.pl);
+                              static_cast<T*>(tr.V[l]) + (slot * rows + node) * D,
+                              static_cast<T*>(tr.Kr[l]) + (slot * rows + node) * D,
+                              static_cast<int>(node % kC), tr.rope, 1, P, sm.pl);
       __syncthreads();
     }
     if (top >= 1) {                    // the top list [0 .. a_top] is fully selected
@@ -152,7 +156,7 @@ __global__ void __launch_bounds__(kFusedThreads)
       for (int gi = w + W * wid; gi < ng; gi += W * NW) {
         const int p0 = gi * kC;
         const int nvalid = min(kC, n - p0);
-        const T* rows = static_cast<const T*>(tr.K[l]) + (slot * rows_l + lv.node(p0)) * D;
+        const T* rows = static_cast<const T*>(tr.Kr[l]) + (slot * rows_l + lv.node(p0)) * D;
         KRows<DT, D> kr;                 // key rows in flight during the rotation
         group_load_k<DT, D>(rows, 0, nvalid, kr);
         rotate_query<DT, D, G>(qs, sm.at.qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);

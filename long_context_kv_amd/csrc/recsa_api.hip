@@ -26,7 +26,7 @@ bool tree_ok(const recsa_tree* t, int* why) {
   if (t->n_levels < recsa_levels_needed(t->L_cap, t->C, t->k)) return false;
   if (!t->rope) return false;
   for (int l = 0; l < t->n_levels; ++l) {
-    if (level_rows_host(t->L_cap, l) > 0 && (!t->K[l] || !t->V[l])) return false;
+    if (level_rows_host(t->L_cap, l) > 0 && (!t->K[l] || !t->V[l] || !t->Kr[l])) return false;
   }
   return true;
 }

@@ -111,6 +111,25 @@ __device__ __forceinline__ void rope_pair(float x, float y, float c, float s,
   yo = xs + yc;
 }
 
+// Key half of the split RoPE for one stored row: the pairs (j, j + D/2) of
+// `src`, rotated by the in-group offset c and rounded to the storage dtype,
+// written to `dst`.  Pairs j0, j0 + jstep, ... are handled by the caller's
+// thread.
+template <int DT, int D>
+__device__ __forceinline__ void rotate_key_row(const typename Stor<DT>::T* src,
+                                               typename Stor<DT>::T* dst, int c,
+                                               const float* __restrict__ rope, int j0,
+                                               int jstep) {
+  constexpr int H2 = D / 2;
+  for (int j = j0; j < H2; j += jstep) {
+    const float* rp = rope + (c * H2 + j) * 2;
+    float xo, yo;
+    rope_pair(Stor<DT>::load(src + j), Stor<DT>::load(src + j + H2), rp[0], rp[1], xo, yo);
+    Stor<DT>::store(dst + j, xo);
+    Stor<DT>::store(dst + j + H2, yo);
+  }
+}
+
 // ------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

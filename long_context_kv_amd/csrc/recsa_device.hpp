@@ -11,11 +11,13 @@ namespace recsa {
 // ------------------------------------------------------------------------
 // Logits of the 16 rows of one list group against G rotated query heads.
 // Lane = (row c = lane/4, quarter s = lane%4); each lane holds 2*E pairs of
-// its row (as raw storage words), rotates them by the in-group offset c (the
-// key half of the split RoPE), rounds them to the storage dtype and dots them
-// with the group's rotated query (LDS, float).  The four quarter lanes of a
-// row are summed, so every lane of row c ends with the G logits of that row.
-// Only rows in [row_lo, nvalid) are read; the others give 0.  Loading and
+// its row (as raw storage words) and dots them with the group's rotated
+// query (LDS, float).  The rows are normally the stored rotated keys Kr,
+// which already hold the key half of the split RoPE; with ROT the rows are
+// raw keys, rotated here by the in-group offset c and rounded to the storage
+// dtype (the same value Kr would hold).  The four quarter lanes of a row are
+// summed, so every lane of row c ends with the G logits of that row.  Only
+// rows in [row_lo, nvalid) are read; the others give 0.  Loading and
 // computing are separate steps so a caller can issue the loads early.
 template <int DT, int D>
 struct KRows {
@@ -61,7 +63,7 @@ __device__ __forceinline__ void group_load_k(const typename Stor<DT>::T* __restr
   }
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool ROT = false>
 __device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int row_lo, int nvalid,
                                                   const float* qt, const float* __restrict__ rope,
                                                   float* lg) {
@@ -89,10 +91,12 @@ __device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int ro
           x = __uint_as_float(kr.xr[hh][m]);
           y = __uint_as_float(kr.yr[hh][m]);
         }
-        float xo, yo;
-        rope_pair(x, y, rp[2 * m], rp[2 * m + 1], xo, yo);
-        xo = Stor<DT>::round(xo);
-        yo = Stor<DT>::round(yo);
+        float xo = x, yo = y;
+        if constexpr (ROT) {
+          rope_pair(x, y, rp[2 * m], rp[2 * m + 1], xo, yo);
+          xo = Stor<DT>::round(xo);
+          yo = Stor<DT>::round(yo);
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g)
           acc[g] += qt[g * D + base + m] * xo + qt[g * D + H2 + base + m] * yo;
@@ -107,15 +111,6 @@ __device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int ro
     v += __shfl_xor(v, 2, kWave);
     lg[g] = v * scale;
   }
-}
-
-template <int DT, int D, int G>
-__device__ __forceinline__ void group_logits(const typename Stor<DT>::T* __restrict__ rows,
-                                             int row_lo, int nvalid, const float* qt,
-                                             const float* __restrict__ rope, float* lg) {
-  KRows<DT, D> kr;
-  group_load_k<DT, D>(rows, row_lo, nvalid, kr);
-  group_logits_from<DT, D, G>(kr, row_lo, nvalid, qt, rope, lg);
 }
 
 // Rotate the G query heads by phi and round (one wave): qt = rnd(R(phi) q),
@@ -619,7 +614,7 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
     float lgv[G];
     if (level == 0) {
       const int p_q = lv.len - 1;
-      const T* krows = static_cast<const T*>(tr.K[0]) + (seq_head * rows_l + node0) * D;
+      const T* krows = static_cast<const T*>(tr.Kr[0]) + (seq_head * rows_l + node0) * D;
       const bool split = ovr >= 0 && ovr < kC;
       // key rows first (in flight during the rotation), then the query turn
       KRows<DT, D> ka, kb;
@@ -631,7 +626,8 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
       if (split) {
         float a[G], b[G];
         group_logits_from<DT, D, G>(ka, 0, ovr, sm.qt[wid], tr.rope, a);
-        group_logits_from<DT, D, G>(kb, ovr, ovr + 1, sm.qt[wid], tr.rope, b);
+        // row t is not in Kr yet (appended in the same launch): rotate it here
+        group_logits_from<DT, D, G, true>(kb, ovr, ovr + 1, sm.qt[wid], tr.rope, b);
 #pragma unroll
         for (int g = 0; g < G; ++g) lgv[g] = (c == ovr) ? b[g] : a[g];
       } else {

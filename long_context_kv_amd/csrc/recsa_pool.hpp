@@ -13,6 +13,7 @@ namespace recsa {
 // Phase 1 (one wave per node): children statistics, alpha, p, value mean.
 // Phase 2/3 (all threads): the pooler MLP for the tile, weights streamed
 // from L2 once per tile.  Phase 4: K = mu + g (p - mu) + sigma m.
+// Phase 5: the rotated key rnd(R(c) K) of each node, c = node index mod C.
 template <int DT, int D, int NODES>
 struct PoolSmem {
   float feat[NODES][2 * D];
@@ -25,6 +26,9 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
                           const typename Stor<DT>::T* __restrict__ vc,  // child V rows
                           typename Stor<DT>::T* __restrict__ ko,        // node K rows
                           typename Stor<DT>::T* __restrict__ vo,        // node V rows
+                          typename Stor<DT>::T* __restrict__ kro,       // rotated node K rows
+                          int c0,                   // index mod C of the tile's first node
+                          const float* __restrict__ rope,
                           int n_valid, const recsa_pooler& P,
                           PoolSmem<DT, D, NODES>& sm) {
   using T = typename Stor<DT>::T;
@@ -200,7 +204,22 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
       const float kv = mu_r[nw][u] + P.g * (p_r[nw][u] - mu_r[nw][u]) +
                        sig_r[nw] * sm.m[n][i0 + u];
       Stor<DT>::store(ko + static_cast<int64_t>(n) * D + i0 + u, kv);
+      sm.feat[n][i0 + u] = Stor<DT>::round(kv);      // the stored value, for phase 5
     }
+  }
+  __syncthreads();
+
+  // ---- phase 5: rotated keys from the stored (rounded) node keys
+  constexpr int H2 = D / 2;
+  for (int item = threadIdx.x; item < NODES * H2; item += NT) {
+    const int n = item / H2, jj = item % H2;
+    if (n >= n_valid) continue;
+    const int c = (c0 + n) % kC;
+    const float* rp = rope + (c * H2 + jj) * 2;
+    float xo, yo;
+    rope_pair(sm.feat[n][jj], sm.feat[n][jj + H2], rp[0], rp[1], xo, yo);
+    Stor<DT>::store(kro + static_cast<int64_t>(n) * D + jj, xo);
+    Stor<DT>::store(kro + static_cast<int64_t>(n) * D + jj + H2, yo);
   }
 }
 

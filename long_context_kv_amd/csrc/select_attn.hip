@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(kBlock)
   const int p_q = lv.len - 1;
   const int nvalid = min(kC, n_others - p0);
   const int64_t rows_l = level_rows_dev(tr.L_cap, level);
-  const T_* rows = static_cast<const T_*>(tr.K[level]) + (qc.seq_head * rows_l + lv.node(p0)) * D;
+  const T_* rows = static_cast<const T_*>(tr.Kr[level]) + (qc.seq_head * rows_l + lv.node(p0)) * D;
   KRows<DT, D> kr;                       // key rows in flight during the rotation
   group_load_k<DT, D>(rows, 0, nvalid, kr);
   rotate_query<DT, D, G>(qs, qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);

@@ -48,6 +48,7 @@ class TreeC(ctypes.Structure):
         ("L_cap", ctypes.c_int64),
         ("K", ctypes.c_void_p * RECSA_MAX_LEVELS),
         ("V", ctypes.c_void_p * RECSA_MAX_LEVELS),
+        ("Kr", ctypes.c_void_p * RECSA_MAX_LEVELS),
         ("rope", ctypes.c_void_p),
     ]
 
@@ -123,7 +124,9 @@ class Tree:
     """One layer's KV tree in device memory (torch tensors) plus its C view.
 
     K[l], V[l]: [B, Hkv, floor(L_cap / 16^l), d] in the storage dtype; level 0
-    is the KV cache itself (pre-RoPE keys).  rope: [C*k, d/2, 2] float32."""
+    is the KV cache itself (pre-RoPE keys).  Kr[l]: the same shape, the rotated
+    keys the library writes next to every key row.  rope: [C*k, d/2, 2]
+    float32."""
     B: int
     Hkv: int
     d: int
@@ -134,6 +137,7 @@ class Tree:
     n_levels: int
     K: list
     V: list
+    Kr: list
     rope: torch.Tensor
 
     @staticmethod
@@ -141,9 +145,10 @@ class Tree:
                  device="cuda", theta=1e6, level0=None):
         n = n_levels or max(2, recsa_levels_needed(L_cap, C, k))
         tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-        K, V = [], []
+        K, V, Kr = [], [], []
         for lvl in range(n):
             rows = recsa_level_rows(L_cap, C, lvl)
+            Kr.append(torch.zeros((B, Hkv, rows, d), dtype=tdt, device=device))
             if lvl == 0 and level0 is not None:
                 K.append(level0[0])
                 V.append(level0[1])
@@ -152,7 +157,7 @@ class Tree:
             V.append(torch.zeros((B, Hkv, rows, d), dtype=tdt, device=device))
         rope = torch.empty((C * k, d // 2, 2), dtype=torch.float32, device=device)
         recsa_init_rope(rope, d, C * k, theta)
-        return Tree(B, Hkv, d, L_cap, k, C, dtype, n, K, V, rope)
+        return Tree(B, Hkv, d, L_cap, k, C, dtype, n, K, V, Kr, rope)
 
     def c(self) -> TreeC:
         t = TreeC()
@@ -162,6 +167,7 @@ class Tree:
         for lvl in range(self.n_levels):
             t.K[lvl] = self.K[lvl].data_ptr() if self.K[lvl].numel() else None
             t.V[lvl] = self.V[lvl].data_ptr() if self.V[lvl].numel() else None
+            t.Kr[lvl] = self.Kr[lvl].data_ptr() if self.Kr[lvl].numel() else None
         t.rope = self.rope.data_ptr()
         return t
 

@@ -51,6 +51,7 @@ def _tree(**over):
     for lvl in range(4):
         t.K[lvl] = 0x1000 * (lvl + 1)       # never dereferenced: validation fails first
         t.V[lvl] = 0x2000 * (lvl + 1)
+        t.Kr[lvl] = 0x5000 * (lvl + 1)
     t.rope = 0x3000
     for k, v in over.items():
         setattr(t, k, v)
@@ -91,6 +92,9 @@ def test_call_validation_without_launch():
     assert L.recsa_build_tree(b(t), b(p), 0, t.L_cap + 1, None) == R.RECSA_E_INVALID
     assert L.recsa_build_tree(b(t), b(p), 10, 5, None) == R.RECSA_E_INVALID
     assert L.recsa_build_tree(b(t), b(p), 7, 7, None) == R.RECSA_OK          # empty range
+    t_nokr = _tree()
+    t_nokr.Kr[1] = None
+    assert L.recsa_build_tree(b(t_nokr), b(p), 0, 16, None) == R.RECSA_E_INVALID
     assert L.recsa_build_tree(b(t), b(_pooler(d=64)), 0, 16, None) == R.RECSA_E_INVALID
     assert L.recsa_build_tree(b(t), b(_pooler(hidden=100)), 0, 16, None) == R.RECSA_E_INVALID
     assert L.recsa_build_tree(b(t), b(_pooler(eps=-1.0)), 0, 16, None) == R.RECSA_E_INVALID

@@ -91,6 +91,28 @@ def test_build_tree_matches_oracle(dtype, d):
                 assert (dk > 0).mean() < (2e-3 if lvl == 1 else 5e-2), (lvl, (dk > 0).mean())
                 dv = np.abs(gv - V[lvl]) / PY.ulp_bf16(V[lvl])
                 assert dv.max() <= 1.0 and (dv > 0).mean() < 1e-3, lvl
+    _check_rotated_keys(tree, [(0, j) for j in range(2)], L)
+
+
+def _check_rotated_keys(tree, heads, n_tokens):
+    """Kr[l][i] must be the key half of the split RoPE of the stored key row,
+    rnd(R(i mod 16) K[l][i]), evaluated as the oracle evaluates it (float32
+    rotation, rounded to the storage dtype).  Equal except where the two
+    RoPE tables differ in a float32 ulp (rare), and then by at most one ulp."""
+    cos, sin = O.rope_table(tree.d, tree.C * tree.k, 1e6)
+    for b, j in heads:
+        for lvl in range(tree.n_levels):
+            n = n_tokens // 16 ** lvl
+            if n == 0:
+                continue
+            K = PY.to64(tree.K[lvl][b, j, :n])
+            c = np.arange(n) % 16
+            want = O.rnd(O.rotate_f32(K, cos[c], sin[c]).astype(np.float64), tree.dtype)
+            got = PY.to64(tree.Kr[lvl][b, j, :n])
+            diff = np.abs(got - want)
+            ulp = PY.ulp_bf16(want) if tree.dtype == "bf16" else np.abs(want) * 2.0 ** -23 + 1e-38
+            assert np.all(diff <= ulp), (lvl, float((diff / ulp).max()))
+            assert (diff > 0).mean() < 1e-3, (lvl, (diff > 0).mean())
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
@@ -116,6 +138,7 @@ def test_append_equals_build(dtype, d):
     for lvl in range(tree.n_levels):
         assert torch.equal(tree.K[lvl], ref.K[lvl]), lvl
         assert torch.equal(tree.V[lvl], ref.V[lvl]), lvl
+        assert torch.equal(tree.Kr[lvl], ref.Kr[lvl]), lvl
 
 
 def _run_select_attn(tree, q, Hq, pos, decode):
@@ -311,6 +334,7 @@ def test_fused_decode_matches_separate_calls(dtype, d, Hkv, G, B):
         assert np.allclose(o, o2, rtol=0, atol=1e-5 * np.abs(o2).max()), t
     for lvl in range(tree.n_levels):
         assert torch.equal(tree.K[lvl], ref.K[lvl]) and torch.equal(tree.V[lvl], ref.V[lvl]), lvl
+        assert torch.equal(tree.Kr[lvl], ref.Kr[lvl]), lvl
     # control block: every arrival flag back at zero, no error word set
     assert torch.count_nonzero(R.decode_control_words(ws, tree, Hq).cpu()) == 0
 
