@@ -533,7 +533,7 @@ __device__ __forceinline__ EntryGroups entry_groups(int64_t t, const recsa_tree&
 template <int D, int G, int NT>
 struct AttnSmem {
   float qt[NT / kWave][G * D];
-  float pw[NT / kWave][G][kC];
+  float ew[NT / kWave][kWave][G];  // a chunk's per-entry logits, then its weights
   float wm[NT / kWave][G];
   float wl[NT / kWave][G];
   float wacc[NT / kWave][G][D];
@@ -544,23 +544,45 @@ struct AttnSmem {
 template <int G, int DPL>
 struct SoftState {
   float m[G], l[G], acc[G][DPL];
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m[g] = -INFINITY;
-      l[g] = 0.f;
-#pragma unroll
-      for (int u = 0; u < DPL; ++u) acc[g][u] = 0.f;
-    }
-  }
 };
 
-// Process entry groups g_lo, g_lo + g_step, ... of one (query, KV head) with
-// the whole workgroup (its waves take every NW-th of those; no block barrier
-// inside the loop), then merge the waves: on return sm.wm[0], sm.wl[0], sm.wacc[0] hold
-// the workgroup's softmax state (valid after the trailing __syncthreads).
-// Value rows of a group are issued before its logits are computed.  If
-// k_t/v_t are given they replace the tree rows of token t (decode append).
+// A wave processes its entries in chunks of NG 16-entry groups, one entry
+// per lane for the softmax.  Each lane keeps the value words of its DPL
+// dims for every entry of the chunk; fp32 rows at d = 128 need two words
+// per entry, so those chunks hold two groups instead of four.
+template <int DT, int D>
+struct ChunkShape {
+  static constexpr int DPL = D / kWave;                    // dims per lane
+  static constexpr int VW = (DT == RECSA_BF16) ? 1 : DPL;  // value words per entry and lane
+  static constexpr int NG = VW == 2 ? 2 : 4;               // groups per chunk
+  static constexpr int NE = NG * kC;                       // entries per chunk
+};
+
+// Per-level array entry with a per-lane level (unrolled selects: no
+// dynamic indexing of the argument struct).
+__device__ __forceinline__ const void* level_ptr(void* const (&arr)[RECSA_MAX_LEVELS], int level) {
+  const void* r = arr[0];
+#pragma unroll
+  for (int l = 1; l < RECSA_MAX_LEVELS; ++l)
+    if (level == l) r = arr[l];
+  return r;
+}
+
+__device__ __forceinline__ const void* lane_ptr(const void* p, int src_lane) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(a), src_lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(a >> 32), src_lane);
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Process the entry chunks g_lo, g_lo + g_step, ... of one (query, KV head)
+// with the whole workgroup (its waves take every NW-th of those; no block
+// barrier inside the loop), then merge the waves: on return sm.res_m,
+// sm.res_l and sm.wacc[0] hold the workgroup's softmax state (valid after
+// the trailing __syncthreads).  Per chunk the level-0 key rows are issued
+// first, then the value rows, so both are in flight during the query
+// rotations.  If k_t/v_t are given they replace the tree rows of token t
+// (decode append in the same launch).
 template <int DT, int D, int G, int NT>
 __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, const int32_t* sel,
                             const int32_t* cnt, const EntryGroups& eg, int g_lo, int g_step,
@@ -569,118 +591,180 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
                             const typename Stor<DT>::T* k_t, const typename Stor<DT>::T* v_t,
                             AttnSmem<D, G, NT>& sm) {
   using T = typename Stor<DT>::T;
-  constexpr int DPL = D / kWave;
+  using CS = ChunkShape<DT, D>;
+  constexpr int DPL = CS::DPL, VW = CS::VW, NG = CS::NG, NE = CS::NE;
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
   const int c = lane >> 2, s = lane & 3;
   const int top = tr.n_levels - 1;
-  SoftState<G, DPL> st;
-  st.init();
-  const int g_hi = eg.total();
-#pragma unroll 1
-  for (int gi = g_lo + wid * g_step; gi < g_hi; gi += NW * g_step) {
-    int level, local;
-    eg.locate(gi, level, local);
-    const int p0 = local * kC;
-    const ListView lv = list_view(t, level, top, tr.k, sel, cnt);
-    const int n_pos = level == 0 ? lv.len : lv.len - 1;
-    const int nvalid = min(kC, n_pos - p0);
-    const int64_t rows_l = level_rows_dev(tr.L_cap, level);
-    const int64_t node0 = lv.node(p0);
-    // token t (the query itself) is the last level-0 position
-    const int ovr = (level == 0 && k_t) ? static_cast<int>(lv.len - 1 - p0) : -1;
-    // ---- value rows (lanes own dims), issued first, kept as raw words
-    constexpr int VW = DT == RECSA_BF16 ? (DPL + 1) / 2 : DPL;   // words per lane per row
-    const T* vrows = static_cast<const T*>(tr.V[level]) + (seq_head * rows_l + node0) * D + lane * DPL;
-    uint32_t vraw[kC][VW];
+  const int bm_words = (CK + 31) / 32;
+  float m[G], lsum[G], acc[G][DPL];
 #pragma unroll
-    for (int r = 0; r < kC; ++r) {
-      const T* vr = (r == ovr) ? v_t + lane * DPL : vrows + static_cast<int64_t>(r) * D;
-      if (r < nvalid) {
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    lsum[g] = 0.f;
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) acc[g][u] = 0.f;
+  }
+  const int n_groups = eg.total();
+  const int n_chunks = (n_groups + NG - 1) / NG;
+#pragma unroll 1
+  for (int ci = g_lo + wid * g_step; ci < n_chunks; ci += NW * g_step) {
+    // ---- this lane's entry: row lane % 16 of group ci*NG + lane / 16
+    const int gi = ci * NG + lane / kC;
+    const bool in_group = lane < NE && gi < n_groups;
+    int level = 0, local = 0;
+    if (in_group) eg.locate(gi, level, local);
+    const ListView lv = list_view(t, level, top, tr.k, sel, cnt);
+    const int p = local * kC + (lane % kC);
+    const int n_pos = level == 0 ? lv.len : lv.len - 1;
+    const bool valid = in_group && p < n_pos;
+    const int64_t rows_l = level_rows_dev(tr.L_cap, level);
+    const int64_t node = valid ? lv.node(p) : 0;
+    const bool own = valid && level == 0 && k_t != nullptr && p == lv.len - 1;
+    const T* vrow = own ? v_t
+                        : static_cast<const T*>(level_ptr(tr.V, level)) + (seq_head * rows_l + node) * D;
+    // per group (read from the group's first lane): level-0 groups get logits here
+    const int grp_nvalid = in_group ? min(kC, n_pos - local * kC) : 0;
+
+    // ---- level-0 key rows of the chunk's groups
+    KRows<DT, D> ka[NG];
+    bool is0[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      const int lead = gg * kC;
+      is0[gg] = __builtin_amdgcn_readlane(static_cast<int>(in_group && level == 0), lead) != 0;
+      if (is0[gg]) {
+        const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
+        const int len = __builtin_amdgcn_readlane(lv.len, lead);
+        const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
+        const T* krow0 = static_cast<const T*>(lane_ptr(static_cast<const T*>(tr.Kr[0]) +
+                                                            (seq_head * rows_l + node) * D, lead));
+        const int ovr = k_t ? len - 1 - p0 : -1;          // row of token t, if in this group
+        group_load_k<DT, D>(krow0, 0, (ovr >= 0 && ovr < kC) ? ovr : nv, ka[gg]);
+      }
+    }
+    // ---- value rows of every entry (uniform loop; entries broadcast by lane)
+    uint32_t vraw[NE][VW];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const bool ve = __builtin_amdgcn_readlane(static_cast<int>(valid), e) != 0;
+      const T* vr = static_cast<const T*>(lane_ptr(vrow, e)) + lane * DPL;
+      if (ve) {
         if constexpr (DT == RECSA_BF16 && DPL == 2) {
-          vraw[r][0] = *reinterpret_cast<const uint32_t*>(vr);
+          vraw[e][0] = *reinterpret_cast<const uint32_t*>(vr);
         } else if constexpr (DT == RECSA_BF16) {
-          vraw[r][0] = static_cast<uint32_t>(*vr) << 16;
+          vraw[e][0] = static_cast<uint32_t>(*vr) << 16;
         } else {
 #pragma unroll
-          for (int u = 0; u < DPL; ++u) vraw[r][u] = __float_as_uint(vr[u]);
+          for (int u = 0; u < DPL; ++u) vraw[e][u] = __float_as_uint(vr[u]);
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < VW; ++u) vraw[r][u] = 0u;
+        for (int u = 0; u < VW; ++u) vraw[e][u] = 0u;
       }
     }
-    // ---- logits of the 16 rows (lane layout: row c, quarter s)
-    float lgv[G];
-    if (level == 0) {
-      const int p_q = lv.len - 1;
-      const T* krows = static_cast<const T*>(tr.Kr[0]) + (seq_head * rows_l + node0) * D;
+    // ---- summary logits (levels >= 1: from scoring, minus the selected ones)
+    float lg[G];
+    {
+      bool ent = false;
+      if (valid && level >= 1) {
+        const uint32_t word = bm_slot[(level - 1) * bm_words + (p >> 5)];
+        ent = ((word >> (p & 31)) & 1u) == 0u;
+      }
+      const float* src = lg_slot + static_cast<int64_t>(level - 1) * G * CK + p;
+#pragma unroll
+      for (int g = 0; g < G; ++g) lg[g] = ent ? src[static_cast<int64_t>(g) * CK] : -INFINITY;
+    }
+    // ---- level-0 logits: split RoPE, one query rotation per group
+    bool any0 = false;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      if (!is0[gg]) continue;
+      any0 = true;
+      const int lead = gg * kC;
+      const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
+      const int len = __builtin_amdgcn_readlane(lv.len, lead);
+      const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
+      const int p_q = len - 1;
+      const int ovr = k_t ? len - 1 - p0 : -1;
       const bool split = ovr >= 0 && ovr < kC;
-      // key rows first (in flight during the rotation), then the query turn
-      KRows<DT, D> ka, kb;
-      group_load_k<DT, D>(krows, 0, split ? ovr : nvalid, ka);
-      // only row ovr is read from this base, i.e. exactly k_t
-      if (split) group_load_k<DT, D>(k_t - static_cast<int64_t>(ovr) * D, ovr, ovr + 1, kb);
       rotate_query<DT, D, G>(qs, sm.qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
       wave_sync();
+      float lgv[G];
       if (split) {
-        float a[G], b[G];
-        group_logits_from<DT, D, G>(ka, 0, ovr, sm.qt[wid], tr.rope, a);
         // row t is not in Kr yet (appended in the same launch): rotate it here
+        KRows<DT, D> kb;
+        group_load_k<DT, D>(k_t - static_cast<int64_t>(ovr) * D, ovr, ovr + 1, kb);
+        float a[G], b[G];
+        group_logits_from<DT, D, G>(ka[gg], 0, ovr, sm.qt[wid], tr.rope, a);
         group_logits_from<DT, D, G, true>(kb, ovr, ovr + 1, sm.qt[wid], tr.rope, b);
 #pragma unroll
         for (int g = 0; g < G; ++g) lgv[g] = (c == ovr) ? b[g] : a[g];
       } else {
-        group_logits_from<DT, D, G>(ka, 0, nvalid, sm.qt[wid], tr.rope, lgv);
+        group_logits_from<DT, D, G>(ka[gg], 0, nv, sm.qt[wid], tr.rope, lgv);
       }
+      if (s == 0) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) if (c >= nvalid) lgv[g] = -INFINITY;
-    } else {
-      const uint32_t word = bm_slot[(level - 1) * ((CK + 31) / 32) + (p0 >> 5)];
-      const bool ent = c < nvalid && !((word >> ((p0 & 31) + c)) & 1u);
-      const float* src = lg_slot + static_cast<int64_t>(level - 1) * G * CK + p0 + c;
-#pragma unroll
-      for (int g = 0; g < G; ++g) lgv[g] = ent ? src[static_cast<int64_t>(g) * CK] : -INFINITY;
+        for (int g = 0; g < G; ++g) sm.ew[wid][lead + c][g] = (c < nv) ? lgv[g] : -INFINITY;
+      }
+      wave_sync();
     }
-    // ---- online softmax update (rows are replicated over the 4 quarter lanes)
+    if (any0 && valid && level == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) lg[g] = sm.ew[wid][lane][g];
+    }
+    wave_sync();
+    // ---- online softmax over the chunk (entry per lane); sums stay per lane
+    float pr[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float mx = wave_max(lgv[g]);
-      const float mnew = fmaxf(st.m[g], mx);
+      const float mnew = fmaxf(m[g], wave_max(lg[g]));
       if (mnew == -INFINITY) {
-        if (s == 0) sm.pw[wid][g][c] = 0.f;
+        pr[g] = 0.f;
         continue;
       }
-      const float pr = (lgv[g] == -INFINITY) ? 0.f : __expf(lgv[g] - mnew);
-      const float rs = wave_sum(s == 0 ? pr : 0.f);
-      const float sc = (st.m[g] == -INFINITY) ? 0.f : __expf(st.m[g] - mnew);
-      st.l[g] = st.l[g] * sc + rs;
-      st.m[g] = mnew;
+      const float sc = (m[g] == -INFINITY) ? 0.f : __expf(m[g] - mnew);
+      pr[g] = (lg[g] == -INFINITY) ? 0.f : __expf(lg[g] - mnew);
+      lsum[g] = lsum[g] * sc + pr[g];
 #pragma unroll
-      for (int u = 0; u < DPL; ++u) st.acc[g][u] *= sc;
-      if (s == 0) sm.pw[wid][g][c] = pr;
+      for (int u = 0; u < DPL; ++u) acc[g][u] *= sc;
+      m[g] = mnew;
     }
-    wave_sync();
 #pragma unroll
-    for (int r = 0; r < kC; ++r) {
+    for (int g = 0; g < G; ++g) sm.ew[wid][lane][g] = pr[g];
+    wave_sync();
+    // ---- P V (every lane: its DPL dims, all entries)
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
       float v[DPL];
       if constexpr (DT == RECSA_BF16 && DPL == 2) {
-        v[0] = __uint_as_float(vraw[r][0] << 16);
-        v[1] = __uint_as_float(vraw[r][0] & 0xFFFF0000u);
+        v[0] = __uint_as_float(vraw[e][0] << 16);
+        v[1] = __uint_as_float(vraw[e][0] & 0xFFFF0000u);
       } else if constexpr (DT == RECSA_BF16) {
-        v[0] = __uint_as_float(vraw[r][0]);
+        v[0] = __uint_as_float(vraw[e][0]);
       } else {
 #pragma unroll
-        for (int u = 0; u < DPL; ++u) v[u] = __uint_as_float(vraw[r][u]);
+        for (int u = 0; u < DPL; ++u) v[u] = __uint_as_float(vraw[e][u]);
       }
+      float w[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) w[g] = sm.ew[wid][e][g];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float w = sm.pw[wid][g][r];
 #pragma unroll
-        for (int u = 0; u < DPL; ++u) st.acc[g][u] += w * v[u];
+        for (int u = 0; u < DPL; ++u) acc[g][u] += w[g] * v[u];
       }
     }
     wave_sync();
+  }
+  SoftState<G, DPL> st;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.m[g] = m[g];
+    st.l[g] = wave_sum(lsum[g]);
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) st.acc[g][u] = acc[g][u];
   }
   // ---- merge the waves
 #pragma unroll
