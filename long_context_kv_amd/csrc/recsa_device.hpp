@@ -19,6 +19,14 @@ namespace recsa {
 // summed, so every lane of row c ends with the G logits of that row.  Only
 // rows in [row_lo, nvalid) are read; the others give 0.  Loading and
 // computing are separate steps so a caller can issue the loads early.
+// Two-term bf16 dot product accumulated in float32: the operands are the
+// rounded (bf16) halves of the split RoPE, so every product is exact.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
 template <int DT, int D>
 struct KRows {
   static constexpr int E = D / 16;
@@ -80,26 +88,49 @@ __device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int ro
       __builtin_amdgcn_sched_barrier(0);
       const int base = hh * QD + s * E;
       const float* rp = rope + (c * H2 + base) * 2;
+      if constexpr (DT == RECSA_BF16) {
+        // packed words: dims (base + 2i, base + 2i + 1) of each half
+        constexpr int WPC = E / 2;
+        uint32_t kx[WPC], ky[WPC];
 #pragma unroll
-      for (int m = 0; m < E; ++m) {
-        float x, y;
-        if constexpr (DT == RECSA_BF16) {
-          const uint32_t wx = kr.xr[hh][m / 2], wy = kr.yr[hh][m / 2];
-          x = __uint_as_float((m & 1) ? (wx & 0xFFFF0000u) : (wx << 16));
-          y = __uint_as_float((m & 1) ? (wy & 0xFFFF0000u) : (wy << 16));
-        } else {
-          x = __uint_as_float(kr.xr[hh][m]);
-          y = __uint_as_float(kr.yr[hh][m]);
+        for (int i = 0; i < WPC; ++i) {
+          kx[i] = kr.xr[hh][i];
+          ky[i] = kr.yr[hh][i];
         }
-        float xo = x, yo = y;
         if constexpr (ROT) {
-          rope_pair(x, y, rp[2 * m], rp[2 * m + 1], xo, yo);
-          xo = Stor<DT>::round(xo);
-          yo = Stor<DT>::round(yo);
-        }
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-          acc[g] += qt[g * D + base + m] * xo + qt[g * D + H2 + base + m] * yo;
+          for (int i = 0; i < WPC; ++i) {
+            float x0, y0, x1, y1;
+            rope_pair(__uint_as_float(kx[i] << 16), __uint_as_float(ky[i] << 16), rp[4 * i],
+                      rp[4 * i + 1], x0, y0);
+            rope_pair(__uint_as_float(kx[i] & 0xFFFF0000u), __uint_as_float(ky[i] & 0xFFFF0000u),
+                      rp[4 * i + 2], rp[4 * i + 3], x1, y1);
+            kx[i] = f32_to_bf16_bits(x0) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
+            ky[i] = f32_to_bf16_bits(y0) | (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+          }
+        }
+        const uint32_t* qw = reinterpret_cast<const uint32_t*>(qt);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint32_t* qx = qw + g * (D / 2) + base / 2;
+          const uint32_t* qy = qw + g * (D / 2) + H2 / 2 + base / 2;
+#pragma unroll
+          for (int i = 0; i < WPC; ++i) {
+            acc[g] = dot2_bf16(kx[i], qx[i], acc[g]);
+            acc[g] = dot2_bf16(ky[i], qy[i], acc[g]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < E; ++m) {
+          const float x = __uint_as_float(kr.xr[hh][m]);
+          const float y = __uint_as_float(kr.yr[hh][m]);
+          float xo = x, yo = y;
+          if constexpr (ROT) rope_pair(x, y, rp[2 * m], rp[2 * m + 1], xo, yo);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            acc[g] += qt[g * D + base + m] * xo + qt[g * D + H2 + base + m] * yo;
+        }
       }
     }
   }
@@ -114,21 +145,38 @@ __device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int ro
 }
 
 // Rotate the G query heads by phi and round (one wave): qt = rnd(R(phi) q),
-// the query half of the split RoPE.
+// the query half of the split RoPE.  Layout of qt: float [G][D] for fp32
+// storage; for bf16 storage the rounded values are packed two per 32-bit
+// word, [G][D/2] words (dims 2i, 2i+1 in word i, low half first), ready for
+// the packed bf16 dot products.
 template <int DT, int D, int G>
 __device__ __forceinline__ void rotate_query(const float* qs, float* qt, int phi,
                                              const float* __restrict__ rope) {
   constexpr int H2 = D / 2;
   const int lane = threadIdx.x & (kWave - 1);
-  for (int idx = lane; idx < G * H2; idx += kWave) {
-    const int g = idx / H2, j = idx % H2;
-    const float* rp = rope + (static_cast<int64_t>(phi) * H2 + j) * 2;
-    float xo, yo;
-    rope_pair(qs[g * D + j], qs[g * D + j + H2], rp[0], rp[1], xo, yo);
-    qt[g * D + j] = Stor<DT>::round(xo);
-    qt[g * D + j + H2] = Stor<DT>::round(yo);
+  const float* rrow = rope + static_cast<int64_t>(phi) * H2 * 2;
+  if constexpr (DT == RECSA_BF16) {
+    uint32_t* qw = reinterpret_cast<uint32_t*>(qt);
+    for (int idx = lane; idx < G * H2 / 2; idx += kWave) {
+      const int g = idx / (H2 / 2), j = 2 * (idx % (H2 / 2));
+      float x0, y0, x1, y1;
+      rope_pair(qs[g * D + j], qs[g * D + j + H2], rrow[2 * j], rrow[2 * j + 1], x0, y0);
+      rope_pair(qs[g * D + j + 1], qs[g * D + j + 1 + H2], rrow[2 * j + 2], rrow[2 * j + 3], x1, y1);
+      qw[g * (D / 2) + j / 2] = f32_to_bf16_bits(x0) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
+      qw[g * (D / 2) + H2 / 2 + j / 2] =
+          f32_to_bf16_bits(y0) | (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+    }
+  } else {
+    for (int idx = lane; idx < G * H2; idx += kWave) {
+      const int g = idx / H2, j = idx % H2;
+      float xo, yo;
+      rope_pair(qs[g * D + j], qs[g * D + j + H2], rrow[2 * j], rrow[2 * j + 1], xo, yo);
+      qt[g * D + j] = xo;
+      qt[g * D + j + H2] = yo;
+    }
   }
 }
+
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
