@@ -669,9 +669,6 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
     const bool valid = in_group && p < n_pos;
     const int64_t rows_l = level_rows_dev(tr.L_cap, level);
     const int64_t node = valid ? lv.node(p) : 0;
-    const bool own = valid && level == 0 && k_t != nullptr && p == lv.len - 1;
-    const T* vrow = own ? v_t
-                        : static_cast<const T*>(level_ptr(tr.V, level)) + (seq_head * rows_l + node) * D;
     // per group (read from the group's first lane): level-0 groups get logits here
     const int grp_nvalid = in_group ? min(kC, n_pos - local * kC) : 0;
 
@@ -692,24 +689,38 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
         group_load_k<DT, D>(krow0, 0, (ovr >= 0 && ovr < kC) ? ovr : nv, ka[gg]);
       }
     }
-    // ---- value rows of every entry (uniform loop; entries broadcast by lane)
+    // ---- value rows of every entry: a group's entries are 16 consecutive
+    // rows (children of one parent), so one base address per group, read
+    // from the group's first lane; token t's row may come from v_t
     uint32_t vraw[NE][VW];
+    const T* vgrp = static_cast<const T*>(level_ptr(tr.V, level)) + (seq_head * rows_l + node) * D;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const bool ve = __builtin_amdgcn_readlane(static_cast<int>(valid), e) != 0;
-      const T* vr = static_cast<const T*>(lane_ptr(vrow, e)) + lane * DPL;
-      if (ve) {
-        if constexpr (DT == RECSA_BF16 && DPL == 2) {
-          vraw[e][0] = *reinterpret_cast<const uint32_t*>(vr);
-        } else if constexpr (DT == RECSA_BF16) {
-          vraw[e][0] = static_cast<uint32_t>(*vr) << 16;
+    for (int gg = 0; gg < NG; ++gg) {
+      const int lead = gg * kC;
+      const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
+      const bool g0 = __builtin_amdgcn_readlane(static_cast<int>(in_group && level == 0), lead) != 0;
+      const int len = __builtin_amdgcn_readlane(lv.len, lead);
+      const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
+      const int own_r = (g0 && k_t) ? len - 1 - p0 : -1;
+      const T* vb = static_cast<const T*>(lane_ptr(vgrp, lead)) + lane * DPL;
+#pragma unroll
+      for (int r = 0; r < kC; ++r) {
+        const int e = lead + r;
+        if (e >= NE) break;
+        const T* vr = (own_r == r) ? v_t + lane * DPL : vb + r * D;
+        if (r < nv) {
+          if constexpr (DT == RECSA_BF16 && DPL == 2) {
+            vraw[e][0] = *reinterpret_cast<const uint32_t*>(vr);
+          } else if constexpr (DT == RECSA_BF16) {
+            vraw[e][0] = static_cast<uint32_t>(*vr) << 16;
+          } else {
+#pragma unroll
+            for (int u = 0; u < DPL; ++u) vraw[e][u] = __float_as_uint(vr[u]);
+          }
         } else {
 #pragma unroll
-          for (int u = 0; u < DPL; ++u) vraw[e][u] = __float_as_uint(vr[u]);
+          for (int u = 0; u < VW; ++u) vraw[e][u] = 0u;
         }
-      } else {
-#pragma unroll
-        for (int u = 0; u < VW; ++u) vraw[e][u] = 0u;
       }
     }
     // ---- summary logits (levels >= 1: from scoring, minus the selected ones)
