@@ -98,6 +98,11 @@ __global__ void __launch_bounds__(kFusedThreads)
   int32_t* sel_q = sel + slot * n_sel * k;
   int32_t* cnt_q = cnt + slot * n_sel;
   float* lg_slot = ws_logits + slot * n_sel * static_cast<int64_t>(G) * CK;
+  // score-share softmax partials [level-1][W][G][2] sit in the partial slots
+  // this launch never uses for attention partials (slots kFusedMaxW and up)
+  float* stats = part + (slot * kPartSlots + kFusedMaxW) * static_cast<int64_t>(G) * (D + 2);
+  static_assert(RECSA_MAX_LEVELS * kFusedMaxW * 2 <= (kPartSlots - kFusedMaxW) * (64 + 2),
+                "softmax partials must fit the spare partial slots");
   uint32_t* ctl = ctl_words + slot * kCtlWords;
   uint32_t* err = ctl + 1;
   uint32_t* flags = ctl + 16;
@@ -153,6 +158,13 @@ __global__ void __launch_bounds__(kFusedThreads)
       const int64_t rows_l = level_rows_dev(tr.L_cap, l);
       const int p_q = lv.len - 1;
       float* out_l = lg_slot + static_cast<int64_t>(l - 1) * G * CK;
+      // running (max, sum of exp) of this lane's logits, per head
+      float st_m[G], st_z[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        st_m[g] = -INFINITY;
+        st_z[g] = 0.f;
+      }
       for (int gi = w + W * wid; gi < ng; gi += W * NW) {
         const int p0 = gi * kC;
         const int nvalid = min(kC, n - p0);
@@ -168,12 +180,51 @@ __global__ void __launch_bounds__(kFusedThreads)
 #pragma unroll
           for (int g = 0; g < G; ++g)
             if ((g & 3) == s) out_l[static_cast<int64_t>(g) * CK + p0 + c] = lg[g];
+          if (s == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const float mn = fmaxf(st_m[g], lg[g]);
+              st_z[g] = st_z[g] * __expf(st_m[g] - mn) + __expf(lg[g] - mn);
+              st_m[g] = mn;
+            }
+          }
         }
         wave_sync();
       }
+      // this workgroup's share: per-head (max, sum of exp) for the top-k
+      float* st_l = stats + static_cast<int64_t>(l - 1) * kFusedMaxW * G * 2;
+      {
+        float wm[G], wz[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          wm[g] = wave_max(st_m[g]);
+          wz[g] = wave_sum(st_m[g] == -INFINITY ? 0.f : st_z[g] * __expf(st_m[g] - wm[g]));
+        }
+        __syncthreads();                 // the scoring's LDS (union) is free now
+        if (lane == 0) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            sm.tk.redg[g][wid] = wm[g];
+            sm.tk.redz[g][wid] = wz[g];
+          }
+        }
+        __syncthreads();
+        if (tid < G) {
+          float mm = -INFINITY, zz = 0.f;
+#pragma unroll
+          for (int v = 0; v < NW; ++v) mm = fmaxf(mm, sm.tk.redg[tid][v]);
+#pragma unroll
+          for (int v = 0; v < NW; ++v) {
+            const float mv = sm.tk.redg[tid][v];
+            if (mv != -INFINITY) zz += sm.tk.redz[tid][v] * __expf(mv - mm);
+          }
+          st_l[(w * G + tid) * 2] = mm;
+          st_l[(w * G + tid) * 2 + 1] = zz;
+        }
+      }
       group_barrier(flags, w, W, ++gen, err, &s_fail);
       wg_topk<G, NT>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1), s_bm + (l - 1) * bm_words,
-                     nullptr, sm.tk);
+                     nullptr, sm.tk, st_l, W);
     }
     __syncthreads();
     if (w == 0) {                      // API outputs

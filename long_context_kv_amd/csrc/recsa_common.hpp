@@ -131,25 +131,64 @@ __device__ __forceinline__ void rotate_key_row(const typename Stor<DT>::T* src,
 }
 
 // ------------------------------------------------------------- reductions
+// Wave-wide reductions and scans with DPP row operations (plain VALU moves,
+// no LDS crossbar): quad permutes and row rotates/shifts within each 16-lane
+// row, then the row broadcasts of lanes 15 and 31 carry row results to the
+// following rows; lane 63 ends with the total, which readlane broadcasts.
+namespace dpp {
+constexpr int kXor1 = 0xB1;                    // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;                    // quad_perm [2,3,0,1]
+constexpr int kRor4 = 0x124, kRor8 = 0x128;    // row_ror:4, row_ror:8
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;   // row_shr:n
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
+}  // namespace dpp
+
+// src moved by the DPP pattern CTRL; lanes whose source is outside the
+// pattern, or whose row is not in ROWS, get `old`.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_mov(int old, int src) {
+  return __builtin_amdgcn_update_dpp(old, src, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_movf(float old, float src) {
+  return __int_as_float(dpp_mov<CTRL, ROWS>(__float_as_int(old), __float_as_int(src)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_movf<dpp::kXor1>(0.f, v);
+  v += dpp_movf<dpp::kXor2>(0.f, v);
+  v += dpp_movf<dpp::kRor4>(0.f, v);
+  v += dpp_movf<dpp::kRor8>(0.f, v);
+  v += dpp_movf<dpp::kBcast15, 0xA>(0.f, v);
+  v += dpp_movf<dpp::kBcast31, 0xC>(0.f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  v = fmaxf(v, dpp_movf<dpp::kXor1>(v, v));
+  v = fmaxf(v, dpp_movf<dpp::kXor2>(v, v));
+  v = fmaxf(v, dpp_movf<dpp::kRor4>(v, v));
+  v = fmaxf(v, dpp_movf<dpp::kRor8>(v, v));
+  v = fmaxf(v, dpp_movf<dpp::kBcast15, 0xA>(v, v));
+  v = fmaxf(v, dpp_movf<dpp::kBcast31, 0xC>(v, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// Sum over each aligned quad of lanes (the result in all four lanes).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_movf<dpp::kXor1>(0.f, v);
+  v += dpp_movf<dpp::kXor2>(0.f, v);
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes (lane order).
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
-  }
+  v += dpp_mov<dpp::kShr1>(0, v);
+  v += dpp_mov<dpp::kShr2>(0, v);
+  v += dpp_mov<dpp::kShr4>(0, v);
+  v += dpp_mov<dpp::kShr8>(0, v);
+  v += dpp_mov<dpp::kBcast15, 0xA>(0, v);
+  v += dpp_mov<dpp::kBcast31, 0xC>(0, v);
   return v;
 }
 

@@ -137,10 +137,7 @@ __device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int ro
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float v = acc[g];
-    v += __shfl_xor(v, 1, kWave);
-    v += __shfl_xor(v, 2, kWave);
-    lg[g] = v * scale;
+    lg[g] = quad_sum(acc[g]) * scale;
   }
 }
 
@@ -219,16 +216,27 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
-  return v;
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+  auto op = [](uint32_t a, int b) {
+    return MAX ? max(a, static_cast<uint32_t>(b)) : min(a, static_cast<uint32_t>(b));
+  };
+  int x = static_cast<int>(v);
+  v = op(v, dpp_mov<dpp::kXor1>(x, x));
+  x = static_cast<int>(v);
+  v = op(v, dpp_mov<dpp::kXor2>(x, x));
+  x = static_cast<int>(v);
+  v = op(v, dpp_mov<dpp::kRor4>(x, x));
+  x = static_cast<int>(v);
+  v = op(v, dpp_mov<dpp::kRor8>(x, x));
+  x = static_cast<int>(v);
+  v = op(v, dpp_mov<dpp::kBcast15, 0xA>(x, x));
+  x = static_cast<int>(v);
+  v = op(v, dpp_mov<dpp::kBcast31, 0xC>(x, x));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), kWave - 1));
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_minmax_u32<false>(v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_minmax_u32<true>(v); }
 
 // Exclusive prefix sum over NT threads in thread order; total in *total.
 template <int NT>
@@ -263,6 +271,7 @@ struct TopkSmem {
   uint32_t small_take[kMaxCK / 32];
   int s_nsmall;
   float redg[kMaxG][16];
+  float redz[kMaxG][16];
   float redf[16];
   int redi[16];
   uint32_t redu[2][16];
@@ -283,7 +292,7 @@ struct TopkSmem {
 template <int G, int NT>
 __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
                         int32_t* out_sel, int32_t* out_cnt, uint32_t* bm, float* imp,
-                        TopkSmem& sm) {
+                        TopkSmem& sm, const float* __restrict__ stats = nullptr, int n_stats = 0) {
   constexpr int PPT = kMaxCK / NT;
   const int tid = threadIdx.x;
   const int p0 = tid * PPT;
@@ -308,47 +317,73 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
 #pragma unroll
     for (int i = 0; i < PPT; ++i) if (p0 + i >= n) e[g][i] = -INFINITY;
   }
-  float M[G], Z[G];
+  if (stats) {
+    // per-head (max, sum of exp) partials of n_stats score shares, merged
+    // by one wave (log-sum-exp), instead of two block reductions
+    if (wid == 0) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) m = fmaxf(m, e[g][i]);
-    M[g] = wave_max(m);
-  }
-  __syncthreads();
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) sm.redg[g][wid] = M[g];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = sm.redg[g][0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) m = fmaxf(m, sm.redg[g][w]);
-    float z = 0.f;
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      e[g][i] = (p0 + i < n) ? __expf(e[g][i] - m) : 0.f;
-      z += e[g][i];
+      for (int g = 0; g < G; ++g) {
+        const float mw = lane < n_stats ? stats[(lane * G + g) * 2] : -INFINITY;
+        const float zw = lane < n_stats ? stats[(lane * G + g) * 2 + 1] : 0.f;
+        const float mm = wave_max(mw);
+        const float zz = wave_sum(mw == -INFINITY ? 0.f : zw * __expf(mw - mm));
+        if (lane == 0) {
+          sm.redg[g][0] = mm;
+          sm.redz[g][0] = zz;
+        }
+      }
     }
-    Z[g] = wave_sum(z);
-  }
-  __syncthreads();
-  if (lane == 0) {
+    __syncthreads();
 #pragma unroll
-    for (int g = 0; g < G; ++g) sm.redg[g][wid] = Z[g];
-  }
-  __syncthreads();
+    for (int g = 0; g < G; ++g) {
+      const float m = sm.redg[g][0];
+      const float inv = 1.0f / sm.redz[g][0];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float z = 0.f;
+      for (int i = 0; i < PPT; ++i) e[g][i] = (p0 + i < n) ? __expf(e[g][i] - m) * inv : 0.f;
+    }
+  } else {
+    float M[G], Z[G];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) z += sm.redg[g][w];
-    const float inv = 1.0f / z;
+    for (int g = 0; g < G; ++g) {
+      float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) e[g][i] *= inv;
+      for (int i = 0; i < PPT; ++i) m = fmaxf(m, e[g][i]);
+      M[g] = wave_max(m);
+    }
+    __syncthreads();
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) sm.redg[g][wid] = M[g];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = sm.redg[g][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) m = fmaxf(m, sm.redg[g][w]);
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        e[g][i] = (p0 + i < n) ? __expf(e[g][i] - m) : 0.f;
+        z += e[g][i];
+      }
+      Z[g] = wave_sum(z);
+    }
+    __syncthreads();
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) sm.redg[g][wid] = Z[g];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float z = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) z += sm.redg[g][w];
+      const float inv = 1.0f / z;
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) e[g][i] *= inv;
+    }
   }
   uint32_t key[PPT];
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -483,7 +518,9 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
     eqm |= (valid && kt == prefix) ? (1u << i) : 0u;
   }
   int tot;
-  const int eq_rank = block_scan_excl<NT>(__popc(eqm), sm.redi, &tot);
+  // the equal keys' ranks by position matter only when the boundary bin is
+  // neither kept whole nor ranked by the small-bin pass
+  const int eq_rank = (small || whole_bin) ? 0 : block_scan_excl<NT>(__popc(eqm), sm.redi, &tot);
   uint32_t inm;
   if (small) {
     inm = (sm.small_take[p0 >> 5] >> (p0 & 31)) & eqm;
@@ -508,11 +545,15 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       ++slot;
     }
   }
+  // the count is k-1 by construction; should it ever fall short, the
+  // remaining slots still name a real node (the current one), never stale data
+  for (int i = tot + tid; i < k - 1; i += NT) out_sel[i] = static_cast<int32_t>(lv.cur);
   uint32_t bits = takem << (p0 & 31);
   // PPT consecutive positions per thread: 32/PPT threads share one word
   constexpr int LPW = 32 / PPT;
-#pragma unroll
-  for (int o = 1; o < LPW; o <<= 1) bits |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), o, kWave));
+  static_assert(LPW <= 4, "bit words are merged within quads");
+  if constexpr (LPW >= 2) bits |= static_cast<uint32_t>(dpp_mov<dpp::kXor1>(0, static_cast<int>(bits)));
+  if constexpr (LPW >= 4) bits |= static_cast<uint32_t>(dpp_mov<dpp::kXor2>(0, static_cast<int>(bits)));
   if ((tid % LPW) == 0 && p0 < CK) bm[p0 / 32] = bits;
   if (tid == 0) {
     out_sel[k - 1] = static_cast<int32_t>(lv.cur);

@@ -106,10 +106,7 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
       a[c] = s;
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-#pragma unroll
-      for (int c = 0; c < kC; ++c) a[c] += __shfl_xor(a[c], o, kWave);
-    }
+    for (int c = 0; c < kC; ++c) a[c] = wave_sum(a[c]);
     const float scale = P.tau / sigma;
     float amax = -INFINITY;
 #pragma unroll
