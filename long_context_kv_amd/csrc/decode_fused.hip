@@ -2,8 +2,9 @@
 // Selection, Eq. 3) and the unified softmax (Unified Softmax, Eq. 4) -- in
 // one persistent launch.
 //
-// Grid (W, Hkv, B), 512 threads per workgroup.  The W workgroups of one
-// (sequence, KV head) cooperate:
+// 1-D grid of W * S workgroups of 512 threads; workgroup id = w * S + g
+// serves (sequence, KV head) group g < B * Hkv as its member w (ids with
+// g >= B * Hkv exit at once).  The W workgroups of a group cooperate:
 //   WG 0 appends token t (row t, and every node whose last token is t: those
 //   are current nodes of this query, never read by it);
 //   for each level from the top down that must be scored: the W workgroups
@@ -11,16 +12,22 @@
 //   at a barrier, and then every workgroup runs the same exact top-(k-1) on
 //   all the logits, keeping S and the kept-position bitmap in its own LDS
 //   (WG 0 also writes them out), so no second barrier is needed;
-//   all W then accumulate interleaved entry groups (token t's row comes from
+//   all W then accumulate interleaved entry chunks (token t's row comes from
 //   k_new/v_new), publish a partial softmax state, and WG 0 waits for them
 //   and merges them into the output.
-// Barrier: each workgroup raises its own arrival flag with an atomic exchange
-// (one 64-byte line per flag, so arrivals do not contend) and polls the
-// group's flags with a
-// bounded spin; if the bound is hit (workgroups of a group not co-resident)
-// the error word is set and the output is poisoned with NaN.  The host only
-// launches this kernel when the grid fits on the device with room to spare.
+// Barriers come in two forms.  XCD-local: the device hands workgroup i to
+// XCD i mod n_xcd, so with S a multiple of n_xcd all workgroups of a group
+// share one XCD and its L2; arrivals are atomic adds on one counter in that
+// L2 and waits read it with an L2 atomic, with no L2 write-back or
+// invalidation (each workgroup checks its own XCD id first).  Device-wide:
+// per-workgroup flags raised and polled with device-scope atomics around
+// release/acquire fences.  Either way every wait is a bounded spin; if the
+// bound is hit the error word is set and the output is poisoned with NaN.
+// The host launches this kernel only when the grid fits on the device (on
+// each XCD, for the local form) with room to spare.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 #include "recsa_common.hpp"
 #include "recsa_device.hpp"
@@ -32,11 +39,44 @@ namespace recsa {
 constexpr int kFusedThreads = 512;
 constexpr uint32_t kSpinLimit = 1u << 19;
 
-// Every wave drains its own memory operations, so after the workgroup
-// barrier all of the workgroup's stores have reached its L2; one thread
-// releases them to the device (one L2 write-back per workgroup), raises this
-// workgroup's flag to `gen`, waits for every flag of the group with relaxed
-// loads, and acquires once (one L2 invalidation per workgroup).
+// Value of *p read by an atomic executed in the L2 (a plain or relaxed
+// workgroup-scope load may be served by this CU's L1).
+__device__ __forceinline__ uint32_t l2_read(uint32_t* p) {
+  uint32_t e = 0xFFFFFFFFu;
+  __hip_atomic_compare_exchange_strong(p, &e, 0xFFFFFFFFu, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+  return e;
+}
+
+// XCD-local barrier.  Every wave drains its own memory operations, so after
+// the workgroup barrier the workgroup's stores are in the XCD's L2; one
+// thread adds this arrival to the group's counter (an L2 atomic), waits for
+// `target` arrivals, and invalidates this CU's L1 so that later loads see
+// what the other workgroups wrote.
+__device__ __forceinline__ void group_barrier_xcd(uint32_t* counter, uint32_t target,
+                                                  uint32_t* err, uint32_t* s_fail) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    uint32_t spins = 0;
+    while (l2_read(counter) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        atomicOr(err, 1u);
+        *s_fail = 1u;
+        break;
+      }
+    }
+    __asm__ __volatile__("buffer_inv sc0" ::: "memory");
+  }
+  __syncthreads();
+}
+
+// Device-wide barrier.  After the workgroup barrier one thread releases the
+// workgroup's stores to the device (one L2 write-back per workgroup), raises
+// this workgroup's flag to `gen`, waits for every flag of the group with
+// relaxed loads, and acquires once (one L2 invalidation per workgroup).
 __device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uint32_t gen,
                                               uint32_t* err, uint32_t* s_fail) {
   __builtin_amdgcn_s_waitcnt(0);
@@ -68,12 +108,12 @@ __device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uin
   __syncthreads();
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool XL>
 __global__ void __launch_bounds__(kFusedThreads)
     decode_fused_kernel(recsa_tree tr, recsa_pooler P, const void* k_new, const void* v_new,
                         const void* q, int Hq, const int64_t* pos, int32_t* sel, int32_t* cnt,
                         float* out, float* ws_logits, float* part, uint32_t* ctl_words, int W,
-                        int n_sel, int CK) {
+                        int S, int n_xcd, int n_sel, int CK) {
   using T = typename Stor<DT>::T;
   constexpr int NT = kFusedThreads;
   constexpr int NW = NT / kWave;
@@ -88,7 +128,9 @@ __global__ void __launch_bounds__(kFusedThreads)
     AttnSmem<D, G, NT> at;
     PoolSmem<DT, D, 1> pl;
   } sm;
-  const int w = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int grp = static_cast<int>(blockIdx.x) % S, w = static_cast<int>(blockIdx.x) / S;
+  if (grp >= tr.B * tr.Hkv) return;                  // padding of the group stride
+  const int j = grp % tr.Hkv, b = grp / tr.Hkv;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
   const int k = tr.k;
   const int top = tr.n_levels - 1;
@@ -98,17 +140,23 @@ __global__ void __launch_bounds__(kFusedThreads)
   int32_t* sel_q = sel + slot * n_sel * k;
   int32_t* cnt_q = cnt + slot * n_sel;
   float* lg_slot = ws_logits + slot * n_sel * static_cast<int64_t>(G) * CK;
-  // score-share softmax partials [level-1][W][G][2] sit in the partial slots
-  // this launch never uses for attention partials (slots kFusedMaxW and up)
-  float* stats = part + (slot * kPartSlots + kFusedMaxW) * static_cast<int64_t>(G) * (D + 2);
-  static_assert(RECSA_MAX_LEVELS * kFusedMaxW * 2 <= (kPartSlots - kFusedMaxW) * (64 + 2),
-                "softmax partials must fit the spare partial slots");
   uint32_t* ctl = ctl_words + slot * kCtlWords;
   uint32_t* err = ctl + 1;
-  uint32_t* flags = ctl + 16;
+  uint32_t* counter = ctl + 2;                       // arrivals (XCD-local barrier)
+  uint32_t* flags = ctl + 16;                        // one flag line per member (device-wide)
   const T* k_t = static_cast<const T*>(k_new) + slot * D;
   const T* v_t = static_cast<const T*>(v_new) + slot * D;
-  if (tid == 0) s_fail = 0u;
+  if (tid == 0) {
+    s_fail = 0u;
+    if constexpr (XL) {
+      // the local barrier needs this workgroup on XCD (id mod n_xcd)
+      const int xcc = __builtin_amdgcn_s_getreg(20 | (15 << 11)) & 0xF;   // hwreg XCC_ID
+      if (xcc != static_cast<int>(blockIdx.x) % n_xcd) {
+        atomicOr(err, 2u);
+        s_fail = 1u;
+      }
+    }
+  }
   load_query_rows<DT, D, G, NT>(q, static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G, qs);
 
   // ---- append (WG 0)
@@ -158,13 +206,6 @@ __global__ void __launch_bounds__(kFusedThreads)
       const int64_t rows_l = level_rows_dev(tr.L_cap, l);
       const int p_q = lv.len - 1;
       float* out_l = lg_slot + static_cast<int64_t>(l - 1) * G * CK;
-      // running (max, sum of exp) of this lane's logits, per head
-      float st_m[G], st_z[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        st_m[g] = -INFINITY;
-        st_z[g] = 0.f;
-      }
       for (int gi = w + W * wid; gi < ng; gi += W * NW) {
         const int p0 = gi * kC;
         const int nvalid = min(kC, n - p0);
@@ -180,51 +221,16 @@ __global__ void __launch_bounds__(kFusedThreads)
 #pragma unroll
           for (int g = 0; g < G; ++g)
             if ((g & 3) == s) out_l[static_cast<int64_t>(g) * CK + p0 + c] = lg[g];
-          if (s == 0) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-              const float mn = fmaxf(st_m[g], lg[g]);
-              st_z[g] = st_z[g] * __expf(st_m[g] - mn) + __expf(lg[g] - mn);
-              st_m[g] = mn;
-            }
-          }
         }
         wave_sync();
       }
-      // this workgroup's share: per-head (max, sum of exp) for the top-k
-      float* st_l = stats + static_cast<int64_t>(l - 1) * kFusedMaxW * G * 2;
-      {
-        float wm[G], wz[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          wm[g] = wave_max(st_m[g]);
-          wz[g] = wave_sum(st_m[g] == -INFINITY ? 0.f : st_z[g] * __expf(st_m[g] - wm[g]));
-        }
-        __syncthreads();                 // the scoring's LDS (union) is free now
-        if (lane == 0) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            sm.tk.redg[g][wid] = wm[g];
-            sm.tk.redz[g][wid] = wz[g];
-          }
-        }
-        __syncthreads();
-        if (tid < G) {
-          float mm = -INFINITY, zz = 0.f;
-#pragma unroll
-          for (int v = 0; v < NW; ++v) mm = fmaxf(mm, sm.tk.redg[tid][v]);
-#pragma unroll
-          for (int v = 0; v < NW; ++v) {
-            const float mv = sm.tk.redg[tid][v];
-            if (mv != -INFINITY) zz += sm.tk.redz[tid][v] * __expf(mv - mm);
-          }
-          st_l[(w * G + tid) * 2] = mm;
-          st_l[(w * G + tid) * 2 + 1] = zz;
-        }
-      }
-      group_barrier(flags, w, W, ++gen, err, &s_fail);
+      ++gen;
+      if constexpr (XL)
+        group_barrier_xcd(counter, gen * static_cast<uint32_t>(W), err, &s_fail);
+      else
+        group_barrier(flags, w, W, gen, err, &s_fail);
       wg_topk<G, NT>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1), s_bm + (l - 1) * bm_words,
-                     nullptr, sm.tk, st_l, W);
+                     nullptr, sm.tk);
     }
     __syncthreads();
     if (w == 0) {                      // API outputs
@@ -248,43 +254,82 @@ __global__ void __launch_bounds__(kFusedThreads)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_exchange(flags + 16 * w, gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (XL) {
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_exchange(flags + 16 * w, gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     return;
   }
-  group_barrier(flags, w, W, gen + 1, err, &s_fail);
+  if constexpr (XL)
+    group_barrier_xcd(counter, (gen + 1) * static_cast<uint32_t>(W), err, &s_fail);
+  else
+    group_barrier(flags, w, W, gen + 1, err, &s_fail);
   float* o = out + (static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G) * D;
   merge_partials<D, G, NT>(part + slot * kPartSlots * static_cast<int64_t>(G) * (D + 2), W, o);
   __syncthreads();
   if (s_fail || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
     for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
   }
-  // every other workgroup has raised its final flag, so none reads them again
-  if (tid < W) __hip_atomic_exchange(flags + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // every other workgroup has arrived for the last time, so none reads the
+  // counter or the flags again
+  if constexpr (XL) {
+    if (tid == 0) __hip_atomic_exchange(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+    if (tid < W) __hip_atomic_exchange(flags + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Largest W such that B*Hkv*W workgroups are resident at once (0: none fit).
+// Launch geometry of one decode step.
+struct FusedGeom {
+  int W = 0;          // workgroups per (sequence, KV head)
+  int S = 0;          // group stride of the workgroup id
+  int n_xcd = 1;
+  bool xl = false;    // XCD-local barrier
+};
+
+// Device facts, cached per device: CUs, co-resident workgroups per CU for
+// both forms of the kernel, and the XCD count when the device is known to
+// hand out workgroups to its XCDs round-robin (gfx950: 32 CUs per XCD).
 template <int DT, int D, int G>
-static int fused_width(const recsa_tree& tr) {
-  static int cached_dev = -1, cached_per_cu = 0, cached_cus = 0;
+static FusedGeom fused_geom(const recsa_tree& tr) {
+  static int cached_dev = -1, cus = 0, per_cu_xl = 0, per_cu = 0, n_xcd = 0;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  FusedGeom g;
+  if (hipGetDevice(&dev) != hipSuccess) return g;
   if (dev != cached_dev) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fused_kernel<DT, D, G>,
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return g;
+    cus = prop.multiProcessorCount;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fused_kernel<DT, D, G, false>,
+                                                     kFusedThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_xl, decode_fused_kernel<DT, D, G, true>,
                                                      kFusedThreads, 0) != hipSuccess)
-      return 0;
+      return g;
+    n_xcd = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && cus % 32 == 0) ? cus / 32 : 0;
+    const char* env = std::getenv("RECSA_FUSED_XCD_LOCAL");
+    if (env && env[0] == '0') n_xcd = 0;
     cached_dev = dev;
-    cached_cus = cus;
-    cached_per_cu = per_cu;
   }
-  // keep a quarter of the device spare so a group never waits on a
-  // workgroup that cannot be placed
-  const int64_t capacity = static_cast<int64_t>(cached_cus) * cached_per_cu * 3 / 4;
   const int64_t groups = static_cast<int64_t>(tr.B) * tr.Hkv;
-  return static_cast<int>(std::min<int64_t>(kFusedMaxW, capacity / groups));
+  // keep a quarter of the capacity spare so a group never waits on a
+  // workgroup that cannot be placed
+  if (n_xcd > 0) {
+    const int64_t S = (groups + n_xcd - 1) / n_xcd * n_xcd;
+    const int64_t cap = static_cast<int64_t>(cus / n_xcd) * per_cu_xl * 3 / 4;
+    g.W = static_cast<int>(std::min<int64_t>(kFusedMaxW, cap / (S / n_xcd)));
+    g.S = static_cast<int>(S);
+    g.n_xcd = n_xcd;
+    g.xl = true;
+  } else {
+    const int64_t cap = static_cast<int64_t>(cus) * per_cu * 3 / 4;
+    g.W = static_cast<int>(std::min<int64_t>(kFusedMaxW, cap / groups));
+    g.S = static_cast<int>(groups);
+  }
+  return g;
 }
 
 template <int DT, int D, int G>
@@ -292,13 +337,21 @@ static hipError_t fused_impl(const recsa_tree& tr, const recsa_pooler& P, const 
                              const void* v_new, const void* q, int Hq, const int64_t* pos,
                              int32_t* sel, int32_t* cnt, float* out, void* ws, const WsLayout& w,
                              hipStream_t s) {
-  const int W = fused_width<DT, D, G>(tr);
-  if (W < 1) return hipErrorLaunchOutOfResources;
+  const FusedGeom g = fused_geom<DT, D, G>(tr);
+  if (g.W < 1) return hipErrorLaunchOutOfResources;
   char* base = static_cast<char*>(ws);
-  decode_fused_kernel<DT, D, G><<<dim3(W, tr.Hkv, tr.B), kFusedThreads, 0, s>>>(
-      tr, P, k_new, v_new, q, Hq, pos, sel, cnt, out, reinterpret_cast<float*>(base + w.logits_off),
-      reinterpret_cast<float*>(base + w.part_off), reinterpret_cast<uint32_t*>(base + w.ctl_off), W,
-      w.n_sel, w.CK);
+  const dim3 grid(static_cast<unsigned>(g.W) * static_cast<unsigned>(g.S));
+  float* lg = reinterpret_cast<float*>(base + w.logits_off);
+  float* part = reinterpret_cast<float*>(base + w.part_off);
+  uint32_t* ctl = reinterpret_cast<uint32_t*>(base + w.ctl_off);
+  if (g.xl)
+    decode_fused_kernel<DT, D, G, true><<<grid, kFusedThreads, 0, s>>>(
+        tr, P, k_new, v_new, q, Hq, pos, sel, cnt, out, lg, part, ctl, g.W, g.S, g.n_xcd, w.n_sel,
+        w.CK);
+  else
+    decode_fused_kernel<DT, D, G, false><<<grid, kFusedThreads, 0, s>>>(
+        tr, P, k_new, v_new, q, Hq, pos, sel, cnt, out, lg, part, ctl, g.W, g.S, g.n_xcd, w.n_sel,
+        w.CK);
   return hipGetLastError();
 }
 

@@ -271,7 +271,6 @@ struct TopkSmem {
   uint32_t small_take[kMaxCK / 32];
   int s_nsmall;
   float redg[kMaxG][16];
-  float redz[kMaxG][16];
   float redf[16];
   int redi[16];
   uint32_t redu[2][16];
@@ -292,7 +291,7 @@ struct TopkSmem {
 template <int G, int NT>
 __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
                         int32_t* out_sel, int32_t* out_cnt, uint32_t* bm, float* imp,
-                        TopkSmem& sm, const float* __restrict__ stats = nullptr, int n_stats = 0) {
+                        TopkSmem& sm) {
   constexpr int PPT = kMaxCK / NT;
   const int tid = threadIdx.x;
   const int p0 = tid * PPT;
@@ -317,31 +316,7 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
 #pragma unroll
     for (int i = 0; i < PPT; ++i) if (p0 + i >= n) e[g][i] = -INFINITY;
   }
-  if (stats) {
-    // per-head (max, sum of exp) partials of n_stats score shares, merged
-    // by one wave (log-sum-exp), instead of two block reductions
-    if (wid == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float mw = lane < n_stats ? stats[(lane * G + g) * 2] : -INFINITY;
-        const float zw = lane < n_stats ? stats[(lane * G + g) * 2 + 1] : 0.f;
-        const float mm = wave_max(mw);
-        const float zz = wave_sum(mw == -INFINITY ? 0.f : zw * __expf(mw - mm));
-        if (lane == 0) {
-          sm.redg[g][0] = mm;
-          sm.redz[g][0] = zz;
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m = sm.redg[g][0];
-      const float inv = 1.0f / sm.redz[g][0];
-#pragma unroll
-      for (int i = 0; i < PPT; ++i) e[g][i] = (p0 + i < n) ? __expf(e[g][i] - m) * inv : 0.f;
-    }
-  } else {
+  {
     float M[G], Z[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
