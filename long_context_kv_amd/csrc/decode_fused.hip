@@ -108,6 +108,50 @@ __device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uin
   __syncthreads();
 }
 
+// Merge the W partial softmax states [W][G][2 + D] (max, sum, weighted
+// values) of one group into the output [G][D]: the W weights per head come
+// from one pass over the (max, sum) pairs, then every output element reads
+// its W partial values at once.
+template <int D, int G, int NT>
+__device__ void merge_partials_fused(const float* __restrict__ pp, int W, float* __restrict__ o,
+                                     float (*scale)[kMaxG], float* inv_l) {
+  constexpr int stride = G * (D + 2);
+  // (max, sum) of every partial, one pair per thread, all loads at once
+  float* m_w = &scale[0][0];                 // [W][G] maxima, then weights
+  __shared__ float l_w[kFusedMaxW][kMaxG];
+  if (threadIdx.x < W * G) {
+    const int w = threadIdx.x / G, g = threadIdx.x % G;
+    m_w[w * kMaxG + g] = pp[w * stride + g * (D + 2)];
+    l_w[w][g] = pp[w * stride + g * (D + 2) + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float M = -INFINITY;
+    for (int w = 0; w < W; ++w) M = fmaxf(M, m_w[w * kMaxG + g]);
+    float L = 0.f;
+    for (int w = 0; w < W; ++w) {
+      const float m = m_w[w * kMaxG + g];
+      const float f = (m == -INFINITY) ? 0.f : __expf(m - M);
+      scale[w][g] = f;
+      L += f * l_w[w][g];
+    }
+    inv_l[g] = 1.0f / L;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += NT) {
+    const int g = e / D, dd = e % D;
+    float v[kFusedMaxW];
+#pragma unroll
+    for (int w = 0; w < kFusedMaxW; ++w) v[w] = w < W ? pp[w * stride + g * (D + 2) + 2 + dd] : 0.f;
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < kFusedMaxW; ++w)
+      if (w < W) a += scale[w][g] * v[w];
+    o[e] = a * inv_l[g];
+  }
+}
+
 template <int DT, int D, int G, bool XL>
 __global__ void __launch_bounds__(kFusedThreads)
     decode_fused_kernel(recsa_tree tr, recsa_pooler P, const void* k_new, const void* v_new,
@@ -268,7 +312,10 @@ __global__ void __launch_bounds__(kFusedThreads)
   else
     group_barrier(flags, w, W, gen + 1, err, &s_fail);
   float* o = out + (static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G) * D;
-  merge_partials<D, G, NT>(part + slot * kPartSlots * static_cast<int64_t>(G) * (D + 2), W, o);
+  __shared__ float s_scale[kFusedMaxW][kMaxG];
+  __shared__ float s_invl[kMaxG];
+  merge_partials_fused<D, G, NT>(part + slot * kPartSlots * static_cast<int64_t>(G) * (D + 2), W, o,
+                                 s_scale, s_invl);
   __syncthreads();
   if (s_fail || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
     for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
@@ -315,11 +362,11 @@ static FusedGeom fused_geom(const recsa_tree& tr) {
     cached_dev = dev;
   }
   const int64_t groups = static_cast<int64_t>(tr.B) * tr.Hkv;
-  // keep a quarter of the capacity spare so a group never waits on a
-  // workgroup that cannot be placed
+  // keep part of the capacity spare so a group never waits on a workgroup
+  // that cannot be placed (an eighth of each XCD; a quarter of the device)
   if (n_xcd > 0) {
     const int64_t S = (groups + n_xcd - 1) / n_xcd * n_xcd;
-    const int64_t cap = static_cast<int64_t>(cus / n_xcd) * per_cu_xl * 3 / 4;
+    const int64_t cap = static_cast<int64_t>(cus / n_xcd) * per_cu_xl * 7 / 8;
     g.W = static_cast<int>(std::min<int64_t>(kFusedMaxW, cap / (S / n_xcd)));
     g.S = static_cast<int>(S);
     g.n_xcd = n_xcd;

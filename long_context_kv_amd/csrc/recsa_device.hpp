@@ -146,6 +146,71 @@ __device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int ro
 // storage; for bf16 storage the rounded values are packed two per 32-bit
 // word, [G][D/2] words (dims 2i, 2i+1 in word i, low half first), ready for
 // the packed bf16 dot products.
+// The (cos, sin) entries of table row phi that this lane's share of the
+// query rotation needs, loaded ahead of the rotation.
+template <int DT, int D, int G>
+struct QRope {
+  static constexpr int H2 = D / 2;
+  static constexpr int ITEMS = DT == RECSA_BF16 ? G * H2 / 2 : G * H2;   // per wave
+  static constexpr int PER_LANE = (ITEMS + kWave - 1) / kWave;
+  float4 cs[PER_LANE];      // bf16: two pairs (cos, sin, cos, sin); fp32: (cos, sin, -, -)
+};
+
+template <int DT, int D, int G>
+__device__ __forceinline__ void load_query_rope(int phi, const float* __restrict__ rope,
+                                                QRope<DT, D, G>& r) {
+  using Q = QRope<DT, D, G>;
+  constexpr int H2 = D / 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float* rrow = rope + static_cast<int64_t>(phi) * H2 * 2;
+#pragma unroll
+  for (int u = 0; u < Q::PER_LANE; ++u) {
+    const int idx = lane + u * kWave;
+    if (idx < Q::ITEMS) {
+      if constexpr (DT == RECSA_BF16) {
+        const int j = 2 * (idx % (H2 / 2));
+        r.cs[u] = *reinterpret_cast<const float4*>(rrow + 2 * j);
+      } else {
+        const int j = idx % H2;
+        const float2 v = *reinterpret_cast<const float2*>(rrow + 2 * j);
+        r.cs[u] = make_float4(v.x, v.y, 0.f, 0.f);
+      }
+    }
+  }
+}
+
+// The rotation itself from preloaded table entries (same result as
+// rotate_query).
+template <int DT, int D, int G>
+__device__ __forceinline__ void rotate_query_from(const float* qs, float* qt,
+                                                  const QRope<DT, D, G>& r) {
+  using Q = QRope<DT, D, G>;
+  constexpr int H2 = D / 2;
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int u = 0; u < Q::PER_LANE; ++u) {
+    const int idx = lane + u * kWave;
+    if (idx >= Q::ITEMS) continue;
+    const float4 cs = r.cs[u];
+    if constexpr (DT == RECSA_BF16) {
+      uint32_t* qw = reinterpret_cast<uint32_t*>(qt);
+      const int g = idx / (H2 / 2), j = 2 * (idx % (H2 / 2));
+      float x0, y0, x1, y1;
+      rope_pair(qs[g * D + j], qs[g * D + j + H2], cs.x, cs.y, x0, y0);
+      rope_pair(qs[g * D + j + 1], qs[g * D + j + 1 + H2], cs.z, cs.w, x1, y1);
+      qw[g * (D / 2) + j / 2] = f32_to_bf16_bits(x0) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
+      qw[g * (D / 2) + H2 / 2 + j / 2] =
+          f32_to_bf16_bits(y0) | (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+    } else {
+      const int g = idx / H2, j = idx % H2;
+      float xo, yo;
+      rope_pair(qs[g * D + j], qs[g * D + j + H2], cs.x, cs.y, xo, yo);
+      qt[g * D + j] = xo;
+      qt[g * D + j + H2] = yo;
+    }
+  }
+}
+
 template <int DT, int D, int G>
 __device__ __forceinline__ void rotate_query(const float* qs, float* qt, int phi,
                                              const float* __restrict__ rope) {
@@ -611,15 +676,18 @@ struct SoftState {
 };
 
 // A wave processes its entries in chunks of NG 16-entry groups, one entry
-// per lane for the softmax.  Each lane keeps the value words of its DPL
-// dims for every entry of the chunk; fp32 rows at d = 128 need two words
-// per entry, so those chunks hold two groups instead of four.
+// per lane for the softmax.
 template <int DT, int D>
 struct ChunkShape {
-  static constexpr int DPL = D / kWave;                    // dims per lane
-  static constexpr int VW = (DT == RECSA_BF16) ? 1 : DPL;  // value words per entry and lane
-  static constexpr int NG = VW == 2 ? 2 : 4;               // groups per chunk
-  static constexpr int NE = NG * kC;                       // entries per chunk
+  // P V: lane = (class c = lane / 16, block b = lane % 16) owns the DPB dims
+  // [b*DPB, (b+1)*DPB) of the entries e = c, c+4, c+8, ... of a chunk (one
+  // 16-byte load per bf16 row, two per fp32 row at d = 128); the four
+  // classes' partial sums are added once, after the last chunk.
+  static constexpr int DPB = D / kC;                               // dims per lane
+  static constexpr int VWE = (DT == RECSA_BF16) ? DPB / 2 : DPB;   // value words per entry
+  static constexpr int NG = VWE == 8 ? 2 : 4;                      // groups per chunk
+  static constexpr int NE = NG * kC;                               // entries per chunk
+  static constexpr int EPL = NE / 4;                               // entries per lane
 };
 
 // Per-level array entry with a per-lane level (unrolled selects: no
@@ -656,19 +724,19 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
                             AttnSmem<D, G, NT>& sm) {
   using T = typename Stor<DT>::T;
   using CS = ChunkShape<DT, D>;
-  constexpr int DPL = CS::DPL, VW = CS::VW, NG = CS::NG, NE = CS::NE;
+  constexpr int DPB = CS::DPB, VWE = CS::VWE, NG = CS::NG, NE = CS::NE, EPL = CS::EPL;
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
   const int c = lane >> 2, s = lane & 3;
   const int top = tr.n_levels - 1;
   const int bm_words = (CK + 31) / 32;
-  float m[G], lsum[G], acc[G][DPL];
+  float m[G], lsum[G], acc[G][DPB];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     lsum[g] = 0.f;
 #pragma unroll
-    for (int u = 0; u < DPL; ++u) acc[g][u] = 0.f;
+    for (int u = 0; u < DPB; ++u) acc[g][u] = 0.f;
   }
   const int n_groups = eg.total();
   const int n_chunks = (n_groups + NG - 1) / NG;
@@ -688,8 +756,10 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
     // per group (read from the group's first lane): level-0 groups get logits here
     const int grp_nvalid = in_group ? min(kC, n_pos - local * kC) : 0;
 
-    // ---- level-0 key rows of the chunk's groups
+    // ---- level-0 key rows and query-rotation table rows of the chunk's
+    // groups (issued before the value rows, which are needed only last)
     KRows<DT, D> ka[NG];
+    QRope<DT, D, G> rq[NG];
     bool is0[NG];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
@@ -703,40 +773,8 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
                                                             (seq_head * rows_l + node) * D, lead));
         const int ovr = k_t ? len - 1 - p0 : -1;          // row of token t, if in this group
         group_load_k<DT, D>(krow0, 0, (ovr >= 0 && ovr < kC) ? ovr : nv, ka[gg]);
-      }
-    }
-    // ---- value rows of every entry: a group's entries are 16 consecutive
-    // rows (children of one parent), so one base address per group, read
-    // from the group's first lane; token t's row may come from v_t
-    uint32_t vraw[NE][VW];
-    const T* vgrp = static_cast<const T*>(level_ptr(tr.V, level)) + (seq_head * rows_l + node) * D;
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      const int lead = gg * kC;
-      const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
-      const bool g0 = __builtin_amdgcn_readlane(static_cast<int>(in_group && level == 0), lead) != 0;
-      const int len = __builtin_amdgcn_readlane(lv.len, lead);
-      const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
-      const int own_r = (g0 && k_t) ? len - 1 - p0 : -1;
-      const T* vb = static_cast<const T*>(lane_ptr(vgrp, lead)) + lane * DPL;
-#pragma unroll
-      for (int r = 0; r < kC; ++r) {
-        const int e = lead + r;
-        if (e >= NE) break;
-        const T* vr = (own_r == r) ? v_t + lane * DPL : vb + r * D;
-        if (r < nv) {
-          if constexpr (DT == RECSA_BF16 && DPL == 2) {
-            vraw[e][0] = *reinterpret_cast<const uint32_t*>(vr);
-          } else if constexpr (DT == RECSA_BF16) {
-            vraw[e][0] = static_cast<uint32_t>(*vr) << 16;
-          } else {
-#pragma unroll
-            for (int u = 0; u < DPL; ++u) vraw[e][u] = __float_as_uint(vr[u]);
-          }
-        } else {
-#pragma unroll
-          for (int u = 0; u < VW; ++u) vraw[e][u] = 0u;
-        }
+        const int p_q = len - 1;
+        load_query_rope<DT, D, G>(kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope, rq[gg]);
       }
     }
     // ---- summary logits (levels >= 1: from scoring, minus the selected ones)
@@ -751,6 +789,47 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
 #pragma unroll
       for (int g = 0; g < G; ++g) lg[g] = ent ? src[static_cast<int64_t>(g) * CK] : -INFINITY;
     }
+    // ---- value rows: a group's entries are 16 consecutive rows (children
+    // of one parent), one base address per group read from its first lane;
+    // this lane loads its DPB dims of rows c, c+4, c+8, c+12 of each group;
+    // token t's row may come from v_t
+    uint32_t vraw[EPL][VWE];
+    const T* vgrp = static_cast<const T*>(level_ptr(tr.V, level)) + (seq_head * rows_l + node) * D;
+    const int vcls = lane >> 4, vdim = (lane & 15) * DPB;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      const int lead = gg * kC;
+      const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
+      const bool g0 = __builtin_amdgcn_readlane(static_cast<int>(in_group && level == 0), lead) != 0;
+      const int len = __builtin_amdgcn_readlane(lv.len, lead);
+      const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
+      const int own_r = (g0 && k_t) ? len - 1 - p0 : -1;
+      const T* vb = static_cast<const T*>(lane_ptr(vgrp, lead)) + vdim;
+#pragma unroll
+      for (int rr = 0; rr < kC / 4; ++rr) {
+        const int r = 4 * rr + vcls;                       // row within the group
+        const int slot = gg * (kC / 4) + rr;               // this lane's entry slot
+        const T* vr = (own_r == r) ? v_t + vdim : vb + r * D;
+        if (r < nv) {
+          if constexpr (VWE == 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(vr);
+            vraw[slot][0] = x.x; vraw[slot][1] = x.y; vraw[slot][2] = x.z; vraw[slot][3] = x.w;
+          } else if constexpr (VWE == 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(vr);
+            vraw[slot][0] = x.x; vraw[slot][1] = x.y;
+          } else {
+#pragma unroll
+            for (int u = 0; u < VWE; u += 4) {
+              const uint4 x = *reinterpret_cast<const uint4*>(vr + u);
+              vraw[slot][u] = x.x; vraw[slot][u + 1] = x.y; vraw[slot][u + 2] = x.z; vraw[slot][u + 3] = x.w;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < VWE; ++u) vraw[slot][u] = 0u;
+        }
+      }
+    }
     // ---- level-0 logits: split RoPE, one query rotation per group
     bool any0 = false;
 #pragma unroll
@@ -761,10 +840,9 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
       const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
       const int len = __builtin_amdgcn_readlane(lv.len, lead);
       const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
-      const int p_q = len - 1;
       const int ovr = k_t ? len - 1 - p0 : -1;
       const bool split = ovr >= 0 && ovr < kC;
-      rotate_query<DT, D, G>(qs, sm.qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
+      rotate_query_from<DT, D, G>(qs, sm.qt[wid], rq[gg]);
       wave_sync();
       float lgv[G];
       if (split) {
@@ -803,43 +881,60 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
       pr[g] = (lg[g] == -INFINITY) ? 0.f : __expf(lg[g] - mnew);
       lsum[g] = lsum[g] * sc + pr[g];
 #pragma unroll
-      for (int u = 0; u < DPL; ++u) acc[g][u] *= sc;
+      for (int u = 0; u < DPB; ++u) acc[g][u] *= sc;
       m[g] = mnew;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) sm.ew[wid][lane][g] = pr[g];
     wave_sync();
-    // ---- P V (every lane: its DPL dims, all entries)
+    // ---- P V (this lane: its DPB dims of its entries)
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      float v[DPL];
-      if constexpr (DT == RECSA_BF16 && DPL == 2) {
-        v[0] = __uint_as_float(vraw[e][0] << 16);
-        v[1] = __uint_as_float(vraw[e][0] & 0xFFFF0000u);
-      } else if constexpr (DT == RECSA_BF16) {
-        v[0] = __uint_as_float(vraw[e][0]);
-      } else {
+    for (int gg = 0; gg < NG; ++gg) {
 #pragma unroll
-        for (int u = 0; u < DPL; ++u) v[u] = __uint_as_float(vraw[e][u]);
-      }
-      float w[G];
+      for (int rr = 0; rr < kC / 4; ++rr) {
+        const int slot = gg * (kC / 4) + rr;
+        const int e = gg * kC + 4 * rr + vcls;
+        float v[DPB];
 #pragma unroll
-      for (int g = 0; g < G; ++g) w[g] = sm.ew[wid][e][g];
+        for (int u = 0; u < DPB; ++u) {
+          if constexpr (DT == RECSA_BF16) {
+            const uint32_t wv = vraw[slot][u / 2];
+            v[u] = __uint_as_float((u & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+          } else {
+            v[u] = __uint_as_float(vraw[slot][u]);
+          }
+        }
+        float wgt[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < G; ++g) wgt[g] = sm.ew[wid][e][g];
 #pragma unroll
-        for (int u = 0; u < DPL; ++u) acc[g][u] += w[g] * v[u];
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+          for (int u = 0; u < DPB; ++u) acc[g][u] += wgt[g] * v[u];
+        }
       }
     }
     wave_sync();
   }
-  SoftState<G, DPL> st;
+  // the four lane classes hold partial sums of the same dims: add them
+  // (lanes 0..15 end with the totals)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int u = 0; u < DPB; ++u) {
+      float v = acc[g][u];
+      v += __shfl_xor(v, 16, kWave);
+      v += __shfl_xor(v, 32, kWave);
+      acc[g][u] = v;
+    }
+  }
+  SoftState<G, DPB> st;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     st.m[g] = m[g];
     st.l[g] = wave_sum(lsum[g]);
 #pragma unroll
-    for (int u = 0; u < DPL; ++u) st.acc[g][u] = acc[g][u];
+    for (int u = 0; u < DPB; ++u) st.acc[g][u] = acc[g][u];
   }
   // ---- merge the waves
 #pragma unroll
@@ -848,8 +943,10 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
       sm.wm[wid][g] = st.m[g];
       sm.wl[wid][g] = st.l[g];
     }
+    if (lane < kC) {
 #pragma unroll
-    for (int u = 0; u < DPL; ++u) sm.wacc[wid][g][lane * DPL + u] = st.acc[g][u];
+      for (int u = 0; u < DPB; ++u) sm.wacc[wid][g][lane * DPB + u] = st.acc[g][u];
+    }
   }
   __syncthreads();
   if (threadIdx.x < G) {
