@@ -63,7 +63,9 @@ __device__ __forceinline__ void group_barrier_xcd(uint32_t* counter, uint32_t ta
     while (l2_read(counter) < target) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
-        atomicOr(err, 1u);
+        atomicOr(err, 1u);                       // for the host (device scope)
+        __hip_atomic_fetch_or(counter + 1, 1u, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);   // for the merge (this L2)
         *s_fail = 1u;
         break;
       }
@@ -109,46 +111,44 @@ __device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uin
 }
 
 // Merge the W partial softmax states [W][G][2 + D] (max, sum, weighted
-// values) of one group into the output [G][D]: the W weights per head come
-// from one pass over the (max, sum) pairs, then every output element reads
-// its W partial values at once.
+// values) of one group into the output [G][D]: the (max, sum) pairs are
+// loaded once each and turned into per-partial weights in LDS, then every
+// output element loads its W values at once.
 template <int D, int G, int NT>
-__device__ void merge_partials_fused(const float* __restrict__ pp, int W, float* __restrict__ o,
-                                     float (*scale)[kMaxG], float* inv_l) {
+__device__ void merge_partials_fused(const float* __restrict__ pp, int W, float* __restrict__ o) {
   constexpr int stride = G * (D + 2);
-  // (max, sum) of every partial, one pair per thread, all loads at once
-  float* m_w = &scale[0][0];                 // [W][G] maxima, then weights
-  __shared__ float l_w[kFusedMaxW][kMaxG];
-  if (threadIdx.x < W * G) {
-    const int w = threadIdx.x / G, g = threadIdx.x % G;
-    m_w[w * kMaxG + g] = pp[w * stride + g * (D + 2)];
-    l_w[w][g] = pp[w * stride + g * (D + 2) + 1];
+  __shared__ float s_m[kFusedMaxW][kMaxG], s_l[kFusedMaxW][kMaxG];
+  __shared__ float s_f[kFusedMaxW][kMaxG], s_inv[kMaxG];
+  const int tid = threadIdx.x;
+  if (tid < W * G) {
+    const int w = tid / G, g = tid % G;
+    s_m[w][g] = pp[w * stride + g * (D + 2)];
+    s_l[w][g] = pp[w * stride + g * (D + 2) + 1];
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
+  if (tid < W * G) {
+    const int w = tid / G, g = tid % G;
     float M = -INFINITY;
-    for (int w = 0; w < W; ++w) M = fmaxf(M, m_w[w * kMaxG + g]);
-    float L = 0.f;
-    for (int w = 0; w < W; ++w) {
-      const float m = m_w[w * kMaxG + g];
-      const float f = (m == -INFINITY) ? 0.f : __expf(m - M);
-      scale[w][g] = f;
-      L += f * l_w[w][g];
-    }
-    inv_l[g] = 1.0f / L;
+    for (int v = 0; v < W; ++v) M = fmaxf(M, s_m[v][g]);
+    s_f[w][g] = (s_m[w][g] == -INFINITY) ? 0.f : __expf(s_m[w][g] - M);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += NT) {
+  if (tid < G) {
+    float L = 0.f;
+    for (int v = 0; v < W; ++v) L += s_f[v][tid] * s_l[v][tid];
+    s_inv[tid] = 1.0f / L;
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += NT) {
     const int g = e / D, dd = e % D;
-    float v[kFusedMaxW];
+    float av[kFusedMaxW];
 #pragma unroll
-    for (int w = 0; w < kFusedMaxW; ++w) v[w] = w < W ? pp[w * stride + g * (D + 2) + 2 + dd] : 0.f;
+    for (int w = 0; w < kFusedMaxW; ++w) av[w] = w < W ? pp[w * stride + g * (D + 2) + 2 + dd] : 0.f;
     float a = 0.f;
 #pragma unroll
     for (int w = 0; w < kFusedMaxW; ++w)
-      if (w < W) a += scale[w][g] * v[w];
-    o[e] = a * inv_l[g];
+      if (w < W) a += s_f[w][g] * av[w];
+    o[e] = a * s_inv[g];
   }
 }
 
@@ -186,7 +186,8 @@ __global__ void __launch_bounds__(kFusedThreads)
   float* lg_slot = ws_logits + slot * n_sel * static_cast<int64_t>(G) * CK;
   uint32_t* ctl = ctl_words + slot * kCtlWords;
   uint32_t* err = ctl + 1;
-  uint32_t* counter = ctl + 2;                       // arrivals (XCD-local barrier)
+  uint32_t* counter = ctl + 2;                       // arrivals (XCD-local barrier);
+                                                     // ctl[3]: a wait timed out (same L2)
   uint32_t* flags = ctl + 16;                        // one flag line per member (device-wide)
   const T* k_t = static_cast<const T*>(k_new) + slot * D;
   const T* v_t = static_cast<const T*>(v_new) + slot * D;
@@ -196,7 +197,7 @@ __global__ void __launch_bounds__(kFusedThreads)
       // the local barrier needs this workgroup on XCD (id mod n_xcd)
       const int xcc = __builtin_amdgcn_s_getreg(20 | (15 << 11)) & 0xF;   // hwreg XCC_ID
       if (xcc != static_cast<int>(blockIdx.x) % n_xcd) {
-        atomicOr(err, 2u);
+        atomicOr(err, 2u);          // the group's waits will time out and poison the output
         s_fail = 1u;
       }
     }
@@ -285,49 +286,66 @@ __global__ void __launch_bounds__(kFusedThreads)
 
   // ---- unified softmax over this workgroup's interleaved entry groups
   const EntryGroups eg = entry_groups(t, tr, n_sel, s_sel, s_cnt);
-  attn_groups<DT, D, G, NT>(tr, t, slot, s_sel, s_cnt, eg, w, W, qs, lg_slot, s_bm, CK, k_t, v_t,
-                            sm.at);
+  // two-group chunks: fewer registers per wave (no spills), more chunks to
+  // spread over the group's waves
+  attn_groups<DT, D, G, NT, 2>(tr, t, slot, s_sel, s_cnt, eg, w, W, qs, lg_slot, s_bm, CK, k_t,
+                               v_t, sm.at);
   float* pp = part + (slot * kPartSlots + w) * static_cast<int64_t>(G) * (D + 2);
   for (int e = tid; e < G * D; e += NT) pp[(e / D) * (D + 2) + 2 + e % D] = sm.at.wacc[0][e / D][e % D];
   if (tid < G) {
     pp[tid * (D + 2)] = sm.at.res_m[tid];
     pp[tid * (D + 2) + 1] = sm.at.res_l[tid];
   }
-  // ---- WG 0 waits for every partial and merges them
-  if (w != 0) {
+  float* o = out + (static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G) * D;
+  const float* pp_group = part + slot * kPartSlots * static_cast<int64_t>(G) * (D + 2);
+  if constexpr (XL) {
+    // ---- the last workgroup to arrive merges (its arrival completes the
+    // count, so every partial is in the L2); the others are done
+    __shared__ uint32_t s_last;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      if constexpr (XL) {
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else {
+      const uint32_t before =
+          __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      s_last = (before + 1 == (gen + 1) * static_cast<uint32_t>(W)) ? 1u : 0u;
+      if (s_last) __asm__ __volatile__("buffer_inv sc0" ::: "memory");
+    }
+    __syncthreads();
+    if (!s_last) return;
+    merge_partials_fused<D, G, NT>(pp_group, W, o);
+    __shared__ uint32_t s_bad;
+    if (tid == 0) s_bad = s_fail | l2_read(counter + 1);
+    __syncthreads();
+    if (s_bad) {
+      for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
+    }
+    // every workgroup has arrived for the last time: none reads the counter again
+    if (tid == 0) {
+      __hip_atomic_exchange(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_exchange(counter + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  } else {
+    // ---- WG 0 waits for every partial and merges them
+    if (w != 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __hip_atomic_exchange(flags + 16 * w, gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      return;
     }
-    return;
-  }
-  if constexpr (XL)
-    group_barrier_xcd(counter, (gen + 1) * static_cast<uint32_t>(W), err, &s_fail);
-  else
     group_barrier(flags, w, W, gen + 1, err, &s_fail);
-  float* o = out + (static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G) * D;
-  __shared__ float s_scale[kFusedMaxW][kMaxG];
-  __shared__ float s_invl[kMaxG];
-  merge_partials_fused<D, G, NT>(part + slot * kPartSlots * static_cast<int64_t>(G) * (D + 2), W, o,
-                                 s_scale, s_invl);
-  __syncthreads();
-  if (s_fail || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-    for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
-  }
-  // every other workgroup has arrived for the last time, so none reads the
-  // counter or the flags again
-  if constexpr (XL) {
-    if (tid == 0) __hip_atomic_exchange(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  } else {
+    merge_partials_fused<D, G, NT>(pp_group, W, o);
+    __syncthreads();
+    if (s_fail || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+      for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
+    }
+    // every other workgroup has raised its final flag, so none reads them again
     if (tid < W) __hip_atomic_exchange(flags + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
+
 
 // Largest W such that B*Hkv*W workgroups are resident at once (0: none fit).
 // Launch geometry of one decode step.

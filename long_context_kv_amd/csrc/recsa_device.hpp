@@ -677,7 +677,7 @@ struct SoftState {
 
 // A wave processes its entries in chunks of NG 16-entry groups, one entry
 // per lane for the softmax.
-template <int DT, int D>
+template <int DT, int D, int NG_MAX>
 struct ChunkShape {
   // P V: lane = (class c = lane / 16, block b = lane % 16) owns the DPB dims
   // [b*DPB, (b+1)*DPB) of the entries e = c, c+4, c+8, ... of a chunk (one
@@ -685,7 +685,7 @@ struct ChunkShape {
   // classes' partial sums are added once, after the last chunk.
   static constexpr int DPB = D / kC;                               // dims per lane
   static constexpr int VWE = (DT == RECSA_BF16) ? DPB / 2 : DPB;   // value words per entry
-  static constexpr int NG = VWE == 8 ? 2 : 4;                      // groups per chunk
+  static constexpr int NG = VWE == 8 ? (NG_MAX < 2 ? NG_MAX : 2) : NG_MAX;   // groups per chunk
   static constexpr int NE = NG * kC;                               // entries per chunk
   static constexpr int EPL = NE / 4;                               // entries per lane
 };
@@ -715,7 +715,7 @@ __device__ __forceinline__ const void* lane_ptr(const void* p, int src_lane) {
 // first, then the value rows, so both are in flight during the query
 // rotations.  If k_t/v_t are given they replace the tree rows of token t
 // (decode append in the same launch).
-template <int DT, int D, int G, int NT>
+template <int DT, int D, int G, int NT, int NG_MAX = 4>
 __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, const int32_t* sel,
                             const int32_t* cnt, const EntryGroups& eg, int g_lo, int g_step,
                             const float* qs, const float* __restrict__ lg_slot,
@@ -723,7 +723,7 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
                             const typename Stor<DT>::T* k_t, const typename Stor<DT>::T* v_t,
                             AttnSmem<D, G, NT>& sm) {
   using T = typename Stor<DT>::T;
-  using CS = ChunkShape<DT, D>;
+  using CS = ChunkShape<DT, D, NG_MAX>;
   constexpr int DPB = CS::DPB, VWE = CS::VWE, NG = CS::NG, NE = CS::NE, EPL = CS::EPL;
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
@@ -778,16 +778,20 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
       }
     }
     // ---- summary logits (levels >= 1: from scoring, minus the selected ones)
+    // (the loads do not wait for the selection bitmap: it masks afterwards)
     float lg[G];
+    uint32_t sel_word = 0u;
+    const bool summ = valid && level >= 1;
     {
-      bool ent = false;
-      if (valid && level >= 1) {
-        const uint32_t word = bm_slot[(level - 1) * bm_words + (p >> 5)];
-        ent = ((word >> (p & 31)) & 1u) == 0u;
-      }
       const float* src = lg_slot + static_cast<int64_t>(level - 1) * G * CK + p;
+      if (summ) {
+        sel_word = bm_slot[(level - 1) * bm_words + (p >> 5)];
 #pragma unroll
-      for (int g = 0; g < G; ++g) lg[g] = ent ? src[static_cast<int64_t>(g) * CK] : -INFINITY;
+        for (int g = 0; g < G; ++g) lg[g] = src[static_cast<int64_t>(g) * CK];
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
+      }
     }
     // ---- value rows: a group's entries are 16 consecutive rows (children
     // of one parent), one base address per group read from its first lane;
@@ -862,6 +866,10 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
         for (int g = 0; g < G; ++g) sm.ew[wid][lead + c][g] = (c < nv) ? lgv[g] : -INFINITY;
       }
       wave_sync();
+    }
+    if (summ && ((sel_word >> (p & 31)) & 1u)) {      // selected: not an entry of E
+#pragma unroll
+      for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
     }
     if (any0 && valid && level == 0) {
 #pragma unroll
