@@ -214,10 +214,12 @@ def main():
 
     for _ in range(args.warmup):
         prefill()
-        graph.replay()
+        decode()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
+    # one step = one prefill chunk, then one decode token (a single launch;
+    # its graph replay is timed separately below)
     evs = [(ev(), ev(), ev()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -225,7 +227,7 @@ def main():
         e0.record()
         prefill()
         e1.record()
-        graph.replay()
+        decode()
         e2.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
