@@ -135,6 +135,23 @@ def kv_rows(wl: Workload, device, layer: int = 0, n_rows: int | None = None,
     return K, V
 
 
+def kv_rows_device(wl: Workload, device, n_rows: int, layer: int = 0):
+    """Level-0 K and V [B, Hkv, n_rows, d] drawn N(0,1) by the device's own
+    generator (seeded per workload, role and layer) and rounded to the
+    storage dtype.  For the largest cases, where drawing on the host would
+    take minutes: the values are reproducible on one kind of device, and the
+    oracle reads the very tensors the kernels read."""
+    K = torch.empty((wl.B, wl.Hkv, n_rows, wl.d), dtype=wl.torch_dtype, device=device)
+    V = torch.empty_like(K)
+    for X, role in ((K, "k"), (V, "v")):
+        g = generator(device, wl.seed, ROLE[role], layer, "device")
+        for b in range(wl.B):
+            for h in range(wl.Hkv):
+                X[b, h] = to_storage(torch.randn((n_rows, wl.d), generator=g, device=device,
+                                                 dtype=torch.float32), wl.dtype)
+    return K, V
+
+
 def plant_needles(wl: Workload, K: torch.Tensor, q: torch.Tensor, layer: int = 0,
                   b_list=None, h_list=None):
     """Overwrite wl.n_needles rows per (sequence, KV head) of K with keys of

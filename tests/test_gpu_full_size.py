@@ -10,7 +10,9 @@ import numpy as np
 import pytest
 import torch
 
-from tests.test_gpu_parity import _check_queries, _need_gpu
+import synth
+from long_context_kv_amd import recsa as R
+from tests.test_gpu_parity import DEV, _check_queries, _need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -49,3 +51,100 @@ def test_524k_bench_configuration_sampled_vs_oracle():
     rep2 = _check_queries(tree, w.pdict, w.q_pre[:, idx], pos_p, sel_p, cnt_p, None, out_p,
                           [2], 1e-5, 2e-3, trees=trees, max_swaps=1)
     assert rep2.matched >= len(idx) - 1, rep2
+
+
+def test_1m_batch4_decode_sampled_vs_oracle():
+    """1M tokens, 4 independent sequences (5 tree levels, 3 of them scored),
+    each at its own position, through the single-launch decode in the
+    benchmark's launch configuration; sampled (sequence, KV head) pairs vs
+    the oracle.  Nodes past a sequence's own position are built too (its walk
+    never reads a node past its current node)."""
+    _need_gpu()
+    wl = synth.WORKLOADS["1m_b4"]
+    L, B = wl.L, wl.B
+    L_cap = L + 64
+    K, V = synth.kv_rows_device(wl, DEV, L_cap)
+    q = synth.decode_queries(wl, DEV)                          # [B, 1, Hq, d]
+    synth.plant_needles(wl, K[:, :, :L], q)
+    pdict = synth.pooler_params(wl.d, wl.d, DEV, wl.seed)
+    pool = R.Pooler.from_dict(pdict, DEV)
+    tree = R.Tree.allocate(B, wl.Hkv, wl.d, L_cap, k=wl.k, dtype="bf16", device=DEV,
+                           level0=(K, V))
+    assert tree.n_levels == 5
+    t_b = [L - 3 * b for b in range(B)]
+    R.recsa_build_tree(tree, pool, 0, L)
+    pos = torch.tensor(t_b, dtype=torch.int64, device=DEV)
+    kn = torch.stack([K[b, :, t_b[b]] for b in range(B)]).contiguous()
+    vn = torch.stack([V[b, :, t_b[b]] for b in range(B)]).contiguous()
+    ws = R.workspace(tree, wl.Hq, B)
+    sel, cnt, _ = tree.selection_buffers(B)
+    out = torch.empty((B, wl.Hq, wl.d), dtype=torch.float32, device=DEV)
+    R.recsa_decode(tree, pool, kn, vn, q, wl.Hq, pos, sel, cnt, out, ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(R.decode_error_words(ws, tree, wl.Hq)).item() == 0
+    n_sel, k = tree.n_sel, tree.k
+    s_np = sel.cpu().numpy().reshape(B, 1, tree.Hkv, n_sel, k)
+    c_np = cnt.cpu().numpy().reshape(B, 1, tree.Hkv, n_sel)
+    o_np = out.cpu().numpy().astype(np.float64).reshape(B, 1, wl.Hq, wl.d)
+    matched = 0
+    for b, j in ((0, 0), (1, 3), (3, 7)):
+        print(f"1M x 4 decode: sequence {b} at t={t_b[b]}, KV head {j}", flush=True)
+        rep = _check_queries(tree, pdict, q[b:b + 1], pos[b:b + 1].view(1, 1).cpu(),
+                             s_np[b:b + 1], c_np[b:b + 1], None, o_np[b:b + 1], [j],
+                             1e-5, 2e-3, trees={}, max_swaps=1, seqs=[b])
+        matched += rep.matched
+    assert matched >= 2
+
+
+def test_2m_layer_decode_and_prefill_sampled_vs_oracle():
+    """One layer of the 2M-token workload: full build over 2M tokens, an
+    8192-query causal prefill chunk (incremental build, T-query selection and
+    attention) and the single-launch decode right after it; sampled queries
+    and KV heads vs the oracle."""
+    _need_gpu()
+    wl = synth.WORKLOADS["2m_l4"]
+    L, T = wl.L, wl.prefill_T
+    t_dec = L + T
+    L_cap = t_dec + 64
+    K, V = synth.kv_rows_device(wl, DEV, L_cap)
+    q_dec = synth.decode_queries(wl, DEV)
+    synth.plant_needles(wl, K[:, :, :L], q_dec)
+    q_pre = synth.new_rows(wl, DEV, T, "chunk")[2]             # [1, T, Hq, d]
+    pdict = synth.pooler_params(wl.d, wl.d, DEV, wl.seed)
+    pool = R.Pooler.from_dict(pdict, DEV)
+    tree = R.Tree.allocate(1, wl.Hkv, wl.d, L_cap, k=wl.k, dtype="bf16", device=DEV,
+                           level0=(K, V))
+    R.recsa_build_tree(tree, pool, 0, L)
+    R.recsa_build_tree(tree, pool, L, L + T)
+    pos_pre = torch.arange(L, L + T, device=DEV).view(1, T)
+    ws = R.workspace(tree, wl.Hq, T)
+    sel, cnt, _ = tree.selection_buffers(T)
+    R.recsa_select(tree, q_pre, wl.Hq, T, pos_pre, sel, cnt, None, ws)
+    out_pre = torch.empty((1, T, wl.Hq, wl.d), dtype=torch.float32, device=DEV)
+    R.recsa_attn_prefill(tree, q_pre, wl.Hq, T, pos_pre, sel, cnt, out_pre, ws)
+    del ws
+    pos = torch.tensor([t_dec], dtype=torch.int64, device=DEV)
+    wsd = R.workspace(tree, wl.Hq, 1)
+    seld, cntd, _ = tree.selection_buffers(1)
+    outd = torch.empty((1, wl.Hq, wl.d), dtype=torch.float32, device=DEV)
+    R.recsa_decode(tree, pool, K[:, :, t_dec].contiguous(), V[:, :, t_dec].contiguous(), q_dec,
+                   wl.Hq, pos, seld, cntd, outd, wsd)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(R.decode_error_words(wsd, tree, wl.Hq)).item() == 0
+    n_sel, k = tree.n_sel, tree.k
+    trees = {}
+    print(f"2M decode at t={t_dec}: KV heads 1, 6", flush=True)
+    rep = _check_queries(tree, pdict, q_dec, pos.view(1, 1).cpu(),
+                         seld.cpu().numpy().reshape(1, 1, tree.Hkv, n_sel, k),
+                         cntd.cpu().numpy().reshape(1, 1, tree.Hkv, n_sel), None,
+                         outd.cpu().numpy().astype(np.float64).reshape(1, 1, wl.Hq, wl.d),
+                         [1, 6], 1e-5, 2e-3, trees=trees, max_swaps=1)
+    assert rep.matched >= 1
+    idx = [0, T // 3, T - 1]
+    print(f"2M prefill chunk: queries {[L + i for i in idx]} on KV head 6", flush=True)
+    rep2 = _check_queries(tree, pdict, q_pre[:, idx], pos_pre[:, idx].cpu(),
+                          sel.cpu().numpy().reshape(1, T, tree.Hkv, n_sel, k)[:, idx],
+                          cnt.cpu().numpy().reshape(1, T, tree.Hkv, n_sel)[:, idx], None,
+                          out_pre.cpu().numpy().astype(np.float64)[:, idx], [6],
+                          1e-5, 2e-3, trees=trees, max_swaps=1)
+    assert rep2.matched >= len(idx) - 1

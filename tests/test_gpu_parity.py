@@ -161,8 +161,9 @@ def _run_select_attn(tree, q, Hq, pos, decode):
 
 
 def _check_queries(tree, pdict, q, pos, sel, cnt, imp, out, heads, tie_rel, out_tol,
-                   trees=None, max_swaps=0):
-    """Walk every (b, query, head in `heads`) in the oracle and compare."""
+                   trees=None, max_swaps=0, seqs=None):
+    """Walk every (b, query, head in `heads`) in the oracle and compare.
+    seqs[b] is the tree's sequence index of row b of the arrays (default b)."""
     B, T = pos.shape
     G = q.shape[2] // tree.Hkv
     cos, sin = O.rope_table(tree.d, tree.C * tree.k, 1e6)
@@ -170,12 +171,13 @@ def _check_queries(tree, pdict, q, pos, sel, cnt, imp, out, heads, tie_rel, out_
     qn = PY.to64(q)
     trees = trees if trees is not None else {}
     for b in range(B):
+        sb = b if seqs is None else seqs[b]
         for j in heads:
-            if (b, j) not in trees:
+            if (sb, j) not in trees:
                 n_tok = int(pos[b].max()) + 1
-                trees[(b, j)] = _oracle_tree(tree, pdict, b, j, n_tok)
-            K, V = trees[(b, j)]
-            gk = {lvl: PY.to64(tree.K[lvl][b, j, :K[lvl].shape[0]]) for lvl in range(1, len(K))}
+                trees[(sb, j)] = _oracle_tree(tree, pdict, sb, j, n_tok)
+            K, V = trees[(sb, j)]
+            gk = {lvl: PY.to64(tree.K[lvl][sb, j, :K[lvl].shape[0]]) for lvl in range(1, len(K))}
             differs = lambda lvl, node: not np.array_equal(gk[lvl][node], K[lvl][node])
             for ti in range(T):
                 t = int(pos[b, ti])
