@@ -162,7 +162,9 @@ __global__ void __launch_bounds__(kFusedThreads)
   constexpr int NT = kFusedThreads;
   constexpr int NW = NT / kWave;
   constexpr int kMaxSel = RECSA_MAX_LEVELS - 1;
-  __shared__ int32_t s_sel[kMaxSel * 256];          // S^(l) of every level, this group
+  // S^(l) of every level for this group, level l at [(l-1)*k, l*k) -- the
+  // stride list_view reads the parent selection with (k <= 256)
+  __shared__ int32_t s_sel[kMaxSel * 256];
   __shared__ int32_t s_cnt[kMaxSel + 1];
   __shared__ uint32_t s_bm[kMaxSel * (kMaxCK / 32)];
   __shared__ uint32_t s_fail;
@@ -242,7 +244,7 @@ __global__ void __launch_bounds__(kFusedThreads)
   uint32_t gen = 0;
   for (int l = top - 1; l >= 1; --l) {
     const ListView lv = list_view(t, l, top, k, s_sel, s_cnt);
-    int32_t* ls = s_sel + (l - 1) * 256;
+    int32_t* ls = s_sel + (l - 1) * k;
     if (lv.len <= k) {
       wg_take_all<NT>(lv, k, ls, s_cnt + (l - 1), nullptr, CK);
     } else {

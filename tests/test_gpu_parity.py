@@ -362,3 +362,44 @@ def test_fused_decode_vs_oracle_bf16():
     rep = _check_queries(tree, pdict, q, pos.view(1, 1).cpu(), s, c, None, o, range(8),
                          1e-5, 2e-3, max_swaps=1)
     assert rep.matched >= 7, rep
+
+
+@pytest.mark.parametrize("k", [64, 16])
+def test_small_k_decode_and_prefill(k):
+    """Selection depths below 256: the pages' k = 64 variant (C*k = 1024
+    positions) and k = 16, both 4 levels at 40K tokens -- the fused decode,
+    the separate decode calls and a causal prefill chunk, sampled queries and
+    heads vs the oracle.  (The fused kernel keeps S^(l) in LDS at stride k,
+    the stride the list of the level below reads it with.)"""
+    _need_gpu()
+    L0, T = 40000, 256
+    L_cap = L0 + T + 64
+    wl, tree, pool, pdict = _setup(1, 4, 128, L_cap, L_cap, k, "bf16", 31)
+    assert tree.n_levels == 4
+    R.recsa_build_tree(tree, pool, 0, L0)
+    R.recsa_build_tree(tree, pool, L0, L0 + T)
+    q = synth.to_storage(synth.normal((1, T, 16, 128), DEV, 31, 97), "bf16")
+    pos = torch.arange(L0, L0 + T, device=DEV).view(1, T)
+    sel, cnt, imp, out = _run_select_attn(tree, q, 16, pos, decode=False)
+    idx = [0, 100, T - 1]
+    rep = _check_queries(tree, pdict, q[:, idx], pos[:, idx].cpu(), sel[:, idx], cnt[:, idx],
+                         imp[:, idx], out[:, idx], [1, 2], 1e-5, 2e-3, max_swaps=1)
+    assert rep.matched >= 2 * len(idx) - 1
+    # decode at t = L0 + T: fused and separate calls agree with each other and the oracle
+    t = L0 + T
+    kn, vn = tree.K[0][:, :, t].clone().contiguous(), tree.V[0][:, :, t].clone().contiguous()
+    qd = synth.to_storage(synth.normal((1, 1, 16, 128), DEV, 31, 98), "bf16")
+    p1 = torch.tensor([t], dtype=torch.int64, device=DEV)
+    ref = R.Tree.allocate(1, 4, 128, L_cap, k=k, dtype="bf16", device=DEV,
+                          level0=(tree.K[0].clone(), tree.V[0].clone()))
+    R.recsa_build_tree(ref, pool, 0, L0 + T)
+    fs, fc, fo, ws = _fused_step(tree, pool, kn, vn, qd, 16, p1)
+    R.recsa_append_decode(ref, pool, kn, vn, p1)
+    s2, c2, m2, o2 = _run_select_attn(ref, qd, 16, p1.view(1, 1), decode=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(fs.cpu().numpy().reshape(s2.shape), s2)
+    assert np.allclose(fo.cpu().numpy().astype(np.float64).reshape(o2.shape), o2, rtol=0,
+                       atol=1e-5 * np.abs(o2).max())
+    rep2 = _check_queries(ref, pdict, qd, p1.view(1, 1).cpu(), s2, c2, m2, o2, [0, 3], 1e-5,
+                          2e-3, max_swaps=1)
+    assert rep2.matched >= 1
