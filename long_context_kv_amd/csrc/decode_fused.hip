@@ -31,6 +31,7 @@
 
 #include "recsa_common.hpp"
 #include "recsa_device.hpp"
+#include "recsa_mfma.hpp"
 #include "recsa_kernels.hpp"
 #include "recsa_pool.hpp"
 
@@ -257,17 +258,33 @@ __global__ void __launch_bounds__(kFusedThreads)
         const int p0 = gi * kC;
         const int nvalid = min(kC, n - p0);
         const T* rows = static_cast<const T*>(tr.Kr[l]) + (slot * rows_l + lv.node(p0)) * D;
-        KRows<DT, D> kr;                 // key rows in flight during the rotation
-        group_load_k<DT, D>(rows, 0, nvalid, kr);
-        rotate_query<DT, D, G>(qs, sm.at.qt[wid], kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope);
-        wave_sync();
-        float lg[G];
-        group_logits_from<DT, D, G>(kr, 0, nvalid, sm.at.qt[wid], tr.rope, lg);
-        const int c = lane >> 2, s = lane & 3;
-        if (c < nvalid) {
+        const int phi = p_q - p0;        // = C (r_q - r) + c_q, r = p0 / C
+        if constexpr (DT == RECSA_BF16) {
+          MFrag<D> kf, qf;               // key rows in flight during the rotation
+          load_key_frag<D>(rows, nvalid, kf);
+          rotate_query<DT, D, G>(qs, sm.at.qt[wid], phi, tr.rope);
+          wave_sync();
+          query_frag_lds<D, G>(reinterpret_cast<const uint16_t*>(sm.at.qt[wid]), qf);
+          const f32x4_t c = mfma_logits<D>(qf, kf);
+          const float scale = 1.0f / sqrtf(static_cast<float>(D));
+          if (lane < nvalid && lane < kC) {
 #pragma unroll
-          for (int g = 0; g < G; ++g)
-            if ((g & 3) == s) out_l[static_cast<int64_t>(g) * CK + p0 + c] = lg[g];
+            for (int g = 0; g < G; ++g)
+              out_l[static_cast<int64_t>(g) * CK + p0 + lane] = c[g] * scale;
+          }
+        } else {
+          KRows<DT, D> kr;               // key rows in flight during the rotation
+          group_load_k<DT, D>(rows, 0, nvalid, kr);
+          rotate_query<DT, D, G>(qs, sm.at.qt[wid], phi, tr.rope);
+          wave_sync();
+          float lg[G];
+          group_logits_from<DT, D, G>(kr, 0, nvalid, sm.at.qt[wid], tr.rope, lg);
+          const int c = lane >> 2, s = lane & 3;
+          if (c < nvalid) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+              if ((g & 3) == s) out_l[static_cast<int64_t>(g) * CK + p0 + c] = lg[g];
+          }
         }
         wave_sync();
       }

@@ -47,6 +47,13 @@ bool heads_ok(const recsa_tree* t, int32_t Hq) {
   return G == 1 || G == 2 || G == 4;
 }
 
+// B*T queries, each launched as up to kQueryLaunchX workgroups along one grid
+// dimension, and B*T*Hkv selection slots, all within 31 bits.
+bool queries_fit(const recsa_tree* t, int32_t T) {
+  const int64_t nq = static_cast<int64_t>(t->B) * T;
+  return nq * kQueryLaunchX <= 0x7FFFFFFF && nq * t->Hkv <= 0x7FFFFFFF;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? RECSA_OK : RECSA_E_HIP; }
 
 }  // namespace
@@ -119,7 +126,7 @@ int recsa_select(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T, c
   if (!tree_ok(tree, &why)) return why;
   if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
   if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !ws) return RECSA_E_INVALID;
-  if (static_cast<int64_t>(tree->B) * T > 0x7FFFFFFF / tree->Hkv) return RECSA_E_INVALID;
+  if (!queries_fit(tree, T)) return RECSA_E_INVALID;
   const WsLayout w = ws_layout(*tree, Hq, static_cast<int64_t>(tree->B) * T);
   if (ws_bytes < static_cast<size_t>(w.total)) return RECSA_E_WORKSPACE;
   if (tree->n_levels < 2) return RECSA_OK;      // a single level: nothing to select
@@ -134,7 +141,7 @@ static int attn_common(const recsa_tree* tree, const void* q, int32_t Hq, int32_
   if (!tree_ok(tree, &why)) return why;
   if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
   if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !out || !ws) return RECSA_E_INVALID;
-  if (static_cast<int64_t>(tree->B) * T > 0x7FFFFFFF / tree->Hkv) return RECSA_E_INVALID;
+  if (!queries_fit(tree, T)) return RECSA_E_INVALID;
   const WsLayout w = ws_layout(*tree, Hq, static_cast<int64_t>(tree->B) * T);
   if (ws_bytes < static_cast<size_t>(w.total)) return RECSA_E_WORKSPACE;
   return hip_status(launch_attn(*tree, q, Hq, T, pos_dev, sel_idx, sel_cnt, out, ws, w, decode,

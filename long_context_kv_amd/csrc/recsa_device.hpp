@@ -661,7 +661,7 @@ __device__ __forceinline__ EntryGroups entry_groups(int64_t t, const recsa_tree&
 
 template <int D, int G, int NT>
 struct AttnSmem {
-  float qt[NT / kWave][G * D];
+  alignas(16) float qt[NT / kWave][G * D];
   float ew[NT / kWave][kWave][G];  // a chunk's per-entry logits, then its weights
   float wm[NT / kWave][G];
   float wl[NT / kWave][G];

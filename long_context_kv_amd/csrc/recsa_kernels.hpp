@@ -13,20 +13,34 @@ inline int64_t level_rows_host(int64_t L_cap, int level) { return L_cap >> (4 * 
 // Workspace layout (bytes, 256-aligned regions):
 //   logits  [n_queries*Hkv][n_sel][G][C*k] float   scored candidates' logits
 //   bitmap  [n_queries*Hkv][n_sel][C*k/32] uint32  kept list positions
+//   buckets (bf16, n_queries*Hkv >= kBucketMinSlots) multi-query scoring by
+//           parent: count/off/cursor [n_keys] int32, tile_key/tile_first
+//           [max_tiles] int32, entries [max_entries] uint2, n_tiles int32,
+//           n_keys = B*Hkv*(N_2+1) (the parents of level 1, the longest lists)
 //   part    [B*Hkv][kPartSlots][G][d+2] float      decode attention partials
 //   ctl     [B*Hkv][kCtlWords] uint32              fused-decode control block:
 //           word 1 = error word, words 16 + 16*w = arrival flag of workgroup w
 // The ctl words must be zero before the first recsa_decode call; every call
 // leaves them zero (except the error word, see recsa.h).
 constexpr int kDecodeSplits = 64;    // attention workgroups per (query, KV head), decode
+// most workgroups per query along the query launch dimension (scoring:
+// C*k/64 <= 64 list blocks; decode attention: kDecodeSplits)
+constexpr int kQueryLaunchX = 64;
 constexpr int kFusedMaxW = 32;       // workgroups per (sequence, KV head), fused decode
 constexpr int kPartSlots = kDecodeSplits > kFusedMaxW ? kDecodeSplits : kFusedMaxW;
 constexpr int kCtlWords = 16 + 16 * kFusedMaxW;   // one 64-byte line per flag
+constexpr int kBucketTile = 64;                   // bucket entries per scoring tile
+constexpr int64_t kBucketMinSlots = 256;          // (query, KV head) slots from which
+                                                  // bf16 scoring is bucketed by parent
 
 struct WsLayout {
   int n_sel, G, CK, d, n_split;
   int64_t n_slots;            // n_queries * Hkv
   int64_t logits_off, bitmap_off, part_off, ctl_off, total;   // bytes
+  bool bucket;                // multi-query scoring by parent
+  int64_t bk_keys, bk_max_tiles, bk_max_entries;
+  int64_t bk_count_off, bk_off_off, bk_cursor_off, bk_tkey_off, bk_tfirst_off, bk_entries_off,
+      bk_ntiles_off;          // bytes
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~static_cast<int64_t>(255); }
@@ -44,7 +58,29 @@ inline WsLayout ws_layout(const recsa_tree& tr, int Hq, int64_t n_queries) {
   const int64_t heads = static_cast<int64_t>(tr.B) * tr.Hkv;
   w.logits_off = 0;
   w.bitmap_off = align256(w.logits_off + w.n_slots * slot_floats * 4);
-  w.part_off = align256(w.bitmap_off + w.n_slots * slot_words * 4);
+  int64_t end = w.bitmap_off + w.n_slots * slot_words * 4;
+  // parents of level-1 lists: nodes 0 .. N_2 of level 2 (node N_2 may be the
+  // incomplete current node, whose complete children are still scored)
+  w.bk_keys = static_cast<int64_t>(tr.B) * tr.Hkv * (level_rows_host(tr.L_cap, 2) + 1);
+  w.bk_max_entries = w.n_slots * tr.k;       // <= k parents per (query, head, level)
+  w.bk_max_tiles = w.bk_max_entries / kBucketTile + w.bk_keys + 1;
+  w.bucket = tr.dtype == RECSA_BF16 && tr.n_levels >= 3 && w.n_slots >= kBucketMinSlots &&
+             w.bk_keys < (int64_t{1} << 30) && w.bk_max_tiles < (int64_t{1} << 30) &&
+             w.bk_max_entries < (int64_t{1} << 31) &&
+             n_queries < (int64_t{1} << 31);
+  w.bk_count_off = w.bk_off_off = w.bk_cursor_off = w.bk_tkey_off = w.bk_tfirst_off =
+      w.bk_entries_off = w.bk_ntiles_off = 0;
+  if (w.bucket) {
+    w.bk_count_off = align256(end);
+    w.bk_off_off = align256(w.bk_count_off + w.bk_keys * 4);
+    w.bk_cursor_off = align256(w.bk_off_off + w.bk_keys * 4);
+    w.bk_tkey_off = align256(w.bk_cursor_off + w.bk_keys * 4);
+    w.bk_tfirst_off = align256(w.bk_tkey_off + w.bk_max_tiles * 4);
+    w.bk_entries_off = align256(w.bk_tfirst_off + w.bk_max_tiles * 4);
+    w.bk_ntiles_off = align256(w.bk_entries_off + w.bk_max_entries * 8);
+    end = w.bk_ntiles_off + 4;
+  }
+  w.part_off = align256(end);
   w.ctl_off = align256(w.part_off + heads * kPartSlots * w.G * (w.d + 2) * 4);
   w.total = w.ctl_off + heads * kCtlWords * 4;   // the control words end the workspace
   return w;

@@ -1,0 +1,142 @@
+// Selection logits on the gfx950 matrix cores (bf16 storage only): the
+// logits of one 16-row candidate group -- the B operand, its rows are the
+// output columns -- against up to 16 rotated query rows -- the A operand --
+// with v_mfma_f32_16x16x32_bf16, D/32 k blocks accumulated in ascending
+// order.  Every path that forms a selection logit (per-query scoring, the
+// fused decode, the bucketed multi-query scoring) goes through
+// mfma_logits, so a (query row, key row) pair gets the same float32 logit
+// whichever kernel computes it and wherever the row sits in the tile.
+//
+// Lane layout of the instruction (checked on the device):
+//   A: lane l holds row l%16, k = 8*(l/16) + [0, 8) of each 32-wide block
+//   B: lane l holds column l%16, the same k
+//   C: lane l holds rows 4*(l/16) + i, i = 0..3, of column l%16
+// The operands are the two rounded halves of the split candidate-local
+// RoPE (picx.dev, Key Theoretical Insight): rnd(R(phi) q) and the stored
+// rotated key rows Kr = rnd(R(c) K); every bf16 product is exact in float32.
+#pragma once
+
+#include "recsa_common.hpp"
+
+namespace recsa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// One lane's share of a 16 x D bf16 operand: 8 dims of each 32-wide block.
+template <int D>
+struct MFrag {
+  static_assert(D % 64 == 0, "head dim");
+  uint4 w[D / 32];
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+// B operand: rows [0, nrows) of a group of 16 consecutive stored rows; the
+// other rows read as 0 (their logits are never stored).
+template <int D>
+__device__ __forceinline__ void load_key_frag(const uint16_t* __restrict__ rows, int nrows,
+                                              MFrag<D>& f) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, h = lane >> 4;
+  if (r < nrows) {
+    const uint16_t* p = rows + static_cast<int64_t>(r) * D + 8 * h;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) f.w[kb] = *reinterpret_cast<const uint4*>(p + 32 * kb);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) f.w[kb] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// A operand from G rotated query heads already in LDS (bf16, [G][D] in
+// natural dim order, 16-byte aligned): row m < G is head m, rows >= G are 0.
+template <int D, int G>
+__device__ __forceinline__ void query_frag_lds(const uint16_t* qt, MFrag<D>& f) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int m = lane & 15, h = lane >> 4;
+  if (m < G) {
+    const uint16_t* p = qt + m * D + 8 * h;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) f.w[kb] = *reinterpret_cast<const uint4*>(p + 32 * kb);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) f.w[kb] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// A operand row of this lane built in registers: the bf16 query row qrow
+// rotated by table row phi and rounded, rnd(R(phi) q).  The block pairs
+// (kb, kb + D/64) hold dims j and j + D/2, the two members of a RoPE pair,
+// so each lane rotates its own 8 pairs per block pair.  !valid gives 0.
+template <int D>
+__device__ __forceinline__ void rotated_query_frag(const uint16_t* __restrict__ qrow, int phi,
+                                                   const float* __restrict__ rope, bool valid,
+                                                   MFrag<D>& f) {
+  constexpr int H2 = D / 2, HKB = D / 64;
+  const int h = (threadIdx.x & (kWave - 1)) >> 4;
+  if (!valid) {
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) f.w[kb] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+  const float* rrow = rope + static_cast<int64_t>(phi) * H2 * 2;
+#pragma unroll
+  for (int kb = 0; kb < HKB; ++kb) {
+    const int j0 = 32 * kb + 8 * h;                 // dims j0 .. j0+7 and their partners
+    const uint4 xw = *reinterpret_cast<const uint4*>(qrow + j0);
+    const uint4 yw = *reinterpret_cast<const uint4*>(qrow + H2 + j0);
+    float4 cs[4];                                   // (cos, sin) of pairs j0 .. j0+7
+#pragma unroll
+    for (int v = 0; v < 4; ++v) cs[v] = *reinterpret_cast<const float4*>(rrow + 2 * j0 + 4 * v);
+    const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w};
+    const uint32_t ya[4] = {yw.x, yw.y, yw.z, yw.w};
+    uint32_t xo[4], yo[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x0, y0, x1, y1;
+      rope_pair(__uint_as_float(xa[v] << 16), __uint_as_float(ya[v] << 16), cs[v].x, cs[v].y,
+                x0, y0);
+      rope_pair(__uint_as_float(xa[v] & 0xFFFF0000u), __uint_as_float(ya[v] & 0xFFFF0000u),
+                cs[v].z, cs[v].w, x1, y1);
+      xo[v] = pack_bf16x2(x0, x1);
+      yo[v] = pack_bf16x2(y0, y1);
+    }
+    f.w[kb] = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+    f.w[kb + HKB] = make_uint4(yo[0], yo[1], yo[2], yo[3]);
+  }
+}
+
+// C = A B^T over the D dims, k blocks in ascending order (unscaled).
+template <int D>
+__device__ __forceinline__ f32x4_t mfma_logits(const MFrag<D>& a, const MFrag<D>& b) {
+  f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb)
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.w[kb]),
+                                                __builtin_bit_cast(bf16x8_t, b.w[kb]), c, 0, 0, 0);
+  return c;
+}
+
+// Logits of one group (rows [0, nvalid) of `rows`, stored rotated keys)
+// against the G rotated query heads in LDS `qt`, written to
+// out[g * CK + n] for n < nvalid by lanes 0..15 (lane n holds row n).
+template <int D, int G>
+__device__ __forceinline__ void group_logits_mfma(const uint16_t* __restrict__ rows, int nvalid,
+                                                  const uint16_t* qt, float* out, int CK) {
+  MFrag<D> kf, qf;
+  load_key_frag<D>(rows, nvalid, kf);
+  query_frag_lds<D, G>(qt, qf);
+  const f32x4_t c = mfma_logits<D>(qf, kf);
+  const int lane = threadIdx.x & (kWave - 1);
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  if (lane < nvalid && lane < 16) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) out[static_cast<int64_t>(g) * CK + lane] = c[g] * scale;
+  }
+}
+
+}  // namespace recsa
