@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--workload", default="524k")
     ap.add_argument("--decode-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="counter pass only: a 512 MiB device copy (the calibration kernel), "
+                         "then the workload's fused decode step 5 times; prints no result")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -186,6 +189,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.pmc_pass:
+        pmc_pass(args.workload)
+        return
     w = setup_workload(args.workload)
     wl, tree, pool, R = w.wl, w.tree, w.pool, w.R
     L, T, B, Hkv, Hq, d = w.L, w.T, wl.B, wl.Hkv, wl.Hq, wl.d
@@ -300,6 +306,13 @@ def main():
         "avg_launch_us": round(split["decode_fused_us"], 2),
     }
     step_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
+    # prefill scoring: 2 d flops per (query head, scored candidate); the
+    # select call also files the candidates and runs the top-k, so the
+    # fraction below is a lower bound for the scoring kernel itself
+    g_q = Hq // Hkv
+    scored = sum(decode_rows(t, 16, wl.k, tree.n_levels)["scored_keys"] for t in range(L, L + T))
+    score_flops = scored * 2 * d * g_q * Hkv * B
+    sel_tflops = score_flops / (split["prefill_select_us"] * 1e-6) / 1e12
 
     result = {
         "metric": "RecSA decode µs/token & prefill tok/s at 524K; % HBM / MFMA peak",
@@ -332,6 +345,10 @@ def main():
         "build_full_GBs": round(bb / build_s / 1e9, 1),
         "build_full_hbm_frac": round(bb / build_s / 1e9 / HBM_PEAK_GBS, 4),
         "split_us": {k_: round(v, 1) for k_, v in split.items()},
+        "prefill_scoring": {"algorithmic_GFLOP": round(score_flops / 1e9, 1),
+                            "select_TFLOPs": round(sel_tflops, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                            "select_frac": round(sel_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "dtype": "bf16 operands, fp32 accumulate (v_mfma_f32_16x16x32_bf16)"},
         "roofline": roof,
         "cache_state": "decode replays after a prefill chunk; levels >= 1 (~134 MB) fit the 256 MB MALL",
     }
@@ -340,6 +357,26 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T)
     print(json.dumps(result), flush=True)
+
+
+COPY_BYTES = 512 << 20
+
+
+def pmc_pass(name):
+    """The launches a hardware-counter run reads: one plain device copy of
+    COPY_BYTES (read once, written once), then the workload's fused decode
+    step, five times, after the full build."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    w = setup_workload(name)
+    w.build_full()
+    for _ in range(5):
+        w.decode()
+    torch.cuda.synchronize()
+    log(f"pmc pass done: copy of {COPY_BYTES} bytes, 5 fused decode steps")
 
 
 def cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T):

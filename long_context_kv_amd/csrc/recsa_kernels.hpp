@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "recsa.h"
 
 namespace recsa {
@@ -14,9 +16,8 @@ inline int64_t level_rows_host(int64_t L_cap, int level) { return L_cap >> (4 * 
 //   logits  [n_queries*Hkv][n_sel][G][C*k] float   scored candidates' logits
 //   bitmap  [n_queries*Hkv][n_sel][C*k/32] uint32  kept list positions
 //   buckets (bf16, n_queries*Hkv >= kBucketMinSlots) multi-query scoring by
-//           parent: count/off/cursor [n_keys] int32, tile_key/tile_first
-//           [max_tiles] int32, entries [max_entries] uint2, n_tiles int32,
-//           n_keys = B*Hkv*(N_2+1) (the parents of level 1, the longest lists)
+//           parent: tiles [max_tiles] uint4, entries [regions][kFileQueries*k]
+//           uint2 (one region per filing workgroup), n_tiles int32
 //   part    [B*Hkv][kPartSlots][G][d+2] float      decode attention partials
 //   ctl     [B*Hkv][kCtlWords] uint32              fused-decode control block:
 //           word 1 = error word, words 16 + 16*w = arrival flag of workgroup w
@@ -32,15 +33,16 @@ constexpr int kCtlWords = 16 + 16 * kFusedMaxW;   // one 64-byte line per flag
 constexpr int kBucketTile = 64;                   // bucket entries per scoring tile
 constexpr int64_t kBucketMinSlots = 256;          // (query, KV head) slots from which
                                                   // bf16 scoring is bucketed by parent
+constexpr int kFileQueries = 256;                 // queries per filing workgroup
+constexpr int kFileMaxUp = 16384;                 // parents per (sequence, head) it bins in LDS
 
 struct WsLayout {
   int n_sel, G, CK, d, n_split;
   int64_t n_slots;            // n_queries * Hkv
   int64_t logits_off, bitmap_off, part_off, ctl_off, total;   // bytes
   bool bucket;                // multi-query scoring by parent
-  int64_t bk_keys, bk_max_tiles, bk_max_entries;
-  int64_t bk_count_off, bk_off_off, bk_cursor_off, bk_tkey_off, bk_tfirst_off, bk_entries_off,
-      bk_ntiles_off;          // bytes
+  int64_t bk_regions, bk_max_tiles, bk_max_entries;
+  int64_t bk_tiles_off, bk_entries_off, bk_ntiles_off;   // bytes
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~static_cast<int64_t>(255); }
@@ -59,24 +61,24 @@ inline WsLayout ws_layout(const recsa_tree& tr, int Hq, int64_t n_queries) {
   w.logits_off = 0;
   w.bitmap_off = align256(w.logits_off + w.n_slots * slot_floats * 4);
   int64_t end = w.bitmap_off + w.n_slots * slot_words * 4;
-  // parents of level-1 lists: nodes 0 .. N_2 of level 2 (node N_2 may be the
-  // incomplete current node, whose complete children are still scored)
-  w.bk_keys = static_cast<int64_t>(tr.B) * tr.Hkv * (level_rows_host(tr.L_cap, 2) + 1);
-  w.bk_max_entries = w.n_slots * tr.k;       // <= k parents per (query, head, level)
-  w.bk_max_tiles = w.bk_max_entries / kBucketTile + w.bk_keys + 1;
+  // parents of level-1 lists (the longest): nodes 0 .. N_2 of level 2 (node
+  // N_2 may be the incomplete current node, whose complete children are
+  // still scored).  Filing workgroups: at most n_queries/kFileQueries + B per
+  // KV head (blocks of one sequence), each with a region of kFileQueries*k
+  // entries (<= k parents per query) and at most one partial tile per parent.
+  const int64_t n_up = level_rows_host(tr.L_cap, 2) + 1;
+  w.bk_regions = (n_queries / kFileQueries + tr.B) * tr.Hkv;
+  w.bk_max_entries = w.bk_regions * kFileQueries * tr.k;
+  w.bk_max_tiles =
+      w.bk_regions * (std::min<int64_t>(n_up, int64_t{kFileQueries} * tr.k) +
+                      int64_t{kFileQueries} * tr.k / kBucketTile);
   w.bucket = tr.dtype == RECSA_BF16 && tr.n_levels >= 3 && w.n_slots >= kBucketMinSlots &&
-             w.bk_keys < (int64_t{1} << 30) && w.bk_max_tiles < (int64_t{1} << 30) &&
-             w.bk_max_entries < (int64_t{1} << 31) &&
-             n_queries < (int64_t{1} << 31);
-  w.bk_count_off = w.bk_off_off = w.bk_cursor_off = w.bk_tkey_off = w.bk_tfirst_off =
-      w.bk_entries_off = w.bk_ntiles_off = 0;
+             n_up <= kFileMaxUp && w.bk_max_entries < (int64_t{1} << 32) &&
+             w.bk_max_tiles < (int64_t{1} << 31) && n_queries < (int64_t{1} << 31);
+  w.bk_tiles_off = w.bk_entries_off = w.bk_ntiles_off = 0;
   if (w.bucket) {
-    w.bk_count_off = align256(end);
-    w.bk_off_off = align256(w.bk_count_off + w.bk_keys * 4);
-    w.bk_cursor_off = align256(w.bk_off_off + w.bk_keys * 4);
-    w.bk_tkey_off = align256(w.bk_cursor_off + w.bk_keys * 4);
-    w.bk_tfirst_off = align256(w.bk_tkey_off + w.bk_max_tiles * 4);
-    w.bk_entries_off = align256(w.bk_tfirst_off + w.bk_max_tiles * 4);
+    w.bk_tiles_off = align256(end);
+    w.bk_entries_off = align256(w.bk_tiles_off + w.bk_max_tiles * 16);
     w.bk_ntiles_off = align256(w.bk_entries_off + w.bk_max_entries * 8);
     end = w.bk_ntiles_off + 4;
   }

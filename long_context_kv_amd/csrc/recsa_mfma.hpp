@@ -68,40 +68,52 @@ __device__ __forceinline__ void query_frag_lds(const uint16_t* qt, MFrag<D>& f) 
   }
 }
 
-// A operand row of this lane built in registers: the bf16 query row qrow
-// rotated by table row phi and rounded, rnd(R(phi) q).  The block pairs
-// (kb, kb + D/64) hold dims j and j + D/2, the two members of a RoPE pair,
-// so each lane rotates its own 8 pairs per block pair.  !valid gives 0.
+// The (cos, sin) entries of table row phi for the pairs this lane rotates in
+// rotate_frag: 8 pairs per block pair, loaded once and reused for every
+// query head of the row.
 template <int D>
-__device__ __forceinline__ void rotated_query_frag(const uint16_t* __restrict__ qrow, int phi,
-                                                   const float* __restrict__ rope, bool valid,
-                                                   MFrag<D>& f) {
-  constexpr int H2 = D / 2, HKB = D / 64;
+struct RopeFrag {
+  float4 cs[D / 64][4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_rope_frag(int phi, const float* __restrict__ rope,
+                                               RopeFrag<D>& r) {
+  constexpr int H2 = D / 2;
   const int h = (threadIdx.x & (kWave - 1)) >> 4;
-  if (!valid) {
-#pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb) f.w[kb] = make_uint4(0u, 0u, 0u, 0u);
-    return;
-  }
   const float* rrow = rope + static_cast<int64_t>(phi) * H2 * 2;
 #pragma unroll
+  for (int kb = 0; kb < D / 64; ++kb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      r.cs[kb][v] = *reinterpret_cast<const float4*>(rrow + 2 * (32 * kb + 8 * h) + 4 * v);
+}
+
+// A operand row of this lane: the bf16 query row qrow rotated with the
+// table entries in r and rounded, rnd(R(phi) q) -- the values rotate_query
+// produces.  The block pairs (kb, kb + D/64) hold dims j and j + D/2, the
+// two members of a RoPE pair, so each lane rotates its own 8 pairs per
+// block pair.
+template <int D>
+__device__ __forceinline__ void rotate_frag(const uint16_t* __restrict__ qrow,
+                                            const RopeFrag<D>& r, MFrag<D>& f) {
+  constexpr int H2 = D / 2, HKB = D / 64;
+  const int h = (threadIdx.x & (kWave - 1)) >> 4;
+#pragma unroll
   for (int kb = 0; kb < HKB; ++kb) {
-    const int j0 = 32 * kb + 8 * h;                 // dims j0 .. j0+7 and their partners
+    const int j0 = 32 * kb + 8 * h;
     const uint4 xw = *reinterpret_cast<const uint4*>(qrow + j0);
     const uint4 yw = *reinterpret_cast<const uint4*>(qrow + H2 + j0);
-    float4 cs[4];                                   // (cos, sin) of pairs j0 .. j0+7
-#pragma unroll
-    for (int v = 0; v < 4; ++v) cs[v] = *reinterpret_cast<const float4*>(rrow + 2 * j0 + 4 * v);
     const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w};
     const uint32_t ya[4] = {yw.x, yw.y, yw.z, yw.w};
     uint32_t xo[4], yo[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float x0, y0, x1, y1;
-      rope_pair(__uint_as_float(xa[v] << 16), __uint_as_float(ya[v] << 16), cs[v].x, cs[v].y,
-                x0, y0);
+      rope_pair(__uint_as_float(xa[v] << 16), __uint_as_float(ya[v] << 16), r.cs[kb][v].x,
+                r.cs[kb][v].y, x0, y0);
       rope_pair(__uint_as_float(xa[v] & 0xFFFF0000u), __uint_as_float(ya[v] & 0xFFFF0000u),
-                cs[v].z, cs[v].w, x1, y1);
+                r.cs[kb][v].z, r.cs[kb][v].w, x1, y1);
       xo[v] = pack_bf16x2(x0, x1);
       yo[v] = pack_bf16x2(y0, y1);
     }
@@ -119,24 +131,6 @@ __device__ __forceinline__ f32x4_t mfma_logits(const MFrag<D>& a, const MFrag<D>
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.w[kb]),
                                                 __builtin_bit_cast(bf16x8_t, b.w[kb]), c, 0, 0, 0);
   return c;
-}
-
-// Logits of one group (rows [0, nvalid) of `rows`, stored rotated keys)
-// against the G rotated query heads in LDS `qt`, written to
-// out[g * CK + n] for n < nvalid by lanes 0..15 (lane n holds row n).
-template <int D, int G>
-__device__ __forceinline__ void group_logits_mfma(const uint16_t* __restrict__ rows, int nvalid,
-                                                  const uint16_t* qt, float* out, int CK) {
-  MFrag<D> kf, qf;
-  load_key_frag<D>(rows, nvalid, kf);
-  query_frag_lds<D, G>(qt, qf);
-  const f32x4_t c = mfma_logits<D>(qf, kf);
-  const int lane = threadIdx.x & (kWave - 1);
-  const float scale = 1.0f / sqrtf(static_cast<float>(D));
-  if (lane < nvalid && lane < 16) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) out[static_cast<int64_t>(g) * CK + lane] = c[g] * scale;
-  }
 }
 
 }  // namespace recsa

@@ -178,93 +178,116 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const float* part, floa
 // Many queries per call (prefill chunks).  The list of a query at level l is
 // the children of its parents -- S^(l+1), or the whole prefix when level l+1
 // is fully selected -- C rows per parent in parent order, so list group r of
-// query q holds the C rows under its r-th parent u.  Each (query, group)
-// pair is filed under the bucket (sequence, KV head, u); a wave loads the
-// parent's C rotated key rows once, as the B operand, and scores them
-// against C/G of the bucket's queries per matrix instruction, each query
-// row rotated by its own phi = p_q - C r.  The logits are the float32 values
-// the per-query kernel computes (same operands, same k order).
+// query q holds the C rows under its r-th parent u.  A filing workgroup
+// takes kFileQueries queries of one sequence and one KV head and sorts
+// their (query, group) pairs by parent into its own region of the entry
+// array (an LDS histogram, its scan, then LDS ranks); each run of one
+// parent becomes tiles of at most kBucketTile entries.  A scoring wave then
+// loads a parent's C rotated key rows once, as the B operand, and scores them
+// against C entries at a time, each query row rotated by its own
+// phi = p_q - C r.  The logits are the float32 values the per-query kernel
+// computes (same operands, same k order).
 struct BucketArgs {
-  int32_t* count;       // [n_keys] entries per bucket
-  int32_t* off;         // [n_keys] first entry of each bucket
-  int32_t* cursor;      // [n_keys] next free entry while filing
-  int32_t* tile_key;    // [max_tiles] bucket of each tile
-  int32_t* tile_first;  // [max_tiles] first entry of each tile
-  uint2* entries;       // [max_entries] {query index, phi | r << 12 | nvalid << 20}
+  uint4* tiles;         // [max_tiles] {first entry, entries, sequence*Hkv + head, parent}
+  uint2* entries;       // [regions][kFileQueries * k] {query index, phi | r << 12 | nvalid << 20}
   int32_t* n_tiles;     // tiles of this level
-  int n_keys;           // B * Hkv * n_up
-  int64_t n_up;         // parents per (sequence, KV head): N_{l+1} + 1
+  int n_up;             // parents per (sequence, KV head): N_{l+1} + 1
 };
 
 __global__ void bucket_clear_kernel(BucketArgs ba) {
-  const int i0 = blockIdx.x * blockDim.x + threadIdx.x;
-  for (int i = i0; i < ba.n_keys; i += gridDim.x * blockDim.x) ba.count[i] = 0;
-  if (i0 == 0) *ba.n_tiles = 0;
+  if (threadIdx.x == 0) *ba.n_tiles = 0;
 }
 
-// FILE = false: count the entries of every bucket; true: file them.
-// Grid (n_queries, Hkv); thread r takes list group r.
-template <bool FILE>
+// Grid (B * ceil(T / kFileQueries), Hkv).
 __global__ void __launch_bounds__(kBlock)
-    bucket_file_kernel(recsa_tree tr, int T, const int64_t* pos, int32_t* sel, int32_t* cnt,
-                       int level, int n_sel, BucketArgs ba) {
-  const QueryCtx qc = query_ctx(tr, T, pos, sel, cnt, n_sel, 1);
-  const ListView lv = list_view(qc.t, level, tr.n_levels - 1, tr.k, qc.sel, qc.cnt);
-  if (lv.len <= tr.k) return;                       // fully selected level
-  const int n = lv.len - 1;                         // scored positions [0, n)
-  const int ng = (n + kC - 1) / kC;
-  for (int r = threadIdx.x; r < ng; r += kBlock) {
-    const int64_t key = qc.seq_head * ba.n_up + lv.node(r * kC) / kC;
-    if constexpr (!FILE) {
-      atomicAdd(&ba.count[key], 1);
-    } else {
-      const int at = atomicAdd(&ba.cursor[key], 1);
-      const uint32_t phi = static_cast<uint32_t>(n - r * kC);      // p_q - C r
-      const uint32_t nvalid = static_cast<uint32_t>(min(kC, n - r * kC));
-      ba.entries[at] = make_uint2(static_cast<uint32_t>(qc.qi),
-                                  phi | (static_cast<uint32_t>(r) << 12) | (nvalid << 20));
-    }
+    bucket_file_kernel(recsa_tree tr, int T, const int64_t* pos, const int32_t* sel,
+                       const int32_t* cnt, int level, int n_sel, BucketArgs ba) {
+  constexpr int NW = kBlock / kWave;
+  __shared__ int bins[kFileMaxUp];          // counts, then entry offsets / ranks
+  __shared__ int red[NW];
+  __shared__ int s_len[kFileQueries];       // |A^(l)| of each query
+  __shared__ int64_t s_up[kFileQueries];    // offset of S^(l+1) in sel, -1 for a prefix list
+  __shared__ int s_tile0;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  const int k = tr.k, top = tr.n_levels - 1, n_up = ba.n_up;
+  const int nblk = (T + kFileQueries - 1) / kFileQueries;
+  const int b = static_cast<int>(blockIdx.x) / nblk;
+  const int tq0 = (static_cast<int>(blockIdx.x) % nblk) * kFileQueries;
+  const int nq = min(kFileQueries, T - tq0);
+  const int j = static_cast<int>(blockIdx.y);
+  const int64_t seq_head = static_cast<int64_t>(b) * tr.Hkv + j;
+  const int64_t qi0 = static_cast<int64_t>(b) * T + tq0;
+  const int64_t region = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) *
+                         static_cast<int64_t>(kFileQueries) * k;
+  // list geometry of every query (one query per thread)
+  for (int i = threadIdx.x; i < nq; i += kBlock) {
+    const int64_t slot = (qi0 + i) * tr.Hkv + j;
+    const ListView lv = list_view(pos[qi0 + i], level, top, k, sel + slot * n_sel * k,
+                                  cnt + slot * n_sel);
+    s_len[i] = lv.len;
+    s_up[i] = lv.up ? (lv.up - sel) : -1;
   }
-}
-
-// One workgroup: bucket offsets (exclusive scan of the counts), fill
-// cursors, and the tile list (every bucket cut into kBucketTile entries).
-constexpr int kScanThreads = 1024;
-__global__ void __launch_bounds__(kScanThreads) bucket_scan_kernel(BucketArgs ba) {
-  __shared__ int red[2][kScanThreads / kWave];
-  const int per = (ba.n_keys + kScanThreads - 1) / kScanThreads;
-  const int k0 = min(static_cast<int>(threadIdx.x) * per, ba.n_keys);
-  const int k1 = min(k0 + per, ba.n_keys);
+  for (int i = threadIdx.x; i < n_up; i += kBlock) bins[i] = 0;
+  __syncthreads();
+  // pass 1: entries per parent
+  for (int i = wid; i < nq; i += NW) {
+    const int len = s_len[i];
+    if (len <= k) continue;                          // fully selected level
+    const int ng = (len - 1 + kC - 1) / kC;
+    const int32_t* up = s_up[i] >= 0 ? sel + s_up[i] : nullptr;
+    for (int r = lane; r < ng; r += kWave) atomicAdd(&bins[up ? up[r] : r], 1);
+  }
+  __syncthreads();
+  // entry offsets and tiles: thread t owns parents [t*per, (t+1)*per)
+  const int per = (n_up + kBlock - 1) / kBlock;
+  const int u0 = min(static_cast<int>(threadIdx.x) * per, n_up), u1 = min(u0 + per, n_up);
   int ne = 0, nt = 0;
-  for (int key = k0; key < k1; ++key) {
-    const int c = ba.count[key];
-    ne += c;
-    nt += (c + kBucketTile - 1) / kBucketTile;
+  for (int u = u0; u < u1; ++u) {
+    ne += bins[u];
+    nt += (bins[u] + kBucketTile - 1) / kBucketTile;
   }
   int tot_e, tot_t;
-  int oe = block_scan_excl<kScanThreads>(ne, red[0], &tot_e);
-  int ot = block_scan_excl<kScanThreads>(nt, red[1], &tot_t);
-  for (int key = k0; key < k1; ++key) {
-    const int c = ba.count[key];
-    ba.off[key] = oe;
-    ba.cursor[key] = oe;
-    for (int f = 0; f < c; f += kBucketTile) {
-      ba.tile_key[ot] = key;
-      ba.tile_first[ot] = oe + f;
-      ++ot;
-    }
+  int oe = block_scan_excl<kBlock>(ne, red, &tot_e);
+  int ot = block_scan_excl<kBlock>(nt, red, &tot_t);
+  if (threadIdx.x == 0) s_tile0 = tot_t ? atomicAdd(ba.n_tiles, tot_t) : 0;
+  __syncthreads();
+  ot += s_tile0;
+  for (int u = u0; u < u1; ++u) {
+    const int c = bins[u];
+    for (int f = 0; f < c; f += kBucketTile)
+      ba.tiles[ot++] = make_uint4(static_cast<uint32_t>(region + oe + f),
+                                  static_cast<uint32_t>(min(kBucketTile, c - f)),
+                                  static_cast<uint32_t>(seq_head), static_cast<uint32_t>(u));
+    bins[u] = oe;
     oe += c;
   }
-  if (threadIdx.x == 0) *ba.n_tiles = tot_t;
+  __syncthreads();
+  // pass 2: file each entry at its parent's next free slot
+  for (int i = wid; i < nq; i += NW) {
+    const int len = s_len[i];
+    if (len <= k) continue;
+    const int n = len - 1;                           // scored positions [0, n)
+    const int ng = (n + kC - 1) / kC;
+    const int32_t* up = s_up[i] >= 0 ? sel + s_up[i] : nullptr;
+    for (int r = lane; r < ng; r += kWave) {
+      const int at = atomicAdd(&bins[up ? up[r] : r], 1);
+      const uint32_t phi = static_cast<uint32_t>(n - r * kC);      // p_q - C r
+      const uint32_t nvalid = static_cast<uint32_t>(min(kC, n - r * kC));
+      ba.entries[region + at] = make_uint2(static_cast<uint32_t>(qi0 + i),
+                                           phi | (static_cast<uint32_t>(r) << 12) | (nvalid << 20));
+    }
+  }
 }
 
 // Waves take tiles (grid-stride); per tile the parent's rows stay in
-// registers while C/G entries at a time are rotated and scored.
+// registers.  A rows are 16 bucket entries of one query head: each lane
+// loads the table row of its entry once, then rotates and scores the G
+// heads in turn; the next 16 entries are fetched while these are scored.
+// Rows past the tile's end compute with query 0 at phi 0 and are not stored.
 template <int D, int G>
 __global__ void __launch_bounds__(kBlock)
     bucket_score_kernel(recsa_tree tr, const void* q, int Hq, float* ws_logits, int level,
                         int n_sel, int CK, BucketArgs ba) {
-  constexpr int EPM = kC / G;                       // entries per matrix instruction
   constexpr int NW = kBlock / kWave;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
   const int m = lane & 15, h = lane >> 4;
@@ -273,37 +296,41 @@ __global__ void __launch_bounds__(kBlock)
   const uint16_t* qb = static_cast<const uint16_t*>(q);
   const int n_tiles = *ba.n_tiles;
   for (int tl = blockIdx.x * NW + wid; tl < n_tiles; tl += gridDim.x * NW) {
-    const int key = ba.tile_key[tl];
-    const int first = ba.tile_first[tl];
-    const int end = min(first + kBucketTile, ba.off[key] + ba.count[key]);
-    const int64_t sh = key / ba.n_up, u = key % ba.n_up;
+    const uint4 tile = ba.tiles[tl];
+    const int64_t first = tile.x, end = first + tile.y;
+    const int64_t sh = tile.z, u = tile.w;
     const int j = static_cast<int>(sh % tr.Hkv);
     MFrag<D> kf;
     load_key_frag<D>(static_cast<const uint16_t*>(tr.Kr[level]) + (sh * rows_l + u * kC) * D,
                      static_cast<int>(min<int64_t>(kC, rows_l - u * kC)), kf);
-    for (int e0 = first; e0 < end; e0 += EPM) {
-      // A row m: entry e0 + m / G, query head m % G
-      const int ei = e0 + m / G;
-      const bool ev = ei < end;
-      const uint2 ent = ev ? ba.entries[ei] : make_uint2(0u, 0u);
-      const uint16_t* qrow =
-          qb + (static_cast<int64_t>(ent.x) * Hq + static_cast<int64_t>(j) * G + m % G) * D;
-      MFrag<D> qf;
-      rotated_query_frag<D>(qrow, static_cast<int>(ent.y & 0xFFFu), tr.rope, ev, qf);
-      const f32x4_t c = mfma_logits<D>(qf, kf);
-      // this lane holds rows 4h + i of column m: entry (4h + i) / G, head (4h + i) % G
+    uint2 nxt = first + m < end ? ba.entries[first + m] : make_uint2(0u, 0u);
+    for (int64_t e0 = first; e0 < end; e0 += kC) {
+      const uint2 ent = nxt;                         // A row m: entry e0 + m
+      nxt = e0 + kC + m < end ? ba.entries[e0 + kC + m] : make_uint2(0u, 0u);
+      RopeFrag<D> rf;
+      load_rope_frag<D>(static_cast<int>(ent.y & 0xFFFu), tr.rope, rf);
+      // this lane's output rows 4h + i: entry e0 + 4h + i (held by lane 4h + i)
+      uint32_t ox[4], oy[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 4 * h + i;
-        const int er = row / G, g = row % G;
-        const uint32_t ex = __shfl(ent.x, er * G);
-        const uint32_t ey = __shfl(ent.y, er * G);
-        const int r = static_cast<int>((ey >> 12) & 0xFFu);
-        const int nvalid = static_cast<int>((ey >> 20) & 0x1Fu);
-        if (e0 + er < end && m < nvalid) {
-          const int64_t slot = static_cast<int64_t>(ex) * tr.Hkv + j;
-          ws_logits[((slot * n_sel + (level - 1)) * G + g) * static_cast<int64_t>(CK) + r * kC + m] =
-              c[i] * scale;
+        ox[i] = __shfl(ent.x, 4 * h + i);
+        oy[i] = __shfl(ent.y, 4 * h + i);
+      }
+      const uint16_t* qrow = qb + (static_cast<int64_t>(ent.x) * Hq + static_cast<int64_t>(j) * G) * D;
+#pragma unroll 1
+      for (int g = 0; g < G; ++g) {
+        MFrag<D> qf;
+        rotate_frag<D>(qrow + g * D, rf, qf);
+        const f32x4_t c = mfma_logits<D>(qf, kf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = static_cast<int>((oy[i] >> 12) & 0xFFu);
+          const int nvalid = static_cast<int>((oy[i] >> 20) & 0x1Fu);
+          if (e0 + 4 * h + i < end && m < nvalid) {
+            const int64_t slot = static_cast<int64_t>(ox[i]) * tr.Hkv + j;
+            ws_logits[((slot * n_sel + (level - 1)) * G + g) * static_cast<int64_t>(CK) + r * kC + m] =
+                c[i] * scale;
+          }
         }
       }
     }
@@ -313,15 +340,10 @@ __global__ void __launch_bounds__(kBlock)
 static BucketArgs bucket_args(const recsa_tree& tr, void* ws, const WsLayout& w, int level) {
   char* b = static_cast<char*>(ws);
   BucketArgs ba;
-  ba.count = reinterpret_cast<int32_t*>(b + w.bk_count_off);
-  ba.off = reinterpret_cast<int32_t*>(b + w.bk_off_off);
-  ba.cursor = reinterpret_cast<int32_t*>(b + w.bk_cursor_off);
-  ba.tile_key = reinterpret_cast<int32_t*>(b + w.bk_tkey_off);
-  ba.tile_first = reinterpret_cast<int32_t*>(b + w.bk_tfirst_off);
+  ba.tiles = reinterpret_cast<uint4*>(b + w.bk_tiles_off);
   ba.entries = reinterpret_cast<uint2*>(b + w.bk_entries_off);
   ba.n_tiles = reinterpret_cast<int32_t*>(b + w.bk_ntiles_off);
-  ba.n_up = level_rows_host(tr.L_cap, level + 1) + 1;     // + the incomplete current node
-  ba.n_keys = static_cast<int>(static_cast<int64_t>(tr.B) * tr.Hkv * ba.n_up);
+  ba.n_up = static_cast<int>(level_rows_host(tr.L_cap, level + 1) + 1);   // + the incomplete current node
   return ba;
 }
 
@@ -344,13 +366,11 @@ static hipError_t select_impl(const recsa_tree& tr, const void* q, int Hq, int T
       if constexpr (DT == RECSA_BF16) {
         if (w.bucket) {
           const BucketArgs ba = bucket_args(tr, ws, w, l);
-          const unsigned clear_blocks = static_cast<unsigned>(std::min(1024, (ba.n_keys + 255) / 256));
-          bucket_clear_kernel<<<clear_blocks, 256, 0, s>>>(ba);
-          bucket_file_kernel<false><<<dim3(nq, tr.Hkv), kBlock, 0, s>>>(tr, T, pos, sel, cnt, l,
-                                                                        w.n_sel, ba);
-          bucket_scan_kernel<<<1, kScanThreads, 0, s>>>(ba);
-          bucket_file_kernel<true><<<dim3(nq, tr.Hkv), kBlock, 0, s>>>(tr, T, pos, sel, cnt, l,
-                                                                       w.n_sel, ba);
+          bucket_clear_kernel<<<1, 64, 0, s>>>(ba);
+          const unsigned nblk = static_cast<unsigned>(tr.B) *
+                                static_cast<unsigned>((T + kFileQueries - 1) / kFileQueries);
+          bucket_file_kernel<<<dim3(nblk, tr.Hkv), kBlock, 0, s>>>(tr, T, pos, sel, cnt, l,
+                                                                  w.n_sel, ba);
           const int64_t wgs = (w.bk_max_tiles + kBlock / kWave - 1) / (kBlock / kWave);
           bucket_score_kernel<D, G><<<static_cast<unsigned>(std::min<int64_t>(wgs, 8192)), kBlock,
                                       0, s>>>(tr, q, Hq, logits, l, w.n_sel, w.CK, ba);

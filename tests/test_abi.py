@@ -127,14 +127,16 @@ def test_workspace_grows_with_queries():
     b = L.recsa_workspace_bytes(ctypes.byref(t), 32, 4096)
     # logits of 3 selection levels x 4 heads x 4096 positions per (query, head),
     # their bitmaps, and (bf16, >= 256 query-head slots) the scoring buckets:
-    # 3 int32 per parent of level 1 (N_2 + 1 per head), 2 int32 per tile,
-    # one uint2 per (query, head, parent), each region 256-byte aligned
+    # one region of 256 queries x k entries (uint2) per filing workgroup
+    # (4096/256 + B blocks per KV head) and its tiles (uint4, at most one
+    # partial tile per parent of level 1, N_2 + 1 of them), plus the tile
+    # count, each region 256-byte aligned
     def al(x):
         return (x + 255) // 256 * 256
-    keys = 8 * (528384 // 256 + 1)
-    entries = 4096 * 8 * 256
-    tiles = entries // 64 + keys + 1
-    buckets = 3 * al(keys * 4) + 2 * al(tiles * 4) + al(entries * 8) + al(4)
+    regions = (4096 // 256 + 1) * 8
+    n_up = 528384 // 256 + 1
+    tiles = regions * (min(n_up, 256 * 256) + 256 * 256 // 64)
+    buckets = al(tiles * 16) + al(regions * 256 * 256 * 8) + al(4)
     assert b - a == 4095 * 8 * (3 * 4 * 4096 * 4 + 3 * 128 * 4) + buckets
     # float32 trees are scored per query: no bucket region
     tf = _tree(dtype=R.RECSA_F32)
