@@ -24,9 +24,11 @@ oracle on a bounded sample of the same workload (rank 0, one thread).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -176,7 +178,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="counter pass only: a 512 MiB device copy (the calibration kernel), "
-                         "then the workload's fused decode step 5 times; prints no result")
+                         "then the workload's fused decode step 5 times and one prefill "
+                         "chunk; prints no result")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -297,11 +300,15 @@ def main():
     dec_us = float(np.mean(dec_ms)) * 1e3
     pre_s = float(np.mean(pre_ms)) / 1e3
     fused_gbs = dec_bytes / (split["decode_fused_us"] * 1e-6) / 1e9
+    traffic_b = measured_traffic(args.workload)
     roof = {
         "kernel": "decode_fused_kernel (recsa_decode: append + select + attention), "
                   "decode at t=%d" % t_dec,
         "bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(fused_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+        "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
+        "traffic": (round(traffic_b / (split["decode_fused_us"] * 1e-6) / 1e9, 1)
+                    if traffic_b else None),
+        "traffic_bytes_per_launch": traffic_b,
         "algorithmic_bytes_per_launch": dec_bytes,
         "avg_launch_us": round(split["decode_fused_us"], 2),
     }
@@ -360,12 +367,43 @@ def main():
 
 
 COPY_BYTES = 512 << 20
+# sources of the fused decode kernel: a counter summary counts only while
+# their hash matches the one recorded with it
+FUSED_SOURCES = ("long_context_kv_amd/csrc/decode_fused.hip", "long_context_kv_amd/csrc/recsa_common.hpp",
+                 "long_context_kv_amd/csrc/recsa_device.hpp", "long_context_kv_amd/csrc/recsa_mfma.hpp",
+                 "long_context_kv_amd/csrc/recsa_pool.hpp", "long_context_kv_amd/csrc/recsa_kernels.hpp",
+                 "include/recsa.h")
+
+
+def fused_sources_sha():
+    h = hashlib.sha256()
+    for f in FUSED_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per fused-decode launch (FETCH_SIZE and WRITE_SIZE, each
+    scaled by its reading of a plain copy of known size) from the committed
+    counter summary of this workload; None if there is none or the kernel's
+    sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_fused_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        txt = fh.read()
+    nb = re.search(r"traffic_bytes_per_launch:\s*(\d+)", txt)
+    sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]+)", txt)
+    if not (nb and sha) or sha.group(1) != fused_sources_sha():
+        return None
+    return int(nb.group(1))
 
 
 def pmc_pass(name):
     """The launches a hardware-counter run reads: one plain device copy of
     COPY_BYTES (read once, written once), then the workload's fused decode
-    step, five times, after the full build."""
+    step, five times, after the full build, then one prefill chunk."""
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -375,8 +413,9 @@ def pmc_pass(name):
     w.build_full()
     for _ in range(5):
         w.decode()
+    w.prefill()
     torch.cuda.synchronize()
-    log(f"pmc pass done: copy of {COPY_BYTES} bytes, 5 fused decode steps")
+    log(f"pmc pass done: copy of {COPY_BYTES} bytes, 5 fused decode steps, one prefill chunk")
 
 
 def cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T):

@@ -117,10 +117,19 @@ __device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uin
 // output element loads its W values at once.
 template <int D, int G, int NT>
 __device__ void merge_partials_fused(const float* __restrict__ pp, int W, float* __restrict__ o) {
+  static_assert(G * D <= NT, "one output element per thread");
   constexpr int stride = G * (D + 2);
   __shared__ float s_m[kFusedMaxW][kMaxG], s_l[kFusedMaxW][kMaxG];
   __shared__ float s_f[kFusedMaxW][kMaxG], s_inv[kMaxG];
   const int tid = threadIdx.x;
+  // the value loads do not depend on the weights: all W of this thread's
+  // element are issued first and land while the weights are formed
+  const bool has_e = tid < G * D;
+  const int ge = tid / D, dd = tid % D;
+  float av[kFusedMaxW];
+#pragma unroll
+  for (int w = 0; w < kFusedMaxW; ++w)
+    av[w] = (has_e && w < W) ? pp[w * stride + ge * (D + 2) + 2 + dd] : 0.f;
   if (tid < W * G) {
     const int w = tid / G, g = tid % G;
     s_m[w][g] = pp[w * stride + g * (D + 2)];
@@ -140,16 +149,12 @@ __device__ void merge_partials_fused(const float* __restrict__ pp, int W, float*
     s_inv[tid] = 1.0f / L;
   }
   __syncthreads();
-  for (int e = tid; e < G * D; e += NT) {
-    const int g = e / D, dd = e % D;
-    float av[kFusedMaxW];
-#pragma unroll
-    for (int w = 0; w < kFusedMaxW; ++w) av[w] = w < W ? pp[w * stride + g * (D + 2) + 2 + dd] : 0.f;
+  if (has_e) {
     float a = 0.f;
 #pragma unroll
     for (int w = 0; w < kFusedMaxW; ++w)
-      if (w < W) a += s_f[w][g] * av[w];
-    o[e] = a * s_inv[g];
+      if (w < W) a += s_f[w][ge] * av[w];
+    o[tid] = a * s_inv[ge];
   }
 }
 

@@ -323,6 +323,26 @@ __device__ __forceinline__ int block_scan_excl(int v, int* red, int* total) {
   return off + inc - v;
 }
 
+// The same scan for a buffer no thread still reads (one used once per
+// call): no barrier before its write.
+template <int NT>
+__device__ __forceinline__ int block_scan_excl_fresh(int v, int* red, int* total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(v);
+  if (lane == kWave - 1) red[wid] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = red[w];
+    off += (w < wid) ? x : 0;
+    tot += x;
+  }
+  *total = tot;
+  return off + inc - v;
+}
+
 // --------------------------------------------------------------- top-k
 constexpr int kHistBits = 11;
 constexpr int kHistBins = 1 << kHistBits;
@@ -335,10 +355,12 @@ struct TopkSmem {
   int small_pos[kSmallBin];
   uint32_t small_take[kMaxCK / 32];
   int s_nsmall;
-  float redg[kMaxG][16];
-  float redf[16];
-  int redi[16];
-  uint32_t redu[2][16];
+  float redg[kMaxG][16];      // per wave: softmax max of each head
+  float reds[kMaxG][16];      // per wave: softmax normaliser of each head
+  int redi[16];               // equal-key ranks
+  int redt[16];               // take ranks
+  int redb[2][16];            // radix bin totals per wave, by pass parity
+  uint32_t redu[2][16];       // key range
   int s_bin, s_need, s_full;
 };
 
@@ -364,6 +386,11 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   const int lane = tid & (kWave - 1), wid = tid >> 6;
   float e[G][PPT];
   float I[PPT];
+  // the first radix pass's bins and the small-bin state start at zero
+  // (ordered before their first use by the exchanges below)
+  for (int b = tid; b < kHistBins; b += NT) sm.hist[b] = 0;
+  for (int wd = tid; wd < kMaxCK / 32; wd += NT) sm.small_take[wd] = 0u;
+  if (tid == 0) sm.s_nsmall = 0;
   // ---- all logits first (one memory round trip), then per-head max and
   // normaliser with one block exchange for all heads
   // (each thread's PPT positions are contiguous and 16-byte aligned; the
@@ -382,6 +409,8 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
     for (int i = 0; i < PPT; ++i) if (p0 + i >= n) e[g][i] = -INFINITY;
   }
   {
+    // per head: the max (one exchange), then the normaliser (a second
+    // exchange on its own buffer, so neither needs a barrier before it)
     float M[G], Z[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -390,7 +419,6 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       for (int i = 0; i < PPT; ++i) m = fmaxf(m, e[g][i]);
       M[g] = wave_max(m);
     }
-    __syncthreads();
     if (lane == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g) sm.redg[g][wid] = M[g];
@@ -409,17 +437,16 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       }
       Z[g] = wave_sum(z);
     }
-    __syncthreads();
     if (lane == 0) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) sm.redg[g][wid] = Z[g];
+      for (int g = 0; g < G; ++g) sm.reds[g][wid] = Z[g];
     }
     __syncthreads();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float z = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) z += sm.redg[g][w];
+      for (int w = 0; w < NW; ++w) z += sm.reds[g][w];
       const float inv = 1.0f / z;
 #pragma unroll
       for (int i = 0; i < PPT; ++i) e[g][i] *= inv;
@@ -449,9 +476,11 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   int need = need0;
   bool whole_bin = false, small = false;
   if (need0 > 0) {
+    // the keys' range: the passes start at the highest bit where they differ,
+    // so the first pass's bins resolve the keys finely (coarse bins would
+    // pile many keys onto a few LDS counters)
     kmin = wave_min_u32(kmin);
     kmax = wave_max_u32(kmax);
-    __syncthreads();
     if ((tid & (kWave - 1)) == 0) {
       sm.redu[0][tid >> 6] = kmin;
       sm.redu[1][tid >> 6] = kmax;
@@ -469,29 +498,41 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
     // count in [0, 32] defined
     const uint32_t diff = kmin ^ kmax;
     int hb = diff ? 31 - __clz(diff) : -1;
+    const int hb0 = hb;
     pmask = static_cast<uint32_t>(0xFFFFFFFFull << (hb + 1));
     prefix = kmin & pmask;
+    int pass = 0;
 #pragma unroll 1
-    while (hb >= 0) {
+    for (; hb >= 0; ++pass) {
       const int lo = max(hb - (kHistBits - 1), 0);
       const int nb = hb - lo + 1;
       const uint32_t dmask = (1u << nb) - 1u;
-      for (int b = tid; b < (1 << nb); b += NT) sm.hist[b] = 0;
-      __syncthreads();
+      if (hb < hb0) {                                // later passes clear their own bins
+        __syncthreads();                             // after every read of the last pass's
+        for (int b = tid; b < (1 << nb); b += NT) sm.hist[b] = 0;
+        __syncthreads();
+      }
 #pragma unroll
       for (int i = 0; i < PPT; ++i)
         if (p0 + i < n && (key[i] & pmask) == prefix) atomicAdd(&sm.hist[(key[i] >> lo) & dmask], 1);
       __syncthreads();
-      // suffix counts over bins: thread t owns bins [t*BPT, (t+1)*BPT)
+      // suffix counts over bins: thread t owns bins [t*BPT, (t+1)*BPT);
+      // the keys above my range are those of the later lanes of my wave
+      // and of the later waves (per-wave totals, one exchange; the two
+      // buffers alternate between passes, so none is still being read)
       const int nbins = 1 << nb;
       const int bpt = (nbins + NT - 1) / NT;
       const int b0 = tid * bpt;
       int local = 0;
       for (int b = b0; b < min(b0 + bpt, nbins); ++b) local += sm.hist[b];
-      // reverse exclusive scan: count in bins above my range
-      int tot;
-      const int below = block_scan_excl<NT>(local, sm.redi, &tot);
-      int above = tot - below - local;
+      const int incl = wave_incl_scan(local);
+      const int wtot = __builtin_amdgcn_readlane(incl, kWave - 1);
+      int* redb = sm.redb[pass & 1];
+      if (lane == 0) redb[wid] = wtot;
+      __syncthreads();
+      int above = wtot - incl;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) above += (w > wid) ? redb[w] : 0;
       for (int b = min(b0 + bpt, nbins) - 1; b >= b0; --b) {
         const int h = sm.hist[b];
         if (above < need && need <= above + h) {
@@ -507,13 +548,10 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       need = sm.s_need;
       whole_bin = sm.s_full != 0;
       const int in_bin = sm.hist[sm.s_bin];
-      __syncthreads();
       if (whole_bin) break;
       if (lo > 0 && in_bin <= kSmallBin) {
         // few keys left in the boundary bin: rank them exactly (key
         // descending, then list position ascending) in one wave
-        if (tid == 0) sm.s_nsmall = 0;
-        __syncthreads();
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
           if (p0 + i < n && (key[i] & pmask) == prefix) {
@@ -522,7 +560,6 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
             sm.small_pos[at] = p0 + i;
           }
         }
-        for (int wd = tid; wd < kMaxCK / 32; wd += NT) sm.small_take[wd] = 0u;
         __syncthreads();
         if (tid < kWave) {
           const int m = sm.s_nsmall;
@@ -560,7 +597,8 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   int tot;
   // the equal keys' ranks by position matter only when the boundary bin is
   // neither kept whole nor ranked by the small-bin pass
-  const int eq_rank = (small || whole_bin) ? 0 : block_scan_excl<NT>(__popc(eqm), sm.redi, &tot);
+  const int eq_rank =
+      (small || whole_bin) ? 0 : block_scan_excl_fresh<NT>(__popc(eqm), sm.redi, &tot);
   uint32_t inm;
   if (small) {
     inm = (sm.small_take[p0 >> 5] >> (p0 & 31)) & eqm;
@@ -577,7 +615,7 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
     }
   }
   const uint32_t takem = gtm | inm;
-  int slot = block_scan_excl<NT>(__popc(takem), sm.redi, &tot);
+  int slot = block_scan_excl_fresh<NT>(__popc(takem), sm.redt, &tot);
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
     if ((takem >> i) & 1u) {
