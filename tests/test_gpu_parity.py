@@ -403,3 +403,31 @@ def test_small_k_decode_and_prefill(k):
     rep2 = _check_queries(ref, pdict, qd, p1.view(1, 1).cpu(), s2, c2, m2, o2, [0, 3], 1e-5,
                           2e-3, max_swaps=1)
     assert rep2.matched >= 1
+
+
+def test_prefill_two_sequences_bucketed_matches_per_query():
+    """Two sequences at different positions in one T-query call (B*T*Hkv =
+    640 slots, so the bf16 scoring is bucketed by parent across filing blocks
+    of both sequences): sampled queries equal the single-query (per-query
+    scoring) path exactly, and the oracle."""
+    _need_gpu()
+    B, Hkv, d, k, T = 2, 2, 128, 16, 160
+    L0 = 8192 + 37
+    L_cap = L0 + T + 16
+    wl, tree, pool, pdict = _setup(B, Hkv, d, L_cap, L_cap, k, "bf16", 41)
+    assert tree.n_levels == 4
+    R.recsa_build_tree(tree, pool, 0, L0 + T)
+    Hq = Hkv * 4
+    q = synth.to_storage(synth.normal((B, T, Hq, d), DEV, 41, 97), "bf16")
+    pos = (torch.arange(L0, L0 + T, device=DEV).view(1, T)
+           - 5 * torch.arange(B, device=DEV).view(B, 1)).contiguous()
+    sel, cnt, imp, out = _run_select_attn(tree, q, Hq, pos, decode=False)
+    idx = [0, 77, T - 1]
+    for i in idx:
+        s2, c2, m2, o2 = _run_select_attn(tree, q[:, i:i + 1].contiguous(), Hq,
+                                          pos[:, i:i + 1].contiguous(), decode=True)
+        assert np.array_equal(s2[:, 0], sel[:, i]) and np.array_equal(c2[:, 0], cnt[:, i])
+        assert np.array_equal(m2[:, 0], imp[:, i])
+    rep = _check_queries(tree, pdict, q[:, idx], pos[:, idx].cpu(), sel[:, idx], cnt[:, idx],
+                         imp[:, idx], out[:, idx], [0, 1], 1e-5, 2e-3, max_swaps=1)
+    assert rep.matched >= B * 2 * len(idx) - 1, rep
