@@ -58,7 +58,7 @@ extern "C" {
 
 #define RECSA_OK 0
 #define RECSA_E_INVALID (-1)     /* null pointer, bad shape, range error      */
-#define RECSA_E_UNSUPPORTED (-2) /* C != 16, d not 64/128, k*C > 4096, dtype  */
+#define RECSA_E_UNSUPPORTED (-2) /* C != 16, d not 64/128, k > 512, dtype    */
 #define RECSA_E_WORKSPACE (-3)   /* workspace smaller than required           */
 #define RECSA_E_HIP (-4)         /* HIP launch error                          */
 

@@ -111,29 +111,37 @@ __device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uin
   __syncthreads();
 }
 
-// Merge the W partial softmax states [W][G][2 + D] (max, sum, weighted
-// values) of one group into the output [G][D]: the (max, sum) pairs are
-// loaded once each and turned into per-partial weights in LDS, then every
-// output element loads its W values at once.
+// Merge the W partial softmax states [W][G][kPartHead + D] (max, sum, -,
+// -, weighted values) of one group into the output [G][D].  Thread
+// (column c, subset q) owns the 4 output values 4c..4c+3 over the partials
+// w = q, q + NQ, ...: it issues those 16-byte loads first, the (max, sum)
+// pairs become per-partial weights while they land, and the NQ subsets'
+// sums meet in LDS.
 template <int D, int G, int NT>
 __device__ void merge_partials_fused(const float* __restrict__ pp, int W, float* __restrict__ o) {
-  static_assert(G * D <= NT, "one output element per thread");
-  constexpr int stride = G * (D + 2);
+  constexpr int PS = D + kPartHead;                  // floats per query head of a partial
+  constexpr int stride = G * PS;
+  constexpr int NC = G * D / 4;                      // float4 columns of the output
+  static_assert(NT % NC == 0, "thread count");
+  constexpr int NQ = NT / NC;                        // partial subsets
+  constexpr int WQ = (kFusedMaxW + NQ - 1) / NQ;     // partials per thread
   __shared__ float s_m[kFusedMaxW][kMaxG], s_l[kFusedMaxW][kMaxG];
   __shared__ float s_f[kFusedMaxW][kMaxG], s_inv[kMaxG];
+  __shared__ float4 s_acc[NQ][NC];
   const int tid = threadIdx.x;
-  // the value loads do not depend on the weights: all W of this thread's
-  // element are issued first and land while the weights are formed
-  const bool has_e = tid < G * D;
-  const int ge = tid / D, dd = tid % D;
-  float av[kFusedMaxW];
+  const int c = tid % NC, qs = tid / NC;
+  const int ge = (4 * c) / D, dd = (4 * c) % D;
+  float4 av[WQ];
 #pragma unroll
-  for (int w = 0; w < kFusedMaxW; ++w)
-    av[w] = (has_e && w < W) ? pp[w * stride + ge * (D + 2) + 2 + dd] : 0.f;
+  for (int i = 0; i < WQ; ++i) {
+    const int w = qs + NQ * i;
+    av[i] = w < W ? *reinterpret_cast<const float4*>(pp + w * stride + ge * PS + kPartHead + dd)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   if (tid < W * G) {
     const int w = tid / G, g = tid % G;
-    s_m[w][g] = pp[w * stride + g * (D + 2)];
-    s_l[w][g] = pp[w * stride + g * (D + 2) + 1];
+    s_m[w][g] = pp[w * stride + g * PS];
+    s_l[w][g] = pp[w * stride + g * PS + 1];
   }
   __syncthreads();
   if (tid < W * G) {
@@ -148,13 +156,29 @@ __device__ void merge_partials_fused(const float* __restrict__ pp, int W, float*
     for (int v = 0; v < W; ++v) L += s_f[v][tid] * s_l[v][tid];
     s_inv[tid] = 1.0f / L;
   }
-  __syncthreads();
-  if (has_e) {
-    float a = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < kFusedMaxW; ++w)
-      if (w < W) a += s_f[w][ge] * av[w];
-    o[tid] = a * s_inv[ge];
+  for (int i = 0; i < WQ; ++i) {
+    const int w = qs + NQ * i;
+    if (w < W) {
+      const float f = s_f[w][ge];
+      a.x += f * av[i].x;
+      a.y += f * av[i].y;
+      a.z += f * av[i].z;
+      a.w += f * av[i].w;
+    }
+  }
+  s_acc[qs][c] = a;
+  __syncthreads();
+  if (tid < NC) {
+    float4 r = s_acc[0][c];
+#pragma unroll
+    for (int q2 = 1; q2 < NQ; ++q2) {
+      const float4 x = s_acc[q2][c];
+      r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+    }
+    const float inv = s_inv[ge];
+    *reinterpret_cast<float4*>(o + 4 * c) = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
   }
 }
 
@@ -169,8 +193,8 @@ __global__ void __launch_bounds__(kFusedThreads)
   constexpr int NW = NT / kWave;
   constexpr int kMaxSel = RECSA_MAX_LEVELS - 1;
   // S^(l) of every level for this group, level l at [(l-1)*k, l*k) -- the
-  // stride list_view reads the parent selection with (k <= 256)
-  __shared__ int32_t s_sel[kMaxSel * 256];
+  // stride list_view reads the parent selection with (k <= kMaxK)
+  __shared__ int32_t s_sel[kMaxSel * kMaxK];
   __shared__ int32_t s_cnt[kMaxSel + 1];
   __shared__ uint32_t s_bm[kMaxSel * (kMaxCK / 32)];
   __shared__ uint32_t s_fail;
@@ -298,8 +322,12 @@ __global__ void __launch_bounds__(kFusedThreads)
         group_barrier_xcd(counter, gen * static_cast<uint32_t>(W), err, &s_fail);
       else
         group_barrier(flags, w, W, gen, err, &s_fail);
-      wg_topk<G, NT>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1), s_bm + (l - 1) * bm_words,
-                     nullptr, sm.tk);
+      if (CK <= 4096)
+        wg_topk<G, NT, 4096>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1), s_bm + (l - 1) * bm_words,
+                             nullptr, sm.tk);
+      else
+        wg_topk<G, NT, kMaxCK>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1),
+                               s_bm + (l - 1) * bm_words, nullptr, sm.tk);
     }
     __syncthreads();
     if (w == 0) {                      // API outputs
@@ -314,14 +342,15 @@ __global__ void __launch_bounds__(kFusedThreads)
   // spread over the group's waves
   attn_groups<DT, D, G, NT, 2>(tr, t, slot, s_sel, s_cnt, eg, w, W, qs, lg_slot, s_bm, CK, k_t,
                                v_t, sm.at);
-  float* pp = part + (slot * kPartSlots + w) * static_cast<int64_t>(G) * (D + 2);
-  for (int e = tid; e < G * D; e += NT) pp[(e / D) * (D + 2) + 2 + e % D] = sm.at.wacc[0][e / D][e % D];
+  float* pp = part + (slot * kPartSlots + w) * static_cast<int64_t>(G) * (D + kPartHead);
+  for (int e = tid; e < G * D; e += NT)
+    pp[(e / D) * (D + kPartHead) + kPartHead + e % D] = sm.at.wacc[0][e / D][e % D];
   if (tid < G) {
-    pp[tid * (D + 2)] = sm.at.res_m[tid];
-    pp[tid * (D + 2) + 1] = sm.at.res_l[tid];
+    pp[tid * (D + kPartHead)] = sm.at.res_m[tid];
+    pp[tid * (D + kPartHead) + 1] = sm.at.res_l[tid];
   }
   float* o = out + (static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G) * D;
-  const float* pp_group = part + slot * kPartSlots * static_cast<int64_t>(G) * (D + 2);
+  const float* pp_group = part + slot * kPartSlots * static_cast<int64_t>(G) * (D + kPartHead);
   if constexpr (XL) {
     // ---- the last workgroup to arrive merges (its arrival completes the
     // count, so every partial is in the L2); the others are done

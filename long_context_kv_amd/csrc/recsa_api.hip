@@ -17,7 +17,7 @@ bool tree_ok(const recsa_tree* t, int* why) {
       t->n_levels > RECSA_MAX_LEVELS)
     return false;
   if (t->dtype != RECSA_F32 && t->dtype != RECSA_BF16) { *why = RECSA_E_UNSUPPORTED; return false; }
-  if (t->C != kC || (t->d != 64 && t->d != 128) || t->k > 256 ||
+  if (t->C != kC || (t->d != 64 && t->d != 128) || t->k > kMaxK ||
       static_cast<int64_t>(t->C) * t->k > kMaxCK) {
     *why = RECSA_E_UNSUPPORTED;
     return false;

@@ -11,7 +11,11 @@ namespace recsa {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;        // 4 waves per workgroup
 constexpr int kC = 16;             // branching factor (picx.dev Tree Construction)
-constexpr int kMaxCK = 4096;       // longest candidate list, C*k
+constexpr int kMaxK = 512;         // largest selection depth k
+// A partial softmax state of one query head: max, sum, two unused floats,
+// then the D weighted values (16-byte aligned for vector loads).
+constexpr int kPartHead = 4;
+constexpr int kMaxCK = 8192;       // longest candidate list, C*k
 constexpr int kMaxG = 8;           // query heads per KV head
 constexpr int kChunk = 256;        // list positions per attention/score chunk
 

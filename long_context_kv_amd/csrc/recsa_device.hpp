@@ -375,11 +375,14 @@ struct TopkSmem {
 // found by 11-bit radix passes starting at the highest bit where the keys
 // differ, and ties at the threshold go to the lower list position (= the
 // lower node index, the list being in ascending node order).
-template <int G, int NT>
+// CKM: the list-size class (C*k <= CKM), so thread i owns PPT = CKM/NT
+// positions; PPT divides C, so each thread's vector loads stay in its row.
+template <int G, int NT, int CKM = 4096>
 __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
                         int32_t* out_sel, int32_t* out_cnt, uint32_t* bm, float* imp,
                         TopkSmem& sm) {
-  constexpr int PPT = kMaxCK / NT;
+  static_assert(CKM <= kMaxCK && kC % (CKM / NT) == 0, "list-size class");
+  constexpr int PPT = CKM / NT;
   const int tid = threadIdx.x;
   const int p0 = tid * PPT;
   constexpr int NW = NT / kWave;
@@ -389,7 +392,7 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   // the first radix pass's bins and the small-bin state start at zero
   // (ordered before their first use by the exchanges below)
   for (int b = tid; b < kHistBins; b += NT) sm.hist[b] = 0;
-  for (int wd = tid; wd < kMaxCK / 32; wd += NT) sm.small_take[wd] = 0u;
+  for (int wd = tid; wd < CKM / 32; wd += NT) sm.small_take[wd] = 0u;
   if (tid == 0) sm.s_nsmall = 0;
   // ---- all logits first (one memory round trip), then per-head max and
   // normaliser with one block exchange for all heads
@@ -561,18 +564,18 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
           }
         }
         __syncthreads();
-        if (tid < kWave) {
-          const int m = sm.s_nsmall;
-          if (tid < m) {
-            const uint32_t ki = sm.small_key[tid];
-            const int pi = sm.small_pos[tid];
-            int rank = 0;
-            for (int q2 = 0; q2 < m; ++q2) {
-              const uint32_t kq = sm.small_key[q2];
-              rank += (kq > ki || (kq == ki && sm.small_pos[q2] < pi)) ? 1 : 0;
-            }
-            if (rank < need) atomicOr(&sm.small_take[pi >> 5], 1u << (pi & 31));
+        if (tid < kWave) {                           // wave 0; candidate q2 sits in lane q2
+          const int m = __builtin_amdgcn_readfirstlane(sm.s_nsmall);
+          const uint32_t ki = tid < m ? sm.small_key[tid] : 0u;
+          const int pi = tid < m ? sm.small_pos[tid] : 0;
+          int rank = 0;
+          for (int q2 = 0; q2 < m; ++q2) {
+            const uint32_t kq = static_cast<uint32_t>(
+                __builtin_amdgcn_readlane(static_cast<int>(ki), q2));
+            const int pq = __builtin_amdgcn_readlane(pi, q2);
+            rank += (kq > ki || (kq == ki && pq < pi)) ? 1 : 0;
           }
+          if (tid < m && rank < need) atomicOr(&sm.small_take[pi >> 5], 1u << (pi & 31));
         }
         __syncthreads();
         small = true;
@@ -1034,7 +1037,7 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
 template <int D, int G, int NT>
 __device__ __forceinline__ void merge_partials(const float* __restrict__ pp, int n_split,
                                                float* __restrict__ o) {
-  const int stride = G * (D + 2);
+  const int stride = G * (D + kPartHead);
   for (int e = threadIdx.x; e < G * D; e += NT) {
     const int g = e / D, dd = e % D;
     float M = -INFINITY, a = 0.f, l = 0.f;
@@ -1043,10 +1046,10 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ pp, int
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const bool ok = s0 + i < n_split;
-        const float* q = pp + (s0 + i) * stride + g * (D + 2);
+        const float* q = pp + (s0 + i) * stride + g * (D + kPartHead);
         ms[i] = ok ? q[0] : -INFINITY;
         ls[i] = ok ? q[1] : 0.f;
-        as[i] = ok ? q[2 + dd] : 0.f;
+        as[i] = ok ? q[kPartHead + dd] : 0.f;
       }
       float mb = M;
 #pragma unroll

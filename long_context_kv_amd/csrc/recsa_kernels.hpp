@@ -7,6 +7,7 @@
 #include <algorithm>
 
 #include "recsa.h"
+#include "recsa_common.hpp"
 
 namespace recsa {
 
@@ -18,15 +19,16 @@ inline int64_t level_rows_host(int64_t L_cap, int level) { return L_cap >> (4 * 
 //   buckets (bf16, n_queries*Hkv >= kBucketMinSlots) multi-query scoring by
 //           parent: tiles [max_tiles] uint4, entries [regions][kFileQueries*k]
 //           uint2 (one region per filing workgroup), n_tiles int32
-//   part    [B*Hkv][kPartSlots][G][d+2] float      decode attention partials
+//   part    [B*Hkv][kPartSlots][G][4+d] float      decode attention partials
+//           (max, sum, -, -, d values per query head)
 //   ctl     [B*Hkv][kCtlWords] uint32              fused-decode control block:
 //           word 1 = error word, words 16 + 16*w = arrival flag of workgroup w
 // The ctl words must be zero before the first recsa_decode call; every call
 // leaves them zero (except the error word, see recsa.h).
 constexpr int kDecodeSplits = 64;    // attention workgroups per (query, KV head), decode
 // most workgroups per query along the query launch dimension (scoring:
-// C*k/64 <= 64 list blocks; decode attention: kDecodeSplits)
-constexpr int kQueryLaunchX = 64;
+// C*k/64 <= 128 list blocks; decode attention: kDecodeSplits)
+constexpr int kQueryLaunchX = 128;
 constexpr int kFusedMaxW = 32;       // workgroups per (sequence, KV head), fused decode
 constexpr int kPartSlots = kDecodeSplits > kFusedMaxW ? kDecodeSplits : kFusedMaxW;
 constexpr int kCtlWords = 16 + 16 * kFusedMaxW;   // one 64-byte line per flag
@@ -83,7 +85,7 @@ inline WsLayout ws_layout(const recsa_tree& tr, int Hq, int64_t n_queries) {
     end = w.bk_ntiles_off + 4;
   }
   w.part_off = align256(end);
-  w.ctl_off = align256(w.part_off + heads * kPartSlots * w.G * (w.d + 2) * 4);
+  w.ctl_off = align256(w.part_off + heads * kPartSlots * w.G * (w.d + kPartHead) * 4);
   w.total = w.ctl_off + heads * kCtlWords * 4;   // the control words end the workspace
   return w;
 }

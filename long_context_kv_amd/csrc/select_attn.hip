@@ -107,8 +107,9 @@ __global__ void __launch_bounds__(kBlock)
 }
 
 // ------------------------------------------------------------------- topk
-template <int G>
-__global__ void __launch_bounds__(kBlock)
+// NT threads per (query, KV head); lists of up to CKM positions.
+template <int G, int NT, int CKM>
+__global__ void __launch_bounds__(NT)
     topk_kernel(recsa_tree tr, int T, const int64_t* pos, int32_t* sel, int32_t* cnt, float* imp,
                 const float* ws_logits, uint32_t* ws_bitmap, int level, int n_sel, int CK) {
   __shared__ TopkSmem sm;
@@ -118,7 +119,7 @@ __global__ void __launch_bounds__(kBlock)
   float* imp_q = imp ? imp + qc.slot * n_sel * static_cast<int64_t>(CK) : nullptr;
   if (level == top - 1) {             // the top list [0 .. a_top] is fully selected
     const ListView lt = list_view(qc.t, top, top, k, qc.sel, qc.cnt);
-    wg_take_all<kBlock>(lt, k, qc.sel + static_cast<int64_t>(top - 1) * k, qc.cnt + (top - 1),
+    wg_take_all<NT>(lt, k, qc.sel + static_cast<int64_t>(top - 1) * k, qc.cnt + (top - 1),
                         imp_q ? imp_q + static_cast<int64_t>(top - 1) * CK : nullptr, CK);
   }
   const ListView lv = list_view(qc.t, level, top, k, qc.sel, qc.cnt);
@@ -126,12 +127,12 @@ __global__ void __launch_bounds__(kBlock)
   int32_t* out_cnt = qc.cnt + (level - 1);
   float* imp_l = imp_q ? imp_q + static_cast<int64_t>(level - 1) * CK : nullptr;
   if (lv.len <= k) {
-    wg_take_all<kBlock>(lv, k, out_sel, out_cnt, imp_l, CK);
+    wg_take_all<NT>(lv, k, out_sel, out_cnt, imp_l, CK);
     return;
   }
   const float* lgs = ws_logits + (qc.slot * n_sel + (level - 1)) * static_cast<int64_t>(G) * CK;
   uint32_t* bm = ws_bitmap + (qc.slot * n_sel + (level - 1)) * static_cast<int64_t>((CK + 31) / 32);
-  wg_topk<G, kBlock>(lgs, lv.len - 1, k, CK, lv, out_sel, out_cnt, bm, imp_l, sm);
+  wg_topk<G, NT, CKM>(lgs, lv.len - 1, k, CK, lv, out_sel, out_cnt, bm, imp_l, sm);
 }
 
 // ------------------------------------------------------------- attention
@@ -155,12 +156,12 @@ __global__ void __launch_bounds__(kBlock)
     float* o = out + (qc.qi * Hq + static_cast<int64_t>(qc.j) * G) * D;
     for (int e = threadIdx.x; e < G * D; e += kBlock) o[e] = sm.wacc[0][e / D][e % D] / sm.res_l[e / D];
   } else {
-    float* pp = part + ((qc.slot * n_split) + qc.x) * static_cast<int64_t>(G) * (D + 2);
+    float* pp = part + ((qc.slot * n_split) + qc.x) * static_cast<int64_t>(G) * (D + kPartHead);
     for (int e = threadIdx.x; e < G * D; e += kBlock)
-      pp[(e / D) * (D + 2) + 2 + e % D] = sm.wacc[0][e / D][e % D];
+      pp[(e / D) * (D + kPartHead) + kPartHead + e % D] = sm.wacc[0][e / D][e % D];
     if (threadIdx.x < G) {
-      pp[threadIdx.x * (D + 2)] = sm.res_m[threadIdx.x];
-      pp[threadIdx.x * (D + 2) + 1] = sm.res_l[threadIdx.x];
+      pp[threadIdx.x * (D + kPartHead)] = sm.res_m[threadIdx.x];
+      pp[threadIdx.x * (D + kPartHead) + 1] = sm.res_l[threadIdx.x];
     }
   }
 }
@@ -170,7 +171,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const float* part, floa
                                                          int Hq, int n_split) {
   const int64_t qi = blockIdx.y;
   const int j = blockIdx.x;
-  const float* pp = part + (qi * Hkv + j) * n_split * static_cast<int64_t>(G) * (D + 2);
+  const float* pp = part + (qi * Hkv + j) * n_split * static_cast<int64_t>(G) * (D + kPartHead);
   merge_partials<D, G, kBlock>(pp, n_split, out + (qi * Hq + static_cast<int64_t>(j) * G) * D);
 }
 
@@ -189,7 +190,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const float* part, floa
 // computes (same operands, same k order).
 struct BucketArgs {
   uint4* tiles;         // [max_tiles] {first entry, entries, sequence*Hkv + head, parent}
-  uint2* entries;       // [regions][kFileQueries * k] {query index, phi | r << 12 | nvalid << 20}
+  uint2* entries;       // [regions][kFileQueries * k] {query index, phi | r << 13 | nvalid << 22}
   int32_t* n_tiles;     // tiles of this level
   int n_up;             // parents per (sequence, KV head): N_{l+1} + 1
 };
@@ -274,7 +275,7 @@ __global__ void __launch_bounds__(kBlock)
       const uint32_t phi = static_cast<uint32_t>(n - r * kC);      // p_q - C r
       const uint32_t nvalid = static_cast<uint32_t>(min(kC, n - r * kC));
       ba.entries[region + at] = make_uint2(static_cast<uint32_t>(qi0 + i),
-                                           phi | (static_cast<uint32_t>(r) << 12) | (nvalid << 20));
+                                           phi | (static_cast<uint32_t>(r) << 13) | (nvalid << 22));
     }
   }
 }
@@ -308,7 +309,7 @@ __global__ void __launch_bounds__(kBlock)
       const uint2 ent = nxt;                         // A row m: entry e0 + m
       nxt = e0 + kC + m < end ? ba.entries[e0 + kC + m] : make_uint2(0u, 0u);
       RopeFrag<D> rf;
-      load_rope_frag<D>(static_cast<int>(ent.y & 0xFFFu), tr.rope, rf);
+      load_rope_frag<D>(static_cast<int>(ent.y & 0x1FFFu), tr.rope, rf);
       // this lane's output rows 4h + i: entry e0 + 4h + i (held by lane 4h + i)
       uint32_t ox[4], oy[4];
 #pragma unroll
@@ -324,8 +325,8 @@ __global__ void __launch_bounds__(kBlock)
         const f32x4_t c = mfma_logits<D>(qf, kf);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = static_cast<int>((oy[i] >> 12) & 0xFFu);
-          const int nvalid = static_cast<int>((oy[i] >> 20) & 0x1Fu);
+          const int r = static_cast<int>((oy[i] >> 13) & 0x1FFu);
+          const int nvalid = static_cast<int>((oy[i] >> 22) & 0x1Fu);
           if (e0 + 4 * h + i < end && m < nvalid) {
             const int64_t slot = static_cast<int64_t>(ox[i]) * tr.Hkv + j;
             ws_logits[((slot * n_sel + (level - 1)) * G + g) * static_cast<int64_t>(CK) + r * kC + m] =
@@ -381,8 +382,12 @@ static hipError_t select_impl(const recsa_tree& tr, const void* q, int Hq, int T
         score_kernel<DT, D, G><<<dim3(score_blocks * nq, tr.Hkv), kBlock, 0, s>>>(
             tr, q, Hq, T, pos, sel, cnt, logits, l, w.n_sel, w.CK);
     }
-    topk_kernel<G><<<dim3(nq, tr.Hkv), kBlock, 0, s>>>(tr, T, pos, sel, cnt, imp, logits,
-                                                          bitmap, l, w.n_sel, w.CK);
+    if (w.CK <= 4096)
+      topk_kernel<G, kBlock, 4096><<<dim3(nq, tr.Hkv), kBlock, 0, s>>>(
+          tr, T, pos, sel, cnt, imp, logits, bitmap, l, w.n_sel, w.CK);
+    else
+      topk_kernel<G, 2 * kBlock, kMaxCK><<<dim3(nq, tr.Hkv), 2 * kBlock, 0, s>>>(
+          tr, T, pos, sel, cnt, imp, logits, bitmap, l, w.n_sel, w.CK);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -70,7 +70,7 @@ def _pooler(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(C=8), R.RECSA_E_UNSUPPORTED),
     (dict(d=96), R.RECSA_E_UNSUPPORTED),
-    (dict(k=512), R.RECSA_E_UNSUPPORTED),
+    (dict(k=513), R.RECSA_E_UNSUPPORTED),      # C*k above 8192
     (dict(dtype=7), R.RECSA_E_UNSUPPORTED),
     (dict(n_levels=3), R.RECSA_E_INVALID),      # top list would exceed k
     (dict(n_levels=9), R.RECSA_E_INVALID),
@@ -82,6 +82,16 @@ def test_tree_validation(over, status):
     t = _tree(**over)
     p = _pooler()
     assert L.recsa_build_tree(ctypes.byref(t), ctypes.byref(p), 0, 16, None) == status
+
+
+def test_k512_is_accepted():
+    """k = 512 (C*k = 8192 list positions) is a supported selection depth:
+    validation passes and the workspace holds 8192 logits per scored level."""
+    L = R.lib()
+    t = _tree(k=512)
+    a = L.recsa_workspace_bytes(ctypes.byref(t), 32, 1)
+    b = L.recsa_workspace_bytes(ctypes.byref(t), 32, 2)
+    assert a > 0 and b - a >= 8 * (3 * 4 * 8192 * 4 + 3 * 256 * 4)
 
 
 def test_call_validation_without_launch():

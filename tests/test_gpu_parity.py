@@ -431,3 +431,42 @@ def test_prefill_two_sequences_bucketed_matches_per_query():
     rep = _check_queries(tree, pdict, q[:, idx], pos[:, idx].cpu(), sel[:, idx], cnt[:, idx],
                          imp[:, idx], out[:, idx], [0, 1], 1e-5, 2e-3, max_swaps=1)
     assert rep.matched >= B * 2 * len(idx) - 1, rep
+
+
+def test_k512_variant_decode_and_prefill():
+    """The pages' k = 512 ablation (C*k = 8192 list positions, a top-(k-1)
+    over up to 8191 keys): 120K tokens give 3 levels whose level-1 lists hold
+    about 7500 candidates.  A causal prefill chunk (bucketed scoring), then
+    the fused decode against the separate calls, sampled vs the oracle."""
+    _need_gpu()
+    L0, T, Hkv, Hq = 120000, 256, 2, 8
+    L_cap = L0 + T + 64
+    wl, tree, pool, pdict = _setup(1, Hkv, 128, L_cap, L_cap, 512, "bf16", 51)
+    assert tree.n_levels == 3
+    R.recsa_build_tree(tree, pool, 0, L0)
+    R.recsa_build_tree(tree, pool, L0, L0 + T)
+    q = synth.to_storage(synth.normal((1, T, Hq, 128), DEV, 51, 97), "bf16")
+    pos = torch.arange(L0, L0 + T, device=DEV).view(1, T)
+    sel, cnt, imp, out = _run_select_attn(tree, q, Hq, pos, decode=False)
+    idx = [0, 100, T - 1]
+    rep = _check_queries(tree, pdict, q[:, idx], pos[:, idx].cpu(), sel[:, idx], cnt[:, idx],
+                         imp[:, idx], out[:, idx], [0, 1], 1e-5, 2e-3, max_swaps=1)
+    assert rep.matched >= 2 * len(idx) - 1, rep
+    t = L0 + T
+    kn, vn = tree.K[0][:, :, t].clone().contiguous(), tree.V[0][:, :, t].clone().contiguous()
+    qd = synth.to_storage(synth.normal((1, 1, Hq, 128), DEV, 51, 98), "bf16")
+    p1 = torch.tensor([t], dtype=torch.int64, device=DEV)
+    ref = R.Tree.allocate(1, Hkv, 128, L_cap, k=512, dtype="bf16", device=DEV,
+                          level0=(tree.K[0].clone(), tree.V[0].clone()))
+    R.recsa_build_tree(ref, pool, 0, L0 + T)
+    fs, fc, fo, ws = _fused_step(tree, pool, kn, vn, qd, Hq, p1)
+    R.recsa_append_decode(ref, pool, kn, vn, p1)
+    s2, c2, m2, o2 = _run_select_attn(ref, qd, Hq, p1.view(1, 1), decode=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(R.decode_error_words(ws, tree, Hq)).item() == 0
+    assert np.array_equal(fs.cpu().numpy().reshape(s2.shape), s2)
+    assert np.allclose(fo.cpu().numpy().astype(np.float64).reshape(o2.shape), o2, rtol=0,
+                       atol=1e-5 * np.abs(o2).max())
+    rep2 = _check_queries(ref, pdict, qd, p1.view(1, 1).cpu(), s2, c2, m2, o2, [0, 1], 1e-5,
+                          2e-3, max_swaps=1)
+    assert rep2.matched >= 1, rep2
