@@ -470,3 +470,42 @@ def test_k512_variant_decode_and_prefill():
     rep2 = _check_queries(ref, pdict, qd, p1.view(1, 1).cpu(), s2, c2, m2, o2, [0, 1], 1e-5,
                           2e-3, max_swaps=1)
     assert rep2.matched >= 1, rep2
+
+
+def test_fused_decode_variable_lengths():
+    """Sequences of very different lengths in one decode batch: t = 70000 (two
+    scored levels), 5000 (one) and 300 (none: every list fits in k), so the
+    groups of one launch run different numbers of selection handoffs.  The
+    fused step equals the separate calls, and each sequence the oracle."""
+    _need_gpu()
+    B, Hkv, d, k = 3, 2, 128, 256
+    L_cap = 70100
+    ts = [70000, 5000, 300]
+    wl, tree, pool, pdict = _setup(B, Hkv, d, L_cap, L_cap, k, "bf16", 61)
+    assert tree.n_levels == 4
+    ref = R.Tree.allocate(B, Hkv, d, L_cap, k=k, dtype="bf16", device=DEV,
+                          level0=(tree.K[0].clone(), tree.V[0].clone()))
+    R.recsa_build_tree(tree, pool, 0, max(ts))
+    R.recsa_build_tree(ref, pool, 0, max(ts))
+    Hq = Hkv * 4
+    pos = torch.tensor(ts, dtype=torch.int64, device=DEV)
+    kn = torch.stack([tree.K[0][b, :, ts[b]] for b in range(B)]).contiguous()
+    vn = torch.stack([tree.V[0][b, :, ts[b]] for b in range(B)]).contiguous()
+    q = synth.to_storage(synth.normal((B, 1, Hq, d), DEV, 61, 99), "bf16")
+    fs, fc, fo, ws = _fused_step(tree, pool, kn, vn, q, Hq, pos)
+    R.recsa_append_decode(ref, pool, kn, vn, pos)
+    s2, c2, m2, o2 = _run_select_attn(ref, q, Hq, pos.view(B, 1), decode=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(R.decode_error_words(ws, tree, Hq)).item() == 0
+    assert torch.count_nonzero(R.decode_control_words(ws, tree, Hq)).item() == 0
+    assert np.array_equal(fs.cpu().numpy().reshape(s2.shape), s2)
+    assert np.array_equal(fc.cpu().numpy().reshape(c2.shape), c2)
+    assert np.allclose(fo.cpu().numpy().astype(np.float64).reshape(o2.shape), o2, rtol=0,
+                       atol=1e-5 * np.abs(o2).max())
+    matched = 0
+    for b in range(B):
+        rep = _check_queries(ref, pdict, q[b:b + 1], pos[b:b + 1].view(1, 1).cpu(), s2[b:b + 1],
+                             c2[b:b + 1], m2[b:b + 1], o2[b:b + 1], [0, 1], 1e-5, 2e-3,
+                             max_swaps=1, seqs=[b])
+        matched += rep.matched
+    assert matched >= 2 * B - 1
