@@ -159,18 +159,17 @@ def _silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def pool_keys(X, P: Pooler):
-    """Eq. 5 for a batch of nodes.
+def pool_parts(X, P: Pooler):
+    """The parts of Eq. 5 for a batch of nodes.
 
-    X: [N, C, d] children keys (float64).  Returns the unrounded node keys
-    [N, d]:
+    X: [N, C, d] children keys (float64).  Returns (mu [N, d], sigma [N],
+    p [N, d], m [N, d]):
         mu    = mean of the children
         sigma = sqrt(mean over children and dims of (x - mu)^2 + eps)
         rho   = sqrt(mean over dims of mu^2 + eps)
         alpha = softmax over children of tau * w.(x_c - mu) / sigma
         p     = sum_c alpha_c x_c
         m     = W2 SiLU(W1 [mu/rho ; (p - mu)/sigma] + b1)
-        K     = mu + g (p - mu) + sigma m
     """
     P = P.as64()
     X = np.asarray(X, dtype=np.float64)
@@ -186,7 +185,14 @@ def pool_keys(X, P: Pooler):
     feat = np.concatenate([mu / rho[:, None], (p - mu) / sigma[:, None]], axis=1)
     hidden = _silu(feat @ P.W1.T + P.b1)                     # [N, h]
     m = hidden @ P.W2.T                                      # [N, d]
-    return mu + P.g * (p - mu) + sigma[:, None] * m
+    return mu, sigma, p, m
+
+
+def pool_keys(X, P: Pooler):
+    """Eq. 5 node keys (unrounded) for a batch of nodes, X: [N, C, d]:
+    K = mu + g (p - mu) + sigma m, with the parts of ``pool_parts``."""
+    mu, sigma, p, m = pool_parts(X, P)
+    return mu + float(P.g) * (p - mu) + sigma[:, None] * m
 
 
 def mean_values(X):
@@ -392,3 +398,71 @@ def decode_reference(qG, t, K, V, C, k, cos, sin, dtype, exact=False, theta=1e6)
     """Walk plus attention for one query on one KV head."""
     tr = walk(qG, t, K, C, k, cos, sin, dtype, exact, theta)
     return attend(tr, V), tr
+
+
+# --------------------------------------------------------------------------
+# Pooler distillation losses (picx.dev "Pooler Distillation", Eq. 6 and
+# Eq. 7).  Readings (the pages give the formulas, not their operands):
+#  * the teacher is the dense causal attention of the same G query heads at
+#    position t over tokens 0..t, standard RoPE at the true positions,
+#    softmax over s[h, tau] = q_h . R(tau - t) k_tau / sqrt(d), float64;
+#  * y_t^(l) is the head-mean teacher mass of each non-current candidate's
+#    subtree (tokens [u C^l, (u+1) C^l) clipped at t), renormalised over
+#    those candidates: the support of pi_t^(l), the walk's importance (R4);
+#  * only scored levels (|A| > k) contribute, where pi is defined;
+#  * the shift penalty of level l averages over every complete level-l node
+#    of every KV head (M_l of them): one pooler serves the layer.
+# --------------------------------------------------------------------------
+
+def teacher_attention(qG, t: int, K0, theta: float):
+    """Dense attention probabilities [G, t+1] of the G query heads at t over
+    the level-0 keys K0[0..t] (pre-RoPE), exact float64 RoPE."""
+    qG = np.asarray(qG, dtype=np.float64)
+    d = qG.shape[1]
+    qr = rotate_exact(qG, t, theta)
+    kr = rotate_exact(np.asarray(K0[: t + 1], dtype=np.float64), np.arange(t + 1), theta)
+    s = (qr @ kr.T) / math.sqrt(d)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def subtree_mass(a, nodes, level: int, C: int):
+    """Sum of a[..., tau] over the tokens under each node of ``level``:
+    tau in [u C^level, (u+1) C^level), clipped at the end of a."""
+    span = C ** level
+    n_tok = a.shape[-1]
+    out = np.zeros(a.shape[:-1] + (len(nodes),))
+    for i, u in enumerate(nodes):
+        lo, hi = int(u) * span, min((int(u) + 1) * span, n_tok)
+        if lo < hi:
+            out[..., i] = a[..., lo:hi].sum(axis=-1)
+    return out
+
+
+def distill_kl(qG, t: int, tr: WalkTrace, K0, C: int, theta: float):
+    """Eq. 6 terms of one query: {level: KL(y || pi)} over the walk's scored
+    levels, with 0 log 0 = 0."""
+    a = teacher_attention(qG, t, K0, theta)
+    out = {}
+    for lvl, lt in tr.levels.items():
+        if not lt.scored:
+            continue
+        others = lt.A[:-1]
+        m = subtree_mass(a, others, lvl, C).mean(axis=0)
+        y = m / m.sum()
+        pi = np.asarray(lt.importance, dtype=np.float64)
+        nz = y > 0
+        out[lvl] = float(np.sum(y[nz] * (np.log(y[nz]) - np.log(pi[nz]))))
+    return out
+
+
+def shift_penalty(children_by_level, P: Pooler):
+    """Eq. 7 per level: ||mean_i sigma_i m_i||^2 / mean_i ||mu_i||^2 over the
+    nodes i of that level.  children_by_level: {level: X [M_l, C, d]} -- the
+    stored children of every complete node of the level (all KV heads)."""
+    out = {}
+    for lvl, X in children_by_level.items():
+        mu, sigma, _, m = pool_parts(X, P)
+        num = (sigma[:, None] * m).mean(axis=0)
+        out[lvl] = float(num @ num / (mu * mu).sum(axis=1).mean())
+    return out

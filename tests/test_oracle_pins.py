@@ -14,6 +14,7 @@ import os
 import numpy as np
 import pytest
 import scipy.special
+import scipy.stats
 import torch
 
 from oracle import recsa_oracle as O
@@ -519,3 +520,88 @@ def test_published_token_budget_and_overhead():
         frac = sum(sizes[1:]) / L2
         assert frac < gold["tree_overhead_bound_percent"]["value"] / 100
         assert abs(frac - 1 / 15) < 1e-3
+
+
+# --------------------------------------------------------------------------
+# pooler distillation losses (Eq. 6, Eq. 7)
+# --------------------------------------------------------------------------
+
+def test_teacher_attention_is_sdpa_with_textbook_rope():
+    """The teacher's probabilities are torch SDPA (causal row t) on queries
+    and keys rotated as complex numbers, read out with one-hot values."""
+    r = np.random.default_rng(71)
+    d, t, theta = 16, 40, 1e4
+    K0 = r.standard_normal((t + 1, d))
+    q = r.standard_normal((3, d))
+    a = O.teacher_attention(q, t, K0, theta)
+    qr = torch.tensor(_complex_rope(q, np.full(3, t), theta))[None, :, None, :]    # [1, G, 1, d]
+    kr = torch.tensor(_complex_rope(K0, np.arange(t + 1), theta))[None, None].expand(1, 3, t + 1, d)
+    eye = torch.eye(t + 1, dtype=torch.float64)[None, None].expand(1, 3, t + 1, t + 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qr, kr, eye)[0, :, 0].numpy()
+    assert np.allclose(a, ref, rtol=0, atol=1e-12)
+    assert np.allclose(a.sum(axis=1), 1.0)
+    # a single token takes all the mass; equal keys give uniform attention
+    assert np.allclose(O.teacher_attention(q, 0, K0, theta), 1.0)
+    flat = O.teacher_attention(q, t, np.zeros((t + 1, d)), theta)
+    assert np.allclose(flat, 1.0 / (t + 1))
+
+
+def test_subtree_masses_partition_the_tokens():
+    r = np.random.default_rng(72)
+    a = r.random((2, 300))
+    a /= a.sum(axis=1, keepdims=True)
+    for lvl, C in ((1, 4), (2, 4), (1, 16), (2, 3)):
+        n_nodes = -(-300 // C ** lvl)
+        m = O.subtree_mass(a, np.arange(n_nodes), lvl, C)
+        assert np.allclose(m.sum(axis=1), 1.0)
+        assert np.allclose(m[:, 0], a[:, :C ** lvl].sum(axis=1))
+
+
+def test_distill_kl_zero_for_zero_query_and_matches_relative_entropy():
+    """q = 0: the teacher is uniform over tokens, so the non-current
+    candidates (complete subtrees of equal size) get uniform y, and every
+    logit is 0, so pi is uniform too: KL = 0 at every scored level.  For
+    random queries each term is scipy's relative entropy of (y, pi) and >= 0."""
+    C, k, d, L = 4, 3, 8, 300
+    K, V, P = _tree(L, d, C, k, 73, "f32")
+    cos, sin = O.rope_table(d, C * k, 1e4)
+    t = L - 1
+    q0 = np.zeros((2, d))
+    tr0 = O.walk(q0, t, K, C, k, cos, sin, "f32", theta=1e4)
+    kl0 = O.distill_kl(q0, t, tr0, K[0], C, 1e4)
+    assert kl0 and all(abs(v) < 1e-14 for v in kl0.values())
+    r = np.random.default_rng(74)
+    for _ in range(4):
+        q = r.standard_normal((2, d))
+        tr = O.walk(q, t, K, C, k, cos, sin, "f32", theta=1e4)
+        kl = O.distill_kl(q, t, tr, K[0], C, 1e4)
+        a = O.teacher_attention(q, t, K[0], 1e4)
+        for lvl, v in kl.items():
+            lt = tr.levels[lvl]
+            m = O.subtree_mass(a, lt.A[:-1], lvl, C).mean(axis=0)
+            assert v >= 0
+            assert abs(v - scipy.stats.entropy(m / m.sum(), lt.importance)) < 1e-12
+
+
+def test_shift_penalty_invariants():
+    """Eq. 7: zero without the MLP term (W2 = 0); unchanged by scaling every
+    child key by c > 0 (sigma and mu scale by c, m does not) up to eps, and
+    by the order of the nodes; one node gives ||sigma m||^2 / ||mu||^2."""
+    r = np.random.default_rng(75)
+    d, h, C = 8, 8, 4
+    X = r.standard_normal((30, C, d)) + 0.3
+    P = _pooler(d, h, 76)
+    base = O.shift_penalty({1: X}, P)[1]
+    assert base > 0
+    assert O.shift_penalty({1: X}, _pooler(d, h, 76, W2=np.zeros((d, h))))[1] == 0.0
+    P0 = _pooler(d, h, 76, eps=0.0)
+    base0 = O.shift_penalty({1: X}, P0)[1]
+    for c in (0.5, 7.0):
+        # exact without eps; with eps = 1e-6 inside the roots, within 1e-4
+        assert abs(O.shift_penalty({1: c * X}, P0)[1] - base0) < 1e-12 * base0
+        assert abs(O.shift_penalty({1: c * X}, P)[1] - base) < 1e-4 * base
+    perm = r.permutation(30)
+    assert abs(O.shift_penalty({1: X[perm]}, P)[1] - base) < 1e-12 * base
+    mu, sigma, _, m = O.pool_parts(X[:1], P)
+    one = O.shift_penalty({1: X[:1]}, P)[1]
+    assert abs(one - np.sum((sigma[0] * m[0]) ** 2) / np.sum(mu[0] ** 2)) < 1e-12 * one
