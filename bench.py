@@ -180,6 +180,9 @@ def main():
                     help="counter pass only: a 512 MiB device copy (the calibration kernel), "
                          "then the workload's fused decode step 5 times and one prefill "
                          "chunk; prints no result")
+    ap.add_argument("--distill", action="store_true",
+                    help="measure the pooler distillation losses (Eq. 6 over every position "
+                         "of a 32768-token sequence, Eq. 7 over every node) instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -194,6 +197,9 @@ def main():
         sys.exit(2)
     if args.pmc_pass:
         pmc_pass(args.workload)
+        return
+    if args.distill:
+        bench_distill(args)
         return
     w = setup_workload(args.workload)
     wl, tree, pool, R = w.wl, w.tree, w.pool, w.R
@@ -465,6 +471,142 @@ def cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T):
         "prefill_tok_s": round(1.0 / (pre_s * heads), 3),
         "build_full_ms": round(build_s * heads * 1e3, 1),
     }
+
+
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def bench_distill(args):
+    """Eq. 6 and Eq. 7 on the distillation workload: one step = selection
+    with importances for every position of the sequence, the KL terms of
+    every (query, KV head, scored level) and the shift penalty of every
+    level.  Roofline: the teacher's dense logits, 2 d flops per (query head,
+    key) pair with key <= query, on the float32 matrix cores; the whole
+    recsa_distill_kl call is charged, so the fraction is a lower bound."""
+    import numpy as np
+    import torch
+
+    import synth
+    from long_context_kv_amd import recsa as R
+
+    R.lib()
+    wl = synth.WORKLOADS["distill_32k"]
+    L, B, Hkv, Hq, d, dev = wl.L, wl.B, wl.Hkv, wl.Hq, wl.d, "cuda"
+    T = L
+    log(f"workload {wl.name}: B={B} Hkv={Hkv} Hq={Hq} d={d} {wl.dtype} L={L} k={wl.k}, "
+        f"{T} queries per sequence")
+    K0, V0 = synth.kv_rows(wl, dev, n_rows=L)
+    pdict = synth.pooler_params(d, d, dev, wl.seed)
+    pool = R.Pooler.from_dict(pdict, dev)
+    tree = R.Tree.allocate(B, Hkv, d, L, k=wl.k, dtype=wl.dtype, device=dev, level0=(K0, V0),
+                           theta=wl.theta)
+    R.recsa_build_tree(tree, pool, 0, L)
+    q = synth.to_storage(synth.normal((B, T, Hq, d), dev, wl.seed, ROLE_DISTILL_Q), wl.dtype)
+    pos = torch.arange(T, device=dev).view(1, T).expand(B, T).contiguous()
+    ws = R.workspace(tree, Hq, B * T)
+    sel, cnt, imp = tree.selection_buffers(B * T, with_importance=True)
+    dws = torch.empty(R.recsa_distill_workspace_bytes(tree, Hq, B * T), dtype=torch.uint8,
+                      device=dev)
+    kl = torch.empty((B, T, Hkv, tree.n_sel), dtype=torch.float32, device=dev)
+    sws = torch.empty(R.recsa_shift_workspace_bytes(tree), dtype=torch.uint8, device=dev)
+    pen = torch.empty((tree.n_levels - 1, d + 2), dtype=torch.float32, device=dev)
+
+    def select():
+        R.recsa_select(tree, q, Hq, T, pos, sel, cnt, imp, ws)
+
+    def distill():
+        R.recsa_distill_kl(tree, q, Hq, T, pos, sel, cnt, imp, wl.theta, kl, dws)
+
+    def shift():
+        R.recsa_shift_penalty(tree, pool, L, pen, sws)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        select(); distill(); shift()
+    torch.cuda.synchronize()
+    evs = [tuple(ev() for _ in range(4)) for _ in range(args.steps)]
+    w0 = time.perf_counter()
+    for e0, e1, e2, e3 in evs:
+        e0.record(); select(); e1.record(); distill(); e2.record(); shift(); e3.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    sel_ms = med([a.elapsed_time(b) for a, b, _, _ in evs])
+    kl_ms = med([b.elapsed_time(c) for _, b, c, _ in evs])
+    sh_ms = med([c.elapsed_time(e) for _, _, c, e in evs])
+    step_ms = med([a.elapsed_time(e) for a, _, _, e in evs])
+    pairs = sum(int(t) + 1 for t in range(T)) * B          # (query, key <= query) pairs
+    flops = 2.0 * d * Hq * pairs
+    tflops = flops / (kl_ms * 1e-3) / 1e12
+    klv = kl.cpu().numpy()
+    result = {
+        "metric": "RecSA pooler distillation step (Eq. 6 over every position + Eq. 7) "
+                  "at the 32K training length; ms per layer",
+        "value": round(step_ms, 3), "unit": "ms/layer-step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: 1 layer, {Hkv} KV heads, {Hq} query heads, d={d}, "
+                               f"{wl.dtype}, L={L}, C=16, k={wl.k}; every position a query",
+                   "seq_len": L, "global_batch": B},
+        "split_ms": {"select_with_importance": round(sel_ms, 3), "distill_kl": round(kl_ms, 3),
+                     "shift_penalty": round(sh_ms, 3)},
+        "queries_per_s": round(B * T / (step_ms * 1e-3), 1),
+        "roofline": {"kernel": "recsa_distill_kl (absolute RoPE table + teacher_lse_kernel + "
+                               "distill_kl_kernel), charged whole",
+                     "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_TFLOP_per_launch": round(flops / 1e12, 3),
+                     "dtype": "fp32 (v_mfma_f32_16x16x4_f32)"},
+        "kl_mean_per_level": [round(float(x), 5) for x in klv.reshape(-1, tree.n_sel).mean(0)],
+        "shift_penalty_per_level": [round(float(x), 6) for x in pen[:, d + 1].cpu().numpy()],
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_distill(wl, tree, pdict, q, L)
+    print(json.dumps(result), flush=True)
+
+
+ROLE_DISTILL_Q = 11
+
+
+def cpu_baseline_distill(wl, tree, pdict, q, L):
+    """The oracle on one thread: KV head 0, 16 evenly spaced positions of the
+    sequence (walk + Eq. 6 each), scaled to every position and KV head."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import recsa_oracle as O
+    from tests import parity as PY
+
+    G = wl.Hq // wl.Hkv
+    with threadpool_limits(limits=1):
+        K0 = PY.to64(tree.K[0][0, 0, :L])
+        V0 = PY.to64(tree.V[0][0, 0, :L])
+        P = PY.oracle_pooler(pdict)
+        t0 = time.time()
+        Kt, _ = O.build_tree(K0, V0, 16, tree.n_levels, P, wl.dtype)
+        cos, sin = O.rope_table(wl.d, 16 * wl.k, wl.theta)
+        qn = PY.to64(q[0, :, :G])
+        idx = np.linspace(0, L - 1, 16).astype(int)
+        t1 = time.time()
+        for t in idx:
+            t = int(t)
+            D = O.n_levels_for(t, 16, wl.k)
+            Ktt = ([Kt[0][: t + 1]] + [Kt[lv][: (t + 1) >> (4 * lv)]
+                                       for lv in range(1, len(Kt))])[: max(D, 1)]
+            tr = O.walk(qn[t], t, Ktt, 16, wl.k, cos, sin, wl.dtype)
+            O.distill_kl(qn[t], t, tr, K0[: t + 1], 16, wl.theta)
+        per_q = (time.time() - t1) / len(idx)
+    total = time.time() - t0
+    heads = wl.Hkv * wl.B
+    scaled_ms = per_q * L * heads * 1e3
+    log(f"cpu baseline distill ({total:.1f}s): {per_q * 1e3:.1f} ms per (query, head)")
+    return {"value": round(scaled_ms, 1), "unit": "ms/layer-step", "cores": 1, "kind": "oracle",
+            "sample": (f"KV head 0 of {heads}, one thread: oracle walk + Eq. 6 at 16 evenly "
+                       f"spaced positions of {L}, scaled x{L} positions x{heads} heads "
+                       f"({total:.1f}s of CPU work; Eq. 7 not included)")}
 
 
 if __name__ == "__main__":

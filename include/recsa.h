@@ -206,6 +206,57 @@ int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler,
                  const int64_t* pos_dev, int32_t* sel_idx, int32_t* sel_cnt,
                  float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Pooler distillation losses (picx.dev Pooler Distillation, Eq. 6 and
+ * Eq. 7).  Readings of their operands: the teacher is the dense causal
+ * attention of the same G query heads at position t over the level-0 tokens
+ * [0, t], with RoPE at the true positions (angle (tau - t) theta^(-2j/d)),
+ * scale 1/sqrt(d); y_t^(l) is its head-mean mass under each non-current
+ * candidate of A_t^(l), renormalised over those candidates (the support of
+ * pi); pi_t^(l) is the importance recsa_select reports; only scored levels
+ * (|A| > k) have a term; the shift penalty of level l averages over every
+ * complete level-l node of every sequence and KV head. */
+
+/* Workspace bytes of recsa_distill_kl for n_queries = B*T queries with Hq
+ * query heads: the RoPE table of the absolute positions [0, L_cap), float32
+ * [L_cap][d/2][2], then the teacher's per-group log-sum-exps, float32
+ * [n_queries][Hkv][ceil(L_cap/16)][Hq/Hkv].  0 on invalid arguments. */
+size_t recsa_distill_workspace_bytes(const recsa_tree* tree, int32_t Hq,
+                                     int64_t n_queries);
+
+/* Eq. 6 terms of T queries per sequence.  q, pos_dev, sel_idx and sel_cnt as
+ * in recsa_select (pos_dev [B][T] device int64); importance: the importance
+ * output of recsa_select for the same queries (required).  theta: the RoPE
+ * base (> 1).  Level-0 rows [0, t] of each query must be in the tree.
+ * kl_out: [B][T][Hkv][n_levels-1] float32: slot l-1 holds KL(y || pi) of
+ * level l when it is scored, else 0; a zero importance under a positive
+ * teacher mass gives +inf.  Arithmetic is float32 (teacher logits on the
+ * float32 matrix cores).  ws: recsa_distill_workspace_bytes(tree, Hq, B*T)
+ * bytes of device memory, overwritten.  RECSA_E_UNSUPPORTED when
+ * ceil(L_cap/16) + C*k exceeds 16376 (the masses of one query are kept on
+ * chip). */
+int recsa_distill_kl(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
+                     const int64_t* pos_dev, const int32_t* sel_idx,
+                     const int32_t* sel_cnt, const float* importance, double theta,
+                     float* kl_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of recsa_shift_penalty: one partial row of d+1 floats per
+ * 16 nodes of every level >= 1, (sequence, KV head).  0 on invalid
+ * arguments. */
+size_t recsa_shift_workspace_bytes(const recsa_tree* tree);
+
+/* Eq. 7 for every level l >= 1 over its complete nodes among the tokens
+ * [0, tok_end) of every sequence and KV head (M_l nodes), each node's pooler
+ * parts recomputed in float32 from its stored children.  out:
+ * [n_levels-1][d+2] float32; slot l-1 holds the sum over those nodes of
+ * sigma*m (d values), the sum of ||mu||^2, then the penalty
+ * ||sum sigma m||^2 / (M_l * sum ||mu||^2) (0 where the level has no complete
+ * node).  The sums are taken in a fixed order: repeated calls give identical
+ * bits.  ws: recsa_shift_workspace_bytes(tree) bytes, overwritten.
+ * 0 < tok_end <= L_cap. */
+int recsa_shift_penalty(const recsa_tree* tree, const recsa_pooler* pooler,
+                        int64_t tok_end, float* out, void* ws, size_t ws_bytes,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

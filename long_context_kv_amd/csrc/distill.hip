@@ -1,0 +1,440 @@
+// Pooler distillation losses (picx.dev Pooler Distillation, Eq. 6 and Eq. 7).
+//
+// Eq. 6 compares, per query and scored level, the student importance pi (the
+// walk's head-mean softmax over the non-current candidates, as recsa_select
+// reports it) with the teacher's subtree mass y: the dense causal attention
+// of the same query heads over the tokens [0, t], at the true RoPE positions,
+// summed over each candidate's subtree and renormalised over the candidates.
+//
+// The teacher is computed in two launches:
+//   teacher_lse_kernel  one pass over the keys of a block of queries with
+//                       float32 matrix-core products (v_mfma_f32_16x16x4_f32);
+//                       a 16x16 output tile is 16 (query, head) rows against
+//                       one level-1 group of 16 tokens, so each tile reduces to
+//                       the group's log-sum-exp per row, which does not depend
+//                       on the row's global maximum: no second pass.
+//   distill_kl_kernel   per (query, KV head): the softmax normaliser from the
+//                       group log-sum-exps, the head-mean mass of every level-1
+//                       group, the candidates' subtree masses at each scored
+//                       level, and KL(y || pi).
+// Eq. 7 reruns the pooler on every complete node (pool_tile in its statistics
+// mode), writes per-tile sums and reduces them in a fixed order.
+#include <math.h>
+
+#include <algorithm>
+
+#include "recsa_common.hpp"
+#include "recsa_kernels.hpp"
+#include "recsa_pool.hpp"
+
+namespace recsa {
+
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTeacherRows = 64;   // (query, head) rows per teacher workgroup
+constexpr int kTeacherKeys = 64;   // keys per tile: four level-1 groups
+
+// Sum over each 16-lane row of the wave (DPP row operations; the result in
+// every lane of the row).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_movf<dpp::kXor1>(0.f, v);
+  v += dpp_movf<dpp::kXor2>(0.f, v);
+  v += dpp_movf<dpp::kRor4>(0.f, v);
+  v += dpp_movf<dpp::kRor8>(0.f, v);
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_movf<dpp::kXor1>(v, v));
+  v = fmaxf(v, dpp_movf<dpp::kXor2>(v, v));
+  v = fmaxf(v, dpp_movf<dpp::kRor4>(v, v));
+  v = fmaxf(v, dpp_movf<dpp::kRor8>(v, v));
+  return v;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < kBlock / kWave; ++w) s += red[w];
+  return s;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < kBlock / kWave; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ teacher
+// Workgroup: 64/G consecutive queries of one (sequence, KV head), i.e. 64
+// rows r = G*(query - first) + h.  Wave w owns rows [16w, 16w + 16) as the A
+// operand (rotated queries, float32, in registers for the whole pass).  Each
+// tile of 64 keys is rotated at its absolute positions into LDS; per level-1
+// group g of the tile, one chain of D/4 MFMAs gives the 16x16 logits, whose
+// rows reduce over the 16 key lanes to the group's log-sum-exp.
+// The k index of the A/B operands is permuted consistently (lane group h
+// supplies dims [h*D/4, (h+1)*D/4)), which only reorders the dot product.
+// lse: [B*T][Hkv][ng_cap][G] float32; entry (v, h) is written for every
+// level-1 group v <= t/16 of the row's query, never beyond.
+template <int DT, int D, int G>
+__global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, const void* qv,
+                                                             int T, const int64_t* __restrict__ pos,
+                                                             const float* __restrict__ arope,
+                                                             float* __restrict__ lse, int ng_cap) {
+  using Ty = typename Stor<DT>::T;
+  constexpr int QB = kTeacherRows / G;
+  constexpr int H2 = D / 2;
+  constexpr int LD = D + 4;            // padded row, 16-byte aligned
+  constexpr int KB = D / 4;            // MFMA steps per logit tile
+  __shared__ __attribute__((aligned(16))) float sbuf[kTeacherKeys][LD];   // queries, then keys
+  __shared__ int st[kTeacherRows];
+  __shared__ int s_tmax;
+  const int j = blockIdx.y, b = blockIdx.z;
+  // longest query blocks first: causal work grows with the position
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * QB;
+  const int Hq = tr.Hkv * G;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
+
+  if (tid < kTeacherRows) {
+    const int qi = q0 + tid / G;
+    st[tid] = qi < T ? static_cast<int>(pos[static_cast<int64_t>(b) * T + qi]) : -1;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    const float m = wave_max(static_cast<float>(st[lane]));
+    if (lane == 0) s_tmax = static_cast<int>(m);
+  }
+  // rotated queries R(t) q, float32 (no fused multiply-add)
+  for (int item = tid; item < kTeacherRows * H2; item += kBlock) {
+    const int r = item / H2, jj = item % H2;
+    const int t = st[r];
+    float xo = 0.f, yo = 0.f;
+    if (t >= 0) {
+      const int qi = q0 + r / G, h = r % G;
+      const Ty* qr =
+          static_cast<const Ty*>(qv) + ((static_cast<int64_t>(b) * T + qi) * Hq + j * G + h) * D;
+      const float* rp = arope + (static_cast<int64_t>(t) * H2 + jj) * 2;
+      rope_pair(Stor<DT>::load(qr + jj), Stor<DT>::load(qr + jj + H2), rp[0], rp[1], xo, yo);
+    }
+    sbuf[r][jj] = xo;
+    sbuf[r][jj + H2] = yo;
+  }
+  __syncthreads();
+  const int tmax = s_tmax;
+  if (tmax < 0) return;   // no query in this block (uniform)
+
+  float af[KB];
+  {
+    const float* src = &sbuf[16 * wid + (lane & 15)][(lane >> 4) * KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; kb += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + kb);
+      af[kb] = v.x;
+      af[kb + 1] = v.y;
+      af[kb + 2] = v.z;
+      af[kb + 3] = v.w;
+    }
+  }
+  int trow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) trow[i] = st[16 * wid + 4 * (lane >> 4) + i];
+  float* lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wid + 4 * (lane >> 4) + i;
+    const int qi = min(q0 + r / G, T - 1);
+    lrow[i] = lse + ((static_cast<int64_t>(b) * T + qi) * tr.Hkv + j) * ng_cap * G + (r % G);
+  }
+  const Ty* k0 = static_cast<const Ty*>(tr.K[0]) +
+                 (static_cast<int64_t>(b) * tr.Hkv + j) * tr.L_cap * D;
+  const float scale = static_cast<float>(1.0 / sqrt(static_cast<double>(D)));
+
+  const int n_tiles = tmax / kTeacherKeys + 1;
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int tau0 = tile * kTeacherKeys;
+    __syncthreads();   // the previous tile (or the query fragments) is read
+    for (int item = tid; item < kTeacherKeys * H2; item += kBlock) {
+      const int kk = item / H2, jj = item % H2;
+      const int tau = tau0 + kk;
+      float xo = 0.f, yo = 0.f;
+      if (tau <= tmax) {
+        const Ty* kr = k0 + static_cast<int64_t>(tau) * D;
+        const float* rp = arope + (static_cast<int64_t>(tau) * H2 + jj) * 2;
+        rope_pair(Stor<DT>::load(kr + jj), Stor<DT>::load(kr + jj + H2), rp[0], rp[1], xo, yo);
+      }
+      sbuf[kk][jj] = xo;
+      sbuf[kk][jj + H2] = yo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < kTeacherKeys / kC; ++g) {
+      const int tg = tau0 + kC * g;   // first token of the level-1 group
+      if (tg > tmax) break;           // uniform
+      const float* src = &sbuf[kC * g + (lane & 15)][(lane >> 4) * KB];
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; kb += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + kb);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kb], v.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kb + 1], v.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kb + 2], v.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kb + 3], v.w, acc, 0, 0, 0);
+      }
+      const int tau = tg + (lane & 15);
+      const int64_t v = tg >> 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = tau <= trow[i] ? acc[i] * scale : -INFINITY;
+        const float m = row16_max(s);
+        const float e = m == -INFINITY ? 0.f : expf(s - m);
+        const float sum = row16_sum(e);
+        if ((lane & 15) == 0 && m != -INFINITY) lrow[i][v * G] = m + logf(sum);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ Eq. 6 terms
+// One workgroup per (query, KV head).  Dynamic LDS: m1[ng_cap] (head-mean
+// teacher mass of each level-1 group), mass[C*k], red[8].
+template <int G>
+__global__ void __launch_bounds__(kBlock) distill_kl_kernel(
+    recsa_tree tr, int T, const int64_t* __restrict__ pos, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ cnt, const float* __restrict__ imp,
+    const float* __restrict__ lse, int ng_cap, float* __restrict__ kl) {
+  extern __shared__ float dsm[];
+  const int qi = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int64_t slot = (static_cast<int64_t>(b) * T + qi) * tr.Hkv + j;
+  const int n_sel = tr.n_levels - 1, k = tr.k, CK = kC * k, top = tr.n_levels - 1;
+  const int64_t t = pos[static_cast<int64_t>(b) * T + qi];
+  const int ng = static_cast<int>(t >> 4) + 1;
+  const float* L = lse + slot * ng_cap * G;
+  float* m1 = dsm;
+  float* mass = dsm + ng_cap;
+  float* red = mass + CK;
+
+  // softmax normaliser of each head: log Z_h = logsumexp over the groups
+  float lz[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = -INFINITY;
+    for (int v = tid; v < ng; v += kBlock) mx = fmaxf(mx, L[static_cast<int64_t>(v) * G + h]);
+    mx = block_max(mx, red);
+    float s = 0.f;
+    for (int v = tid; v < ng; v += kBlock) s += expf(L[static_cast<int64_t>(v) * G + h] - mx);
+    lz[h] = mx + logf(block_sum(s, red));
+  }
+  for (int v = tid; v < ng; v += kBlock) {
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) s += expf(L[static_cast<int64_t>(v) * G + h] - lz[h]);
+    m1[v] = s * (1.0f / G);
+  }
+  __syncthreads();
+
+  const int32_t* sl = sel + slot * n_sel * k;
+  const int32_t* cl = cnt + slot * n_sel;
+  const float* il = imp + slot * n_sel * CK;
+  float* ko = kl + slot * n_sel;
+  for (int l = 1; l <= n_sel; ++l) {
+    const ListView lv = list_view(t, l, top, k, sl, cl);
+    if (lv.len <= k) {   // unscored (uniform)
+      if (tid == 0) ko[l - 1] = 0.f;
+      continue;
+    }
+    const int n_oth = lv.len - 1;
+    const int64_t span = int64_t{1} << (4 * (l - 1));   // level-1 groups under a level-l node
+    float part = 0.f;
+    for (int p = tid; p < n_oth; p += kBlock) {
+      const int64_t u = lv.node(p);
+      const int64_t lo = u * span, hi = min((u + 1) * span, static_cast<int64_t>(ng));
+      float s = 0.f;
+      for (int64_t v = lo; v < hi; ++v) s += m1[v];
+      mass[p] = s;
+      part += s;
+    }
+    const float tot = block_sum(part, red);
+    float acc = 0.f;
+    for (int p = tid; p < n_oth; p += kBlock) {
+      const float y = mass[p] / tot;
+      if (y > 0.f) acc += y * (logf(y) - logf(il[static_cast<int64_t>(l - 1) * CK + p]));
+    }
+    const float v = block_sum(acc, red);
+    if (tid == 0) ko[l - 1] = v;
+  }
+}
+
+// ------------------------------------------------------------ Eq. 7
+// Per level: one workgroup per tile of 16 complete nodes of one (sequence,
+// KV head); partial row [D + 1] = (sum of sigma*m, sum of ||mu||^2).
+template <int DT, int D>
+__global__ void __launch_bounds__(kBlock) shift_stats_kernel(recsa_tree tr, recsa_pooler P,
+                                                             int level, int64_t n_nodes,
+                                                             float* __restrict__ part) {
+  using Ty = typename Stor<DT>::T;
+  constexpr int NODES = 16;
+  __shared__ PoolSmem<DT, D, NODES> sm;
+  const int j = blockIdx.y, b = blockIdx.z;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * NODES;
+  const int n_valid = static_cast<int>(min<int64_t>(NODES, n_nodes - first));
+  const int64_t rows_up = level_rows_dev(tr.L_cap, level - 1);
+  const int64_t head = static_cast<int64_t>(b) * tr.Hkv + j;
+  const Ty* kc = static_cast<const Ty*>(tr.K[level - 1]) + (head * rows_up + first * kC) * D;
+  float* out = part + (head * gridDim.x + blockIdx.x) * (D + 1);
+  pool_tile<DT, D, NODES, kBlock, true>(kc, nullptr, nullptr, nullptr, nullptr, 0, nullptr,
+                                        n_valid, P, sm, out);
+}
+
+struct ShiftLevels {
+  int64_t part_off[RECSA_MAX_LEVELS];   // floats
+  int64_t n_rows[RECSA_MAX_LEVELS];     // partial rows (tiles * heads)
+  int64_t n_nodes[RECSA_MAX_LEVELS];    // complete nodes, all heads
+};
+
+// One workgroup per level >= 1: sums the partial rows in a fixed order
+// (four row groups of 64 columns each, float64), then the penalty
+// ||sum sigma m||^2 / (M * sum ||mu||^2) = ||mean sigma m||^2 / mean ||mu||^2.
+template <int D>
+__global__ void __launch_bounds__(kBlock) shift_reduce_kernel(const float* __restrict__ part,
+                                                              ShiftLevels lv,
+                                                              float* __restrict__ out) {
+  constexpr int NCOL = D + 1;
+  constexpr int NCB = (NCOL + kWave - 1) / kWave;
+  __shared__ double acc_s[kBlock / kWave][NCB * kWave];
+  __shared__ double s_num;
+  const int l = blockIdx.x + 1;
+  const int lane = threadIdx.x & (kWave - 1), rg = threadIdx.x >> 6;
+  const float* base = part + lv.part_off[l];
+  const int64_t n_rows = lv.n_rows[l];
+  double acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = 0.0;
+  for (int64_t r = rg; r < n_rows; r += kBlock / kWave) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int c = cb * kWave + lane;
+      if (c < NCOL) acc[cb] += static_cast<double>(base[r * NCOL + c]);
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc_s[rg][cb * kWave + lane] = acc[cb];
+  __syncthreads();
+  float* o = out + static_cast<int64_t>(l - 1) * (D + 2);
+  if (threadIdx.x < kWave) {
+    double num = 0.0;
+    for (int c = lane; c < NCOL; c += kWave) {
+      double s = 0.0;
+      for (int g = 0; g < kBlock / kWave; ++g) s += acc_s[g][c];
+      o[c] = static_cast<float>(s);
+      if (c < D) num += s * s;
+      acc_s[0][c] = s;
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) num += __shfl_xor(num, off);
+    if (lane == 0) s_num = num;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double m = static_cast<double>(lv.n_nodes[l]);
+    const double den = m * acc_s[0][D];
+    o[D + 1] = (lv.n_nodes[l] > 0 && den > 0.0) ? static_cast<float>(s_num / den) : 0.f;
+  }
+}
+
+// ------------------------------------------------------------ launchers
+int64_t distill_groups(int64_t L_cap) { return (L_cap + kC - 1) / kC; }
+
+template <int DT, int D, int G>
+static hipError_t distill_impl(const recsa_tree& tr, const void* q, int Hq, int T,
+                               const int64_t* pos, const int32_t* sel, const int32_t* cnt,
+                               const float* imp, double theta, float* kl, void* ws,
+                               hipStream_t s) {
+  (void)Hq;
+  float* arope = static_cast<float*>(ws);
+  const int64_t rope_bytes = align256(tr.L_cap * D * 4);
+  float* lse = reinterpret_cast<float*>(static_cast<char*>(ws) + rope_bytes);
+  const int ng_cap = static_cast<int>(distill_groups(tr.L_cap));
+  hipError_t e = launch_rope_table(arope, D, static_cast<int>(tr.L_cap), theta, s);
+  if (e != hipSuccess) return e;
+  constexpr int QB = kTeacherRows / G;
+  dim3 g1(static_cast<unsigned>((T + QB - 1) / QB), tr.Hkv, tr.B);
+  teacher_lse_kernel<DT, D, G><<<g1, kBlock, 0, s>>>(tr, q, T, pos, arope, lse, ng_cap);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(static_cast<unsigned>(T), tr.Hkv, tr.B);
+  const size_t lds = (static_cast<size_t>(ng_cap) + kC * tr.k + 8) * sizeof(float);
+  distill_kl_kernel<G><<<g2, kBlock, lds, s>>>(tr, T, pos, sel, cnt, imp, lse, ng_cap, kl);
+  return hipGetLastError();
+}
+
+int64_t distill_ws_bytes(const recsa_tree& tr, int Hq, int64_t n_queries) {
+  return align256(tr.L_cap * tr.d * 4) + n_queries * Hq * distill_groups(tr.L_cap) * 4;
+}
+
+hipError_t launch_distill_kl(const recsa_tree& tr, const void* q, int Hq, int T,
+                             const int64_t* pos, const int32_t* sel, const int32_t* cnt,
+                             const float* imp, double theta, float* kl, void* ws,
+                             hipStream_t s) {
+  RECSA_DISPATCH(distill_impl, tr, q, Hq, T, pos, sel, cnt, imp, theta, kl, ws, s);
+}
+
+static ShiftLevels shift_levels(const recsa_tree& tr, int64_t tok_end) {
+  ShiftLevels lv{};
+  const int64_t heads = static_cast<int64_t>(tr.B) * tr.Hkv;
+  int64_t off = 0;
+  for (int l = 1; l < tr.n_levels; ++l) {
+    const int64_t cap_tiles = (level_rows_host(tr.L_cap, l) + 15) / 16;
+    const int64_t n = std::min(tok_end >> (4 * l), level_rows_host(tr.L_cap, l));
+    lv.part_off[l] = off;
+    lv.n_rows[l] = (n + 15) / 16 * heads;
+    lv.n_nodes[l] = n * heads;
+    off += cap_tiles * heads * (tr.d + 1);
+  }
+  lv.part_off[0] = off;   // total floats
+  return lv;
+}
+
+int64_t shift_ws_bytes(const recsa_tree& tr) {
+  return shift_levels(tr, tr.L_cap).part_off[0] * 4;
+}
+
+template <int DT, int D>
+static hipError_t shift_impl(const recsa_tree& tr, const recsa_pooler& P, int64_t tok_end,
+                             float* out, void* ws, hipStream_t s) {
+  const ShiftLevels lv = shift_levels(tr, tok_end);
+  float* part = static_cast<float*>(ws);
+  for (int l = 1; l < tr.n_levels; ++l) {
+    const int64_t n = lv.n_nodes[l] / (static_cast<int64_t>(tr.B) * tr.Hkv);
+    if (n == 0) continue;
+    dim3 grid(static_cast<unsigned>((n + 15) / 16), tr.Hkv, tr.B);
+    shift_stats_kernel<DT, D><<<grid, kBlock, 0, s>>>(tr, P, l, n, part + lv.part_off[l]);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  shift_reduce_kernel<D><<<tr.n_levels - 1, kBlock, 0, s>>>(part, lv, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_shift_penalty(const recsa_tree& tr, const recsa_pooler& P, int64_t tok_end,
+                                float* out, void* ws, hipStream_t s) {
+  if (tr.dtype == RECSA_BF16)
+    return tr.d == 128 ? shift_impl<RECSA_BF16, 128>(tr, P, tok_end, out, ws, s)
+                       : shift_impl<RECSA_BF16, 64>(tr, P, tok_end, out, ws, s);
+  return tr.d == 128 ? shift_impl<RECSA_F32, 128>(tr, P, tok_end, out, ws, s)
+                     : shift_impl<RECSA_F32, 64>(tr, P, tok_end, out, ws, s);
+}
+
+}  // namespace recsa

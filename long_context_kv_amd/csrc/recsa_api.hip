@@ -178,4 +178,58 @@ int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler, const void*
   return hip_status(e);
 }
 
+// ---- pooler distillation losses
+
+static bool distill_fits(const recsa_tree* t) {
+  return distill_groups(t->L_cap) + static_cast<int64_t>(t->C) * t->k + 8 <= 16384;
+}
+
+size_t recsa_distill_workspace_bytes(const recsa_tree* tree, int32_t Hq, int64_t n_queries) {
+  int why;
+  if (!tree_ok(tree, &why) || !heads_ok(tree, Hq) || n_queries < 1 || !distill_fits(tree))
+    return 0;
+  return static_cast<size_t>(distill_ws_bytes(*tree, Hq, n_queries));
+}
+
+int recsa_distill_kl(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
+                     const int64_t* pos_dev, const int32_t* sel_idx, const int32_t* sel_cnt,
+                     const float* importance, double theta, float* kl_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
+  if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !importance || !kl_out || !ws)
+    return RECSA_E_INVALID;
+  if (!(theta > 1.0) || !queries_fit(tree, T)) return RECSA_E_INVALID;
+  if (!distill_fits(tree)) return RECSA_E_UNSUPPORTED;
+  if (ws_bytes < static_cast<size_t>(distill_ws_bytes(*tree, Hq, static_cast<int64_t>(tree->B) * T)))
+    return RECSA_E_WORKSPACE;
+  if (tree->n_levels < 2) return RECSA_OK;      // no level above the tokens: no term
+  return hip_status(launch_distill_kl(*tree, q, Hq, T, pos_dev, sel_idx, sel_cnt, importance,
+                                      theta, kl_out, ws, static_cast<hipStream_t>(stream)));
+}
+
+static bool shift_fits(const recsa_tree* t) {
+  return (level_rows_host(t->L_cap, 1) + 15) / 16 <= 0x7FFFFFFF;
+}
+
+size_t recsa_shift_workspace_bytes(const recsa_tree* tree) {
+  int why;
+  if (!tree_ok(tree, &why) || !shift_fits(tree)) return 0;
+  return static_cast<size_t>(shift_ws_bytes(*tree));
+}
+
+int recsa_shift_penalty(const recsa_tree* tree, const recsa_pooler* pooler, int64_t tok_end,
+                        float* out, void* ws, size_t ws_bytes, void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!pooler_ok(pooler, tree) || !out || !ws) return RECSA_E_INVALID;
+  if (tok_end < 1 || tok_end > tree->L_cap) return RECSA_E_INVALID;
+  if (!shift_fits(tree)) return RECSA_E_UNSUPPORTED;
+  if (ws_bytes < static_cast<size_t>(shift_ws_bytes(*tree))) return RECSA_E_WORKSPACE;
+  if (tree->n_levels < 2) return RECSA_OK;
+  return hip_status(launch_shift_penalty(*tree, *pooler, tok_end, out, ws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -14,6 +14,9 @@ namespace recsa {
 // Phase 2/3 (all threads): the pooler MLP for the tile, weights streamed
 // from L2 once per tile.  Phase 4: K = mu + g (p - mu) + sigma m.
 // Phase 5: the rotated key rnd(R(c) K) of each node, c = node index mod C.
+// With STATS set (the shift penalty of Eq. 7) nothing is stored: phases 4-5
+// are replaced by the tile's sums of sigma*m (D values) and of ||mu||^2,
+// written to stats[0 .. D]; vc, vo, ko and kro are not used.
 template <int DT, int D, int NODES>
 struct PoolSmem {
   float feat[NODES][2 * D];
@@ -21,7 +24,7 @@ struct PoolSmem {
   float m[NODES][D];
 };
 
-template <int DT, int D, int NODES, int NT>
+template <int DT, int D, int NODES, int NT, bool STATS = false>
 __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child K rows
                           const typename Stor<DT>::T* __restrict__ vc,  // child V rows
                           typename Stor<DT>::T* __restrict__ ko,        // node K rows
@@ -30,7 +33,7 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
                           int c0,                   // index mod C of the tile's first node
                           const float* __restrict__ rope,
                           int n_valid, const recsa_pooler& P,
-                          PoolSmem<DT, D, NODES>& sm) {
+                          PoolSmem<DT, D, NODES>& sm, float* __restrict__ stats = nullptr) {
   using T = typename Stor<DT>::T;
   constexpr int DPL = D / kWave;                 // dims per lane (1 or 2)
   constexpr int NWAVES = NT / kWave;
@@ -39,13 +42,14 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
   const int wid = threadIdx.x >> 6;
   const int i0 = lane * DPL;
 
-  float mu_r[NPW][DPL], p_r[NPW][DPL], sig_r[NPW];
+  float mu_r[NPW][DPL], p_r[NPW][DPL], sig_r[NPW], mu2_r[NPW];
 
   // ---- phase 1
 #pragma unroll
   for (int nw = 0; nw < NPW; ++nw) {
     const int n = wid * NPW + nw;
     sig_r[nw] = 0.f;
+    mu2_r[nw] = 0.f;
     if (n >= NODES || n >= n_valid) continue;
     float x[kC][DPL];
     float vs[DPL];
@@ -54,22 +58,28 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
       const T* kr = kc + (static_cast<int64_t>(n) * kC + c) * D + i0;
-      const T* vr = vc + (static_cast<int64_t>(n) * kC + c) * D + i0;
-      float tmp[2];
-      if constexpr (DPL == 2) {
+      if constexpr (DPL == 2)
         load_vec<DT, 2>(kr, x[c]);
-        load_vec<DT, 2>(vr, tmp);
-        vs[0] += tmp[0];
-        vs[1] += tmp[1];
-      } else {
+      else
         x[c][0] = Stor<DT>::load(kr);
-        vs[0] += Stor<DT>::load(vr);
+      if constexpr (!STATS) {
+        const T* vr = vc + (static_cast<int64_t>(n) * kC + c) * D + i0;
+        if constexpr (DPL == 2) {
+          float tmp[2];
+          load_vec<DT, 2>(vr, tmp);
+          vs[0] += tmp[0];
+          vs[1] += tmp[1];
+        } else {
+          vs[0] += Stor<DT>::load(vr);
+        }
       }
     }
     // value mean (Eq. 1)
+    if constexpr (!STATS) {
 #pragma unroll
-    for (int u = 0; u < DPL; ++u)
-      Stor<DT>::store(vo + static_cast<int64_t>(n) * D + i0 + u, vs[u] * (1.0f / kC));
+      for (int u = 0; u < DPL; ++u)
+        Stor<DT>::store(vo + static_cast<int64_t>(n) * D + i0 + u, vs[u] * (1.0f / kC));
+    }
     // mu, sigma, rho
     float mu[DPL];
 #pragma unroll
@@ -138,6 +148,7 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
       p_r[nw][u] = p[u];
     }
     sig_r[nw] = sigma;
+    mu2_r[nw] = mq;
   }
   __syncthreads();
 
@@ -190,6 +201,27 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
     for (int q = 0; q < NPG; ++q) sm.m[g0 + q][j] = acc[q];
   }
   __syncthreads();
+
+  if constexpr (STATS) {
+    // sigma and ||mu||^2 of each node next to its m (feat is free after
+    // phase 2), then per-dimension sums over the tile's nodes in node order
+#pragma unroll
+    for (int nw = 0; nw < NPW; ++nw) {
+      const int n = wid * NPW + nw;
+      if (n < NODES && lane == 0) {
+        sm.feat[n][0] = n < n_valid ? sig_r[nw] : 0.f;
+        sm.feat[n][1] = n < n_valid ? mu2_r[nw] : 0.f;
+      }
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j <= D; j += NT) {
+      float acc = 0.f;
+      for (int n = 0; n < n_valid && n < NODES; ++n)
+        acc += j < D ? sm.feat[n][0] * sm.m[n][j] : sm.feat[n][1];
+      stats[j] = acc;
+    }
+    return;
+  }
 
   // ---- phase 4: K = mu + g (p - mu) + sigma m
 #pragma unroll

@@ -30,7 +30,8 @@ EXPORTS = (
     "recsa_status_string", "recsa_level_rows", "recsa_levels_needed",
     "recsa_init_rope", "recsa_workspace_bytes", "recsa_build_tree",
     "recsa_append_decode", "recsa_select", "recsa_attn_decode",
-    "recsa_attn_prefill", "recsa_decode",
+    "recsa_attn_prefill", "recsa_decode", "recsa_distill_workspace_bytes",
+    "recsa_distill_kl", "recsa_shift_workspace_bytes", "recsa_shift_penalty",
 )
 
 
@@ -88,6 +89,11 @@ def lib():
             "recsa_attn_decode": (ctypes.c_int, [T, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "recsa_attn_prefill": (ctypes.c_int, [T, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "recsa_decode": (ctypes.c_int, [T, P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "recsa_distill_workspace_bytes": (sz, [T, i32, i64]),
+            "recsa_distill_kl": (ctypes.c_int, [T, vp, i32, i32, vp, vp, vp, vp,
+                                                 ctypes.c_double, vp, vp, sz, vp]),
+            "recsa_shift_workspace_bytes": (sz, [T]),
+            "recsa_shift_penalty": (ctypes.c_int, [T, P, i64, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -289,6 +295,33 @@ def recsa_decode(tree, pooler, k_new, v_new, q, Hq: int, pos_dev, sel_idx, sel_c
     _check("recsa_decode", lib().recsa_decode(
         ctypes.byref(tc), ctypes.byref(pc), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, _ptr(pos_dev),
         _ptr(sel_idx), _ptr(sel_cnt), _ptr(out), _ptr(ws), nb, _stream(stream)))
+
+
+def recsa_distill_workspace_bytes(tree, Hq: int, n_queries: int) -> int:
+    tc = _tc(tree)
+    return int(lib().recsa_distill_workspace_bytes(ctypes.byref(tc), Hq, n_queries))
+
+
+def recsa_distill_kl(tree, q, Hq: int, T: int, pos_dev, sel_idx, sel_cnt, importance,
+                     theta: float, kl_out, ws, ws_bytes: int | None = None, stream=None):
+    tc = _tc(tree)
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("recsa_distill_kl", lib().recsa_distill_kl(
+        ctypes.byref(tc), _ptr(q), Hq, T, _ptr(pos_dev), _ptr(sel_idx), _ptr(sel_cnt),
+        _ptr(importance), theta, _ptr(kl_out), _ptr(ws), nb, _stream(stream)))
+
+
+def recsa_shift_workspace_bytes(tree) -> int:
+    tc = _tc(tree)
+    return int(lib().recsa_shift_workspace_bytes(ctypes.byref(tc)))
+
+
+def recsa_shift_penalty(tree, pooler, tok_end: int, out, ws, ws_bytes: int | None = None,
+                        stream=None):
+    tc, pc = _tc(tree), _pc(pooler)
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("recsa_shift_penalty", lib().recsa_shift_penalty(
+        ctypes.byref(tc), ctypes.byref(pc), tok_end, _ptr(out), _ptr(ws), nb, _stream(stream)))
 
 
 def workspace(tree, Hq: int, n_queries: int):

@@ -10,6 +10,7 @@ Workloads (Qwen3-4B-shaped single attention layer unless stated):
   524k      same shape, L=524288, decode batch 1 + a 4096-query prefill chunk
   1m_b4     same shape, L=1048576, decode batch 4 (independent sequences)
   2m_l4     4 layers of the same shape at L=2097152
+  distill_32k  same shape at L=32768 with k=64, every position a query
 
 K and V rows are N(0,1); decode queries are N(0,1); 16 "needle" keys per
 (sequence, KV head) are planted at uniform random positions, aligned with
@@ -66,6 +67,10 @@ WORKLOADS = {
     "1m_b4": Workload("1m_b4", 4, 8, 32, 128, "bf16", 1048576, 16, 256, 3),
     "2m_l4": Workload("2m_l4", 1, 8, 32, 128, "bf16", 2097152, 16, 256, 4,
                       prefill_T=8192, n_layers=4, decode_steps=256),
+    # pooler distillation at the training length: every position of a
+    # 32768-token sequence is a query, k = 64
+    "distill_32k": Workload("distill_32k", 1, 8, 32, 128, "bf16", 32768, 16, 64, 5,
+                            n_needles=0),
 }
 
 

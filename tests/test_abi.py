@@ -153,3 +153,48 @@ def test_workspace_grows_with_queries():
     af = L.recsa_workspace_bytes(ctypes.byref(tf), 32, 1)
     bf = L.recsa_workspace_bytes(ctypes.byref(tf), 32, 4096)
     assert bf - af == 4095 * 8 * (3 * 4 * 4096 * 4 + 3 * 128 * 4)
+
+
+def test_distillation_calls_validate_without_launch():
+    """The Eq. 6 / Eq. 7 calls: workspace sizes from their documented layout,
+    and bad arguments rejected before any launch."""
+    L = R.lib()
+    b = ctypes.byref
+    # a 32K-token tree at k = 64 (4 levels), the pages' pooler-training shape
+    t = _tree(k=64, L_cap=32768, n_levels=4)
+    p = _pooler()
+    def al(x):
+        return (x + 255) // 256 * 256
+    need = L.recsa_distill_workspace_bytes(b(t), 32, 100)
+    assert need == al(32768 * 128 * 4) + 100 * 32 * (32768 // 16) * 4
+    assert L.recsa_distill_workspace_bytes(b(t), 30, 100) == 0              # Hq % Hkv
+    # ceil(L_cap/16) + C*k > 16376: the per-query masses no longer fit on chip
+    big = _tree(k=256, L_cap=528384, n_levels=4)
+    assert L.recsa_distill_workspace_bytes(b(big), 32, 1) == 0
+    args = [b(big), 0x10, 32, 1, 0x10, 0x10, 0x10, 0x10, 1e6, 0x10, 0x10, 1 << 40, None]
+    assert L.recsa_distill_kl(*args) == R.RECSA_E_UNSUPPORTED
+    ok = [b(t), 0x10, 32, 100, 0x10, 0x10, 0x10, 0x10, 1e6, 0x10, 0x10, need, None]
+    for i in (1, 4, 5, 6, 7, 9, 10):                      # required pointers
+        a = list(ok)
+        a[i] = None
+        assert L.recsa_distill_kl(*a) == R.RECSA_E_INVALID, i
+    a = list(ok)
+    a[8] = 1.0                                            # theta must exceed 1
+    assert L.recsa_distill_kl(*a) == R.RECSA_E_INVALID
+    a = list(ok)
+    a[11] = need - 1
+    assert L.recsa_distill_kl(*a) == R.RECSA_E_WORKSPACE
+    a = list(ok)
+    a[2] = 24                                             # G = 3
+    assert L.recsa_distill_kl(*a) == R.RECSA_E_UNSUPPORTED
+    # shift penalty: one partial row of d+1 floats per 16 nodes, every level
+    sw = L.recsa_shift_workspace_bytes(b(t))
+    rows = sum((32768 // 16 ** lvl + 15) // 16 for lvl in (1, 2, 3)) * 8
+    assert sw == rows * 129 * 4
+    assert L.recsa_shift_penalty(b(t), b(p), 0, 0x10, 0x10, sw, None) == R.RECSA_E_INVALID
+    assert L.recsa_shift_penalty(b(t), b(p), 32769, 0x10, 0x10, sw, None) == R.RECSA_E_INVALID
+    assert L.recsa_shift_penalty(b(t), b(p), 4096, None, 0x10, sw, None) == R.RECSA_E_INVALID
+    assert L.recsa_shift_penalty(b(t), b(p), 4096, 0x10, 0x10, sw - 1, None) \
+        == R.RECSA_E_WORKSPACE
+    assert L.recsa_shift_penalty(b(t), b(_pooler(d=64)), 4096, 0x10, 0x10, sw, None) \
+        == R.RECSA_E_INVALID

@@ -1,0 +1,198 @@
+"""Pooler distillation losses of the HIP path vs the CPU oracle, through the
+C ABI (picx.dev Pooler Distillation, Eq. 6 KL terms and Eq. 7 shift penalty).
+
+Bars (derived in the design notes): per (query, KV head, scored level),
+|KL_gpu - KL_oracle| <= 2e-4 + 2e-3 |KL_oracle|; unscored levels exactly 0.
+The shift penalty within 1e-4 relative, its sums of sigma*m within 1e-4 of
+their largest magnitude and of ||mu||^2 within 1e-5 relative; repeated calls
+bit-identical.  Only (query, head) pairs whose selection equals the oracle's
+are compared (a near-tie swap changes the lower candidate lists).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import recsa_oracle as O
+from tests import parity as PY
+
+pytestmark = pytest.mark.gpu
+
+R = pytest.importorskip("long_context_kv_amd.recsa")
+DEV = "cuda"
+THETA = 1e6
+KL_ATOL, KL_RTOL = 2e-4, 2e-3
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    R.lib()
+
+
+def _tree(B, Hkv, d, L0, k, dtype, seed):
+    wl = synth.Workload("distill", B, Hkv, Hkv * 4, d, dtype, L0, 16, k, seed)
+    K, V = synth.kv_rows(wl, DEV, n_rows=L0)
+    pdict = synth.pooler_params(d, d, DEV, seed)
+    tree = R.Tree.allocate(B, Hkv, d, L0, k=k, dtype=dtype, device=DEV, level0=(K, V))
+    pool = R.Pooler.from_dict(pdict, DEV)
+    R.recsa_build_tree(tree, pool, 0, L0)
+    return tree, pool, pdict
+
+
+def run_distill(tree, q, Hq, pos):
+    """recsa_select (with importance), then recsa_distill_kl on its outputs."""
+    B, T = pos.shape
+    nq = B * T
+    ws = R.workspace(tree, Hq, nq)
+    sel, cnt, imp = tree.selection_buffers(nq, with_importance=True)
+    R.recsa_select(tree, q, Hq, T, pos, sel, cnt, imp, ws)
+    dws = torch.empty(R.recsa_distill_workspace_bytes(tree, Hq, nq), dtype=torch.uint8,
+                      device=tree.rope.device)
+    kl = torch.full((B, T, tree.Hkv, tree.n_sel), float("nan"), dtype=torch.float32,
+                    device=tree.rope.device)
+    R.recsa_distill_kl(tree, q, Hq, T, pos, sel, cnt, imp, THETA, kl, dws)
+    torch.cuda.synchronize()
+    return (sel.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel, tree.k),
+            cnt.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel),
+            imp.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel, -1),
+            kl.cpu().numpy().astype(np.float64))
+
+
+def check_kl(tree, pdict, q, pos, sel, cnt, imp, kl, heads):
+    """Oracle walk + Eq. 6 for every (b, query, head in heads); returns
+    (pairs compared, scored levels compared, max abs error)."""
+    B, T = pos.shape
+    G = q.shape[2] // tree.Hkv
+    cos, sin = O.rope_table(tree.d, 16 * tree.k, THETA)
+    qn = PY.to64(q)
+    rep = PY.WalkReport()
+    n_pairs = n_levels = 0
+    worst = 0.0
+    for b in range(B):
+        n_tok = int(pos[b].max()) + 1
+        for j in heads:
+            K0 = PY.to64(tree.K[0][b, j, :n_tok])
+            V0 = PY.to64(tree.V[0][b, j, :n_tok])
+            K, _ = O.build_tree(K0, V0, 16, tree.n_levels, PY.oracle_pooler(pdict), tree.dtype)
+            for ti in range(T):
+                t = int(pos[b, ti])
+                D = O.n_levels_for(t, 16, tree.k)
+                Kt = ([K[0][: t + 1]] + [K[lvl][: (t + 1) // 16 ** lvl]
+                                         for lvl in range(1, len(K))])[: max(D, 1)]
+                qG = qn[b, ti, j * G:(j + 1) * G]
+                tr = O.walk(qG, t, Kt, 16, tree.k, cos, sin, tree.dtype)
+                if not PY.compare_walk(tr, sel[b, ti, j], cnt[b, ti, j], imp[b, ti, j], rep,
+                                       1e-5):
+                    continue
+                ref = O.distill_kl(qG, t, tr, K0[: t + 1], 16, THETA)
+                n_pairs += 1
+                for lvl in range(1, tree.n_levels):
+                    g = kl[b, ti, j, lvl - 1]
+                    if lvl in ref:
+                        err = abs(g - ref[lvl])
+                        worst = max(worst, err)
+                        n_levels += 1
+                        assert err <= KL_ATOL + KL_RTOL * abs(ref[lvl]), (b, t, j, lvl, g, ref[lvl])
+                    else:
+                        assert g == 0.0, (b, t, j, lvl, g)
+    assert rep.swapped <= 1, rep.notes
+    return n_pairs, n_levels, worst
+
+
+def positions(L0, T, seed):
+    """T query positions in [0, L0): the first and last tokens, the edges of
+    the all-unscored range t < C*k, and seeded uniform draws."""
+    g = torch.Generator().manual_seed(seed)
+    fixed = [0, 1, 255, 256, L0 - 1, L0 - 17]
+    rnd = torch.randint(0, L0, (T - len(fixed),), generator=g).tolist()
+    return sorted(fixed + rnd)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_distill_kl_matches_oracle(dtype, d):
+    """Eq. 6 terms of 40 queries x 2 KV heads (G = 4) on a 5000-token tree at
+    k = 16: levels 1 and 2 scored for most positions, none below C*k = 256."""
+    _need_gpu()
+    L0, T, k = 5000, 40, 16
+    tree, pool, pdict = _tree(1, 2, d, L0, k, dtype, 61)
+    assert tree.n_levels == 4
+    Hq = 8
+    q = synth.to_storage(synth.normal((1, T, Hq, d), DEV, 61, 1), dtype)
+    pos = torch.tensor([positions(L0, T, 61)], dtype=torch.int64, device=DEV)
+    sel, cnt, imp, kl = run_distill(tree, q, Hq, pos)
+    assert np.all(np.isfinite(kl))
+    assert np.all(kl >= -1e-6)                         # a KL divergence
+    n_pairs, n_lv, worst = check_kl(tree, pdict, q, pos.cpu(), sel, cnt, imp, kl, [0, 1])
+    assert n_pairs >= 2 * T - 1 and n_lv >= T, (n_pairs, n_lv)
+    # queries below C*k see every level whole: no term at all
+    small = (pos.cpu().numpy()[0] < 16 * k)
+    assert np.all(kl[0, small] == 0.0)
+
+
+def test_distill_kl_two_sequences_and_head_ratios():
+    """Two sequences, G = 2 and G = 1 (64 / G queries per teacher block, a
+    ragged last block), k = 64 (the pages' pooler-training depth) on 9000
+    tokens: level 1 scored from t = 1024 on."""
+    _need_gpu()
+    L0, T, k, d = 9000, 37, 64, 64
+    tree, pool, pdict = _tree(2, 2, d, L0, k, "bf16", 62)
+    for G in (2, 1):
+        Hq = 2 * G
+        q = synth.to_storage(synth.normal((2, T, Hq, d), DEV, 62, G), "bf16")
+        pos = torch.stack([torch.tensor(positions(L0, T, 62 + s)) for s in range(2)]).to(DEV)
+        sel, cnt, imp, kl = run_distill(tree, q, Hq, pos)
+        n_pairs, n_lv, _ = check_kl(tree, pdict, q, pos.cpu(), sel, cnt, imp, kl, [0, 1])
+        assert n_pairs >= 4 * T - 1 and n_lv >= 2 * T
+
+
+def _shift_oracle(tree, pdict, tok_end):
+    """Per level: (sum sigma*m [d], sum ||mu||^2, penalty) over the complete
+    nodes of every (sequence, KV head), from the oracle's own trees."""
+    P = PY.oracle_pooler(pdict)
+    by_level = {}
+    for b in range(tree.B):
+        for j in range(tree.Hkv):
+            K0 = PY.to64(tree.K[0][b, j, :tok_end])
+            V0 = PY.to64(tree.V[0][b, j, :tok_end])
+            K, _ = O.build_tree(K0, V0, 16, tree.n_levels, P, tree.dtype)
+            for lvl in range(1, tree.n_levels):
+                n = tok_end // 16 ** lvl
+                if n:
+                    by_level.setdefault(lvl, []).append(K[lvl - 1][: n * 16].reshape(n, 16, -1))
+    X = {lvl: np.concatenate(v) for lvl, v in by_level.items()}
+    pen = O.shift_penalty(X, P)
+    out = {}
+    for lvl, x in X.items():
+        mu, sigma, _, m = O.pool_parts(x, P)
+        out[lvl] = ((sigma[:, None] * m).sum(axis=0), float((mu * mu).sum()), pen[lvl])
+    return out
+
+
+@pytest.mark.parametrize("dtype,d,B,Hkv,L0,tok_end", [
+    ("f32", 64, 1, 1, 4096, 4096),
+    ("bf16", 128, 2, 2, 8200, 8200),
+    ("bf16", 128, 1, 2, 8200, 300),        # one complete level-1 tile, ragged
+])
+def test_shift_penalty_matches_oracle(dtype, d, B, Hkv, L0, tok_end):
+    _need_gpu()
+    tree, pool, pdict = _tree(B, Hkv, d, L0, 16, dtype, 63)
+    ws = torch.empty(R.recsa_shift_workspace_bytes(tree), dtype=torch.uint8, device=DEV)
+    out = torch.full((tree.n_levels - 1, d + 2), float("nan"), device=DEV)
+    R.recsa_shift_penalty(tree, pool, tok_end, out, ws)
+    out2 = torch.zeros_like(out)
+    R.recsa_shift_penalty(tree, pool, tok_end, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)                      # fixed summation order
+    g = out.cpu().numpy().astype(np.float64)
+    ref = _shift_oracle(tree, pdict, tok_end)
+    for lvl in range(1, tree.n_levels):
+        row = g[lvl - 1]
+        if lvl not in ref:
+            assert np.all(row == 0.0), lvl
+            continue
+        s, mu2, pen = ref[lvl]
+        assert np.max(np.abs(row[:d] - s)) <= 1e-4 * np.max(np.abs(s)), lvl
+        assert abs(row[d] - mu2) <= 1e-5 * mu2, lvl
+        assert abs(row[d + 1] - pen) <= 1e-4 * pen, (lvl, row[d + 1], pen)
