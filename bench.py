@@ -572,7 +572,7 @@ ROLE_DISTILL_Q = 11
 
 
 def cpu_baseline_distill(wl, tree, pdict, q, L):
-    """The oracle on one thread: KV head 0, 16 evenly spaced positions of the
+    """The oracle on one thread: KV head 0, 400 evenly spaced positions of the
     sequence (walk + Eq. 6 each), scaled to every position and KV head."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -589,7 +589,7 @@ def cpu_baseline_distill(wl, tree, pdict, q, L):
         Kt, _ = O.build_tree(K0, V0, 16, tree.n_levels, P, wl.dtype)
         cos, sin = O.rope_table(wl.d, 16 * wl.k, wl.theta)
         qn = PY.to64(q[0, :, :G])
-        idx = np.linspace(0, L - 1, 16).astype(int)
+        idx = np.linspace(0, L - 1, 400).astype(int)
         t1 = time.time()
         for t in idx:
             t = int(t)
@@ -604,7 +604,7 @@ def cpu_baseline_distill(wl, tree, pdict, q, L):
     scaled_ms = per_q * L * heads * 1e3
     log(f"cpu baseline distill ({total:.1f}s): {per_q * 1e3:.1f} ms per (query, head)")
     return {"value": round(scaled_ms, 1), "unit": "ms/layer-step", "cores": 1, "kind": "oracle",
-            "sample": (f"KV head 0 of {heads}, one thread: oracle walk + Eq. 6 at 16 evenly "
+            "sample": (f"KV head 0 of {heads}, one thread: oracle walk + Eq. 6 at 400 evenly "
                        f"spaced positions of {L}, scaled x{L} positions x{heads} heads "
                        f"({total:.1f}s of CPU work; Eq. 7 not included)")}
 
