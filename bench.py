@@ -83,7 +83,7 @@ class Work:
     """Device-resident state of one benchmark workload (see module doc)."""
 
 
-def setup_workload(name="524k", dev="cuda"):
+def setup_workload(name="524k", dev="cuda", level0_host=False):
     """Build the inputs of a workload in HBM and return the step closures.
 
     Level-0 K/V of L tokens plus the prefill chunk's rows and the decode
@@ -110,13 +110,16 @@ def setup_workload(name="524k", dev="cuda"):
     w.pdict = synth.pooler_params(d, d, dev, wl.seed)
     w.pool = R.Pooler.from_dict(w.pdict, dev)
     w.tree = R.Tree.allocate(B, Hkv, d, L_cap, k=wl.k, dtype=wl.dtype, device=dev,
-                             level0=(K0, V0), theta=wl.theta)
+                             level0=(K0, V0), theta=wl.theta, level0_host=level0_host)
     tree = w.tree
+    if level0_host:
+        del K0, V0                              # level 0 now lives in pinned host memory
+        torch.cuda.empty_cache()
     ck, cv, w.q_pre = synth.new_rows(wl, dev, T, "chunk")
     tree.K[0][:, :, L:L + T] = ck
     tree.V[0][:, :, L:L + T] = cv
-    w.k_new = tree.K[0][:, :, t_dec].clone().contiguous()
-    w.v_new = tree.V[0][:, :, t_dec].clone().contiguous()
+    w.k_new = tree.K[0][:, :, t_dec].to(dev, copy=True).contiguous()
+    w.v_new = tree.V[0][:, :, t_dec].to(dev, copy=True).contiguous()
     w.pos_pre = torch.arange(L, L + T, device=dev).view(1, T).expand(B, T).contiguous()
     w.pos_dec = torch.full((B,), t_dec, dtype=torch.int64, device=dev)
     w.ws_pre = R.workspace(tree, Hq, B * T)
@@ -183,6 +186,9 @@ def main():
     ap.add_argument("--distill", action="store_true",
                     help="measure the pooler distillation losses (Eq. 6 over every position "
                          "of a 32768-token sequence, Eq. 7 over every node) instead")
+    ap.add_argument("--offload", action="store_true",
+                    help="measure decode and prefill with level 0 of the cache in pinned host "
+                         "memory (read over PCIe in place) instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -200,6 +206,9 @@ def main():
         return
     if args.distill:
         bench_distill(args)
+        return
+    if args.offload:
+        bench_offload(args)
         return
     w = setup_workload(args.workload)
     wl, tree, pool, R = w.wl, w.tree, w.pool, w.R
@@ -258,6 +267,9 @@ def main():
         b.record()
     torch.cuda.synchronize()
     dec_rep_us = sorted(a.elapsed_time(b) * 1e3 for a, b in reps)
+    if torch.count_nonzero(R.decode_error_words(ws_dec, tree, Hq)).item() or \
+            not torch.isfinite(out_dec).all():
+        raise RuntimeError("a replayed decode step reported an error word or a non-finite output")
 
     # the same decode step as three calls (append, select, attention)
     graph_split = capture_decode(w, w.decode_split)
@@ -474,6 +486,86 @@ def cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T):
 
 
 FP32_MFMA_PEAK_TFLOPS = 157.3
+PCIE_PEAK_GBS = 63.0           # PCIe 5.0 x16, one direction, after 128b/130b encoding
+
+
+def bench_offload(args):
+    """The workload's decode step and prefill chunk with level 0 (K, V and
+    the rotated keys Kr) in pinned host memory and levels >= 1 in HBM.  The
+    kernels are the device-resident ones; each reads the level-0 rows it
+    selected straight from host memory over PCIe.  Roofline: the level-0
+    bytes one decode must read (Kr and V rows of A^(0) per KV head) against
+    the PCIe peak."""
+    import numpy as np
+    import torch
+
+    w = setup_workload(args.workload, level0_host=True)
+    wl, tree, R = w.wl, w.tree, w.R
+    L, T, B, Hkv, Hq, d = w.L, w.T, wl.B, wl.Hkv, wl.Hq, wl.d
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    a, b = ev(), ev()
+    a.record()
+    w.build_full()
+    b.record()
+    torch.cuda.synchronize()
+    build_ms = a.elapsed_time(b)
+    log(f"full build with level 0 in host memory: {build_ms:.1f} ms")
+    for _ in range(args.warmup):
+        w.prefill()
+    torch.cuda.synchronize()
+    pre = []
+    for _ in range(args.steps):
+        a, b = ev(), ev()
+        a.record()
+        w.prefill()
+        b.record()
+        pre.append((a, b))
+    torch.cuda.synchronize()
+    pre_ms = sorted(x.elapsed_time(y) for x, y in pre)[len(pre) // 2]
+    graph = capture_decode(w)
+    for _ in range(5):
+        graph.replay()
+    reps = [(ev(), ev()) for _ in range(args.decode_reps)]
+    for x, y in reps:
+        x.record()
+        graph.replay()
+        y.record()
+    torch.cuda.synchronize()
+    dec = sorted(x.elapsed_time(y) * 1e3 for x, y in reps)
+    dec_us = dec[len(dec) // 2]
+    err = torch.count_nonzero(R.decode_error_words(w.ws_dec, tree, Hq)).item()
+    if err:
+        raise RuntimeError("fused decode reported a timed-out wait")
+    sizes = list_sizes(w.t_dec, 16, wl.k, tree.n_levels)
+    host_bytes = 2 * sizes[0] * ROW_BYTES * Hkv * B
+    gbs = host_bytes / (dec_us * 1e-6) / 1e9
+    result = {
+        "metric": "RecSA decode µs/token with level 0 in host memory (KV offload); "
+                  "% of PCIe peak",
+        "value": round(dec_us, 2), "unit": "us/token", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(pre_ms + dec_us / 1e3, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name} with level 0 (K, V, Kr) in pinned host memory: "
+                               f"1 layer, {Hkv} KV heads, {Hq} query heads, d={d}, {wl.dtype}, "
+                               f"L={L}, C=16, k={wl.k}; decode B={B} at t={w.t_dec}; "
+                               f"prefill chunk T={wl.prefill_T}",
+                   "seq_len": L, "global_batch": B},
+        "decode_us_p10_p90": [round(dec[len(dec) // 10], 2), round(dec[(9 * len(dec)) // 10], 2)],
+        "prefill_ms_per_chunk": round(pre_ms, 3),
+        "prefill_tok_s": round(B * T / (pre_ms * 1e-3), 1),
+        "build_full_ms": round(build_ms, 1),
+        "gpu_resident_bytes": int(sum(x.numel() * x.element_size()
+                                      for name in ("K", "V", "Kr")
+                                      for x in getattr(tree, name)[1:])),
+        "host_resident_bytes": int(3 * tree.K[0].numel() * tree.K[0].element_size()),
+        "roofline": {"kernel": "decode_fused_kernel, level-0 reads over PCIe",
+                     "bound": "pcie", "achieved": round(gbs, 2), "peak": PCIE_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_host_bytes_per_launch": host_bytes},
+    }
+    print(json.dumps(result), flush=True)
 
 
 def bench_distill(args):

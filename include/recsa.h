@@ -82,6 +82,12 @@ extern "C" {
  *   list of the top level has at most k nodes for every position < L_cap);
  *   more levels do not change any result.
  * rope: float32 table [C*k][d/2][2] of (cos, sin), filled by recsa_init_rope.
+ * Level 0 (K[0], V[0], Kr[0]) may be page-locked host memory that the device
+ * can address (hipHostMalloc; pass the address hipHostGetDevicePointer
+ * returns): every call then reads and writes the level-0 rows it needs in
+ * place over PCIe, with identical results, while levels >= 1 (1/15 of the
+ * cache) stay in device memory (picx.dev Efficiency Results, KV offloading;
+ * Practical Implications, bounded GPU memory).
  */
 typedef struct recsa_tree {
   int32_t dtype;

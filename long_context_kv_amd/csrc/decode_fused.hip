@@ -15,11 +15,15 @@
 //   all W then accumulate interleaved entry chunks (token t's row comes from
 //   k_new/v_new), publish a partial softmax state, and WG 0 waits for them
 //   and merges them into the output.
-// Barriers come in two forms.  XCD-local: the device hands workgroup i to
-// XCD i mod n_xcd, so with S a multiple of n_xcd all workgroups of a group
-// share one XCD and its L2; arrivals are atomic adds on one counter in that
-// L2 and waits read it with an L2 atomic, with no L2 write-back or
-// invalidation (each workgroup checks its own XCD id first).  Device-wide:
+// Barriers come in two forms.  XCD-local: the device hands the workgroups of
+// a dispatch to its XCDs round-robin, workgroup i to XCD (i + s) mod n_xcd
+// for an offset s that varies between dispatches (graph replays start at
+// other XCDs than direct launches), so with S a multiple of n_xcd all
+// workgroups of a group share one XCD and its L2; arrivals are atomic adds on
+// one counter in that L2 and waits read it with an L2 atomic, with no L2
+// write-back or invalidation.  Each workgroup also ORs its XCD id into a
+// placement mask with a device-scope atomic; the merging workgroup checks
+// that the group's mask names a single XCD.  Device-wide:
 // per-workgroup flags raised and polled with device-scope atomics around
 // release/acquire fences.  Either way every wait is a bounded spin; if the
 // bound is hit the error word is set and the output is poisoned with NaN.
@@ -226,12 +230,14 @@ __global__ void __launch_bounds__(kFusedThreads)
   if (tid == 0) {
     s_fail = 0u;
     if constexpr (XL) {
-      // the local barrier needs this workgroup on XCD (id mod n_xcd)
+      // the local barrier needs every workgroup of the group on one XCD:
+      // record this one's XCD in the group's placement mask (flags[0], its
+      // own line; unused by this form's barriers).  The returned value keeps
+      // the atomic performed before this workgroup's first arrival.
       const int xcc = __builtin_amdgcn_s_getreg(20 | (15 << 11)) & 0xF;   // hwreg XCC_ID
-      if (xcc != static_cast<int>(blockIdx.x) % n_xcd) {
-        atomicOr(err, 2u);          // the group's waits will time out and poison the output
-        s_fail = 1u;
-      }
+      const uint32_t prev =
+          __hip_atomic_fetch_or(flags, 1u << xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev & 0x80000000u) s_fail = 1u;     // never set: keeps the result live
     }
   }
   load_query_rows<DT, D, G, NT>(q, static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G, qs);
@@ -367,7 +373,12 @@ __global__ void __launch_bounds__(kFusedThreads)
     if (!s_last) return;
     merge_partials_fused<D, G, NT>(pp_group, W, o);
     __shared__ uint32_t s_bad;
-    if (tid == 0) s_bad = s_fail | l2_read(counter + 1);
+    if (tid == 0) {
+      const uint32_t mask = __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool split = __popc(mask) != 1;     // members on more than one XCD
+      if (split) atomicOr(err, 2u);
+      s_bad = s_fail | l2_read(counter + 1) | (split ? 1u : 0u);
+    }
     __syncthreads();
     if (s_bad) {
       for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
@@ -376,6 +387,7 @@ __global__ void __launch_bounds__(kFusedThreads)
     if (tid == 0) {
       __hip_atomic_exchange(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       __hip_atomic_exchange(counter + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_exchange(flags, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
     // ---- WG 0 waits for every partial and merges them

@@ -102,6 +102,28 @@ def lib():
     return _lib
 
 
+_hip = None
+
+
+def host_device_pointer(t: torch.Tensor) -> int:
+    """Device address of a pinned host tensor (hipHostGetDevicePointer).
+    Raises unless the memory is page-locked host memory that the device can
+    address, so no kernel is ever handed an unmapped host pointer."""
+    global _hip
+    if t.device.type != "cpu" or not t.is_pinned():
+        raise ValueError("expected a pinned host tensor")
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                 ctypes.c_void_p, ctypes.c_uint]
+    dp = ctypes.c_void_p()
+    err = _hip.hipHostGetDevicePointer(ctypes.byref(dp), ctypes.c_void_p(t.data_ptr()), 0)
+    if err != 0 or not dp.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({err}): host memory not mapped")
+    return int(dp.value)
+
+
 def _ptr(x) -> int | None:
     if x is None:
         return None
@@ -132,7 +154,9 @@ class Tree:
     K[l], V[l]: [B, Hkv, floor(L_cap / 16^l), d] in the storage dtype; level 0
     is the KV cache itself (pre-RoPE keys).  Kr[l]: the same shape, the rotated
     keys the library writes next to every key row.  rope: [C*k, d/2, 2]
-    float32."""
+    float32.  With level0_host, K[0], V[0] and Kr[0] are pinned host tensors
+    that the kernels read and write in place over PCIe (level0_dptr holds
+    their device addresses); levels >= 1 stay in device memory."""
     B: int
     Hkv: int
     d: int
@@ -145,15 +169,26 @@ class Tree:
     V: list
     Kr: list
     rope: torch.Tensor
+    level0_dptr: tuple | None = None
 
     @staticmethod
     def allocate(B, Hkv, d, L_cap, k=256, C=16, dtype="bf16", n_levels=None,
-                 device="cuda", theta=1e6, level0=None):
+                 device="cuda", theta=1e6, level0=None, level0_host=False):
         n = n_levels or max(2, recsa_levels_needed(L_cap, C, k))
         tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
         K, V, Kr = [], [], []
         for lvl in range(n):
             rows = recsa_level_rows(L_cap, C, lvl)
+            if lvl == 0 and level0_host:
+                shape = (B, Hkv, rows, d)
+                pin = lambda: torch.zeros(shape, dtype=tdt, pin_memory=True)
+                Kr.append(pin())
+                K.append(pin())
+                V.append(pin())
+                if level0 is not None:
+                    K[0].copy_(level0[0])
+                    V[0].copy_(level0[1])
+                continue
             Kr.append(torch.zeros((B, Hkv, rows, d), dtype=tdt, device=device))
             if lvl == 0 and level0 is not None:
                 K.append(level0[0])
@@ -163,7 +198,10 @@ class Tree:
             V.append(torch.zeros((B, Hkv, rows, d), dtype=tdt, device=device))
         rope = torch.empty((C * k, d // 2, 2), dtype=torch.float32, device=device)
         recsa_init_rope(rope, d, C * k, theta)
-        return Tree(B, Hkv, d, L_cap, k, C, dtype, n, K, V, Kr, rope)
+        dptr = None
+        if level0_host:
+            dptr = tuple(host_device_pointer(x) for x in (K[0], V[0], Kr[0]))
+        return Tree(B, Hkv, d, L_cap, k, C, dtype, n, K, V, Kr, rope, dptr)
 
     def c(self) -> TreeC:
         t = TreeC()
@@ -174,6 +212,8 @@ class Tree:
             t.K[lvl] = self.K[lvl].data_ptr() if self.K[lvl].numel() else None
             t.V[lvl] = self.V[lvl].data_ptr() if self.V[lvl].numel() else None
             t.Kr[lvl] = self.Kr[lvl].data_ptr() if self.Kr[lvl].numel() else None
+        if self.level0_dptr is not None:
+            t.K[0], t.V[0], t.Kr[0] = self.level0_dptr
         t.rope = self.rope.data_ptr()
         return t
 

@@ -300,6 +300,59 @@ def _fused_step(tree, pool, k_new, v_new, q, Hq, pos, ws=None):
     return sel, cnt, out, ws
 
 
+def test_fused_decode_graph_replays_match_eager():
+    """recsa_decode captured in a HIP graph and replayed: each replay starts
+    its workgroups at another XCD than a direct launch does, so the groups'
+    placement differs, yet every replay -- synchronised or back to back, with
+    eager library and torch work in between -- gives the eager call's bits,
+    raises no error word and leaves the control block zero."""
+    _need_gpu()
+    L0, B, Hkv, G, d, k = 40000, 2, 4, 4, 128, 64
+    wl, tree, pool, pdict = _setup(B, Hkv, d, L0 + 64, L0 + 64, k, "bf16", 33)
+    R.recsa_build_tree(tree, pool, 0, L0)
+    Hq = Hkv * G
+    t = L0 - 5
+    kn = tree.K[0][:, :, t].clone().contiguous()
+    vn = tree.V[0][:, :, t].clone().contiguous()
+    q = synth.to_storage(synth.normal((B, 1, Hq, d), DEV, 33, 3), "bf16")
+    pos = torch.full((B,), t, dtype=torch.int64, device=DEV)
+    ws = R.workspace(tree, Hq, B)
+    sel, cnt, _ = tree.selection_buffers(B)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+    step = lambda: R.recsa_decode(tree, pool, kn, vn, q, Hq, pos, sel, cnt, out, ws)
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_s = out.clone(), sel.clone()
+    assert torch.isfinite(ref_o).all()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    ctl = R.decode_control_words(ws, tree, Hq)
+    # the selection of a different query through the split calls between replays
+    ws2 = R.workspace(tree, Hq, B)
+    s2, c2, _ = tree.selection_buffers(B)
+    q2 = synth.to_storage(synth.normal((B, 1, Hq, d), DEV, 33, 4), "bf16")
+    for i in range(6):
+        out.fill_(0.0)
+        graph.replay()
+        R.recsa_select(tree, q2, Hq, 1, pos.view(B, 1), s2, c2, None, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o), i
+        assert torch.equal(sel, ref_s), i
+        assert torch.count_nonzero(ctl).item() == 0, (i, ctl[:, :4].tolist())
+    for i in range(20):                            # back to back
+        graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_o)
+    assert torch.count_nonzero(ctl).item() == 0
+
+
 @pytest.mark.parametrize("dtype,d,Hkv,G,B", [("bf16", 128, 8, 4, 1), ("f32", 64, 2, 4, 2),
                                              ("bf16", 128, 4, 2, 3)])
 def test_fused_decode_matches_separate_calls(dtype, d, Hkv, G, B):
