@@ -466,3 +466,66 @@ def shift_penalty(children_by_level, P: Pooler):
         num = (sigma[:, None] * m).mean(axis=0)
         out[lvl] = float(num @ num / (mu * mu).sum(axis=1).mean())
     return out
+
+
+# --------------------------------------------------------------------------
+# Pooler backward (picx.dev "Pooler Distillation", Eq. 5 trained with Eq. 6
+# and Eq. 7; "Training Stages", stage 1).  The vector-Jacobian product of
+# Eq. 5 with respect to the pooler parameters, for a batch of nodes whose
+# children are inputs (no gradient flows into the children: every level is
+# pooled from stored, rounded rows).  Storage rounding of the node key is
+# taken as the identity in the backward pass.
+# --------------------------------------------------------------------------
+
+def pool_backward(X, P: Pooler, dK, dm_extra=None):
+    """Gradients of  L = sum_i dK_i . K_i + sum_i dm_extra_i . m_i  with
+    respect to (w, tau, g, W1, b1, W2), K_i and m_i as in ``pool_parts``.
+    X: [N, C, d] children; dK, dm_extra: [N, d].  Returns a dict of arrays
+    shaped like the parameters (tau and g as floats)."""
+    P = P.as64()
+    X = np.asarray(X, dtype=np.float64)
+    d = X.shape[2]
+    # forward, keeping what the chain rule needs
+    mu = X.mean(axis=1)
+    dev = X - mu[:, None, :]
+    sigma = np.sqrt((dev * dev).mean(axis=(1, 2)) + P.eps)
+    rho = np.sqrt((mu * mu).mean(axis=1) + P.eps)
+    u = (dev @ P.w) / sigma[:, None]                         # w.(x_c - mu)/sigma
+    a = P.tau * u
+    a = a - a.max(axis=1, keepdims=True)
+    e = np.exp(a)
+    alpha = e / e.sum(axis=1, keepdims=True)
+    p = np.einsum("nc,ncd->nd", alpha, X)
+    feat = np.concatenate([mu / rho[:, None], (p - mu) / sigma[:, None]], axis=1)
+    z = feat @ P.W1.T + P.b1
+    sg = 1.0 / (1.0 + np.exp(-z))
+    hid = z * sg
+    # backward: K = mu + g (p - mu) + sigma m,  m = W2 SiLU(z),  z = W1 feat + b1
+    dK = np.asarray(dK, dtype=np.float64)
+    dm = sigma[:, None] * dK
+    if dm_extra is not None:
+        dm = dm + np.asarray(dm_extra, dtype=np.float64)
+    g_g = float(np.sum(dK * (p - mu)))
+    g_W2 = dm.T @ hid                                         # [d, h]
+    dz = (dm @ P.W2) * (sg * (1.0 + z * (1.0 - sg)))          # SiLU'(z)
+    g_W1 = dz.T @ feat                                        # [h, 2d]
+    g_b1 = dz.sum(axis=0)
+    dfeat = dz @ P.W1                                         # [N, 2d]
+    dp = P.g * dK + dfeat[:, d:] / sigma[:, None]             # mu/rho does not depend on
+    dalpha = np.einsum("nd,ncd->nc", dp, X)                   # the parameters
+    da = alpha * (dalpha - (alpha * dalpha).sum(axis=1, keepdims=True))
+    g_tau = float(np.sum(da * u))
+    g_w = P.tau * np.einsum("nc,ncd->d", da, dev / sigma[:, None, None])
+    return {"w": g_w, "tau": g_tau, "g": g_g, "W1": g_W1, "b1": g_b1, "W2": g_W2}
+
+
+def shift_penalty_dm(X, P: Pooler):
+    """Gradient of the Eq. 7 penalty of one level with respect to each node's
+    MLP output m_i (the only part of the penalty the parameters reach):
+    with S = sum_i sigma_i m_i and U = sum_i ||mu_i||^2 over the level's M
+    nodes, penalty = ||S||^2 / (M U), so d penalty / d m_i = 2 sigma_i S / (M U)."""
+    mu, sigma, _, m = pool_parts(X, P)
+    S = (sigma[:, None] * m).sum(axis=0)
+    U = float((mu * mu).sum())
+    M = X.shape[0]
+    return 2.0 * sigma[:, None] * S[None, :] / (M * U)

@@ -605,3 +605,71 @@ def test_shift_penalty_invariants():
     mu, sigma, _, m = O.pool_parts(X[:1], P)
     one = O.shift_penalty({1: X[:1]}, P)[1]
     assert abs(one - np.sum((sigma[0] * m[0]) ** 2) / np.sum(mu[0] ** 2)) < 1e-12 * one
+
+
+def _fd_grads(loss, P, step=1e-6, picks=None):
+    """Central differences of loss(P) for every parameter entry (or the
+    entries listed in picks[name])."""
+    out = {}
+    for name in ("w", "W1", "b1", "W2"):
+        arr = getattr(P, name)
+        g = np.zeros_like(arr)
+        idx = picks[name] if picks and name in picks else list(np.ndindex(arr.shape))
+        for ix in idx:
+            old = arr[ix]
+            arr[ix] = old + step
+            fp = loss(P)
+            arr[ix] = old - step
+            fm = loss(P)
+            arr[ix] = old
+            g[ix] = (fp - fm) / (2 * step)
+        out[name] = (g, idx)
+    for name in ("tau", "g"):
+        old = getattr(P, name)
+        setattr(P, name, old + step)
+        fp = loss(P)
+        setattr(P, name, old - step)
+        fm = loss(P)
+        setattr(P, name, old)
+        out[name] = ((fp - fm) / (2 * step), None)
+    return out
+
+
+def _check_fd(an, fd, rtol):
+    for name, (g, idx) in fd.items():
+        a = an[name]
+        if idx is None:
+            assert abs(a - g) <= rtol * max(1.0, abs(g)), (name, a, g)
+            continue
+        scale = max(1e-12, float(np.max(np.abs(a))))
+        for ix in idx:
+            assert abs(a[ix] - g[ix]) <= rtol * scale, (name, ix, a[ix], g[ix])
+
+
+def test_pool_backward_matches_finite_differences():
+    """The VJP of Eq. 5 against central differences of the (separately
+    pinned) forward pool_keys, for every parameter: a dropped term or a
+    transposed weight shows up as a mismatch."""
+    rng = np.random.default_rng(5)
+    d, h, N = 8, 16, 4
+    P = O.Pooler(rng.normal(size=d) / np.sqrt(d), 0.8, 0.4, rng.normal(size=(h, 2 * d)) / np.sqrt(d),
+                 rng.normal(size=h) * 0.3, rng.normal(size=(d, h)) / np.sqrt(h), 1e-6)
+    X = rng.normal(size=(N, 16, d))
+    dK = rng.normal(size=(N, d))
+    an = O.pool_backward(X, P, dK)
+    fd = _fd_grads(lambda Q: float(np.sum(dK * O.pool_keys(X, Q))), P)
+    _check_fd(an, fd, 1e-6)
+
+
+def test_pool_backward_of_shift_penalty_matches_finite_differences():
+    """The gradient of the Eq. 7 penalty (shift_penalty_dm fed to
+    pool_backward) against central differences of shift_penalty itself."""
+    rng = np.random.default_rng(6)
+    d, h, N = 8, 16, 6
+    P = O.Pooler(rng.normal(size=d) / np.sqrt(d), 1.3, 0.5, rng.normal(size=(h, 2 * d)) / np.sqrt(d),
+                 rng.normal(size=h) * 0.3, rng.normal(size=(d, h)) / np.sqrt(h), 1e-6)
+    X = rng.normal(size=(N, 16, d)) + 0.5
+    an = O.pool_backward(X, P, np.zeros((N, d)), O.shift_penalty_dm(X, P))
+    fd = _fd_grads(lambda Q: O.shift_penalty({1: X}, Q)[1], P)
+    _check_fd(an, fd, 1e-6)
+    assert an["g"] == 0.0                   # the penalty does not involve g
