@@ -571,8 +571,9 @@ def bench_offload(args):
 def bench_distill(args):
     """Eq. 6 and Eq. 7 on the distillation workload: one step = selection
     with importances for every position of the sequence, the KL terms of
-    every (query, KV head, scored level) and the shift penalty of every
-    level.  Roofline: the teacher's dense logits, 2 d flops per (query head,
+    every (query, KV head, scored level), the shift penalty of every level
+    and the pooler backward of every level (a seeded key gradient plus the
+    penalty).  Roofline: the teacher's dense logits, 2 d flops per (query head,
     key) pair with key <= query, on the float32 matrix cores; the whole
     recsa_distill_kl call is charged, so the fraction is a lower bound."""
     import numpy as np
@@ -612,28 +613,44 @@ def bench_distill(args):
     def shift():
         R.recsa_shift_penalty(tree, pool, L, pen, sws)
 
+    # pooler backward of every level: a seeded key gradient (standing in for
+    # the KL's) plus the shift penalty with weight 1
+    levels = range(1, tree.n_levels)
+    dKs = {lv: synth.normal((B, Hkv, R.recsa_level_rows(L, 16, lv), d), dev, wl.seed, 20 + lv)
+           for lv in levels}
+    bws = {lv: torch.empty(R.recsa_pooler_backward_workspace_bytes(tree, pool, lv),
+                           dtype=torch.uint8, device=dev) for lv in levels}
+    grads = {lv: R.pooler_grad_buffers(pool) for lv in levels}
+
+    def backward():
+        for lv in levels:
+            R.recsa_pooler_backward(tree, pool, lv, L, dKs[lv], pen[lv - 1], 1.0, grads[lv],
+                                    bws[lv])
+
     ev = lambda: torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
-        select(); distill(); shift()
+        select(); distill(); shift(); backward()
     torch.cuda.synchronize()
-    evs = [tuple(ev() for _ in range(4)) for _ in range(args.steps)]
+    evs = [tuple(ev() for _ in range(5)) for _ in range(args.steps)]
     w0 = time.perf_counter()
-    for e0, e1, e2, e3 in evs:
+    for e0, e1, e2, e3, e4 in evs:
         e0.record(); select(); e1.record(); distill(); e2.record(); shift(); e3.record()
+        backward(); e4.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     med = lambda xs: sorted(xs)[len(xs) // 2]
-    sel_ms = med([a.elapsed_time(b) for a, b, _, _ in evs])
-    kl_ms = med([b.elapsed_time(c) for _, b, c, _ in evs])
-    sh_ms = med([c.elapsed_time(e) for _, _, c, e in evs])
-    step_ms = med([a.elapsed_time(e) for a, _, _, e in evs])
+    sel_ms = med([x[0].elapsed_time(x[1]) for x in evs])
+    kl_ms = med([x[1].elapsed_time(x[2]) for x in evs])
+    sh_ms = med([x[2].elapsed_time(x[3]) for x in evs])
+    bw_ms = med([x[3].elapsed_time(x[4]) for x in evs])
+    step_ms = med([x[0].elapsed_time(x[4]) for x in evs])
     pairs = sum(int(t) + 1 for t in range(T)) * B          # (query, key <= query) pairs
     flops = 2.0 * d * Hq * pairs
     tflops = flops / (kl_ms * 1e-3) / 1e12
     klv = kl.cpu().numpy()
     result = {
-        "metric": "RecSA pooler distillation step (Eq. 6 over every position + Eq. 7) "
-                  "at the 32K training length; ms per layer",
+        "metric": "RecSA pooler distillation step (Eq. 6 over every position + Eq. 7 + "
+                  "pooler backward of every level) at the 32K training length; ms per layer",
         "value": round(step_ms, 3), "unit": "ms/layer-step", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 3),
@@ -643,7 +660,7 @@ def bench_distill(args):
                                f"{wl.dtype}, L={L}, C=16, k={wl.k}; every position a query",
                    "seq_len": L, "global_batch": B},
         "split_ms": {"select_with_importance": round(sel_ms, 3), "distill_kl": round(kl_ms, 3),
-                     "shift_penalty": round(sh_ms, 3)},
+                     "shift_penalty": round(sh_ms, 3), "pooler_backward_all_levels": round(bw_ms, 3)},
         "queries_per_s": round(B * T / (step_ms * 1e-3), 1),
         "roofline": {"kernel": "recsa_distill_kl (absolute RoPE table + teacher_lse_kernel + "
                                "distill_kl_kernel), charged whole",

@@ -263,6 +263,47 @@ int recsa_shift_penalty(const recsa_tree* tree, const recsa_pooler* pooler,
                         int64_t tok_end, float* out, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* Gradients of the pooler parameters, float32 device arrays shaped like the
+ * fields of recsa_pooler (tau and g: one float each). */
+typedef struct recsa_pooler_grad {
+  float* w;    /* [d] */
+  float* W1;   /* [hidden][2d] */
+  float* b1;   /* [hidden] */
+  float* W2;   /* [d][hidden] */
+  float* tau;  /* [1] */
+  float* g;    /* [1] */
+} recsa_pooler_grad;
+
+/* Workspace bytes of recsa_pooler_backward at `level` (one row of
+ * 3d + 2*hidden floats per node slot, plus d+2 floats per 16 nodes).  0 on
+ * invalid arguments. */
+size_t recsa_pooler_backward_workspace_bytes(const recsa_tree* tree,
+                                             const recsa_pooler* pooler,
+                                             int32_t level);
+
+/* Pooler backward (picx.dev Pooler Distillation, Eq. 5; Training Stages,
+ * stage 1): gradients of
+ *     L = sum_i dK_i . K_i + shift_weight * penalty_level
+ * with respect to every pooler parameter, over the complete nodes i of
+ * `level` (>= 1) among the tokens [0, tok_end) of every sequence and KV
+ * head.  Each node's key K_i is recomputed in float32 from its stored
+ * children, which are inputs (no gradient flows into lower levels); the
+ * rounding of the stored key is taken as the identity.
+ * dK: [B][Hkv][recsa_level_rows(L_cap, C, level)][d] float32 device array
+ *   (rows of nodes beyond the range are not read), or NULL for zero.
+ * shift_sums: the level's row of recsa_shift_penalty output for the same
+ *   tok_end (sum of sigma*m [d], sum of ||mu||^2, penalty), or NULL for no
+ *   penalty term; its gradient reaches the parameters through m only.
+ * grad: overwritten (not accumulated); every element is a float64 sum in
+ *   node order, so repeated calls give identical bits.
+ * ws: recsa_pooler_backward_workspace_bytes bytes, overwritten.
+ * 0 < tok_end <= L_cap; 1 <= level < n_levels. */
+int recsa_pooler_backward(const recsa_tree* tree, const recsa_pooler* pooler,
+                          int32_t level, int64_t tok_end, const float* dK,
+                          const float* shift_sums, float shift_weight,
+                          const recsa_pooler_grad* grad, void* ws,
+                          size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librecsa.so")
-SOURCES = ["recsa_api.hip", "build.hip", "select_attn.hip", "decode_fused.hip", "distill.hip"]
+SOURCES = ["recsa_api.hip", "build.hip", "select_attn.hip", "decode_fused.hip", "distill.hip",
+           "pool_backward.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -232,4 +232,35 @@ int recsa_shift_penalty(const recsa_tree* tree, const recsa_pooler* pooler, int6
                                          static_cast<hipStream_t>(stream)));
 }
 
+// ---- pooler backward
+
+static bool grad_ok(const recsa_pooler_grad* g) {
+  return g && g->w && g->W1 && g->b1 && g->W2 && g->tau && g->g;
+}
+
+size_t recsa_pooler_backward_workspace_bytes(const recsa_tree* tree, const recsa_pooler* pooler,
+                                             int32_t level) {
+  int why;
+  if (!tree_ok(tree, &why) || !pooler_ok(pooler, tree) || !shift_fits(tree)) return 0;
+  if (level < 1 || level >= tree->n_levels) return 0;
+  return static_cast<size_t>(pool_bwd_ws_bytes(*tree, *pooler, level));
+}
+
+int recsa_pooler_backward(const recsa_tree* tree, const recsa_pooler* pooler, int32_t level,
+                          int64_t tok_end, const float* dK, const float* shift_sums,
+                          float shift_weight, const recsa_pooler_grad* grad, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!pooler_ok(pooler, tree) || !grad_ok(grad) || !ws) return RECSA_E_INVALID;
+  if (level < 1 || level >= tree->n_levels) return RECSA_E_INVALID;
+  if (tok_end < 1 || tok_end > tree->L_cap || !isfinite(shift_weight)) return RECSA_E_INVALID;
+  if (!shift_fits(tree)) return RECSA_E_UNSUPPORTED;
+  if (ws_bytes < static_cast<size_t>(pool_bwd_ws_bytes(*tree, *pooler, level)))
+    return RECSA_E_WORKSPACE;
+  return hip_status(launch_pool_backward(*tree, *pooler, level, tok_end, dK, shift_sums,
+                                         shift_weight, *grad, ws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

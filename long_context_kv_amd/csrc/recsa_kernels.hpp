@@ -116,6 +116,13 @@ int64_t shift_ws_bytes(const recsa_tree& tr);
 hipError_t launch_shift_penalty(const recsa_tree& tr, const recsa_pooler& P, int64_t tok_end,
                                 float* out, void* ws, hipStream_t s);
 
+// Pooler backward (Eq. 5 VJP)
+int64_t pool_bwd_ws_bytes(const recsa_tree& tr, const recsa_pooler& P, int level);
+hipError_t launch_pool_backward(const recsa_tree& tr, const recsa_pooler& P, int level,
+                                int64_t tok_end, const float* dK, const float* shift_sums,
+                                float shift_weight, const recsa_pooler_grad& G, void* ws,
+                                hipStream_t s);
+
 #define RECSA_DISPATCH(FN, ...)                                                     \
   do {                                                                              \
     const int G = Hq / tr.Hkv;                                                      \

@@ -32,6 +32,7 @@ EXPORTS = (
     "recsa_append_decode", "recsa_select", "recsa_attn_decode",
     "recsa_attn_prefill", "recsa_decode", "recsa_distill_workspace_bytes",
     "recsa_distill_kl", "recsa_shift_workspace_bytes", "recsa_shift_penalty",
+    "recsa_pooler_backward_workspace_bytes", "recsa_pooler_backward",
 )
 
 
@@ -61,6 +62,11 @@ class PoolerC(ctypes.Structure):
         ("w", ctypes.c_void_p), ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
         ("W2", ctypes.c_void_p),
     ]
+
+
+class PoolerGradC(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+                ("W2", ctypes.c_void_p), ("tau", ctypes.c_void_p), ("g", ctypes.c_void_p)]
 
 
 _lib = None
@@ -94,6 +100,9 @@ def lib():
                                                  ctypes.c_double, vp, vp, sz, vp]),
             "recsa_shift_workspace_bytes": (sz, [T]),
             "recsa_shift_penalty": (ctypes.c_int, [T, P, i64, vp, vp, sz, vp]),
+            "recsa_pooler_backward_workspace_bytes": (sz, [T, P, i32]),
+            "recsa_pooler_backward": (ctypes.c_int, [T, P, i32, i64, vp, vp, ctypes.c_float,
+                                                      ctypes.POINTER(PoolerGradC), vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -362,6 +371,32 @@ def recsa_shift_penalty(tree, pooler, tok_end: int, out, ws, ws_bytes: int | Non
     nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check("recsa_shift_penalty", lib().recsa_shift_penalty(
         ctypes.byref(tc), ctypes.byref(pc), tok_end, _ptr(out), _ptr(ws), nb, _stream(stream)))
+
+
+def recsa_pooler_backward_workspace_bytes(tree, pooler, level: int) -> int:
+    tc, pc = _tc(tree), _pc(pooler)
+    return int(lib().recsa_pooler_backward_workspace_bytes(ctypes.byref(tc), ctypes.byref(pc),
+                                                           level))
+
+
+def pooler_grad_buffers(pooler) -> dict:
+    """Zeroed float32 gradient arrays shaped like the pooler's parameters."""
+    dev = pooler.w.device
+    return {"w": torch.zeros_like(pooler.w), "W1": torch.zeros_like(pooler.W1),
+            "b1": torch.zeros_like(pooler.b1), "W2": torch.zeros_like(pooler.W2),
+            "tau": torch.zeros(1, dtype=torch.float32, device=dev),
+            "g": torch.zeros(1, dtype=torch.float32, device=dev)}
+
+
+def recsa_pooler_backward(tree, pooler, level: int, tok_end: int, dK, shift_sums,
+                          shift_weight: float, grad: dict, ws, ws_bytes: int | None = None,
+                          stream=None):
+    tc, pc = _tc(tree), _pc(pooler)
+    gc = PoolerGradC(*(grad[n].data_ptr() for n in ("w", "W1", "b1", "W2", "tau", "g")))
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("recsa_pooler_backward", lib().recsa_pooler_backward(
+        ctypes.byref(tc), ctypes.byref(pc), level, tok_end, _ptr(dK), _ptr(shift_sums),
+        float(shift_weight), ctypes.byref(gc), _ptr(ws), nb, _stream(stream)))
 
 
 def workspace(tree, Hq: int, n_queries: int):

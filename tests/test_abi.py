@@ -198,3 +198,34 @@ def test_distillation_calls_validate_without_launch():
         == R.RECSA_E_WORKSPACE
     assert L.recsa_shift_penalty(b(t), b(_pooler(d=64)), 4096, 0x10, 0x10, sw, None) \
         == R.RECSA_E_INVALID
+
+
+def test_pooler_backward_validates_without_launch():
+    L = R.lib()
+    b = ctypes.byref
+    t = _tree(k=64, L_cap=32768, n_levels=4)
+    p = _pooler()
+    need = L.recsa_pooler_backward_workspace_bytes(b(t), b(p), 1)
+    # one row of 3d + 2*hidden floats per node slot (16 per tile), then d+2
+    # floats per tile, 256-byte aligned
+    tiles = (2048 + 15) // 16 * 8
+    rows = tiles * 16 * (3 * 128 + 2 * 128) * 4
+    assert need == (rows + 255) // 256 * 256 + tiles * 130 * 4
+    assert L.recsa_pooler_backward_workspace_bytes(b(t), b(p), 0) == 0    # level >= 1
+    assert L.recsa_pooler_backward_workspace_bytes(b(t), b(p), 4) == 0    # level < n_levels
+    g = R.PoolerGradC(0x10, 0x10, 0x10, 0x10, 0x10, 0x10)
+    ok = [b(t), b(p), 1, 4096, 0x10, 0x10, 0.5, b(g), 0x10, need, None]
+    for i, bad in ((2, 0), (2, 4), (3, 0), (3, 32769), (8, None)):
+        a = list(ok)
+        a[i] = bad
+        assert L.recsa_pooler_backward(*a) == R.RECSA_E_INVALID, (i, bad)
+    a = list(ok)
+    a[6] = float("inf")
+    assert L.recsa_pooler_backward(*a) == R.RECSA_E_INVALID
+    a = list(ok)
+    a[9] = need - 1
+    assert L.recsa_pooler_backward(*a) == R.RECSA_E_WORKSPACE
+    g_missing = R.PoolerGradC(0x10, None, 0x10, 0x10, 0x10, 0x10)
+    a = list(ok)
+    a[7] = b(g_missing)
+    assert L.recsa_pooler_backward(*a) == R.RECSA_E_INVALID
