@@ -8,11 +8,11 @@
 //
 // The teacher is computed in two launches:
 //   teacher_lse_kernel  one pass over the keys of a block of queries with
-//                       float32 matrix-core products (v_mfma_f32_16x16x4_f32);
-//                       a 16x16 output tile is 16 (query, head) rows against
-//                       one level-1 group of 16 tokens, so each tile reduces to
-//                       the group's log-sum-exp per row, which does not depend
-//                       on the row's global maximum: no second pass.
+//                       split-bf16 matrix-core products (float32-level
+//                       accuracy); a 16x16 output tile is one level-1 group of
+//                       16 tokens against 16 (query, head) rows, so each tile
+//                       reduces to the group's log-sum-exp per row, which does
+//                       not depend on the row's global maximum: no second pass.
 //   distill_kl_kernel   per (query, KV head): the softmax normaliser from the
 //                       group log-sum-exps, the head-mean mass of every level-1
 //                       group, the candidates' subtree masses at each scored
@@ -25,33 +25,15 @@
 
 #include "recsa_common.hpp"
 #include "recsa_kernels.hpp"
+#include "recsa_mfma.hpp"
 #include "recsa_pool.hpp"
 
 namespace recsa {
 
 namespace {
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kTeacherRows = 64;   // (query, head) rows per teacher workgroup
 constexpr int kTeacherKeys = 64;   // keys per tile: four level-1 groups
-
-// Sum over each 16-lane row of the wave (DPP row operations; the result in
-// every lane of the row).
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_movf<dpp::kXor1>(0.f, v);
-  v += dpp_movf<dpp::kXor2>(0.f, v);
-  v += dpp_movf<dpp::kRor4>(0.f, v);
-  v += dpp_movf<dpp::kRor8>(0.f, v);
-  return v;
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_movf<dpp::kXor1>(v, v));
-  v = fmaxf(v, dpp_movf<dpp::kXor2>(v, v));
-  v = fmaxf(v, dpp_movf<dpp::kRor4>(v, v));
-  v = fmaxf(v, dpp_movf<dpp::kRor8>(v, v));
-  return v;
-}
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
@@ -80,15 +62,58 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 // ------------------------------------------------------------ teacher
 // Workgroup: 64/G consecutive queries of one (sequence, KV head), i.e. 64
-// rows r = G*(query - first) + h.  Wave w owns rows [16w, 16w + 16) as the A
-// operand (rotated queries, float32, in registers for the whole pass).  Each
-// tile of 64 keys is rotated at its absolute positions into LDS; per level-1
-// group g of the tile, one chain of D/4 MFMAs gives the 16x16 logits, whose
-// rows reduce over the 16 key lanes to the group's log-sum-exp.
-// The k index of the A/B operands is permuted consistently (lane group h
-// supplies dims [h*D/4, (h+1)*D/4)), which only reorders the dot product.
+// rows r = G*(query - first) + h; wave w owns rows [16w, 16w + 16).
+// Logits on the bf16 matrix cores at float32-level accuracy: every rotated
+// float32 operand x is split into x_hi = rnd(x) and x_lo = rnd(x - x_hi)
+// (bf16; |x - x_hi - x_lo| <= 2^-18 |x|), and each 32-dim block takes the
+// products lo.hi + hi.lo + hi.hi; the dropped lo.lo term and the split
+// residuals stay below 4 * 2^-18 of each product (float32 accumulation of
+// d = 128 products carries a similar bound).  v_mfma_f32_16x16x32_bf16 runs
+// with the keys as the A operand and the wave's 16 query rows as B, so one
+// 16 x 16 tile is one level-1 group (rows) against 16 query rows (columns)
+// and lane l holds 4 keys of column l % 16: a row's log-sum-exp over the
+// group reduces 4 registers and the 4 lanes l % 16 + 16 i.  The group's
+// log-sum-exp does not depend on the row's global maximum: one pass.
+// Each tile of 64 keys is rotated at its absolute positions and split once,
+// into LDS, by all 256 threads (16-byte loads of 8 consecutive dims).
 // lse: [B*T][Hkv][ng_cap][G] float32; entry (v, h) is written for every
 // level-1 group v <= t/16 of the row's query, never beyond.
+__device__ __forceinline__ void split_bf16x8(const float* v, uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t a = f32_to_bf16_bits(v[2 * i]), b = f32_to_bf16_bits(v[2 * i + 1]);
+    const float ar = v[2 * i] - bf16_bits_to_f32(a);          // exact in float32
+    const float br = v[2 * i + 1] - bf16_bits_to_f32(b);
+    h[i] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+    l[i] = static_cast<uint32_t>(f32_to_bf16_bits(ar)) |
+           (static_cast<uint32_t>(f32_to_bf16_bits(br)) << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Pairs (j, j + D/2), j in [j0, j0 + 8), of one storage row rotated by the
+// absolute table row `rrow`: outputs xo (dims j) and yo (dims j + D/2).
+template <int DT, int D>
+__device__ __forceinline__ void rotate8_abs(const typename Stor<DT>::T* row, int j0,
+                                            const float* __restrict__ rrow, float* xo, float* yo) {
+  float x[8], y[8];
+  load_vec<DT, 8>(row + j0, x);
+  load_vec<DT, 8>(row + D / 2 + j0, y);
+  float cs[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(rrow + 2 * j0 + 4 * i);
+    cs[4 * i] = v.x;
+    cs[4 * i + 1] = v.y;
+    cs[4 * i + 2] = v.z;
+    cs[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rope_pair(x[e], y[e], cs[2 * e], cs[2 * e + 1], xo[e], yo[e]);
+}
+
 template <int DT, int D, int G>
 __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, const void* qv,
                                                              int T, const int64_t* __restrict__ pos,
@@ -97,9 +122,11 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
   using Ty = typename Stor<DT>::T;
   constexpr int QB = kTeacherRows / G;
   constexpr int H2 = D / 2;
-  constexpr int LD = D + 4;            // padded row, 16-byte aligned
-  constexpr int KB = D / 4;            // MFMA steps per logit tile
-  __shared__ __attribute__((aligned(16))) float sbuf[kTeacherKeys][LD];   // queries, then keys
+  constexpr int KB = D / 32;             // 32-dim blocks
+  constexpr int LDK = D + 8;             // bf16 elements per LDS key row (16-byte aligned)
+  constexpr int PQ = H2 / 4;             // rotation pairs per thread per key
+  __shared__ __attribute__((aligned(16))) uint16_t khi[kTeacherKeys][LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t klo[kTeacherKeys][LDK];
   __shared__ int st[kTeacherRows];
   __shared__ int s_tmax;
   const int j = blockIdx.y, b = blockIdx.z;
@@ -107,6 +134,7 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
   const int q0 = (gridDim.x - 1 - blockIdx.x) * QB;
   const int Hq = tr.Hkv * G;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
+  const int col = lane & 15, hh = lane >> 4;
 
   if (tid < kTeacherRows) {
     const int qi = q0 + tid / G;
@@ -117,92 +145,106 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
     const float m = wave_max(static_cast<float>(st[lane]));
     if (lane == 0) s_tmax = static_cast<int>(m);
   }
-  // rotated queries R(t) q, float32 (no fused multiply-add)
-  for (int item = tid; item < kTeacherRows * H2; item += kBlock) {
-    const int r = item / H2, jj = item % H2;
-    const int t = st[r];
-    float xo = 0.f, yo = 0.f;
-    if (t >= 0) {
-      const int qi = q0 + r / G, h = r % G;
-      const Ty* qr =
-          static_cast<const Ty*>(qv) + ((static_cast<int64_t>(b) * T + qi) * Hq + j * G + h) * D;
-      const float* rp = arope + (static_cast<int64_t>(t) * H2 + jj) * 2;
-      rope_pair(Stor<DT>::load(qr + jj), Stor<DT>::load(qr + jj + H2), rp[0], rp[1], xo, yo);
+  // B operand: this wave's 16 query rows R(t) q, split; lane holds column
+  // `col`, dims 32 kb + 8 hh + [0, 8) (both members of each RoPE pair)
+  const int r_col = 16 * wid + col;
+  const int t_col = st[r_col];
+  uint4 bhi[KB], blo[KB];
+  {
+    const int qi = min(q0 + r_col / G, T - 1), h = r_col % G;
+    const Ty* qr =
+        static_cast<const Ty*>(qv) + ((static_cast<int64_t>(b) * T + qi) * Hq + j * G + h) * D;
+#pragma unroll
+    for (int kb = 0; kb < KB / 2; ++kb) {
+      float xo[8], yo[8];
+      if (t_col >= 0) {
+        rotate8_abs<DT, D>(qr, 32 * kb + 8 * hh, arope + static_cast<int64_t>(t_col) * H2 * 2,
+                           xo, yo);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xo[e] = yo[e] = 0.f;
+      }
+      split_bf16x8(xo, bhi[kb], blo[kb]);
+      split_bf16x8(yo, bhi[kb + KB / 2], blo[kb + KB / 2]);
     }
-    sbuf[r][jj] = xo;
-    sbuf[r][jj + H2] = yo;
   }
   __syncthreads();
   const int tmax = s_tmax;
   if (tmax < 0) return;   // no query in this block (uniform)
-
-  float af[KB];
+  float* lcol;
   {
-    const float* src = &sbuf[16 * wid + (lane & 15)][(lane >> 4) * KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; kb += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(src + kb);
-      af[kb] = v.x;
-      af[kb + 1] = v.y;
-      af[kb + 2] = v.z;
-      af[kb + 3] = v.w;
-    }
-  }
-  int trow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) trow[i] = st[16 * wid + 4 * (lane >> 4) + i];
-  float* lrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * wid + 4 * (lane >> 4) + i;
-    const int qi = min(q0 + r / G, T - 1);
-    lrow[i] = lse + ((static_cast<int64_t>(b) * T + qi) * tr.Hkv + j) * ng_cap * G + (r % G);
+    const int qi = min(q0 + r_col / G, T - 1);
+    lcol = lse + ((static_cast<int64_t>(b) * T + qi) * tr.Hkv + j) * ng_cap * G + (r_col % G);
   }
   const Ty* k0 = static_cast<const Ty*>(tr.K[0]) +
                  (static_cast<int64_t>(b) * tr.Hkv + j) * tr.L_cap * D;
   const float scale = static_cast<float>(1.0 / sqrt(static_cast<double>(D)));
+  const int kk = tid >> 2, qq = tid & 3;     // the key row and pair quarter this thread rotates
 
   const int n_tiles = tmax / kTeacherKeys + 1;
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int tau0 = tile * kTeacherKeys;
-    __syncthreads();   // the previous tile (or the query fragments) is read
-    for (int item = tid; item < kTeacherKeys * H2; item += kBlock) {
-      const int kk = item / H2, jj = item % H2;
+    __syncthreads();   // the previous tile is read
+    {
       const int tau = tau0 + kk;
-      float xo = 0.f, yo = 0.f;
-      if (tau <= tmax) {
-        const Ty* kr = k0 + static_cast<int64_t>(tau) * D;
-        const float* rp = arope + (static_cast<int64_t>(tau) * H2 + jj) * 2;
-        rope_pair(Stor<DT>::load(kr + jj), Stor<DT>::load(kr + jj + H2), rp[0], rp[1], xo, yo);
+#pragma unroll
+      for (int c = 0; c < PQ / 8; ++c) {
+        const int j0 = qq * PQ + 8 * c;
+        float xo[8], yo[8];
+        if (tau <= tmax) {
+          rotate8_abs<DT, D>(k0 + static_cast<int64_t>(tau) * D, j0,
+                             arope + static_cast<int64_t>(tau) * H2 * 2, xo, yo);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xo[e] = yo[e] = 0.f;
+        }
+        uint4 xh, xl, yh, yl;
+        split_bf16x8(xo, xh, xl);
+        split_bf16x8(yo, yh, yl);
+        *reinterpret_cast<uint4*>(&khi[kk][j0]) = xh;
+        *reinterpret_cast<uint4*>(&klo[kk][j0]) = xl;
+        *reinterpret_cast<uint4*>(&khi[kk][H2 + j0]) = yh;
+        *reinterpret_cast<uint4*>(&klo[kk][H2 + j0]) = yl;
       }
-      sbuf[kk][jj] = xo;
-      sbuf[kk][jj + H2] = yo;
     }
     __syncthreads();
 #pragma unroll
     for (int g = 0; g < kTeacherKeys / kC; ++g) {
       const int tg = tau0 + kC * g;   // first token of the level-1 group
       if (tg > tmax) break;           // uniform
-      const float* src = &sbuf[kC * g + (lane & 15)][(lane >> 4) * KB];
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; kb += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + kb);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kb], v.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kb + 1], v.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kb + 2], v.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[kb + 3], v.w, acc, 0, 0, 0);
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint4 ah = *reinterpret_cast<const uint4*>(&khi[kC * g + col][32 * kb + 8 * hh]);
+        const uint4 al = *reinterpret_cast<const uint4*>(&klo[kC * g + col][32 * kb + 8 * hh]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                      __builtin_bit_cast(bf16x8_t, bhi[kb]), acc,
+                                                      0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                      __builtin_bit_cast(bf16x8_t, blo[kb]), acc,
+                                                      0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                      __builtin_bit_cast(bf16x8_t, bhi[kb]), acc,
+                                                      0, 0, 0);
       }
-      const int tau = tg + (lane & 15);
-      const int64_t v = tg >> 4;
+      // keys tg + 4 hh + i against the query of column `col`
+      float sv[4];
+      float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float s = tau <= trow[i] ? acc[i] * scale : -INFINITY;
-        const float m = row16_max(s);
-        const float e = m == -INFINITY ? 0.f : expf(s - m);
-        const float sum = row16_sum(e);
-        if ((lane & 15) == 0 && m != -INFINITY) lrow[i][v * G] = m + logf(sum);
+        sv[i] = tg + 4 * hh + i <= t_col ? acc[i] * scale : -INFINITY;
+        m = fmaxf(m, sv[i]);
       }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      float e = 0.f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e += expf(sv[i] - m);
+      }
+      e += __shfl_xor(e, 16);
+      e += __shfl_xor(e, 32);
+      if (hh == 0 && m != -INFINITY) lcol[static_cast<int64_t>(tg >> 4) * G] = m + logf(e);
     }
   }
 }
