@@ -238,7 +238,7 @@ size_t recsa_distill_workspace_bytes(const recsa_tree* tree, int32_t Hq,
  * teacher mass gives +inf.  Arithmetic is float32 (teacher logits on the
  * float32 matrix cores).  ws: recsa_distill_workspace_bytes(tree, Hq, B*T)
  * bytes of device memory, overwritten.  RECSA_E_UNSUPPORTED when
- * ceil(L_cap/16) + C*k exceeds 16376 (the masses of one query are kept on
+ * ceil(L_cap/16) + C*k exceeds 16352 (the masses of one query are kept on
  * chip). */
 int recsa_distill_kl(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
                      const int64_t* pos_dev, const int32_t* sel_idx,
@@ -274,8 +274,9 @@ typedef struct recsa_pooler_grad {
   float* g;    /* [1] */
 } recsa_pooler_grad;
 
-/* Workspace bytes of recsa_pooler_backward at `level` (one row of
- * 3d + 2*hidden floats per node slot, plus d+2 floats per 16 nodes).  0 on
+/* Workspace bytes of recsa_pooler_backward at `level`: one row of
+ * 3d + 2*hidden floats per node slot, d+2 floats per 16 nodes, and one
+ * float64 partial of every gradient element per 512 node slots.  0 on
  * invalid arguments. */
 size_t recsa_pooler_backward_workspace_bytes(const recsa_tree* tree,
                                              const recsa_pooler* pooler,

@@ -35,6 +35,24 @@ namespace {
 constexpr int kTeacherRows = 64;   // (query, head) rows per teacher workgroup
 constexpr int kTeacherKeys = 64;   // keys per tile: four level-1 groups
 
+// The G log-sum-exps of one level-1 group (consecutive floats).
+template <int G>
+__device__ __forceinline__ void load_group(const float* p, float* x) {
+  if constexpr (G == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x;
+    x[1] = v.y;
+    x[2] = v.z;
+    x[3] = v.w;
+  } else if constexpr (G == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    x[0] = v.x;
+    x[1] = v.y;
+  } else {
+    x[0] = *p;
+  }
+}
+
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
   v = wave_sum(v);
@@ -46,18 +64,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   for (int w = 0; w < kBlock / kWave; ++w) s += red[w];
   return s;
 }
-__device__ __forceinline__ float block_max(float v, float* red) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-  v = wave_max(v);
-  __syncthreads();
-  if (lane == 0) red[wid] = v;
-  __syncthreads();
-  float m = red[0];
-#pragma unroll
-  for (int w = 1; w < kBlock / kWave; ++w) m = fmaxf(m, red[w]);
-  return m;
-}
-
 }  // namespace
 
 // ------------------------------------------------------------ teacher
@@ -251,7 +257,7 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
 
 // ------------------------------------------------------------ Eq. 6 terms
 // One workgroup per (query, KV head).  Dynamic LDS: m1[ng_cap] (head-mean
-// teacher mass of each level-1 group), mass[C*k], red[8].
+// teacher mass of each level-1 group), mass[C*k], red[32].
 template <int G>
 __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
     recsa_tree tr, int T, const int64_t* __restrict__ pos, const int32_t* __restrict__ sel,
@@ -269,21 +275,61 @@ __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
   float* mass = dsm + ng_cap;
   float* red = mass + CK;
 
-  // softmax normaliser of each head: log Z_h = logsumexp over the groups
-  float lz[G];
+  // softmax normaliser of each head, log Z_h = logsumexp over the groups:
+  // one pass of G-wide loads with a running (max, sum) per head, then one
+  // block exchange for all heads
+  float mx[G], sx[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float mx = -INFINITY;
-    for (int v = tid; v < ng; v += kBlock) mx = fmaxf(mx, L[static_cast<int64_t>(v) * G + h]);
-    mx = block_max(mx, red);
-    float s = 0.f;
-    for (int v = tid; v < ng; v += kBlock) s += expf(L[static_cast<int64_t>(v) * G + h] - mx);
-    lz[h] = mx + logf(block_sum(s, red));
+    mx[h] = -INFINITY;
+    sx[h] = 0.f;
   }
   for (int v = tid; v < ng; v += kBlock) {
+    float x[G];
+    load_group<G>(L + static_cast<int64_t>(v) * G, x);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (x[h] > mx[h]) {
+        sx[h] = sx[h] * expf(mx[h] - x[h]) + 1.0f;   // exp(-inf) = 0 on the first value
+        mx[h] = x[h];
+      } else {
+        sx[h] += expf(x[h] - mx[h]);
+      }
+    }
+  }
+  float lz[G];
+  {
+    const int lane = tid & (kWave - 1), wid = tid >> 6;
+    float* rm = red;               // [G][4] wave maxima, then [G][4] wave sums
+    float* rs = red + 4 * G;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float wm = wave_max(mx[h]);
+      const float ws = wave_sum(mx[h] == -INFINITY ? 0.f : sx[h] * expf(mx[h] - wm));
+      if (lane == 0) {
+        rm[4 * h + wid] = wm;
+        rs[4 * h + wid] = ws;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float m = rm[4 * h];
+#pragma unroll
+      for (int w = 1; w < kBlock / kWave; ++w) m = fmaxf(m, rm[4 * h + w]);
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kBlock / kWave; ++w)
+        sum += rm[4 * h + w] == -INFINITY ? 0.f : rs[4 * h + w] * expf(rm[4 * h + w] - m);
+      lz[h] = m + logf(sum);
+    }
+  }
+  for (int v = tid; v < ng; v += kBlock) {
+    float x[G];
+    load_group<G>(L + static_cast<int64_t>(v) * G, x);
     float s = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) s += expf(L[static_cast<int64_t>(v) * G + h] - lz[h]);
+    for (int h = 0; h < G; ++h) s += expf(x[h] - lz[h]);
     m1[v] = s * (1.0f / G);
   }
   __syncthreads();
@@ -417,7 +463,7 @@ static hipError_t distill_impl(const recsa_tree& tr, const void* q, int Hq, int 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(static_cast<unsigned>(T), tr.Hkv, tr.B);
-  const size_t lds = (static_cast<size_t>(ng_cap) + kC * tr.k + 8) * sizeof(float);
+  const size_t lds = (static_cast<size_t>(ng_cap) + kC * tr.k + 32) * sizeof(float);
   distill_kl_kernel<G><<<g2, kBlock, lds, s>>>(tr, T, pos, sel, cnt, imp, lse, ng_cap, kl);
   return hipGetLastError();
 }

@@ -15,9 +15,9 @@
 //   head) recomputes the forward parts and writes, per node, the rows the
 //   weight gradients contract over (feat, dm, dz, SiLU(z)), and per tile the
 //   sums of the w, tau and g gradients.
-// pool_bwd_reduce_kernel: each output element sums its node rows (or tile
-//   partials) in node order in float64: fixed order, identical bits on every
-//   call.
+// pool_bwd_chunk_kernel + pool_bwd_reduce_kernel: each output element sums
+//   its node rows (or tile partials) in chunks of 512 rows, then the chunks,
+//   in float64 and in a fixed order: identical bits on every call.
 #include <algorithm>
 
 #include "recsa_common.hpp"
@@ -325,47 +325,78 @@ __global__ void __launch_bounds__(kBlock) pool_bwd_tile_kernel(
 }
 
 // Output element e of [dW1 (H x 2D) | dW2 (D x H) | db1 (H) | dw (D) | dtau | dg].
+// Stage 1: workgroup (x, c) sums node rows [c*kBwdChunk, (c+1)*kBwdChunk)
+// (and their tiles' partials) for 256 output elements, in float64, into
+// acc[c][e].  Stage 2: each element sums its chunks in order.  Both orders
+// are fixed: identical bits on every call.
+constexpr int kBwdChunk = 512;            // node rows per stage-1 workgroup (32 tiles)
+
+__host__ __device__ inline int64_t bwd_outputs(int D, int H) {
+  return static_cast<int64_t>(H) * 3 * D + H + D + 2;
+}
+
 template <int D>
-__global__ void __launch_bounds__(kBlock) pool_bwd_reduce_kernel(
-    const float* __restrict__ rows, const float* __restrict__ part, int64_t n_rows,
-    int64_t n_parts, int H, recsa_pooler_grad G) {
+__global__ void __launch_bounds__(kBlock) pool_bwd_chunk_kernel(
+    const float* __restrict__ rows, const float* __restrict__ part, int64_t n_rows, int H,
+    double* __restrict__ acc_out) {
   const int64_t RF = bwd_row_floats(D, H);
   const int64_t n_w1 = static_cast<int64_t>(H) * 2 * D, n_w2 = static_cast<int64_t>(D) * H;
-  const int64_t total = n_w1 + n_w2 + H + D + 2;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * kBlock) {
-    double acc = 0.0;
-    if (e < n_w1) {                                   // dW1[i][k] = sum dz_i feat_k
-      const int i = static_cast<int>(e / (2 * D)), k = static_cast<int>(e % (2 * D));
-      for (int64_t r = 0; r < n_rows; ++r)
-        acc += static_cast<double>(rows[r * RF + 3 * D + i]) * rows[r * RF + k];
-      G.W1[e] = static_cast<float>(acc);
-    } else if (e < n_w1 + n_w2) {                     // dW2[jj][i] = sum dm_jj SiLU(z)_i
-      const int64_t f = e - n_w1;
-      const int jj = static_cast<int>(f / H), i = static_cast<int>(f % H);
-      for (int64_t r = 0; r < n_rows; ++r)
-        acc += static_cast<double>(rows[r * RF + 2 * D + jj]) * rows[r * RF + 3 * D + H + i];
-      G.W2[f] = static_cast<float>(acc);
-    } else if (e < n_w1 + n_w2 + H) {                 // db1[i] = sum dz_i
-      const int i = static_cast<int>(e - n_w1 - n_w2);
-      for (int64_t r = 0; r < n_rows; ++r) acc += rows[r * RF + 3 * D + i];
-      G.b1[i] = static_cast<float>(acc);
-    } else {                                          // dw, dtau, dg from the tile sums
-      const int c = static_cast<int>(e - n_w1 - n_w2 - H);
-      for (int64_t r = 0; r < n_parts; ++r) acc += part[r * (D + 2) + c];
-      if (c < D)
-        G.w[c] = static_cast<float>(acc);
-      else if (c == D)
-        G.tau[0] = static_cast<float>(acc);
-      else
-        G.g[0] = static_cast<float>(acc);
-    }
+  const int64_t total = bwd_outputs(D, H);
+  const int64_t e = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kBwdChunk;
+  const int64_t r1 = min(r0 + kBwdChunk, n_rows);
+  if (e >= total) return;
+  double acc = 0.0;
+  if (e < n_w1) {                                   // dW1[i][k] = sum dz_i feat_k
+    const int i = static_cast<int>(e / (2 * D)), k = static_cast<int>(e % (2 * D));
+    for (int64_t r = r0; r < r1; ++r)
+      acc += static_cast<double>(rows[r * RF + 3 * D + i]) * rows[r * RF + k];
+  } else if (e < n_w1 + n_w2) {                     // dW2[jj][i] = sum dm_jj SiLU(z)_i
+    const int64_t f = e - n_w1;
+    const int jj = static_cast<int>(f / H), i = static_cast<int>(f % H);
+    for (int64_t r = r0; r < r1; ++r)
+      acc += static_cast<double>(rows[r * RF + 2 * D + jj]) * rows[r * RF + 3 * D + H + i];
+  } else if (e < n_w1 + n_w2 + H) {                 // db1[i] = sum dz_i
+    const int i = static_cast<int>(e - n_w1 - n_w2);
+    for (int64_t r = r0; r < r1; ++r) acc += rows[r * RF + 3 * D + i];
+  } else {                                          // dw, dtau, dg from the tile sums
+    const int c = static_cast<int>(e - n_w1 - n_w2 - H);
+    for (int64_t t = r0 / kBwdNodes; t < r1 / kBwdNodes; ++t) acc += part[t * (D + 2) + c];
+  }
+  acc_out[static_cast<int64_t>(blockIdx.y) * total + e] = acc;
+}
+
+template <int D>
+__global__ void __launch_bounds__(kBlock) pool_bwd_reduce_kernel(const double* __restrict__ acc_in,
+                                                                 int n_chunks, int H,
+                                                                 recsa_pooler_grad G) {
+  const int64_t n_w1 = static_cast<int64_t>(H) * 2 * D, n_w2 = static_cast<int64_t>(D) * H;
+  const int64_t total = bwd_outputs(D, H);
+  const int64_t e = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x;
+  if (e >= total) return;
+  double acc = 0.0;
+  for (int c = 0; c < n_chunks; ++c) acc += acc_in[static_cast<int64_t>(c) * total + e];
+  const float v = static_cast<float>(acc);
+  if (e < n_w1) {
+    G.W1[e] = v;
+  } else if (e < n_w1 + n_w2) {
+    G.W2[e - n_w1] = v;
+  } else if (e < n_w1 + n_w2 + H) {
+    G.b1[e - n_w1 - n_w2] = v;
+  } else {
+    const int c = static_cast<int>(e - n_w1 - n_w2 - H);
+    if (c < D)
+      G.w[c] = v;
+    else if (c == D)
+      G.tau[0] = v;
+    else
+      G.g[0] = v;
   }
 }
 
 // ------------------------------------------------------------ launchers
 struct BwdLayout {
-  int64_t tiles, n_rows, n_parts, rows_off, part_off, total;
+  int64_t tiles, n_rows, n_parts, n_chunks, rows_off, part_off, acc_off, total;
 };
 
 static BwdLayout bwd_layout(const recsa_tree& tr, int H, int level, int64_t n_nodes) {
@@ -374,9 +405,11 @@ static BwdLayout bwd_layout(const recsa_tree& tr, int H, int level, int64_t n_no
   L.tiles = (n_nodes + kBwdNodes - 1) / kBwdNodes;
   L.n_rows = L.tiles * kBwdNodes * heads;
   L.n_parts = L.tiles * heads;
+  L.n_chunks = (L.n_rows + kBwdChunk - 1) / kBwdChunk;
   L.rows_off = 0;
   L.part_off = align256(L.n_rows * bwd_row_floats(tr.d, H) * 4);
-  L.total = L.part_off + L.n_parts * (tr.d + 2) * 4;
+  L.acc_off = align256(L.part_off + L.n_parts * (tr.d + 2) * 4);
+  L.total = L.acc_off + std::max<int64_t>(L.n_chunks, 1) * bwd_outputs(tr.d, H) * 8;
   (void)level;
   return L;
 }
@@ -404,10 +437,15 @@ static hipError_t pool_bwd_impl(const recsa_tree& tr, const recsa_pooler& P, int
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t total = static_cast<int64_t>(P.hidden) * 3 * D + P.hidden + D + 2;
-  const int grid2 = static_cast<int>(std::min<int64_t>((total + kBlock - 1) / kBlock, 1024));
-  pool_bwd_reduce_kernel<D><<<grid2, kBlock, 0, s>>>(rows, part, n > 0 ? L.n_rows : 0,
-                                                     n > 0 ? L.n_parts : 0, P.hidden, G);
+  double* acc = reinterpret_cast<double*>(static_cast<char*>(ws) + L.acc_off);
+  const int64_t total = bwd_outputs(D, P.hidden);
+  const unsigned gx = static_cast<unsigned>((total + kBlock - 1) / kBlock);
+  const int n_chunks = n > 0 ? static_cast<int>(L.n_chunks) : 1;
+  pool_bwd_chunk_kernel<D><<<dim3(gx, n_chunks), kBlock, 0, s>>>(rows, part, n > 0 ? L.n_rows : 0,
+                                                                 P.hidden, acc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  pool_bwd_reduce_kernel<D><<<gx, kBlock, 0, s>>>(acc, n_chunks, P.hidden, G);
   return hipGetLastError();
 }
 

@@ -181,7 +181,7 @@ int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler, const void*
 // ---- pooler distillation losses
 
 static bool distill_fits(const recsa_tree* t) {
-  return distill_groups(t->L_cap) + static_cast<int64_t>(t->C) * t->k + 8 <= 16384;
+  return distill_groups(t->L_cap) + static_cast<int64_t>(t->C) * t->k + 32 <= 16384;
 }
 
 size_t recsa_distill_workspace_bytes(const recsa_tree* tree, int32_t Hq, int64_t n_queries) {

@@ -207,10 +207,13 @@ def test_pooler_backward_validates_without_launch():
     p = _pooler()
     need = L.recsa_pooler_backward_workspace_bytes(b(t), b(p), 1)
     # one row of 3d + 2*hidden floats per node slot (16 per tile), then d+2
-    # floats per tile, 256-byte aligned
+    # floats per tile, then one float64 partial of every gradient element per
+    # 512 node slots, each region 256-byte aligned
+    al = lambda x: (x + 255) // 256 * 256
     tiles = (2048 + 15) // 16 * 8
     rows = tiles * 16 * (3 * 128 + 2 * 128) * 4
-    assert need == (rows + 255) // 256 * 256 + tiles * 130 * 4
+    outputs = 128 * 3 * 128 + 128 + 128 + 2
+    assert need == al(rows) + al(tiles * 130 * 4) + (tiles * 16 // 512) * outputs * 8
     assert L.recsa_pooler_backward_workspace_bytes(b(t), b(p), 0) == 0    # level >= 1
     assert L.recsa_pooler_backward_workspace_bytes(b(t), b(p), 4) == 0    # level < n_levels
     g = R.PoolerGradC(0x10, 0x10, 0x10, 0x10, 0x10, 0x10)
