@@ -148,3 +148,54 @@ def test_2m_layer_decode_and_prefill_sampled_vs_oracle():
                           out_pre.cpu().numpy().astype(np.float64)[:, idx], [6],
                           1e-5, 2e-3, trees=trees, max_swaps=1)
     assert rep2.matched >= len(idx) - 1
+
+
+def test_distill_32k_bench_configuration_sampled_vs_oracle():
+    """The distillation workload exactly as `bench.py --distill` runs it: a
+    32768-token tree at k = 64, every position a query (selection with
+    importances, Eq. 6 terms), the Eq. 7 penalty over every node, and the
+    pooler backward of levels 1 and 2 with the benchmark's seeded key
+    gradients; sampled queries and heads against the oracle, the penalty and
+    the gradients over all heads, to the small tests' bars."""
+    _need_gpu()
+    import bench
+    from oracle import recsa_oracle as O
+    from tests import parity as PY
+    from tests import test_gpu_distill as TD
+    from tests import test_gpu_pool_backward as TB
+    wl = synth.WORKLOADS["distill_32k"]
+    L, B, Hkv, Hq, d = wl.L, wl.B, wl.Hkv, wl.Hq, wl.d
+    K0, V0 = synth.kv_rows(wl, DEV, n_rows=L)
+    pdict = synth.pooler_params(d, d, DEV, wl.seed)
+    pool = R.Pooler.from_dict(pdict, DEV)
+    tree = R.Tree.allocate(B, Hkv, d, L, k=wl.k, dtype=wl.dtype, device=DEV, level0=(K0, V0),
+                           theta=wl.theta)
+    R.recsa_build_tree(tree, pool, 0, L)
+    q = synth.to_storage(synth.normal((B, L, Hq, d), DEV, wl.seed, bench.ROLE_DISTILL_Q),
+                         wl.dtype)
+    pos = torch.arange(L, device=DEV).view(1, L).contiguous()
+    sel, cnt, imp, kl = TD.run_distill(tree, q, Hq, pos)
+    assert np.all(np.isfinite(kl)) and np.all(kl >= -1e-6)
+    idx = [1023, 1024, 16383, L - 1]
+    print(f"distill 32K: queries {idx} on KV heads 0, 5", flush=True)
+    for j in (0, 5):
+        n_pairs, n_lv, worst = TD.check_kl(tree, pdict, q[:, idx], pos[:, idx].cpu(), sel[:, idx],
+                                           cnt[:, idx], imp[:, idx], kl[:, idx], [j])
+        assert n_pairs >= len(idx) - 1 and n_lv >= 2, (j, n_pairs, n_lv)
+    # Eq. 7 over every node of every head, and the backward of levels 1, 2
+    print("distill 32K: shift penalty and pooler backward, all heads", flush=True)
+    sws = torch.empty(R.recsa_shift_workspace_bytes(tree), dtype=torch.uint8, device=DEV)
+    pen = torch.zeros((tree.n_levels - 1, d + 2), dtype=torch.float32, device=DEV)
+    R.recsa_shift_penalty(tree, pool, L, pen, sws)
+    torch.cuda.synchronize()
+    g = pen.cpu().numpy().astype(np.float64)
+    ref = TD._shift_oracle(tree, pdict, L)
+    for lvl, (s, mu2, p) in ref.items():
+        assert np.max(np.abs(g[lvl - 1, :d] - s)) <= 1e-4 * np.max(np.abs(s)), lvl
+        assert abs(g[lvl - 1, d] - mu2) <= 1e-5 * mu2, lvl
+        assert abs(g[lvl - 1, d + 1] - p) <= 1e-4 * p, lvl
+    for lv in (2, 1):
+        dK = synth.normal((B, Hkv, R.recsa_level_rows(L, 16, lv), d), DEV, wl.seed, 20 + lv)
+        gg = TB.gpu_backward(tree, pool, lv, L, dK, 1.0)
+        TB.compare(gg, TB.oracle_backward(tree, pdict, lv, L, dK, 1.0),
+                   1e-3 if lv > 1 else 1e-4)

@@ -122,3 +122,43 @@ def test_offloaded_level0_fp32_small():
     r_host = TP._run_select_attn(host, q, 4, pos, decode=False)
     for a, b in zip(r_dev, r_host):
         assert np.array_equal(a, b)
+
+
+def test_offloaded_level0_524k_bench_shape_matches_device_resident():
+    """The 524K workload shape as `bench.py --offload` runs it (8 KV heads,
+    32 query heads, d = 128, k = 256, 4 levels): full build, a 256-query
+    causal chunk and the fused decode after it, with level 0 in host memory,
+    bit for bit against the same steps on the device-resident tree."""
+    _need_gpu()
+    wl = synth.WORKLOADS["524k"]
+    L, T = wl.L, 256
+    t_dec = L + T
+    L_cap = t_dec + 64
+    K, V = synth.kv_rows_device(wl, DEV, L_cap)
+    pdict = synth.pooler_params(wl.d, wl.d, DEV, wl.seed)
+    pool = R.Pooler.from_dict(pdict, DEV)
+    dev = R.Tree.allocate(1, wl.Hkv, wl.d, L_cap, k=wl.k, dtype="bf16", device=DEV, level0=(K, V))
+    host = R.Tree.allocate(1, wl.Hkv, wl.d, L_cap, k=wl.k, dtype="bf16", device=DEV,
+                           level0=(K, V), level0_host=True)
+    q_pre = synth.to_storage(synth.normal((1, T, wl.Hq, wl.d), DEV, wl.seed, 41), "bf16")
+    q_dec = synth.decode_queries(wl, DEV)
+    kn = K[:, :, t_dec].clone().contiguous()
+    vn = V[:, :, t_dec].clone().contiguous()
+    pos = torch.arange(L, L + T, device=DEV).view(1, T)
+    p1 = torch.tensor([t_dec], dtype=torch.int64, device=DEV)
+    res = []
+    for tr in (dev, host):
+        print("524K offload:", "host" if tr is host else "device", flush=True)
+        R.recsa_build_tree(tr, pool, 0, L)
+        R.recsa_build_tree(tr, pool, L, L + T)
+        r = TP._run_select_attn(tr, q_pre, wl.Hq, pos, decode=False)
+        fs, fc, fo, ws = TP._fused_step(tr, pool, kn, vn, q_dec, wl.Hq, p1)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(R.decode_error_words(ws, tr, wl.Hq)).item() == 0
+        res.append(list(r) + [fs.cpu().numpy(), fo.cpu().numpy()])
+        del ws
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+    for lvl in range(1, dev.n_levels):
+        assert torch.equal(dev.K[lvl], host.K[lvl]) and torch.equal(dev.Kr[lvl], host.Kr[lvl])
+    assert torch.equal(dev.Kr[0].cpu(), host.Kr[0])
