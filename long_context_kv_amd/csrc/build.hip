@@ -27,9 +27,15 @@ __global__ void __launch_bounds__(kBlock) rope_table_kernel(float* table, int d,
   }
 }
 
-// Build nodes [n_lo, n_hi) of `level` for every (sequence, KV head).
-template <int DT, int D>
-__global__ void __launch_bounds__(kBlock) build_level_kernel(recsa_tree tr, recsa_pooler P,
+// Build nodes [n_lo, n_hi) of `level` for every (sequence, KV head): 16 nodes
+// per workgroup of NT threads.  Few tiles (an incremental chunk) take 512
+// threads, so each wave pools two nodes instead of four and the short grid
+// finishes sooner; many tiles (a full build) take 256, which keeps more
+// tiles resident per CU.  Results are identical either way.
+constexpr int kBuildWideTiles = 1024;     // below this many tiles: 512 threads
+
+template <int DT, int D, int NT>
+__global__ void __launch_bounds__(NT) build_level_kernel(recsa_tree tr, recsa_pooler P,
                                                              int level, int64_t n_lo,
                                                              int64_t n_hi) {
   using T = typename Stor<DT>::T;
@@ -46,23 +52,45 @@ __global__ void __launch_bounds__(kBlock) build_level_kernel(recsa_tree tr, recs
   T* ko = static_cast<T*>(tr.K[level]) + (head * rows + first) * D;
   T* vo = static_cast<T*>(tr.V[level]) + (head * rows + first) * D;
   T* kro = static_cast<T*>(tr.Kr[level]) + (head * rows + first) * D;
-  pool_tile<DT, D, NODES, kBlock>(kc, vc, ko, vo, kro, static_cast<int>(first % kC), tr.rope,
-                                  n_valid, P, sm);
+  pool_tile<DT, D, NODES, NT>(kc, vc, ko, vo, kro, static_cast<int>(first % kC), tr.rope,
+                              n_valid, P, sm);
 }
 
-// Rotated keys Kr[0] of the level-0 rows [tb, te): one row per wave, one
-// pair per lane (D/2 <= 64), 4 rows per workgroup.
+// Rotated keys Kr[0] of the level-0 rows [tb, te): each thread rotates 8
+// pairs (j, j + D/2) of one row with 16-byte loads and stores, so a row takes
+// D/16 threads and a workgroup 256 * 16 / D rows.  The same float32 rotation
+// as rotate_key_row, element for element.
 template <int DT, int D>
 __global__ void __launch_bounds__(kBlock) rotate_level0_kernel(recsa_tree tr, int64_t tb,
                                                                int64_t te) {
   using T = typename Stor<DT>::T;
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const int64_t t = tb + static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + wid;
+  constexpr int H2 = D / 2;
+  constexpr int TPR = H2 / 8;                        // threads per row
+  constexpr int RPB = kBlock / TPR;                  // rows per workgroup
+  const int64_t t = tb + static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
   if (t >= te) return;
+  const int j0 = 8 * (threadIdx.x % TPR);
   const int64_t head = static_cast<int64_t>(blockIdx.z) * tr.Hkv + blockIdx.y;
   const int64_t off = (head * tr.L_cap + t) * D;
-  rotate_key_row<DT, D>(static_cast<const T*>(tr.K[0]) + off, static_cast<T*>(tr.Kr[0]) + off,
-                        static_cast<int>(t % kC), tr.rope, lane, kWave);
+  const T* src = static_cast<const T*>(tr.K[0]) + off;
+  T* dst = static_cast<T*>(tr.Kr[0]) + off;
+  float x[8], y[8], cs[16];
+  load_vec<DT, 8>(src + j0, x);
+  load_vec<DT, 8>(src + H2 + j0, y);
+  const float* rp = tr.rope + (static_cast<int64_t>(t % kC) * H2 + j0) * 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(rp + 4 * i);
+    cs[4 * i] = v.x;
+    cs[4 * i + 1] = v.y;
+    cs[4 * i + 2] = v.z;
+    cs[4 * i + 3] = v.w;
+  }
+  float xo[8], yo[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rope_pair(x[e], y[e], cs[2 * e], cs[2 * e + 1], xo[e], yo[e]);
+  store_vec8<DT>(dst + j0, xo);
+  store_vec8<DT>(dst + H2 + j0, yo);
 }
 
 // Decode append: write row t, then complete each node whose last token is t.
@@ -119,7 +147,7 @@ template <int DT, int D>
 static hipError_t build_impl(const recsa_tree& tr, const recsa_pooler& P, int64_t tb, int64_t te,
                              hipStream_t s) {
   {
-    constexpr int RPB = kBlock / kWave;
+    constexpr int RPB = kBlock / (D / 16);            // rows per workgroup
     dim3 grid(static_cast<unsigned>((te - tb + RPB - 1) / RPB), tr.Hkv, tr.B);
     rotate_level0_kernel<DT, D><<<grid, kBlock, 0, s>>>(tr, tb, te);
     hipError_t e = hipGetLastError();
@@ -134,7 +162,10 @@ static hipError_t build_impl(const recsa_tree& tr, const recsa_pooler& P, int64_
     if (n_hi <= n_lo) continue;
     const int64_t tiles = (n_hi - n_lo + 15) / 16;
     dim3 grid(static_cast<unsigned>(tiles), tr.Hkv, tr.B);
-    build_level_kernel<DT, D><<<grid, kBlock, 0, s>>>(tr, P, l, n_lo, n_hi);
+    if (tiles * tr.Hkv * tr.B < kBuildWideTiles)
+      build_level_kernel<DT, D, 512><<<grid, 512, 0, s>>>(tr, P, l, n_lo, n_hi);
+    else
+      build_level_kernel<DT, D, kBlock><<<grid, kBlock, 0, s>>>(tr, P, l, n_lo, n_hi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -99,6 +99,23 @@ __device__ __forceinline__ void load_vec(const typename Stor<DT>::T* p, float* o
   }
 }
 
+// Store 8 floats as 8 consecutive storage elements (one 16-byte store for
+// bf16, two for float32), each rounded to the storage dtype.
+template <int DT>
+__device__ __forceinline__ void store_vec8(typename Stor<DT>::T* p, const float* v) {
+  if constexpr (DT == RECSA_BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
 // ------------------------------------------------------------------- RoPE
 // Rotate-half pair (x, y) by the angle whose (cos, sin) = (c, s):
 // (x*c - y*s, x*s + y*c), each product and sum rounded to float32 separately

@@ -153,7 +153,11 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
   __syncthreads();
 
   // ---- phase 2: hid = SiLU(W1 feat + b1)
-  constexpr int NPG = NODES < 8 ? NODES : 8;     // nodes per thread
+  // nodes per thread: 8 with 256 threads, 4 with 512 (one item per thread
+  // for 16 nodes and 128 hidden units); the per-element sums run in the same
+  // order either way
+  constexpr int NPG0 = NODES * 128 / NT;
+  constexpr int NPG = NODES < 8 ? NODES : (NPG0 >= 8 ? 8 : (NPG0 < 1 ? 1 : NPG0));
   constexpr int NGRP = NODES / NPG;
   const int H = P.hidden;
   for (int item = threadIdx.x; item < NGRP * H; item += NT) {
