@@ -235,7 +235,11 @@ size_t recsa_distill_workspace_bytes(const recsa_tree* tree, int32_t Hq,
  * base (> 1).  Level-0 rows [0, t] of each query must be in the tree.
  * kl_out: [B][T][Hkv][n_levels-1] float32: slot l-1 holds KL(y || pi) of
  * level l when it is scored, else 0; a zero importance under a positive
- * teacher mass gives +inf.  Arithmetic is float32 (teacher logits on the
+ * teacher mass gives +inf.
+ * teacher_or_null: optional [B][T][Hkv][n_levels-1][C*k] float32, laid out
+ * like the importance: entry p is y of the candidate at list position p (0
+ * for the current node, past the list and at unscored levels).  With the
+ * importance and the logits it gives d KL / d logit in closed form.  Arithmetic is float32 (teacher logits on the
  * float32 matrix cores).  ws: recsa_distill_workspace_bytes(tree, Hq, B*T)
  * bytes of device memory, overwritten.  RECSA_E_UNSUPPORTED when
  * ceil(L_cap/16) + C*k exceeds 16352 (the masses of one query are kept on
@@ -243,7 +247,8 @@ size_t recsa_distill_workspace_bytes(const recsa_tree* tree, int32_t Hq,
 int recsa_distill_kl(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
                      const int64_t* pos_dev, const int32_t* sel_idx,
                      const int32_t* sel_cnt, const float* importance, double theta,
-                     float* kl_out, void* ws, size_t ws_bytes, void* stream);
+                     float* kl_out, float* teacher_or_null, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* Workspace bytes of recsa_shift_penalty: one partial row of d+1 floats per
  * 16 nodes of every level >= 1, (sequence, KV head).  0 on invalid

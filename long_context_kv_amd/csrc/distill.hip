@@ -262,7 +262,7 @@ template <int G>
 __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
     recsa_tree tr, int T, const int64_t* __restrict__ pos, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ cnt, const float* __restrict__ imp,
-    const float* __restrict__ lse, int ng_cap, float* __restrict__ kl) {
+    const float* __restrict__ lse, int ng_cap, float* __restrict__ kl, float* __restrict__ yout) {
   extern __shared__ float dsm[];
   const int qi = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -338,10 +338,13 @@ __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
   const int32_t* cl = cnt + slot * n_sel;
   const float* il = imp + slot * n_sel * CK;
   float* ko = kl + slot * n_sel;
+  float* yo = yout ? yout + slot * n_sel * CK : nullptr;
   for (int l = 1; l <= n_sel; ++l) {
     const ListView lv = list_view(t, l, top, k, sl, cl);
     if (lv.len <= k) {   // unscored (uniform)
       if (tid == 0) ko[l - 1] = 0.f;
+      if (yo)
+        for (int p = tid; p < CK; p += kBlock) yo[static_cast<int64_t>(l - 1) * CK + p] = 0.f;
       continue;
     }
     const int n_oth = lv.len - 1;
@@ -361,6 +364,9 @@ __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
       const float y = mass[p] / tot;
       if (y > 0.f) acc += y * (logf(y) - logf(il[static_cast<int64_t>(l - 1) * CK + p]));
     }
+    if (yo)
+      for (int p = tid; p < CK; p += kBlock)
+        yo[static_cast<int64_t>(l - 1) * CK + p] = p < n_oth ? mass[p] / tot : 0.f;
     const float v = block_sum(acc, red);
     if (tid == 0) ko[l - 1] = v;
   }
@@ -448,7 +454,7 @@ int64_t distill_groups(int64_t L_cap) { return (L_cap + kC - 1) / kC; }
 template <int DT, int D, int G>
 static hipError_t distill_impl(const recsa_tree& tr, const void* q, int Hq, int T,
                                const int64_t* pos, const int32_t* sel, const int32_t* cnt,
-                               const float* imp, double theta, float* kl, void* ws,
+                               const float* imp, double theta, float* kl, float* y, void* ws,
                                hipStream_t s) {
   (void)Hq;
   float* arope = static_cast<float*>(ws);
@@ -464,7 +470,7 @@ static hipError_t distill_impl(const recsa_tree& tr, const void* q, int Hq, int 
   if (e != hipSuccess) return e;
   dim3 g2(static_cast<unsigned>(T), tr.Hkv, tr.B);
   const size_t lds = (static_cast<size_t>(ng_cap) + kC * tr.k + 32) * sizeof(float);
-  distill_kl_kernel<G><<<g2, kBlock, lds, s>>>(tr, T, pos, sel, cnt, imp, lse, ng_cap, kl);
+  distill_kl_kernel<G><<<g2, kBlock, lds, s>>>(tr, T, pos, sel, cnt, imp, lse, ng_cap, kl, y);
   return hipGetLastError();
 }
 
@@ -474,9 +480,9 @@ int64_t distill_ws_bytes(const recsa_tree& tr, int Hq, int64_t n_queries) {
 
 hipError_t launch_distill_kl(const recsa_tree& tr, const void* q, int Hq, int T,
                              const int64_t* pos, const int32_t* sel, const int32_t* cnt,
-                             const float* imp, double theta, float* kl, void* ws,
+                             const float* imp, double theta, float* kl, float* y, void* ws,
                              hipStream_t s) {
-  RECSA_DISPATCH(distill_impl, tr, q, Hq, T, pos, sel, cnt, imp, theta, kl, ws, s);
+  RECSA_DISPATCH(distill_impl, tr, q, Hq, T, pos, sel, cnt, imp, theta, kl, y, ws, s);
 }
 
 static ShiftLevels shift_levels(const recsa_tree& tr, int64_t tok_end) {

@@ -193,8 +193,8 @@ size_t recsa_distill_workspace_bytes(const recsa_tree* tree, int32_t Hq, int64_t
 
 int recsa_distill_kl(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
                      const int64_t* pos_dev, const int32_t* sel_idx, const int32_t* sel_cnt,
-                     const float* importance, double theta, float* kl_out, void* ws,
-                     size_t ws_bytes, void* stream) {
+                     const float* importance, double theta, float* kl_out,
+                     float* teacher_or_null, void* ws, size_t ws_bytes, void* stream) {
   int why;
   if (!tree_ok(tree, &why)) return why;
   if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
@@ -206,7 +206,8 @@ int recsa_distill_kl(const recsa_tree* tree, const void* q, int32_t Hq, int32_t 
     return RECSA_E_WORKSPACE;
   if (tree->n_levels < 2) return RECSA_OK;      // no level above the tokens: no term
   return hip_status(launch_distill_kl(*tree, q, Hq, T, pos_dev, sel_idx, sel_cnt, importance,
-                                      theta, kl_out, ws, static_cast<hipStream_t>(stream)));
+                                      theta, kl_out, teacher_or_null, ws,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 static bool shift_fits(const recsa_tree* t) {

@@ -111,7 +111,8 @@ int64_t distill_groups(int64_t L_cap);
 int64_t distill_ws_bytes(const recsa_tree& tr, int Hq, int64_t n_queries);
 hipError_t launch_distill_kl(const recsa_tree& tr, const void* q, int Hq, int T,
                              const int64_t* pos, const int32_t* sel, const int32_t* cnt,
-                             const float* imp, double theta, float* kl, void* ws, hipStream_t s);
+                             const float* imp, double theta, float* kl, float* y, void* ws,
+                             hipStream_t s);
 int64_t shift_ws_bytes(const recsa_tree& tr);
 hipError_t launch_shift_penalty(const recsa_tree& tr, const recsa_pooler& P, int64_t tok_end,
                                 float* out, void* ws, hipStream_t s);

@@ -97,7 +97,7 @@ def lib():
             "recsa_decode": (ctypes.c_int, [T, P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "recsa_distill_workspace_bytes": (sz, [T, i32, i64]),
             "recsa_distill_kl": (ctypes.c_int, [T, vp, i32, i32, vp, vp, vp, vp,
-                                                 ctypes.c_double, vp, vp, sz, vp]),
+                                                 ctypes.c_double, vp, vp, vp, sz, vp]),
             "recsa_shift_workspace_bytes": (sz, [T]),
             "recsa_shift_penalty": (ctypes.c_int, [T, P, i64, vp, vp, sz, vp]),
             "recsa_pooler_backward_workspace_bytes": (sz, [T, P, i32]),
@@ -352,12 +352,13 @@ def recsa_distill_workspace_bytes(tree, Hq: int, n_queries: int) -> int:
 
 
 def recsa_distill_kl(tree, q, Hq: int, T: int, pos_dev, sel_idx, sel_cnt, importance,
-                     theta: float, kl_out, ws, ws_bytes: int | None = None, stream=None):
+                     theta: float, kl_out, ws, ws_bytes: int | None = None, stream=None,
+                     teacher=None):
     tc = _tc(tree)
     nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check("recsa_distill_kl", lib().recsa_distill_kl(
         ctypes.byref(tc), _ptr(q), Hq, T, _ptr(pos_dev), _ptr(sel_idx), _ptr(sel_cnt),
-        _ptr(importance), theta, _ptr(kl_out), _ptr(ws), nb, _stream(stream)))
+        _ptr(importance), theta, _ptr(kl_out), _ptr(teacher), _ptr(ws), nb, _stream(stream)))
 
 
 def recsa_shift_workspace_bytes(tree) -> int:

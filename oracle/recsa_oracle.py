@@ -439,18 +439,25 @@ def subtree_mass(a, nodes, level: int, C: int):
     return out
 
 
-def distill_kl(qG, t: int, tr: WalkTrace, K0, C: int, theta: float):
-    """Eq. 6 terms of one query: {level: KL(y || pi)} over the walk's scored
-    levels, with 0 log 0 = 0."""
+def distill_targets(qG, t: int, tr: WalkTrace, K0, C: int, theta: float):
+    """The teacher distributions y_t^(l) of one query: {level: y} over the
+    walk's scored levels, y[i] for the i-th non-current candidate of A^(l)."""
     a = teacher_attention(qG, t, K0, theta)
     out = {}
     for lvl, lt in tr.levels.items():
         if not lt.scored:
             continue
-        others = lt.A[:-1]
-        m = subtree_mass(a, others, lvl, C).mean(axis=0)
-        y = m / m.sum()
-        pi = np.asarray(lt.importance, dtype=np.float64)
+        m = subtree_mass(a, lt.A[:-1], lvl, C).mean(axis=0)
+        out[lvl] = m / m.sum()
+    return out
+
+
+def distill_kl(qG, t: int, tr: WalkTrace, K0, C: int, theta: float):
+    """Eq. 6 terms of one query: {level: KL(y || pi)} over the walk's scored
+    levels, with 0 log 0 = 0."""
+    out = {}
+    for lvl, y in distill_targets(qG, t, tr, K0, C, theta).items():
+        pi = np.asarray(tr.levels[lvl].importance, dtype=np.float64)
         nz = y > 0
         out[lvl] = float(np.sum(y[nz] * (np.log(y[nz]) - np.log(pi[nz]))))
     return out

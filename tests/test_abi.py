@@ -171,10 +171,10 @@ def test_distillation_calls_validate_without_launch():
     # ceil(L_cap/16) + C*k > 16376: the per-query masses no longer fit on chip
     big = _tree(k=256, L_cap=528384, n_levels=4)
     assert L.recsa_distill_workspace_bytes(b(big), 32, 1) == 0
-    args = [b(big), 0x10, 32, 1, 0x10, 0x10, 0x10, 0x10, 1e6, 0x10, 0x10, 1 << 40, None]
+    args = [b(big), 0x10, 32, 1, 0x10, 0x10, 0x10, 0x10, 1e6, 0x10, None, 0x10, 1 << 40, None]
     assert L.recsa_distill_kl(*args) == R.RECSA_E_UNSUPPORTED
-    ok = [b(t), 0x10, 32, 100, 0x10, 0x10, 0x10, 0x10, 1e6, 0x10, 0x10, need, None]
-    for i in (1, 4, 5, 6, 7, 9, 10):                      # required pointers
+    ok = [b(t), 0x10, 32, 100, 0x10, 0x10, 0x10, 0x10, 1e6, 0x10, None, 0x10, need, None]
+    for i in (1, 4, 5, 6, 7, 9, 11):                      # required pointers
         a = list(ok)
         a[i] = None
         assert L.recsa_distill_kl(*a) == R.RECSA_E_INVALID, i
@@ -182,7 +182,7 @@ def test_distillation_calls_validate_without_launch():
     a[8] = 1.0                                            # theta must exceed 1
     assert L.recsa_distill_kl(*a) == R.RECSA_E_INVALID
     a = list(ok)
-    a[11] = need - 1
+    a[12] = need - 1
     assert L.recsa_distill_kl(*a) == R.RECSA_E_WORKSPACE
     a = list(ok)
     a[2] = 24                                             # G = 3

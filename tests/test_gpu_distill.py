@@ -41,8 +41,10 @@ def _tree(B, Hkv, d, L0, k, dtype, seed):
     return tree, pool, pdict
 
 
-def run_distill(tree, q, Hq, pos):
-    """recsa_select (with importance), then recsa_distill_kl on its outputs."""
+def run_distill(tree, q, Hq, pos, with_teacher=False):
+    """recsa_select (with importance), then recsa_distill_kl on its outputs;
+    with_teacher also returns the teacher distributions y [B, T, Hkv, n_sel,
+    C*k] as a fifth array."""
     B, T = pos.shape
     nq = B * T
     ws = R.workspace(tree, Hq, nq)
@@ -52,17 +54,24 @@ def run_distill(tree, q, Hq, pos):
                       device=tree.rope.device)
     kl = torch.full((B, T, tree.Hkv, tree.n_sel), float("nan"), dtype=torch.float32,
                     device=tree.rope.device)
-    R.recsa_distill_kl(tree, q, Hq, T, pos, sel, cnt, imp, THETA, kl, dws)
+    y = (torch.full((B, T, tree.Hkv, tree.n_sel, 16 * tree.k), float("nan"), dtype=torch.float32,
+                    device=tree.rope.device) if with_teacher else None)
+    R.recsa_distill_kl(tree, q, Hq, T, pos, sel, cnt, imp, THETA, kl, dws, teacher=y)
     torch.cuda.synchronize()
-    return (sel.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel, tree.k),
-            cnt.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel),
-            imp.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel, -1),
-            kl.cpu().numpy().astype(np.float64))
+    out = (sel.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel, tree.k),
+           cnt.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel),
+           imp.cpu().numpy().reshape(B, T, tree.Hkv, tree.n_sel, -1),
+           kl.cpu().numpy().astype(np.float64))
+    if with_teacher:
+        out = out + (y.cpu().numpy().astype(np.float64),)
+    return out
 
 
-def check_kl(tree, pdict, q, pos, sel, cnt, imp, kl, heads):
+def check_kl(tree, pdict, q, pos, sel, cnt, imp, kl, heads, y=None):
     """Oracle walk + Eq. 6 for every (b, query, head in heads); returns
-    (pairs compared, scored levels compared, max abs error)."""
+    (pairs compared, scored levels compared, max abs error).  With y (the
+    teacher output), each scored level's y must match the oracle's within
+    1e-5 of its largest entry, and be 0 elsewhere."""
     B, T = pos.shape
     G = q.shape[2] // tree.Hkv
     cos, sin = O.rope_table(tree.d, 16 * tree.k, THETA)
@@ -87,6 +96,16 @@ def check_kl(tree, pdict, q, pos, sel, cnt, imp, kl, heads):
                                        1e-5):
                     continue
                 ref = O.distill_kl(qG, t, tr, K0[: t + 1], 16, THETA)
+                if y is not None:
+                    yref = O.distill_targets(qG, t, tr, K0[: t + 1], 16, THETA)
+                    for lvl in range(1, tree.n_levels):
+                        g = y[b, ti, j, lvl - 1]
+                        if lvl in yref:
+                            n = len(yref[lvl])
+                            assert np.max(np.abs(g[:n] - yref[lvl])) <= 1e-5 * yref[lvl].max()
+                            assert np.all(g[n:] == 0.0)
+                        else:
+                            assert np.all(g == 0.0), (t, lvl)
                 n_pairs += 1
                 for lvl in range(1, tree.n_levels):
                     g = kl[b, ti, j, lvl - 1]
@@ -121,10 +140,10 @@ def test_distill_kl_matches_oracle(dtype, d):
     Hq = 8
     q = synth.to_storage(synth.normal((1, T, Hq, d), DEV, 61, 1), dtype)
     pos = torch.tensor([positions(L0, T, 61)], dtype=torch.int64, device=DEV)
-    sel, cnt, imp, kl = run_distill(tree, q, Hq, pos)
+    sel, cnt, imp, kl, y = run_distill(tree, q, Hq, pos, with_teacher=True)
     assert np.all(np.isfinite(kl))
     assert np.all(kl >= -1e-6)                         # a KL divergence
-    n_pairs, n_lv, worst = check_kl(tree, pdict, q, pos.cpu(), sel, cnt, imp, kl, [0, 1])
+    n_pairs, n_lv, worst = check_kl(tree, pdict, q, pos.cpu(), sel, cnt, imp, kl, [0, 1], y)
     assert n_pairs >= 2 * T - 1 and n_lv >= T, (n_pairs, n_lv)
     # queries below C*k see every level whole: no term at all
     small = (pos.cpu().numpy()[0] < 16 * k)
