@@ -224,8 +224,10 @@ int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler,
 
 /* Workspace bytes of recsa_distill_kl for n_queries = B*T queries with Hq
  * query heads: the RoPE table of the absolute positions [0, L_cap), float32
- * [L_cap][d/2][2], then the teacher's per-group log-sum-exps, float32
- * [n_queries][Hkv][ceil(L_cap/16)][Hq/Hkv].  0 on invalid arguments. */
+ * [L_cap][d/2][2]; every level-0 key rotated at its position and split into
+ * two bf16 halves, [B][Hkv][L_cap][2][d]; then the teacher's per-group
+ * log-sum-exps, float32 [n_queries][Hkv][ceil(L_cap/16)][Hq/Hkv].  0 on
+ * invalid arguments. */
 size_t recsa_distill_workspace_bytes(const recsa_tree* tree, int32_t Hq,
                                      int64_t n_queries);
 

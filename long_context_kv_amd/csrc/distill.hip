@@ -80,8 +80,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // and lane l holds 4 keys of column l % 16: a row's log-sum-exp over the
 // group reduces 4 registers and the 4 lanes l % 16 + 16 i.  The group's
 // log-sum-exp does not depend on the row's global maximum: one pass.
-// Each tile of 64 keys is rotated at its absolute positions and split once,
-// into LDS, by all 256 threads (16-byte loads of 8 consecutive dims).
+// Every key row is rotated at its absolute position and split once for the
+// whole call (teacher_keys_kernel); each tile of 64 keys is then staged into
+// LDS with 16-byte loads by all 256 threads.
 // lse: [B*T][Hkv][ng_cap][G] float32; entry (v, h) is written for every
 // level-1 group v <= t/16 of the row's query, never beyond.
 __device__ __forceinline__ void split_bf16x8(const float* v, uint4& hi, uint4& lo) {
@@ -120,17 +121,46 @@ __device__ __forceinline__ void rotate8_abs(const typename Stor<DT>::T* row, int
   for (int e = 0; e < 8; ++e) rope_pair(x[e], y[e], cs[2 * e], cs[2 * e + 1], xo[e], yo[e]);
 }
 
+// Every level-0 key row rotated at its absolute position and split once:
+// ksplit[b][j][tau] = {hi[D], lo[D]} (bf16), each thread 8 RoPE pairs of one
+// row.  The key tiles of every query block are then plain 16-byte loads.
+template <int DT, int D>
+__global__ void __launch_bounds__(kBlock) teacher_keys_kernel(recsa_tree tr,
+                                                              const float* __restrict__ arope,
+                                                              uint16_t* __restrict__ ksplit) {
+  using Ty = typename Stor<DT>::T;
+  constexpr int H2 = D / 2;
+  constexpr int TPR = H2 / 8;                     // threads per row
+  constexpr int RPB = kBlock / TPR;               // rows per workgroup
+  const int64_t tau = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
+  if (tau >= tr.L_cap) return;
+  const int j0 = 8 * (threadIdx.x % TPR);
+  const int64_t head = static_cast<int64_t>(blockIdx.z) * tr.Hkv + blockIdx.y;
+  const Ty* row = static_cast<const Ty*>(tr.K[0]) + (head * tr.L_cap + tau) * D;
+  float xo[8], yo[8];
+  rotate8_abs<DT, D>(row, j0, arope + tau * H2 * 2, xo, yo);
+  uint4 xh, xl, yh, yl;
+  split_bf16x8(xo, xh, xl);
+  split_bf16x8(yo, yh, yl);
+  uint16_t* dst = ksplit + (head * tr.L_cap + tau) * 2 * D;
+  *reinterpret_cast<uint4*>(dst + j0) = xh;
+  *reinterpret_cast<uint4*>(dst + H2 + j0) = yh;
+  *reinterpret_cast<uint4*>(dst + D + j0) = xl;
+  *reinterpret_cast<uint4*>(dst + D + H2 + j0) = yl;
+}
+
 template <int DT, int D, int G>
 __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, const void* qv,
                                                              int T, const int64_t* __restrict__ pos,
                                                              const float* __restrict__ arope,
+                                                             const uint16_t* __restrict__ ksplit,
                                                              float* __restrict__ lse, int ng_cap) {
   using Ty = typename Stor<DT>::T;
   constexpr int QB = kTeacherRows / G;
   constexpr int H2 = D / 2;
   constexpr int KB = D / 32;             // 32-dim blocks
   constexpr int LDK = D + 8;             // bf16 elements per LDS key row (16-byte aligned)
-  constexpr int PQ = H2 / 4;             // rotation pairs per thread per key
+  constexpr int DQ = D / 4;              // dims per thread per key row in a tile load
   __shared__ __attribute__((aligned(16))) uint16_t khi[kTeacherKeys][LDK];
   __shared__ __attribute__((aligned(16))) uint16_t klo[kTeacherKeys][LDK];
   __shared__ int st[kTeacherRows];
@@ -182,10 +212,9 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
     const int qi = min(q0 + r_col / G, T - 1);
     lcol = lse + ((static_cast<int64_t>(b) * T + qi) * tr.Hkv + j) * ng_cap * G + (r_col % G);
   }
-  const Ty* k0 = static_cast<const Ty*>(tr.K[0]) +
-                 (static_cast<int64_t>(b) * tr.Hkv + j) * tr.L_cap * D;
+  const uint16_t* ks = ksplit + (static_cast<int64_t>(b) * tr.Hkv + j) * tr.L_cap * 2 * D;
   const float scale = static_cast<float>(1.0 / sqrt(static_cast<double>(D)));
-  const int kk = tid >> 2, qq = tid & 3;     // the key row and pair quarter this thread rotates
+  const int kk = tid >> 2, qq = tid & 3;     // the key row and quarter this thread loads
 
   const int n_tiles = tmax / kTeacherKeys + 1;
   for (int tile = 0; tile < n_tiles; ++tile) {
@@ -193,24 +222,16 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
     __syncthreads();   // the previous tile is read
     {
       const int tau = tau0 + kk;
+      const uint16_t* src = ks + static_cast<int64_t>(tau) * 2 * D + qq * DQ;
 #pragma unroll
-      for (int c = 0; c < PQ / 8; ++c) {
-        const int j0 = qq * PQ + 8 * c;
-        float xo[8], yo[8];
+      for (int c = 0; c < DQ / 8; ++c) {
+        uint4 hv = make_uint4(0u, 0u, 0u, 0u), lv = hv;
         if (tau <= tmax) {
-          rotate8_abs<DT, D>(k0 + static_cast<int64_t>(tau) * D, j0,
-                             arope + static_cast<int64_t>(tau) * H2 * 2, xo, yo);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xo[e] = yo[e] = 0.f;
+          hv = *reinterpret_cast<const uint4*>(src + 8 * c);
+          lv = *reinterpret_cast<const uint4*>(src + D + 8 * c);
         }
-        uint4 xh, xl, yh, yl;
-        split_bf16x8(xo, xh, xl);
-        split_bf16x8(yo, yh, yl);
-        *reinterpret_cast<uint4*>(&khi[kk][j0]) = xh;
-        *reinterpret_cast<uint4*>(&klo[kk][j0]) = xl;
-        *reinterpret_cast<uint4*>(&khi[kk][H2 + j0]) = yh;
-        *reinterpret_cast<uint4*>(&klo[kk][H2 + j0]) = yl;
+        *reinterpret_cast<uint4*>(&khi[kk][qq * DQ + 8 * c]) = hv;
+        *reinterpret_cast<uint4*>(&klo[kk][qq * DQ + 8 * c]) = lv;
       }
     }
     __syncthreads();
@@ -459,13 +480,22 @@ static hipError_t distill_impl(const recsa_tree& tr, const void* q, int Hq, int 
   (void)Hq;
   float* arope = static_cast<float*>(ws);
   const int64_t rope_bytes = align256(tr.L_cap * D * 4);
-  float* lse = reinterpret_cast<float*>(static_cast<char*>(ws) + rope_bytes);
+  uint16_t* ksplit = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rope_bytes);
+  const int64_t ks_bytes = align256(static_cast<int64_t>(tr.B) * tr.Hkv * tr.L_cap * D * 4);
+  float* lse = reinterpret_cast<float*>(static_cast<char*>(ws) + rope_bytes + ks_bytes);
   const int ng_cap = static_cast<int>(distill_groups(tr.L_cap));
   hipError_t e = launch_rope_table(arope, D, static_cast<int>(tr.L_cap), theta, s);
   if (e != hipSuccess) return e;
+  {
+    constexpr int RPB = kBlock / (D / 16);
+    dim3 gk(static_cast<unsigned>((tr.L_cap + RPB - 1) / RPB), tr.Hkv, tr.B);
+    teacher_keys_kernel<DT, D><<<gk, kBlock, 0, s>>>(tr, arope, ksplit);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   constexpr int QB = kTeacherRows / G;
   dim3 g1(static_cast<unsigned>((T + QB - 1) / QB), tr.Hkv, tr.B);
-  teacher_lse_kernel<DT, D, G><<<g1, kBlock, 0, s>>>(tr, q, T, pos, arope, lse, ng_cap);
+  teacher_lse_kernel<DT, D, G><<<g1, kBlock, 0, s>>>(tr, q, T, pos, arope, ksplit, lse, ng_cap);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(static_cast<unsigned>(T), tr.Hkv, tr.B);
@@ -475,7 +505,9 @@ static hipError_t distill_impl(const recsa_tree& tr, const void* q, int Hq, int 
 }
 
 int64_t distill_ws_bytes(const recsa_tree& tr, int Hq, int64_t n_queries) {
-  return align256(tr.L_cap * tr.d * 4) + n_queries * Hq * distill_groups(tr.L_cap) * 4;
+  return align256(tr.L_cap * tr.d * 4) +
+         align256(static_cast<int64_t>(tr.B) * tr.Hkv * tr.L_cap * tr.d * 4) +
+         n_queries * Hq * distill_groups(tr.L_cap) * 4;
 }
 
 hipError_t launch_distill_kl(const recsa_tree& tr, const void* q, int Hq, int T,

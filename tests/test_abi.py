@@ -166,7 +166,7 @@ def test_distillation_calls_validate_without_launch():
     def al(x):
         return (x + 255) // 256 * 256
     need = L.recsa_distill_workspace_bytes(b(t), 32, 100)
-    assert need == al(32768 * 128 * 4) + 100 * 32 * (32768 // 16) * 4
+    assert need == al(32768 * 128 * 4) + al(8 * 32768 * 128 * 4) + 100 * 32 * (32768 // 16) * 4
     assert L.recsa_distill_workspace_bytes(b(t), 30, 100) == 0              # Hq % Hkv
     # ceil(L_cap/16) + C*k > 16376: the per-query masses no longer fit on chip
     big = _tree(k=256, L_cap=528384, n_levels=4)
