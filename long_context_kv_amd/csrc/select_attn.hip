@@ -349,6 +349,8 @@ static BucketArgs bucket_args(const recsa_tree& tr, void* ws, const WsLayout& w,
 }
 
 // ------------------------------------------------------------- launchers
+constexpr int64_t kTopkWideLists = 1024;   // below this many lists: 512-thread top-k
+
 template <int DT, int D, int G>
 static hipError_t select_impl(const recsa_tree& tr, const void* q, int Hq, int T,
                               const int64_t* pos, int32_t* sel, int32_t* cnt, float* imp,
@@ -382,7 +384,12 @@ static hipError_t select_impl(const recsa_tree& tr, const void* q, int Hq, int T
         score_kernel<DT, D, G><<<dim3(score_blocks * nq, tr.Hkv), kBlock, 0, s>>>(
             tr, q, Hq, T, pos, sel, cnt, logits, l, w.n_sel, w.CK);
     }
-    if (w.CK <= 4096)
+    // few lists (decode): 512 threads each, for the shortest latency; many
+    // lists (prefill): 256, so more lists are resident per CU
+    if (w.CK <= 4096 && static_cast<int64_t>(nq) * tr.Hkv < kTopkWideLists)
+      topk_kernel<G, 2 * kBlock, 4096><<<dim3(nq, tr.Hkv), 2 * kBlock, 0, s>>>(
+          tr, T, pos, sel, cnt, imp, logits, bitmap, l, w.n_sel, w.CK);
+    else if (w.CK <= 4096)
       topk_kernel<G, kBlock, 4096><<<dim3(nq, tr.Hkv), kBlock, 0, s>>>(
           tr, T, pos, sel, cnt, imp, logits, bitmap, l, w.n_sel, w.CK);
     else
