@@ -20,7 +20,7 @@ exactly to float64.  Rounding happens only where stated:
   decides a quantised code, so it is taken in the float32 precision the
   kernels use, with the operation order written out in ``rotate_f32``.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
   current node a_t^(l) = floor(t / C^l); the walk starts at the first level
   whose list [0..a] has at most k nodes; candidate lists are concatenated in
   ascending node order and the query sits at the last position; importance is
