@@ -536,3 +536,51 @@ def shift_penalty_dm(X, P: Pooler):
     U = float((mu * mu).sum())
     M = X.shape[0]
     return 2.0 * sigma[:, None] * S[None, :] / (M * U)
+
+
+def kl_key_grad(qG, t: int, tr: WalkTrace, K0, C: int, theta: float, cos=None, sin=None,
+                dtype: str = "f32", exact: bool = False):
+    """Gradient of one query's Eq. 6 terms, sum over scored levels of
+    KL(y^(l) || pi^(l)), with respect to the stored key of every non-current
+    candidate: {level: (nodes [n], dK [n, d])}.
+
+    y does not depend on the tree (the teacher reads level-0 tokens only);
+    pi = mean_h softmax_h(s_h) over the non-current candidates, so with
+    r = y / pi and P_h = softmax_h(s_h),
+        d KL / d s_h,e = -(P_h,e / G) (r_e - sum_f r_f P_h,f),
+    and s_h,e = q~_h . k~_e / sqrt(d) gives d s / d K_e = R(c_e)^T q~_h / sqrt(d)
+    in the split form (the operand roundings taken as the identity, the same
+    float32 table entries), or R(p_q - p_e) q_h / sqrt(d) in exact mode."""
+    ys = distill_targets(qG, t, tr, K0, C, theta)
+    qG = np.asarray(qG, dtype=np.float64)
+    G, d = qG.shape
+    h = d // 2
+    out = {}
+    for lvl, y in ys.items():
+        lt = tr.levels[lvl]
+        others = lt.A[:-1]
+        n = len(others)
+        s = np.asarray(lt.logits, dtype=np.float64)                 # [G, n]
+        P = np.exp(s - s.max(axis=1, keepdims=True))
+        P = P / P.sum(axis=1, keepdims=True)
+        r = y / P.mean(axis=0)
+        coef = -(P / G) * (r[None, :] - (P * r[None, :]).sum(axis=1, keepdims=True))
+        p_q = len(lt.A) - 1
+        pos_e = np.arange(n)
+        if exact:
+            qrot = rotate_exact(qG[:, None, :], (p_q - pos_e)[None, :], theta)   # [G, n, d]
+        else:
+            r_q, c_q = divmod(p_q, C)
+            r_e, c_e = pos_e // C, pos_e % C
+            qt = np.empty((G, n, d))
+            for rr in np.unique(r_e):
+                idx = np.nonzero(r_e == rr)[0]
+                phi = C * (r_q - int(rr)) + c_q
+                qt[:, idx] = rnd(rotate_f32(qG, cos[phi], sin[phi]).astype(np.float64),
+                                 dtype)[:, None, :]
+            cc = cos[c_e].astype(np.float64)[None]                   # [1, n, d/2]
+            ss = sin[c_e].astype(np.float64)[None]
+            x, yv = qt[..., :h], qt[..., h:]
+            qrot = np.concatenate([x * cc + yv * ss, -x * ss + yv * cc], axis=-1)  # R(c)^T q~
+        out[lvl] = (others, np.einsum("gn,gnd->nd", coef, qrot) / math.sqrt(d))
+    return out

@@ -673,3 +673,42 @@ def test_pool_backward_of_shift_penalty_matches_finite_differences():
     fd = _fd_grads(lambda Q: O.shift_penalty({1: X}, Q)[1], P)
     _check_fd(an, fd, 1e-6)
     assert an["g"] == 0.0                   # the penalty does not involve g
+
+
+def test_kl_key_grad_matches_finite_differences():
+    """The gradient of a query's Eq. 6 terms with respect to node keys
+    (exact-mode logits) against central differences of distill_kl over a
+    perturbed tree, at two scored levels; the split form agrees with it to
+    the float32 rounding of its operands."""
+    rng = np.random.default_rng(9)
+    d, C, k, L, theta = 8, 16, 3, 5000, 1e4
+    P = _pooler(d, 16, 3)
+    K0 = rng.normal(size=(L, d))
+    K, _ = O.build_tree(K0, rng.normal(size=(L, d)), C, 4, P, "f32")
+    t = L - 1
+    qG = rng.normal(size=(2, d))
+    tr = O.walk(qG, t, K, C, k, exact=True, theta=theta)
+    assert sorted(l for l, lt in tr.levels.items() if lt.scored) == [1, 2]
+    an = O.kl_key_grad(qG, t, tr, K0, C, theta, exact=True)
+    step = 1e-6
+    for lvl in (1, 2):
+        nodes, g = an[lvl]
+        for i in (0, len(nodes) // 2, len(nodes) - 1):
+            u = int(nodes[i])
+            for jj in (0, d - 1):
+                Kp = [x.copy() for x in K]
+                Km = [x.copy() for x in K]
+                Kp[lvl][u, jj] += step
+                Km[lvl][u, jj] -= step
+                fp = sum(O.distill_kl(qG, t, O.walk(qG, t, Kp, C, k, exact=True, theta=theta),
+                                      K0, C, theta).values())
+                fm = sum(O.distill_kl(qG, t, O.walk(qG, t, Km, C, k, exact=True, theta=theta),
+                                      K0, C, theta).values())
+                fd = (fp - fm) / (2 * step)
+                assert abs(g[i, jj] - fd) <= 1e-6 * max(1.0, np.abs(g).max()), (lvl, u, jj, g[i, jj], fd)
+    cos, sin = O.rope_table(d, C * k, theta)
+    trs = O.walk(qG, t, K, C, k, cos, sin, "f32", theta=theta)
+    sp = O.kl_key_grad(qG, t, trs, K0, C, theta, cos, sin, "f32")
+    for lvl in (1, 2):
+        assert np.array_equal(sp[lvl][0], an[lvl][0])
+        assert np.max(np.abs(sp[lvl][1] - an[lvl][1])) <= 1e-5 * np.abs(an[lvl][1]).max()
