@@ -270,6 +270,36 @@ int recsa_shift_penalty(const recsa_tree* tree, const recsa_pooler* pooler,
                         int64_t tok_end, float* out, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* Workspace bytes of recsa_distill_key_grad: one float32 coefficient per
+ * scored candidate and query head, [B*T][Hkv][n_levels-1][Hq/Hkv][C*k].  0 on
+ * invalid arguments. */
+size_t recsa_distill_key_grad_workspace_bytes(const recsa_tree* tree, int32_t Hq,
+                                              int64_t n_queries);
+
+/* Gradient of the Eq. 6 terms of T queries per sequence, sum over queries,
+ * KV heads and scored levels of KL(y || pi), with respect to every stored
+ * node key (picx.dev Pooler Distillation, Eq. 6).  With P_h the softmax of
+ * head h's logits over a level's non-current candidates, pi = mean_h P_h and
+ * r = y / pi: d KL / d s_h,e = -(P_h,e / G) (r_e - sum_f r_f P_h,f); each logit
+ * s_h,e = q~_h . k~_e / sqrt(d) (the split candidate-local RoPE of
+ * recsa_select, operand roundings taken as the identity) adds
+ * R(c_e)^T q~_h / sqrt(d) times that to its key.  This is the dK that
+ * recsa_pooler_backward takes.
+ * q, pos_dev, sel_idx, sel_cnt, importance: as given to and returned by
+ * recsa_select; select_ws: that call's workspace (its logits are read);
+ * teacher: the teacher distributions of recsa_distill_kl for the same queries.
+ * dK_out: float32 device array, the levels 1 .. n_levels-1 one after another,
+ * level l as [B][Hkv][recsa_level_rows(L_cap, C, l)][d]; every element is
+ * written (0 where no query scores the node).  Each element is summed over
+ * the queries in order: identical bits on every call.  ws:
+ * recsa_distill_key_grad_workspace_bytes(tree, Hq, B*T) bytes. */
+int recsa_distill_key_grad(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
+                           const int64_t* pos_dev, const int32_t* sel_idx,
+                           const int32_t* sel_cnt, const float* importance,
+                           const float* teacher, const void* select_ws,
+                           size_t select_ws_bytes, float* dK_out, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* Gradients of the pooler parameters, float32 device arrays shaped like the
  * fields of recsa_pooler (tau and g: one float each). */
 typedef struct recsa_pooler_grad {

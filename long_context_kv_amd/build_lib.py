@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librecsa.so")
 SOURCES = ["recsa_api.hip", "build.hip", "select_attn.hip", "decode_fused.hip", "distill.hip",
-           "pool_backward.hip"]
+           "pool_backward.hip", "kl_backward.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

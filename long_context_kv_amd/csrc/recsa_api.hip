@@ -233,6 +233,40 @@ int recsa_shift_penalty(const recsa_tree* tree, const recsa_pooler* pooler, int6
                                          static_cast<hipStream_t>(stream)));
 }
 
+// ---- gradient of the Eq. 6 terms with respect to the node keys
+
+size_t recsa_distill_key_grad_workspace_bytes(const recsa_tree* tree, int32_t Hq,
+                                              int64_t n_queries) {
+  int why;
+  if (!tree_ok(tree, &why) || !heads_ok(tree, Hq) || n_queries < 1) return 0;
+  return static_cast<size_t>(kgrad_ws_bytes(*tree, Hq, n_queries));
+}
+
+int recsa_distill_key_grad(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T,
+                           const int64_t* pos_dev, const int32_t* sel_idx,
+                           const int32_t* sel_cnt, const float* importance,
+                           const float* teacher, const void* select_ws,
+                           size_t select_ws_bytes, float* dK_out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
+  if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !importance || !teacher ||
+      !select_ws || !dK_out || !ws)
+    return RECSA_E_INVALID;
+  if (!queries_fit(tree, T)) return RECSA_E_INVALID;
+  const int64_t nq = static_cast<int64_t>(tree->B) * T;
+  const WsLayout w = ws_layout(*tree, Hq, nq);
+  if (select_ws_bytes < static_cast<size_t>(w.total) ||
+      ws_bytes < static_cast<size_t>(kgrad_ws_bytes(*tree, Hq, nq)))
+    return RECSA_E_WORKSPACE;
+  if (tree->n_levels < 2) return RECSA_OK;
+  const float* logits = reinterpret_cast<const float*>(static_cast<const char*>(select_ws) +
+                                                       w.logits_off);
+  return hip_status(launch_kgrad(*tree, q, Hq, T, pos_dev, sel_idx, sel_cnt, importance, teacher,
+                                 logits, dK_out, ws, static_cast<hipStream_t>(stream)));
+}
+
 // ---- pooler backward
 
 static bool grad_ok(const recsa_pooler_grad* g) {

@@ -117,6 +117,14 @@ int64_t shift_ws_bytes(const recsa_tree& tr);
 hipError_t launch_shift_penalty(const recsa_tree& tr, const recsa_pooler& P, int64_t tok_end,
                                 float* out, void* ws, hipStream_t s);
 
+// Gradient of the Eq. 6 terms with respect to the node keys
+int64_t kgrad_ws_bytes(const recsa_tree& tr, int Hq, int64_t n_queries);
+int64_t kgrad_out_floats(const recsa_tree& tr);
+hipError_t launch_kgrad(const recsa_tree& tr, const void* q, int Hq, int T, const int64_t* pos,
+                        const int32_t* sel, const int32_t* cnt, const float* imp,
+                        const float* teacher, const float* logits, float* dK, void* ws,
+                        hipStream_t s);
+
 // Pooler backward (Eq. 5 VJP)
 int64_t pool_bwd_ws_bytes(const recsa_tree& tr, const recsa_pooler& P, int level);
 hipError_t launch_pool_backward(const recsa_tree& tr, const recsa_pooler& P, int level,

@@ -33,6 +33,7 @@ EXPORTS = (
     "recsa_attn_prefill", "recsa_decode", "recsa_distill_workspace_bytes",
     "recsa_distill_kl", "recsa_shift_workspace_bytes", "recsa_shift_penalty",
     "recsa_pooler_backward_workspace_bytes", "recsa_pooler_backward",
+    "recsa_distill_key_grad_workspace_bytes", "recsa_distill_key_grad",
 )
 
 
@@ -101,6 +102,9 @@ def lib():
             "recsa_shift_workspace_bytes": (sz, [T]),
             "recsa_shift_penalty": (ctypes.c_int, [T, P, i64, vp, vp, sz, vp]),
             "recsa_pooler_backward_workspace_bytes": (sz, [T, P, i32]),
+            "recsa_distill_key_grad_workspace_bytes": (sz, [T, i32, i64]),
+            "recsa_distill_key_grad": (ctypes.c_int, [T, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz,
+                                                       vp, vp, sz, vp]),
             "recsa_pooler_backward": (ctypes.c_int, [T, P, i32, i64, vp, vp, ctypes.c_float,
                                                       ctypes.POINTER(PoolerGradC), vp, sz, vp]),
         }
@@ -378,6 +382,36 @@ def recsa_pooler_backward_workspace_bytes(tree, pooler, level: int) -> int:
     tc, pc = _tc(tree), _pc(pooler)
     return int(lib().recsa_pooler_backward_workspace_bytes(ctypes.byref(tc), ctypes.byref(pc),
                                                            level))
+
+
+def recsa_distill_key_grad_workspace_bytes(tree, Hq: int, n_queries: int) -> int:
+    tc = _tc(tree)
+    return int(lib().recsa_distill_key_grad_workspace_bytes(ctypes.byref(tc), Hq, n_queries))
+
+
+def key_grad_buffer(tree):
+    """Zeroed float32 buffer for recsa_distill_key_grad's output and the
+    per-level views [B, Hkv, rows_l, d] into it (level l at index l - 1)."""
+    sizes = [tree.B * tree.Hkv * recsa_level_rows(tree.L_cap, tree.C, l) * tree.d
+             for l in range(1, tree.n_levels)]
+    buf = torch.zeros(max(sum(sizes), 1), dtype=torch.float32, device=tree.rope.device)
+    views, off = [], 0
+    for l, n in zip(range(1, tree.n_levels), sizes):
+        views.append(buf[off:off + n].view(tree.B, tree.Hkv, -1, tree.d))
+        off += n
+    return buf, views
+
+
+def recsa_distill_key_grad(tree, q, Hq: int, T: int, pos_dev, sel_idx, sel_cnt, importance,
+                           teacher, select_ws, dK_out, ws, ws_bytes: int | None = None,
+                           stream=None):
+    tc = _tc(tree)
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    sb = select_ws.numel() * select_ws.element_size()
+    _check("recsa_distill_key_grad", lib().recsa_distill_key_grad(
+        ctypes.byref(tc), _ptr(q), Hq, T, _ptr(pos_dev), _ptr(sel_idx), _ptr(sel_cnt),
+        _ptr(importance), _ptr(teacher), _ptr(select_ws), sb, _ptr(dK_out), _ptr(ws), nb,
+        _stream(stream)))
 
 
 def pooler_grad_buffers(pooler) -> dict:

@@ -539,7 +539,7 @@ def shift_penalty_dm(X, P: Pooler):
 
 
 def kl_key_grad(qG, t: int, tr: WalkTrace, K0, C: int, theta: float, cos=None, sin=None,
-                dtype: str = "f32", exact: bool = False):
+                dtype: str = "f32", exact: bool = False, magnitude: bool = False):
     """Gradient of one query's Eq. 6 terms, sum over scored levels of
     KL(y^(l) || pi^(l)), with respect to the stored key of every non-current
     candidate: {level: (nodes [n], dK [n, d])}.
@@ -550,7 +550,10 @@ def kl_key_grad(qG, t: int, tr: WalkTrace, K0, C: int, theta: float, cos=None, s
         d KL / d s_h,e = -(P_h,e / G) (r_e - sum_f r_f P_h,f),
     and s_h,e = q~_h . k~_e / sqrt(d) gives d s / d K_e = R(c_e)^T q~_h / sqrt(d)
     in the split form (the operand roundings taken as the identity, the same
-    float32 table entries), or R(p_q - p_e) q_h / sqrt(d) in exact mode."""
+    float32 table entries), or R(p_q - p_e) q_h / sqrt(d) in exact mode.
+    With magnitude, each term is replaced by its size without cancellation,
+    (P_h,e / G)(|r_e| + |sum_f r_f P_h,f|) |R^T q~_h| / sqrt(d), which bounds
+    how far a computation with relative error eps per input can move it."""
     ys = distill_targets(qG, t, tr, K0, C, theta)
     qG = np.asarray(qG, dtype=np.float64)
     G, d = qG.shape
@@ -564,7 +567,10 @@ def kl_key_grad(qG, t: int, tr: WalkTrace, K0, C: int, theta: float, cos=None, s
         P = np.exp(s - s.max(axis=1, keepdims=True))
         P = P / P.sum(axis=1, keepdims=True)
         r = y / P.mean(axis=0)
-        coef = -(P / G) * (r[None, :] - (P * r[None, :]).sum(axis=1, keepdims=True))
+        S = (P * r[None, :]).sum(axis=1, keepdims=True)
+        coef = -(P / G) * (r[None, :] - S)
+        if magnitude:
+            coef = (P / G) * (np.abs(r[None, :]) + np.abs(S))
         p_q = len(lt.A) - 1
         pos_e = np.arange(n)
         if exact:
@@ -582,5 +588,7 @@ def kl_key_grad(qG, t: int, tr: WalkTrace, K0, C: int, theta: float, cos=None, s
             ss = sin[c_e].astype(np.float64)[None]
             x, yv = qt[..., :h], qt[..., h:]
             qrot = np.concatenate([x * cc + yv * ss, -x * ss + yv * cc], axis=-1)  # R(c)^T q~
+        if magnitude:
+            qrot = np.abs(qrot)
         out[lvl] = (others, np.einsum("gn,gnd->nd", coef, qrot) / math.sqrt(d))
     return out
