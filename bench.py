@@ -571,9 +571,10 @@ def bench_offload(args):
 def bench_distill(args):
     """Eq. 6 and Eq. 7 on the distillation workload: one step = selection
     with importances for every position of the sequence, the KL terms of
-    every (query, KV head, scored level), the shift penalty of every level
-    and the pooler backward of every level (a seeded key gradient plus the
-    penalty).  Roofline: the teacher's dense logits, 2 d flops per (query head,
+    every (query, KV head, scored level) with the teacher distributions, the
+    shift penalty of every level, the KL's gradient with respect to every
+    node key, and the pooler backward of every level from that gradient plus
+    the penalty.  Roofline: the teacher's dense logits, 2 d flops per (query head,
     key) pair with key <= query, executed as three bf16 matrix products per
     pair (split operands); the whole recsa_distill_kl call is charged, so the
     fraction is a lower bound."""
@@ -609,49 +610,57 @@ def bench_distill(args):
         R.recsa_select(tree, q, Hq, T, pos, sel, cnt, imp, ws)
 
     def distill():
-        R.recsa_distill_kl(tree, q, Hq, T, pos, sel, cnt, imp, wl.theta, kl, dws)
+        R.recsa_distill_kl(tree, q, Hq, T, pos, sel, cnt, imp, wl.theta, kl, dws,
+                           teacher=teacher)
 
     def shift():
         R.recsa_shift_penalty(tree, pool, L, pen, sws)
 
-    # pooler backward of every level: a seeded key gradient (standing in for
-    # the KL's) plus the shift penalty with weight 1
+    # the KL's gradient with respect to every node key, then the pooler
+    # backward of every level from it plus the shift penalty with weight 1
     levels = range(1, tree.n_levels)
-    dKs = {lv: synth.normal((B, Hkv, R.recsa_level_rows(L, 16, lv), d), dev, wl.seed, 20 + lv)
-           for lv in levels}
+    teacher = torch.empty((B * T, Hkv, tree.n_sel, 16 * wl.k), dtype=torch.float32, device=dev)
+    kws = torch.empty(R.recsa_distill_key_grad_workspace_bytes(tree, Hq, B * T),
+                      dtype=torch.uint8, device=dev)
+    kbuf, dKs = R.key_grad_buffer(tree)
     bws = {lv: torch.empty(R.recsa_pooler_backward_workspace_bytes(tree, pool, lv),
                            dtype=torch.uint8, device=dev) for lv in levels}
     grads = {lv: R.pooler_grad_buffers(pool) for lv in levels}
 
+    def key_grad():
+        R.recsa_distill_key_grad(tree, q, Hq, T, pos, sel, cnt, imp, teacher, ws, kbuf, kws)
+
     def backward():
         for lv in levels:
-            R.recsa_pooler_backward(tree, pool, lv, L, dKs[lv], pen[lv - 1], 1.0, grads[lv],
+            R.recsa_pooler_backward(tree, pool, lv, L, dKs[lv - 1], pen[lv - 1], 1.0, grads[lv],
                                     bws[lv])
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
-        select(); distill(); shift(); backward()
+        select(); distill(); shift(); key_grad(); backward()
     torch.cuda.synchronize()
-    evs = [tuple(ev() for _ in range(5)) for _ in range(args.steps)]
+    evs = [tuple(ev() for _ in range(6)) for _ in range(args.steps)]
     w0 = time.perf_counter()
-    for e0, e1, e2, e3, e4 in evs:
+    for e0, e1, e2, e3, e4, e5 in evs:
         e0.record(); select(); e1.record(); distill(); e2.record(); shift(); e3.record()
-        backward(); e4.record()
+        key_grad(); e4.record(); backward(); e5.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     med = lambda xs: sorted(xs)[len(xs) // 2]
     sel_ms = med([x[0].elapsed_time(x[1]) for x in evs])
     kl_ms = med([x[1].elapsed_time(x[2]) for x in evs])
     sh_ms = med([x[2].elapsed_time(x[3]) for x in evs])
-    bw_ms = med([x[3].elapsed_time(x[4]) for x in evs])
-    step_ms = med([x[0].elapsed_time(x[4]) for x in evs])
+    kg_ms = med([x[3].elapsed_time(x[4]) for x in evs])
+    bw_ms = med([x[4].elapsed_time(x[5]) for x in evs])
+    step_ms = med([x[0].elapsed_time(x[5]) for x in evs])
     pairs = sum(int(t) + 1 for t in range(T)) * B          # (query, key <= query) pairs
     flops = 2.0 * d * Hq * pairs
     tflops = flops / (kl_ms * 1e-3) / 1e12
     klv = kl.cpu().numpy()
     result = {
-        "metric": "RecSA pooler distillation step (Eq. 6 over every position + Eq. 7 + "
-                  "pooler backward of every level) at the 32K training length; ms per layer",
+        "metric": "RecSA pooler distillation step (Eq. 6 over every position + Eq. 7, the KL's "
+                  "key gradient and the pooler backward of every level) at the 32K training "
+                  "length; ms per layer",
         "value": round(step_ms, 3), "unit": "ms/layer-step", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 3),
@@ -661,7 +670,8 @@ def bench_distill(args):
                                f"{wl.dtype}, L={L}, C=16, k={wl.k}; every position a query",
                    "seq_len": L, "global_batch": B},
         "split_ms": {"select_with_importance": round(sel_ms, 3), "distill_kl": round(kl_ms, 3),
-                     "shift_penalty": round(sh_ms, 3), "pooler_backward_all_levels": round(bw_ms, 3)},
+                     "shift_penalty": round(sh_ms, 3), "kl_key_grad": round(kg_ms, 3),
+                     "pooler_backward_all_levels": round(bw_ms, 3)},
         "queries_per_s": round(B * T / (step_ms * 1e-3), 1),
         "roofline": {"kernel": "recsa_distill_kl (absolute RoPE table + teacher_lse_kernel + "
                                "distill_kl_kernel), charged whole",

@@ -14,11 +14,12 @@
 //
 // kgrad_coef_kernel   per (query, KV head, scored level): the coefficients
 //                     d KL / d s_h,e from the selection logits, pi and y.
-// kgrad_accum_kernel  per (sequence, KV head, level, parent node w): walks the
-//                     sequence's queries in order, finds w among each query's
-//                     parents, and accumulates coefficient x rotated query for
-//                     w's 16 children; then R(c)^T / sqrt(d) and the rows out.
-//                     Fixed order: identical bits on every call.
+// kgrad_accum_kernel  per (sequence, KV head, level, parent node w, chunk of
+//                     2048 queries): walks the chunk's queries in order, finds
+//                     w among each query's parents, and accumulates coefficient
+//                     x rotated query for w's 16 children.
+// kgrad_finish_kernel per parent: the chunks in order, R(c)^T / sqrt(d), the
+//                     rows out.  Fixed orders: identical bits on every call.
 #include <math.h>
 
 #include <algorithm>
@@ -31,6 +32,7 @@ namespace recsa {
 namespace {
 
 constexpr int kKgMatch = 8;        // matched queries per accumulation step
+constexpr int kKgChunk = 2048;     // queries per accumulation workgroup
 
 __device__ __forceinline__ float kg_block_max(float v, float* red) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
@@ -107,24 +109,27 @@ __global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
   }
 }
 
-// One workgroup per parent node w of level l (children 16w .. 16w+15) of one
-// (sequence, KV head).  Thread (child c = tid / 16, dims DPT*(tid % 16) ...)
-// owns DPT accumulators.
+// One workgroup per (parent node w of level l, chunk of kKgChunk queries) of
+// one (sequence, KV head): the sum over the chunk's queries, in order, for
+// w's children 16w .. 16w+15, before R(c)^T, into part[head][w][chunk][16][D].
+// Thread (child c = tid / 16, dims DPT*(tid % 16) ...) owns DPT accumulators.
 template <int DT, int D, int G>
 __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
     recsa_tree tr, const void* qv, int Hq, int T, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
-    const float* __restrict__ coef, int level, float* __restrict__ dK) {
+    const float* __restrict__ coef, int level, int n_chunks, float* __restrict__ part) {
   using Ty = typename Stor<DT>::T;
   constexpr int H2 = D / 2;
   constexpr int DPT = D / 16;
   __shared__ float qt[kKgMatch][G][D];
   __shared__ float cf[kKgMatch][G][kC];
-  __shared__ float acc_s[kC][D];
   __shared__ int m_qi[kBlock], m_rho[kBlock], m_nv[kBlock], m_phi[kBlock];
   __shared__ int red_i[kBlock / kWave];
-  const int64_t w = blockIdx.x;
+  const int64_t w = blockIdx.x / n_chunks;
+  const int chunk = static_cast<int>(blockIdx.x % n_chunks);
   const int j = blockIdx.y, b = blockIdx.z;
+  const int64_t q_lo = static_cast<int64_t>(b) * T + static_cast<int64_t>(chunk) * kKgChunk;
+  const int64_t q_hi = min(q_lo + kKgChunk, static_cast<int64_t>(b + 1) * T);
   const int tid = threadIdx.x;
   const int n_sel = tr.n_levels - 1, k = tr.k, CK = kC * k, top = tr.n_levels - 1;
   const int c_own = tid / 16, d0 = DPT * (tid % 16);
@@ -132,12 +137,11 @@ __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
 #pragma unroll
   for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
 
-  for (int64_t q0 = static_cast<int64_t>(b) * T; q0 < static_cast<int64_t>(b + 1) * T;
-       q0 += kBlock) {
+  for (int64_t q0 = q_lo; q0 < q_hi; q0 += kBlock) {
     // ---- which queries of this batch hold w among their level-l parents
     const int64_t qi = q0 + tid;
     int rho = -1, nv = 0, phi = 0;
-    if (qi < static_cast<int64_t>(b + 1) * T) {
+    if (qi < q_hi) {
       const int64_t slot = qi * tr.Hkv + j;
       const int64_t t = pos[qi];
       const ListView lv = list_view(t, level, top, k, sel + slot * n_sel * k, cnt + slot * n_sel);
@@ -217,28 +221,61 @@ __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
       __syncthreads();
     }
   }
-  // ---- R(c)^T / sqrt(d) and the child rows out
+  const int64_t n_par = gridDim.x / n_chunks;
+  float* pp = part + (((static_cast<int64_t>(b) * tr.Hkv + j) * n_par + w) * n_chunks + chunk) *
+                         (kC * D);
 #pragma unroll
-  for (int e = 0; e < DPT; ++e) acc_s[c_own][d0 + e] = acc[e];
-  __syncthreads();
+  for (int e = 0; e < DPT; ++e) pp[c_own * D + d0 + e] = acc[e];
+}
+
+// Per parent node: the chunks' sums in chunk order, then R(c)^T / sqrt(d) and
+// the child rows out (every child row below rows_l, zero when no query scores
+// it).
+template <int D>
+__global__ void __launch_bounds__(kBlock) kgrad_finish_kernel(recsa_tree tr, int level,
+                                                              int n_chunks,
+                                                              const float* __restrict__ part,
+                                                              float* __restrict__ dK) {
+  constexpr int H2 = D / 2;
+  const int64_t w = blockIdx.x, n_par = gridDim.x;
+  const int j = blockIdx.y, b = blockIdx.z;
   const int64_t rows_l = level_rows_dev(tr.L_cap, level);
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const float* pp = part + ((static_cast<int64_t>(b) * tr.Hkv + j) * n_par + w) * n_chunks *
+                               (kC * D);
   float* out = dK + (static_cast<int64_t>(b) * tr.Hkv + j) * rows_l * D;
-  for (int item = tid; item < kC * H2; item += kBlock) {
+  for (int item = threadIdx.x; item < kC * H2; item += kBlock) {
     const int c = item / H2, jj = item % H2;
     const int64_t u = kC * w + c;
     if (u >= rows_l) continue;
+    float x = 0.f, y = 0.f;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      x += pp[static_cast<int64_t>(ch) * kC * D + c * D + jj];
+      y += pp[static_cast<int64_t>(ch) * kC * D + c * D + jj + H2];
+    }
     const float* rp = tr.rope + (static_cast<int64_t>(c) * H2 + jj) * 2;
-    const float x = acc_s[c][jj], y = acc_s[c][jj + H2];
     out[u * D + jj] = (x * rp[0] + y * rp[1]) * scale;
     out[u * D + jj + H2] = (-x * rp[1] + y * rp[0]) * scale;
   }
 }
 
 // ------------------------------------------------------------ launchers
-int64_t kgrad_ws_bytes(const recsa_tree& tr, int Hq, int64_t n_queries) {
+// Workspace: the coefficients [n_queries*Hkv][n_sel][G][C*k], then the
+// chunk sums of the largest level, [B*Hkv][parents][chunks][16][d].
+static int64_t kgrad_coef_bytes(const recsa_tree& tr, int Hq, int64_t n_queries) {
   const int n_sel = tr.n_levels > 1 ? tr.n_levels - 1 : 1;
-  return n_queries * tr.Hkv * n_sel * static_cast<int64_t>(Hq / tr.Hkv) * kC * tr.k * 4;
+  return align256(n_queries * tr.Hkv * n_sel * static_cast<int64_t>(Hq / tr.Hkv) * kC * tr.k * 4);
+}
+
+static int64_t kgrad_chunks(const recsa_tree& tr, int64_t n_queries) {
+  const int64_t T = n_queries / tr.B;
+  return (T + kKgChunk - 1) / kKgChunk;
+}
+
+int64_t kgrad_ws_bytes(const recsa_tree& tr, int Hq, int64_t n_queries) {
+  const int64_t parents = (level_rows_host(tr.L_cap, 1) + kC - 1) / kC;   // level 1 is largest
+  return kgrad_coef_bytes(tr, Hq, n_queries) +
+         static_cast<int64_t>(tr.B) * tr.Hkv * parents * kgrad_chunks(tr, n_queries) * kC * tr.d * 4;
 }
 
 int64_t kgrad_out_floats(const recsa_tree& tr) {
@@ -255,6 +292,8 @@ static hipError_t kgrad_impl(const recsa_tree& tr, const void* q, int Hq, int T,
                              float* dK, void* ws, hipStream_t s) {
   float* coef = static_cast<float*>(ws);
   const int64_t nq = static_cast<int64_t>(tr.B) * T;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + kgrad_coef_bytes(tr, Hq, nq));
+  const int n_chunks = static_cast<int>(kgrad_chunks(tr, nq));
   kgrad_coef_kernel<G><<<dim3(static_cast<unsigned>(nq), tr.Hkv), kBlock, 0, s>>>(
       tr, T, pos, sel, cnt, imp, teacher, logits, coef);
   hipError_t e = hipGetLastError();
@@ -263,9 +302,14 @@ static hipError_t kgrad_impl(const recsa_tree& tr, const void* q, int Hq, int T,
   for (int l = 1; l < tr.n_levels; ++l) {
     const int64_t rows = level_rows_host(tr.L_cap, l);
     if (rows > 0) {
-      dim3 grid(static_cast<unsigned>((rows + kC - 1) / kC), tr.Hkv, tr.B);
-      kgrad_accum_kernel<DT, D, G><<<grid, kBlock, 0, s>>>(tr, q, Hq, T, pos, sel, cnt, coef, l,
-                                                           dK + off);
+      const unsigned parents = static_cast<unsigned>((rows + kC - 1) / kC);
+      dim3 ga(parents * n_chunks, tr.Hkv, tr.B);
+      kgrad_accum_kernel<DT, D, G><<<ga, kBlock, 0, s>>>(tr, q, Hq, T, pos, sel, cnt, coef, l,
+                                                         n_chunks, part);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      dim3 gf(parents, tr.Hkv, tr.B);
+      kgrad_finish_kernel<D><<<gf, kBlock, 0, s>>>(tr, l, n_chunks, part, dK + off);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
