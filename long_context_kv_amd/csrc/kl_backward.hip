@@ -14,10 +14,10 @@
 //
 // kgrad_coef_kernel   per (query, KV head, scored level): the coefficients
 //                     d KL / d s_h,e from the selection logits, pi and y.
-// kgrad_accum_kernel  per (sequence, KV head, level, parent node w, chunk of
-//                     2048 queries): walks the chunk's queries in order, finds
-//                     w among each query's parents, and accumulates coefficient
-//                     x rotated query for w's 16 children.
+// kgrad_accum_kernel  per (sequence, KV head, level, chunk of 2048 queries,
+//                     parent node w): walks the chunk's queries in order, finds
+//                     w among each query's parents, and contracts coefficient
+//                     x rotated query for w's 16 children on the matrix cores.
 // kgrad_finish_kernel per parent: the chunks in order, R(c)^T / sqrt(d), the
 //                     rows out.  Fixed orders: identical bits on every call.
 #include <math.h>
@@ -26,6 +26,7 @@
 
 #include "recsa_common.hpp"
 #include "recsa_kernels.hpp"
+#include "recsa_mfma.hpp"
 
 namespace recsa {
 
@@ -34,41 +35,23 @@ namespace {
 constexpr int kKgMatch = 8;        // matched queries per accumulation step
 constexpr int kKgChunk = 2048;     // queries per accumulation workgroup
 
-__device__ __forceinline__ float kg_block_max(float v, float* red) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-  v = wave_max(v);
-  __syncthreads();
-  if (lane == 0) red[wid] = v;
-  __syncthreads();
-  float m = red[0];
-#pragma unroll
-  for (int w = 1; w < kBlock / kWave; ++w) m = fmaxf(m, red[w]);
-  return m;
-}
-__device__ __forceinline__ float kg_block_sum(float v, float* red) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-  v = wave_sum(v);
-  __syncthreads();
-  if (lane == 0) red[wid] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < kBlock / kWave; ++w) s += red[w];
-  return s;
-}
-
 }  // namespace
 
-// coef: [n_queries * Hkv][n_sel][G][C*k], like the selection logits.
+// coef: [n_queries * Hkv][n_sel][G][C*k], like the selection logits.  Per
+// scored level, one pass keeps each head's running (max, sum exp, sum r exp)
+// for the thread's candidates, one block combine gives every head's softmax
+// and sum_f r_f P_h,f, and a second pass writes the coefficients.
 template <int G>
 __global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
     recsa_tree tr, int T, const int64_t* __restrict__ pos, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ cnt, const float* __restrict__ imp,
     const float* __restrict__ teacher, const float* __restrict__ logits,
     float* __restrict__ coef) {
-  __shared__ float red[kBlock / kWave];
+  constexpr int NW = kBlock / kWave;
+  __shared__ float red[3 * G][NW];
   const int64_t qi = blockIdx.x;
   const int j = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wid = tid >> 6;
   const int n_sel = tr.n_levels - 1, k = tr.k, CK = kC * k, top = tr.n_levels - 1;
   const int64_t slot = qi * tr.Hkv + j;
   const int64_t t = pos[qi];
@@ -81,29 +64,77 @@ __global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
     const int64_t base = (slot * n_sel + (l - 1)) * static_cast<int64_t>(CK);
     const float* yv = teacher + base;
     const float* pv = imp + base;
-#pragma unroll 1
+    const float* s = logits + base * G;
+    float* cf = coef + base * G;
+    float mx[G], z[G], w[G];
+#pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float* s = logits + (slot * n_sel + (l - 1)) * static_cast<int64_t>(G) * CK +
-                       static_cast<int64_t>(h) * CK;
-      float m = -INFINITY;
-      for (int p = tid; p < n; p += kBlock) m = fmaxf(m, s[p]);
-      m = kg_block_max(m, red);
-      float z = 0.f;
-      for (int p = tid; p < n; p += kBlock) z += expf(s[p] - m);
-      z = kg_block_sum(z, red);
-      const float inv = 1.0f / z;
-      float sr = 0.f;                                // sum_f r_f P_h,f
-      for (int p = tid; p < n; p += kBlock) {
-        const float r = pv[p] > 0.f ? yv[p] / pv[p] : 0.f;
-        sr += r * (expf(s[p] - m) * inv);
+      mx[h] = -INFINITY;
+      z[h] = 0.f;
+      w[h] = 0.f;
+    }
+    for (int p = tid; p < n; p += kBlock) {
+      const float r = pv[p] > 0.f ? yv[p] / pv[p] : 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float x = s[static_cast<int64_t>(h) * CK + p];
+        if (x > mx[h]) {
+          const float sc = expf(mx[h] - x);
+          z[h] = z[h] * sc + 1.f;
+          w[h] = w[h] * sc + r;
+          mx[h] = x;
+        } else {
+          const float e = expf(x - mx[h]);
+          z[h] += e;
+          w[h] += r * e;
+        }
       }
-      sr = kg_block_sum(sr, red);
-      float* cf = coef + (slot * n_sel + (l - 1)) * static_cast<int64_t>(G) * CK +
-                  static_cast<int64_t>(h) * CK;
-      for (int p = tid; p < n; p += kBlock) {
-        const float r = pv[p] > 0.f ? yv[p] / pv[p] : 0.f;
-        const float P = expf(s[p] - m) * inv;
-        cf[p] = -(P / G) * (r - sr);
+    }
+    // block combine: every head's max, then its rescaled sums
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float v = wave_max(mx[h]);
+      if (lane == 0) red[h][wid] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float m = red[h][0];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) m = fmaxf(m, red[h][q]);
+      const float sc = mx[h] == -INFINITY ? 0.f : expf(mx[h] - m);
+      mx[h] = m;
+      z[h] *= sc;
+      w[h] *= sc;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float zs = wave_sum(z[h]), ws = wave_sum(w[h]);
+      if (lane == 0) {
+        red[G + h][wid] = zs;
+        red[2 * G + h][wid] = ws;
+      }
+    }
+    __syncthreads();
+    float inv[G], sr[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float zs = 0.f, ws = 0.f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        zs += red[G + h][q];
+        ws += red[2 * G + h][q];
+      }
+      inv[h] = 1.0f / zs;
+      sr[h] = ws * inv[h];                           // sum_f r_f P_h,f
+    }
+    __syncthreads();                                 // red is reused by the next level
+    for (int p = tid; p < n; p += kBlock) {
+      const float r = pv[p] > 0.f ? yv[p] / pv[p] : 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float P = expf(s[static_cast<int64_t>(h) * CK + p] - mx[h]) * inv[h];
+        cf[static_cast<int64_t>(h) * CK + p] = -(P / G) * (r - sr[h]);
       }
     }
   }
@@ -112,7 +143,11 @@ __global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
 // One workgroup per (parent node w of level l, chunk of kKgChunk queries) of
 // one (sequence, KV head): the sum over the chunk's queries, in order, for
 // w's children 16w .. 16w+15, before R(c)^T, into part[head][w][chunk][16][D].
-// Thread (child c = tid / 16, dims DPT*(tid % 16) ...) owns DPT accumulators.
+// The chunk is the slow grid index, so the workgroups running together share
+// one chunk's query rows in L2.  Per batch of kKgMatch matched queries the
+// contraction coef[16 children][(m, h)] x q~[(m, h)][D] runs on the fp32
+// matrix cores (v_mfma_f32_16x16x4_f32, exact fp32 products, fp32
+// accumulation); wave wv owns the D/64 column tiles wv*D/64 ...
 template <int DT, int D, int G>
 __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
     recsa_tree tr, const void* qv, int Hq, int T, const int64_t* __restrict__ pos,
@@ -120,22 +155,24 @@ __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
     const float* __restrict__ coef, int level, int n_chunks, float* __restrict__ part) {
   using Ty = typename Stor<DT>::T;
   constexpr int H2 = D / 2;
-  constexpr int DPT = D / 16;
-  __shared__ float qt[kKgMatch][G][D];
-  __shared__ float cf[kKgMatch][G][kC];
+  constexpr int TPW = D / 64;                        // 16-column tiles per wave
+  constexpr int KB = kKgMatch * G;                   // contraction length per batch
+  static_assert(KB % 4 == 0, "batch must fill whole 16x16x4 steps");
+  __shared__ float qt[KB][D];                        // row m*G + h
+  __shared__ float cf[KB][kC];
   __shared__ int m_qi[kBlock], m_rho[kBlock], m_nv[kBlock], m_phi[kBlock];
   __shared__ int red_i[kBlock / kWave];
-  const int64_t w = blockIdx.x / n_chunks;
-  const int chunk = static_cast<int>(blockIdx.x % n_chunks);
+  const int64_t n_par = gridDim.x / n_chunks;
+  const int64_t w = blockIdx.x % n_par;
+  const int chunk = static_cast<int>(blockIdx.x / n_par);
   const int j = blockIdx.y, b = blockIdx.z;
   const int64_t q_lo = static_cast<int64_t>(b) * T + static_cast<int64_t>(chunk) * kKgChunk;
   const int64_t q_hi = min(q_lo + kKgChunk, static_cast<int64_t>(b + 1) * T);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int n_sel = tr.n_levels - 1, k = tr.k, CK = kC * k, top = tr.n_levels - 1;
-  const int c_own = tid / 16, d0 = DPT * (tid % 16);
-  float acc[DPT];
+  f32x4_t acc[TPW];
 #pragma unroll
-  for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+  for (int u = 0; u < TPW; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t q0 = q_lo; q0 < q_hi; q0 += kBlock) {
     // ---- which queries of this batch hold w among their level-l parents
@@ -184,9 +221,10 @@ __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
     // ---- matched queries in order, kKgMatch at a time
     for (int m0 = 0; m0 < total; m0 += kKgMatch) {
       const int mc = min(kKgMatch, total - m0);
-      // rotated, rounded query rows q~ = rnd(R(phi) q_h)
-      for (int item = tid; item < kKgMatch * G * H2; item += kBlock) {
-        const int m = item / (G * H2), h = (item / H2) % G, jj = item % H2;
+      // rotated, rounded query rows q~ = rnd(R(phi) q_h); zero past mc
+      for (int item = tid; item < KB * H2; item += kBlock) {
+        const int row = item / H2, jj = item % H2;
+        const int m = row / G, h = row % G;
         float xo = 0.f, yo = 0.f;
         if (m < mc) {
           const int64_t qq = q0 + m_qi[m0 + m];
@@ -196,36 +234,43 @@ __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
           xo = Stor<DT>::round(xo);
           yo = Stor<DT>::round(yo);
         }
-        qt[m][h][jj] = xo;
-        qt[m][h][jj + H2] = yo;
+        qt[row][jj] = xo;
+        qt[row][jj + H2] = yo;
       }
-      for (int item = tid; item < kKgMatch * G * kC; item += kBlock) {
-        const int m = item / (G * kC), h = (item / kC) % G, c = item % kC;
+      for (int item = tid; item < KB * kC; item += kBlock) {
+        const int row = item / kC, c = item % kC;
+        const int m = row / G, h = row % G;
         float v = 0.f;
         if (m < mc && c < m_nv[m0 + m]) {
           const int64_t slot = (q0 + m_qi[m0 + m]) * tr.Hkv + j;
           v = coef[((slot * n_sel + (level - 1)) * G + h) * static_cast<int64_t>(CK) +
                    kC * m_rho[m0 + m] + c];
         }
-        cf[m][h][c] = v;
+        cf[row][c] = v;
       }
       __syncthreads();
-      for (int m = 0; m < mc; ++m) {
+      // A[child][kk] = cf[kk][child], B[kk][col] = qt[kk][col], kk = 4s + lane/16
+      const int ks = (mc * G + 3) / 4;
+      for (int st = 0; st < ks; ++st) {
+        const int kk = 4 * st + (lane >> 4);
+        const float a = cf[kk][lane & 15];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float a = cf[m][h][c_own];
-#pragma unroll
-          for (int e = 0; e < DPT; ++e) acc[e] += a * qt[m][h][d0 + e];
+        for (int u = 0; u < TPW; ++u) {
+          const float bv = qt[kk][(wv * TPW + u) * 16 + (lane & 15)];
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc[u], 0, 0, 0);
         }
       }
       __syncthreads();
     }
   }
-  const int64_t n_par = gridDim.x / n_chunks;
   float* pp = part + (((static_cast<int64_t>(b) * tr.Hkv + j) * n_par + w) * n_chunks + chunk) *
                          (kC * D);
+  // C[row 4*(lane/16) + r][column lane % 16] of each tile
 #pragma unroll
-  for (int e = 0; e < DPT; ++e) pp[c_own * D + d0 + e] = acc[e];
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      pp[(4 * (lane >> 4) + r) * D + (wv * TPW + u) * 16 + (lane & 15)] = acc[u][r];
 }
 
 // Per parent node: the chunks' sums in chunk order, then R(c)^T / sqrt(d) and
