@@ -32,7 +32,8 @@ namespace recsa {
 
 namespace {
 
-constexpr int kTeacherRows = 64;   // (query, head) rows per teacher workgroup
+constexpr int kTeacherSets = 2;    // 16-row query sets per teacher wave
+constexpr int kTeacherRows = 16 * kTeacherSets * (kBlock / kWave);   // rows per workgroup
 constexpr int kTeacherKeys = 64;   // keys per tile: four level-1 groups
 
 // The G log-sum-exps of one level-1 group (consecutive floats).
@@ -149,6 +150,71 @@ __global__ void __launch_bounds__(kBlock) teacher_keys_kernel(recsa_tree tr,
   *reinterpret_cast<uint4*>(dst + D + H2 + j0) = yl;
 }
 
+// One staged key tile (kTeacherKeys keys = four level-1 groups) against a
+// wave's kTeacherSets sets of 16 query columns: per group, the 16x16 logits of
+// each set on the matrix cores (split products lo.hi + hi.lo + hi.hi; each key
+// fragment read from LDS once for all sets), then per column the group's
+// log-sum-exp, stored in natural-log units.  MASK applies causality (keys
+// after the column's position drop out); without it every key counts.
+template <bool MASK, int D, int G>
+__device__ __forceinline__ void teacher_tile_lse(const uint16_t (*khi)[D + 8],
+                                                 const uint16_t (*klo)[D + 8],
+                                                 const uint4 (*bhi)[D / 32],
+                                                 const uint4 (*blo)[D / 32], int tau0, int tmax,
+                                                 const int* t_col, int col, int hh, float scale2,
+                                                 float* const* lcol) {
+  constexpr int KB = D / 32;
+  constexpr int NS = kTeacherSets;
+  constexpr float kLn2 = 0.69314718055994531f;
+#pragma unroll
+  for (int g = 0; g < kTeacherKeys / kC; ++g) {
+    const int tg = tau0 + kC * g;   // first token of the level-1 group
+    if (MASK && tg > tmax) break;   // uniform
+    f32x4_t acc[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint4 ah = *reinterpret_cast<const uint4*>(&khi[kC * g + col][32 * kb + 8 * hh]);
+      const uint4 al = *reinterpret_cast<const uint4*>(&klo[kC * g + col][32 * kb + 8 * hh]);
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                         __builtin_bit_cast(bf16x8_t, bhi[u][kb]),
+                                                         acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                         __builtin_bit_cast(bf16x8_t, blo[u][kb]),
+                                                         acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                         __builtin_bit_cast(bf16x8_t, bhi[u][kb]),
+                                                         acc[u], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      // keys tg + 4 hh + i against the query of column `col`, base-2 logits
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = acc[u][i] * scale2;
+        if (MASK && tg + 4 * hh + i > t_col[u]) sv[i] = -INFINITY;
+      }
+      float m = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      // exp2(-inf) = 0 drops masked keys; a column with no key left has
+      // m = -inf and stores nothing
+      float e = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e += __builtin_amdgcn_exp2f(sv[i] - m);
+      e += __shfl_xor(e, 16);
+      e += __shfl_xor(e, 32);
+      if (hh == 0 && t_col[u] >= 0 && (!MASK || m != -INFINITY))
+        lcol[u][static_cast<int64_t>(tg >> 4) * G] = (m + __builtin_amdgcn_logf(e)) * kLn2;
+    }
+  }
+}
+
 template <int DT, int D, int G>
 __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, const void* qv,
                                                              int T, const int64_t* __restrict__ pos,
@@ -164,7 +230,7 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
   __shared__ __attribute__((aligned(16))) uint16_t khi[kTeacherKeys][LDK];
   __shared__ __attribute__((aligned(16))) uint16_t klo[kTeacherKeys][LDK];
   __shared__ int st[kTeacherRows];
-  __shared__ int s_tmax;
+  __shared__ int s_tmax, s_tmin;
   const int j = blockIdx.y, b = blockIdx.z;
   // longest query blocks first: causal work grows with the position
   const int q0 = (gridDim.x - 1 - blockIdx.x) * QB;
@@ -178,101 +244,91 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
   }
   __syncthreads();
   if (wid == 0) {
-    const float m = wave_max(static_cast<float>(st[lane]));
-    if (lane == 0) s_tmax = static_cast<int>(m);
+    static_assert(kTeacherRows % kWave == 0, "rows fill whole waves");
+    float m = -1.f, mn = 3.0e7f;
+#pragma unroll
+    for (int r = lane; r < kTeacherRows; r += kWave) {
+      const int t = st[r];
+      m = fmaxf(m, static_cast<float>(t));
+      if (t >= 0) mn = fminf(mn, static_cast<float>(t));
+    }
+    m = wave_max(m);
+    mn = -wave_max(-mn);
+    if (lane == 0) {
+      s_tmax = static_cast<int>(m);
+      s_tmin = static_cast<int>(mn);
+    }
   }
-  // B operand: this wave's 16 query rows R(t) q, split; lane holds column
-  // `col`, dims 32 kb + 8 hh + [0, 8) (both members of each RoPE pair)
-  const int r_col = 16 * wid + col;
-  const int t_col = st[r_col];
-  uint4 bhi[KB], blo[KB];
-  {
+  // B operand: this wave's kTeacherSets x 16 query rows R(t) q, split; lane
+  // holds column `col` of each set, dims 32 kb + 8 hh + [0, 8) (both members
+  // of each RoPE pair)
+  constexpr int NS = kTeacherSets;
+  int t_col[NS];
+  float* lcol[NS];
+  uint4 bhi[NS][KB], blo[NS][KB];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int r_col = 16 * (NS * wid + u) + col;
+    t_col[u] = st[r_col];
     const int qi = min(q0 + r_col / G, T - 1), h = r_col % G;
+    lcol[u] = lse + ((static_cast<int64_t>(b) * T + qi) * tr.Hkv + j) * ng_cap * G + h;
     const Ty* qr =
         static_cast<const Ty*>(qv) + ((static_cast<int64_t>(b) * T + qi) * Hq + j * G + h) * D;
 #pragma unroll
     for (int kb = 0; kb < KB / 2; ++kb) {
       float xo[8], yo[8];
-      if (t_col >= 0) {
-        rotate8_abs<DT, D>(qr, 32 * kb + 8 * hh, arope + static_cast<int64_t>(t_col) * H2 * 2,
-                           xo, yo);
+      if (t_col[u] >= 0) {
+        rotate8_abs<DT, D>(qr, 32 * kb + 8 * hh,
+                           arope + static_cast<int64_t>(t_col[u]) * H2 * 2, xo, yo);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xo[e] = yo[e] = 0.f;
       }
-      split_bf16x8(xo, bhi[kb], blo[kb]);
-      split_bf16x8(yo, bhi[kb + KB / 2], blo[kb + KB / 2]);
+      split_bf16x8(xo, bhi[u][kb], blo[u][kb]);
+      split_bf16x8(yo, bhi[u][kb + KB / 2], blo[u][kb + KB / 2]);
     }
   }
   __syncthreads();
-  const int tmax = s_tmax;
+  const int tmax = s_tmax, tmin = s_tmin;
   if (tmax < 0) return;   // no query in this block (uniform)
-  float* lcol;
-  {
-    const int qi = min(q0 + r_col / G, T - 1);
-    lcol = lse + ((static_cast<int64_t>(b) * T + qi) * tr.Hkv + j) * ng_cap * G + (r_col % G);
-  }
   const uint16_t* ks = ksplit + (static_cast<int64_t>(b) * tr.Hkv + j) * tr.L_cap * 2 * D;
-  const float scale = static_cast<float>(1.0 / sqrt(static_cast<double>(D)));
+  // logits in base-2 units: log2(e) / sqrt(d) folded into the scale, so each
+  // exponential and the final logarithm are single hardware instructions
+  const float scale2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(D)));
   const int kk = tid >> 2, qq = tid & 3;     // the key row and quarter this thread loads
 
+  // the next tile's rows are fetched into registers while this one computes
+  uint4 ph[DQ / 8], pl[DQ / 8];
+  auto fetch = [&](int tau0) {
+    const int tau = tau0 + kk;
+    const uint16_t* src = ks + static_cast<int64_t>(tau) * 2 * D + qq * DQ;
+#pragma unroll
+    for (int c = 0; c < DQ / 8; ++c) {
+      ph[c] = make_uint4(0u, 0u, 0u, 0u);
+      pl[c] = ph[c];
+      if (tau <= tmax) {
+        ph[c] = *reinterpret_cast<const uint4*>(src + 8 * c);
+        pl[c] = *reinterpret_cast<const uint4*>(src + D + 8 * c);
+      }
+    }
+  };
   const int n_tiles = tmax / kTeacherKeys + 1;
+  fetch(0);
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int tau0 = tile * kTeacherKeys;
     __syncthreads();   // the previous tile is read
-    {
-      const int tau = tau0 + kk;
-      const uint16_t* src = ks + static_cast<int64_t>(tau) * 2 * D + qq * DQ;
 #pragma unroll
-      for (int c = 0; c < DQ / 8; ++c) {
-        uint4 hv = make_uint4(0u, 0u, 0u, 0u), lv = hv;
-        if (tau <= tmax) {
-          hv = *reinterpret_cast<const uint4*>(src + 8 * c);
-          lv = *reinterpret_cast<const uint4*>(src + D + 8 * c);
-        }
-        *reinterpret_cast<uint4*>(&khi[kk][qq * DQ + 8 * c]) = hv;
-        *reinterpret_cast<uint4*>(&klo[kk][qq * DQ + 8 * c]) = lv;
-      }
+    for (int c = 0; c < DQ / 8; ++c) {
+      *reinterpret_cast<uint4*>(&khi[kk][qq * DQ + 8 * c]) = ph[c];
+      *reinterpret_cast<uint4*>(&klo[kk][qq * DQ + 8 * c]) = pl[c];
     }
     __syncthreads();
-#pragma unroll
-    for (int g = 0; g < kTeacherKeys / kC; ++g) {
-      const int tg = tau0 + kC * g;   // first token of the level-1 group
-      if (tg > tmax) break;           // uniform
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const uint4 ah = *reinterpret_cast<const uint4*>(&khi[kC * g + col][32 * kb + 8 * hh]);
-        const uint4 al = *reinterpret_cast<const uint4*>(&klo[kC * g + col][32 * kb + 8 * hh]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
-                                                      __builtin_bit_cast(bf16x8_t, bhi[kb]), acc,
-                                                      0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
-                                                      __builtin_bit_cast(bf16x8_t, blo[kb]), acc,
-                                                      0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
-                                                      __builtin_bit_cast(bf16x8_t, bhi[kb]), acc,
-                                                      0, 0, 0);
-      }
-      // keys tg + 4 hh + i against the query of column `col`
-      float sv[4];
-      float m = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[i] = tg + 4 * hh + i <= t_col ? acc[i] * scale : -INFINITY;
-        m = fmaxf(m, sv[i]);
-      }
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      float e = 0.f;
-      if (m != -INFINITY) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e += expf(sv[i] - m);
-      }
-      e += __shfl_xor(e, 16);
-      e += __shfl_xor(e, 32);
-      if (hh == 0 && m != -INFINITY) lcol[static_cast<int64_t>(tg >> 4) * G] = m + logf(e);
-    }
+    if (tile + 1 < n_tiles) fetch(tau0 + kTeacherKeys);
+    // tiles wholly at or before every query of the block need no causal mask
+    if (tau0 + kTeacherKeys - 1 <= tmin)
+      teacher_tile_lse<false, D, G>(khi, klo, bhi, blo, tau0, tmax, t_col, col, hh, scale2, lcol);
+    else
+      teacher_tile_lse<true, D, G>(khi, klo, bhi, blo, tau0, tmax, t_col, col, hh, scale2, lcol);
   }
 }
 

@@ -15,7 +15,7 @@
 // kgrad_coef_kernel   per (query, KV head, scored level): the coefficients
 //                     d KL / d s_h,e from the selection logits, pi and y.
 // kgrad_accum_kernel  per (sequence, KV head, level, chunk of 2048 queries,
-//                     parent node w): walks the chunk's queries in order, finds
+//                     parent node w; XCD-contiguous): walks the chunk's queries in order, finds
 //                     w among each query's parents, and contracts coefficient
 //                     x rotated query for w's 16 children on the matrix cores.
 // kgrad_finish_kernel per parent: the chunks in order, R(c)^T / sqrt(d), the
@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kKgMatch = 8;        // matched queries per accumulation step
 constexpr int kKgChunk = 2048;     // queries per accumulation workgroup
+constexpr int kKgXcds = 8;         // XCDs the workgroups are dealt to
 
 }  // namespace
 
@@ -143,8 +144,8 @@ __global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
 // One workgroup per (parent node w of level l, chunk of kKgChunk queries) of
 // one (sequence, KV head): the sum over the chunk's queries, in order, for
 // w's children 16w .. 16w+15, before R(c)^T, into part[head][w][chunk][16][D].
-// The chunk is the slow grid index, so the workgroups running together share
-// one chunk's query rows in L2.  Per batch of kKgMatch matched queries the
+// Workgroups of one XCD take consecutive (chunk, parent) ids, so those running
+// together share one chunk's query rows in their L2.  Per batch of kKgMatch matched queries the
 // contraction coef[16 children][(m, h)] x q~[(m, h)][D] runs on the fp32
 // matrix cores (v_mfma_f32_16x16x4_f32, exact fp32 products, fp32
 // accumulation); wave wv owns the D/64 column tiles wv*D/64 ...
@@ -152,7 +153,8 @@ template <int DT, int D, int G>
 __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
     recsa_tree tr, const void* qv, int Hq, int T, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
-    const float* __restrict__ coef, int level, int n_chunks, float* __restrict__ part) {
+    const float* __restrict__ coef, int level, int64_t n_par, int n_chunks,
+    float* __restrict__ part) {
   using Ty = typename Stor<DT>::T;
   constexpr int H2 = D / 2;
   constexpr int TPW = D / 64;                        // 16-column tiles per wave
@@ -162,10 +164,21 @@ __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
   __shared__ float cf[KB][kC];
   __shared__ int m_qi[kBlock], m_rho[kBlock], m_nv[kBlock], m_phi[kBlock];
   __shared__ int red_i[kBlock / kWave];
-  const int64_t n_par = gridDim.x / n_chunks;
-  const int64_t w = blockIdx.x % n_par;
-  const int chunk = static_cast<int>(blockIdx.x / n_par);
-  const int j = blockIdx.y, b = blockIdx.z;
+  // The device deals workgroups to its XCDs round-robin; renumber so that
+  // each XCD takes one contiguous run of (chunk, parent) ids and its L2 holds
+  // about one chunk's query rows at a time (placement only: any mapping is
+  // correct).
+  int64_t lin;
+  {
+    const int64_t nb = gridDim.x, bid = blockIdx.x;
+    const int64_t x = bid % kKgXcds, per = nb / kKgXcds, extra = nb % kKgXcds;
+    lin = x * per + min(x, extra) + bid / kKgXcds;
+  }
+  const int64_t w = lin % n_par;
+  lin /= n_par;
+  const int chunk = static_cast<int>(lin % n_chunks);
+  lin /= n_chunks;
+  const int j = static_cast<int>(lin % tr.Hkv), b = static_cast<int>(lin / tr.Hkv);
   const int64_t q_lo = static_cast<int64_t>(b) * T + static_cast<int64_t>(chunk) * kKgChunk;
   const int64_t q_hi = min(q_lo + kKgChunk, static_cast<int64_t>(b + 1) * T);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
@@ -348,9 +361,10 @@ static hipError_t kgrad_impl(const recsa_tree& tr, const void* q, int Hq, int T,
     const int64_t rows = level_rows_host(tr.L_cap, l);
     if (rows > 0) {
       const unsigned parents = static_cast<unsigned>((rows + kC - 1) / kC);
-      dim3 ga(parents * n_chunks, tr.Hkv, tr.B);
-      kgrad_accum_kernel<DT, D, G><<<ga, kBlock, 0, s>>>(tr, q, Hq, T, pos, sel, cnt, coef, l,
-                                                         n_chunks, part);
+      const int64_t n_wg = static_cast<int64_t>(parents) * n_chunks * tr.Hkv * tr.B;
+      if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
+      kgrad_accum_kernel<DT, D, G><<<dim3(static_cast<unsigned>(n_wg)), kBlock, 0, s>>>(
+          tr, q, Hq, T, pos, sel, cnt, coef, l, parents, n_chunks, part);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       dim3 gf(parents, tr.Hkv, tr.B);
