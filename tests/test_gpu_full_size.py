@@ -155,8 +155,9 @@ def test_distill_32k_bench_configuration_sampled_vs_oracle():
     32768-token tree at k = 64, every position a query (selection with
     importances, Eq. 6 terms), the Eq. 7 penalty over every node, and the
     pooler backward of levels 1 and 2 with the benchmark's seeded key
-    gradients; sampled queries and heads against the oracle, the penalty and
-    the gradients over all heads, to the small tests' bars."""
+    gradients, the KL key gradient of every position; sampled queries and
+    heads against the oracle, the penalty and the pooler gradients over all
+    heads, to the small tests' bars."""
     _need_gpu()
     import bench
     from oracle import recsa_oracle as O
@@ -199,3 +200,24 @@ def test_distill_32k_bench_configuration_sampled_vs_oracle():
         gg = TB.gpu_backward(tree, pool, lv, L, dK, 1.0)
         TB.compare(gg, TB.oracle_backward(tree, pdict, lv, L, dK, 1.0),
                    1e-3 if lv > 1 else 1e-4)
+    # KL key gradient: every position in one launch, as the benchmark runs it
+    # (finite, identical bits on a second call, nothing at the top level,
+    # whose list never exceeds k); the sampled queries alone against the
+    # oracle (the gradient is a sum over queries)
+    from tests import test_gpu_kl_backward as TK
+    print("distill 32K: KL key gradient, every position", flush=True)
+    _, _, _, full = TK.run_key_grad(tree, q, Hq, pos)
+    for l, v in enumerate(full):
+        assert np.all(np.isfinite(v)), l + 1
+    assert np.all(full[-1] == 0.0) and np.any(full[0] != 0.0)
+    print(f"distill 32K: KL key gradient of queries {idx} one at a time vs oracle, KV heads 0, 5",
+          flush=True)
+    n_cmp, n_scored = 0, 0
+    for i in idx:
+        qs, ps = q[:, [i]].contiguous(), pos[:, [i]].contiguous()
+        sel_s, cnt_s, imp_s, dKs = TK.run_key_grad(tree, qs, Hq, ps)
+        c, sc = TK.compare_with_oracle(tree, pdict, qs, ps.cpu(), sel_s, cnt_s, imp_s, dKs, (0, 5),
+                                       TK.tolerance(2e-4, 16 * wl.k), strict=False)
+        n_cmp += c
+        n_scored += int(sc)
+    assert n_cmp >= 2 * len(idx) - 1 and n_scored >= len(idx) - 2, (n_cmp, n_scored)

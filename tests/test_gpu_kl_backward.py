@@ -71,14 +71,38 @@ def test_key_grad_matches_oracle(dtype, d, tol):
     pos = torch.tensor([TD.positions(L0, T, 91)], dtype=torch.int64, device=DEV)
     T = pos.shape[1]
     sel, cnt, imp, dK = run_key_grad(tree, q, Hq, pos)
+    assert compare_with_oracle(tree, pdict, q, pos, sel, cnt, imp, dK, range(tree.Hkv),
+                               tol) == (tree.Hkv, True)
+
+
+def tolerance(base, n_cand):
+    """The bar for lists of up to n_cand candidates: the small cases' base
+    (lists of at most 256) plus 4 n_cand 2^-24, the worst-case relative error
+    of the four float32 sums over a list (the student softmax's normaliser,
+    the importance's, the teacher mass's renormalisation and sum_f r_f P_f),
+    which grows with the list length."""
+    return base + 4.0 * max(n_cand - 256, 0) * 2.0 ** -24
+
+
+def compare_with_oracle(tree, pdict, q, pos, sel, cnt, imp, dK, heads, tol, strict=True):
+    """The oracle's kl_key_grad summed over the queries of pos (one sequence),
+    per KV head in heads, against dK to the magnitude-scaled bar.  Every walk
+    must match the oracle's selection; with strict=False a head whose walk
+    differs (a near-tie swap) is skipped instead.  Returns the number of
+    heads compared and whether any of them had a scored term."""
+    compared, scored = 0, False
+    k, d, dtype = tree.k, tree.d, tree.dtype
+    Hq = q.shape[2]
+    T = pos.shape[1]
     cos, sin = O.rope_table(d, 16 * k, TD.THETA)
     qn = PY.to64(q)
     G = Hq // tree.Hkv
     rep = PY.WalkReport()
     P = PY.oracle_pooler(pdict)
-    for j in range(tree.Hkv):
-        K0 = PY.to64(tree.K[0][0, j, :L0])
-        V0 = PY.to64(tree.V[0][0, j, :L0])
+    n_tok = int(pos.max()) + 1
+    for j in heads:
+        K0 = PY.to64(tree.K[0][0, j, :n_tok])
+        V0 = PY.to64(tree.V[0][0, j, :n_tok])
         K, _ = O.build_tree(K0, V0, 16, tree.n_levels, P, dtype)
         ref = [np.zeros_like(dK[l][0, j]) for l in range(tree.n_levels - 1)]
         mag = [np.zeros_like(dK[l][0, j]) for l in range(tree.n_levels - 1)]
@@ -88,18 +112,29 @@ def test_key_grad_matches_oracle(dtype, d, tol):
             Kt = ([K[0][: t + 1]] + [K[l][: (t + 1) // 16 ** l] for l in range(1, len(K))])[: max(D, 1)]
             qG = qn[0, ti, j * G:(j + 1) * G]
             tr = O.walk(qG, t, Kt, 16, k, cos, sin, dtype)
-            assert PY.compare_walk(tr, sel[0, ti, j], cnt[0, ti, j], imp[0, ti, j], rep, 1e-5), \
-                (j, t, rep.notes)
+            same = PY.compare_walk(tr, sel[0, ti, j], cnt[0, ti, j], imp[0, ti, j], rep, 1e-5)
+            if not same and not strict:
+                break
+            assert same, (j, t, rep.notes)
             g = O.kl_key_grad(qG, t, tr, K0[: t + 1], 16, TD.THETA, cos, sin, dtype)
             m = O.kl_key_grad(qG, t, tr, K0[: t + 1], 16, TD.THETA, cos, sin, dtype, magnitude=True)
             for lvl, (nodes, v) in g.items():
                 ref[lvl - 1][nodes] += v
                 mag[lvl - 1][nodes] += m[lvl][1]
-        for l in range(tree.n_levels - 1):
-            got = dK[l][0, j]
-            assert np.all(np.isfinite(got)), l
-            untouched = mag[l].max(axis=1) == 0
-            assert np.all(got[untouched] == 0.0), l
-            err = np.abs(got - ref[l])
-            assert np.all(err <= tol * mag[l] + 1e-30), (j, l + 1, float(np.max(err / (mag[l] + 1e-30))))
-        assert any(m_.max() > 0 for m_ in mag)
+        else:
+            _check_head(tree, dK, j, ref, mag, tol)
+            compared += 1
+            scored |= any(m_.max() > 0 for m_ in mag)
+    return compared, scored
+
+
+def _check_head(tree, dK, j, ref, mag, tol):
+    """Rows no query scores exactly 0, the rest within tol of their terms'
+    summed magnitude."""
+    for l in range(tree.n_levels - 1):
+        got = dK[l][0, j]
+        assert np.all(np.isfinite(got)), l
+        untouched = mag[l].max(axis=1) == 0
+        assert np.all(got[untouched] == 0.0), l
+        err = np.abs(got - ref[l])
+        assert np.all(err <= tol * mag[l] + 1e-30), (j, l + 1, float(np.max(err / (mag[l] + 1e-30))))
