@@ -271,7 +271,9 @@ int recsa_shift_penalty(const recsa_tree* tree, const recsa_pooler* pooler,
                         void* stream);
 
 /* Workspace bytes of recsa_distill_key_grad: one float32 coefficient per
- * scored candidate and query head, [B*T][Hkv][n_levels-1][Hq/Hkv][C*k].  0 on
+ * scored candidate and query head, [B*T][Hkv][n_levels-1][Hq/Hkv][C*k]
+ * (rounded up to 256 bytes), then float32 partial sums per chunk of 2048
+ * queries, [B][Hkv][ceil(rows of level 1 / C)][ceil(T/2048)][C][d].  0 on
  * invalid arguments. */
 size_t recsa_distill_key_grad_workspace_bytes(const recsa_tree* tree, int32_t Hq,
                                               int64_t n_queries);

@@ -232,3 +232,38 @@ def test_pooler_backward_validates_without_launch():
     a = list(ok)
     a[7] = b(g_missing)
     assert L.recsa_pooler_backward(*a) == R.RECSA_E_INVALID
+
+
+def test_key_grad_validates_without_launch():
+    """recsa_distill_key_grad: workspace size from its documented layout
+    (coefficients, then the per-chunk partial sums of level 1), and bad
+    arguments rejected before any launch."""
+    L = R.lib()
+    b = ctypes.byref
+    t = _tree(k=64, L_cap=32768, n_levels=4)
+    al = lambda x: (x + 255) // 256 * 256
+    nq = 5000
+    need = L.recsa_distill_key_grad_workspace_bytes(b(t), 32, nq)
+    coef = al(nq * 8 * 3 * 4 * 16 * 64 * 4)
+    parents, chunks = 2048 // 16, (nq + 2047) // 2048
+    assert need == coef + 8 * parents * chunks * 16 * 128 * 4
+    assert L.recsa_distill_key_grad_workspace_bytes(b(t), 30, nq) == 0     # Hq % Hkv
+    assert L.recsa_distill_key_grad_workspace_bytes(b(t), 32, 0) == 0
+    sws = L.recsa_workspace_bytes(b(t), 32, nq)
+    ok = [b(t), 0x10, 32, nq, 0x10, 0x10, 0x10, 0x10, 0x10, 0x10, sws, 0x10, 0x10, need, None]
+    for i in (1, 4, 5, 6, 7, 8, 9, 11, 12):                # required pointers
+        a = list(ok)
+        a[i] = None
+        assert L.recsa_distill_key_grad(*a) == R.RECSA_E_INVALID, i
+    a = list(ok)
+    a[3] = 0                                              # T >= 1
+    assert L.recsa_distill_key_grad(*a) == R.RECSA_E_INVALID
+    a = list(ok)
+    a[10] = sws - 1
+    assert L.recsa_distill_key_grad(*a) == R.RECSA_E_WORKSPACE
+    a = list(ok)
+    a[13] = need - 1
+    assert L.recsa_distill_key_grad(*a) == R.RECSA_E_WORKSPACE
+    a = list(ok)
+    a[2] = 24                                             # G = 3
+    assert L.recsa_distill_key_grad(*a) == R.RECSA_E_UNSUPPORTED
