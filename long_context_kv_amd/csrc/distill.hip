@@ -27,6 +27,7 @@
 #include "recsa_kernels.hpp"
 #include "recsa_mfma.hpp"
 #include "recsa_pool.hpp"
+#include "recsa_rope8.hpp"
 
 namespace recsa {
 
@@ -101,27 +102,6 @@ __device__ __forceinline__ void split_bf16x8(const float* v, uint4& hi, uint4& l
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-// Pairs (j, j + D/2), j in [j0, j0 + 8), of one storage row rotated by the
-// absolute table row `rrow`: outputs xo (dims j) and yo (dims j + D/2).
-template <int DT, int D>
-__device__ __forceinline__ void rotate8_abs(const typename Stor<DT>::T* row, int j0,
-                                            const float* __restrict__ rrow, float* xo, float* yo) {
-  float x[8], y[8];
-  load_vec<DT, 8>(row + j0, x);
-  load_vec<DT, 8>(row + D / 2 + j0, y);
-  float cs[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 v = *reinterpret_cast<const float4*>(rrow + 2 * j0 + 4 * i);
-    cs[4 * i] = v.x;
-    cs[4 * i + 1] = v.y;
-    cs[4 * i + 2] = v.z;
-    cs[4 * i + 3] = v.w;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) rope_pair(x[e], y[e], cs[2 * e], cs[2 * e + 1], xo[e], yo[e]);
-}
-
 // Every level-0 key row rotated at its absolute position and split once:
 // ksplit[b][j][tau] = {hi[D], lo[D]} (bf16), each thread 8 RoPE pairs of one
 // row.  The key tiles of every query block are then plain 16-byte loads.
@@ -139,7 +119,7 @@ __global__ void __launch_bounds__(kBlock) teacher_keys_kernel(recsa_tree tr,
   const int64_t head = static_cast<int64_t>(blockIdx.z) * tr.Hkv + blockIdx.y;
   const Ty* row = static_cast<const Ty*>(tr.K[0]) + (head * tr.L_cap + tau) * D;
   float xo[8], yo[8];
-  rotate8_abs<DT, D>(row, j0, arope + tau * H2 * 2, xo, yo);
+  rotate8_pairs<DT, D>(row, j0, arope + tau * H2 * 2, xo, yo);
   uint4 xh, xl, yh, yl;
   split_bf16x8(xo, xh, xl);
   split_bf16x8(yo, yh, yl);
@@ -278,7 +258,7 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
     for (int kb = 0; kb < KB / 2; ++kb) {
       float xo[8], yo[8];
       if (t_col[u] >= 0) {
-        rotate8_abs<DT, D>(qr, 32 * kb + 8 * hh,
+        rotate8_pairs<DT, D>(qr, 32 * kb + 8 * hh,
                            arope + static_cast<int64_t>(t_col[u]) * H2 * 2, xo, yo);
       } else {
 #pragma unroll

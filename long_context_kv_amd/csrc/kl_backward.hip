@@ -27,6 +27,7 @@
 #include "recsa_common.hpp"
 #include "recsa_kernels.hpp"
 #include "recsa_mfma.hpp"
+#include "recsa_rope8.hpp"
 
 namespace recsa {
 
@@ -160,8 +161,9 @@ __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
   constexpr int TPW = D / 64;                        // 16-column tiles per wave
   constexpr int KB = kKgMatch * G;                   // contraction length per batch
   static_assert(KB % 4 == 0, "batch must fill whole 16x16x4 steps");
-  __shared__ float qt[KB][D];                        // row m*G + h
-  __shared__ float cf[KB][kC];
+  constexpr int P8 = H2 / 8;                         // 8-pair items per query row
+  __shared__ __attribute__((aligned(16))) float qt[KB][D];   // row m*G + h
+  __shared__ __attribute__((aligned(16))) float cf[KB][kC];
   __shared__ int m_qi[kBlock], m_rho[kBlock], m_nv[kBlock], m_phi[kBlock];
   __shared__ int red_i[kBlock / kWave];
   // The device deals workgroups to its XCDs round-robin; renumber so that
@@ -234,32 +236,53 @@ __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
     // ---- matched queries in order, kKgMatch at a time
     for (int m0 = 0; m0 < total; m0 += kKgMatch) {
       const int mc = min(kKgMatch, total - m0);
-      // rotated, rounded query rows q~ = rnd(R(phi) q_h); zero past mc
-      for (int item = tid; item < KB * H2; item += kBlock) {
-        const int row = item / H2, jj = item % H2;
+      // rotated, rounded query rows q~ = rnd(R(phi) q_h), 8 RoPE pairs per
+      // item; zero past mc
+      for (int item = tid; item < KB * P8; item += kBlock) {
+        const int row = item / P8, j0 = 8 * (item % P8);
         const int m = row / G, h = row % G;
-        float xo = 0.f, yo = 0.f;
+        float xo[8], yo[8];
         if (m < mc) {
           const int64_t qq = q0 + m_qi[m0 + m];
           const Ty* qr = static_cast<const Ty*>(qv) + (qq * Hq + static_cast<int64_t>(j) * G + h) * D;
-          const float* rp = tr.rope + (static_cast<int64_t>(m_phi[m0 + m]) * H2 + jj) * 2;
-          rope_pair(Stor<DT>::load(qr + jj), Stor<DT>::load(qr + jj + H2), rp[0], rp[1], xo, yo);
-          xo = Stor<DT>::round(xo);
-          yo = Stor<DT>::round(yo);
+          rotate8_pairs<DT, D>(qr, j0, tr.rope + static_cast<int64_t>(m_phi[m0 + m]) * H2 * 2, xo,
+                               yo);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xo[e] = Stor<DT>::round(xo[e]);
+            yo[e] = Stor<DT>::round(yo[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xo[e] = yo[e] = 0.f;
         }
-        qt[row][jj] = xo;
-        qt[row][jj + H2] = yo;
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+          *reinterpret_cast<float4*>(&qt[row][j0 + e]) =
+              make_float4(xo[e], xo[e + 1], xo[e + 2], xo[e + 3]);
+          *reinterpret_cast<float4*>(&qt[row][H2 + j0 + e]) =
+              make_float4(yo[e], yo[e + 1], yo[e + 2], yo[e + 3]);
+        }
       }
-      for (int item = tid; item < KB * kC; item += kBlock) {
-        const int row = item / kC, c = item % kC;
+      // coefficients, four children per item (the row's 16 slots lie inside
+      // its C*k coefficients; slots past nv are zeroed)
+      for (int item = tid; item < KB * (kC / 4); item += kBlock) {
+        const int row = item / (kC / 4), c0 = 4 * (item % (kC / 4));
         const int m = row / G, h = row % G;
-        float v = 0.f;
-        if (m < mc && c < m_nv[m0 + m]) {
-          const int64_t slot = (q0 + m_qi[m0 + m]) * tr.Hkv + j;
-          v = coef[((slot * n_sel + (level - 1)) * G + h) * static_cast<int64_t>(CK) +
-                   kC * m_rho[m0 + m] + c];
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (m < mc) {
+          const int nvm = m_nv[m0 + m];
+          if (c0 < nvm) {
+            const int64_t slot = (q0 + m_qi[m0 + m]) * tr.Hkv + j;
+            v = *reinterpret_cast<const float4*>(
+                coef + ((slot * n_sel + (level - 1)) * G + h) * static_cast<int64_t>(CK) +
+                kC * m_rho[m0 + m] + c0);
+            if (c0 + 1 >= nvm) v.y = 0.f;
+            if (c0 + 2 >= nvm) v.z = 0.f;
+            if (c0 + 3 >= nvm) v.w = 0.f;
+          }
         }
-        cf[row][c] = v;
+        *reinterpret_cast<float4*>(&cf[row][c0]) = v;
       }
       __syncthreads();
       // A[child][kk] = cf[kk][child], B[kk][col] = qt[kk][col], kk = 4s + lane/16
