@@ -42,6 +42,14 @@
  *   - Importance at a scored level (the pages leave it open) is the mean over
  *     the G query heads of the softmax of s over the non-current candidates;
  *     ties go to the smaller node index.
+ *   - Alignment: arrays of float32 or bf16 values (tree levels, rope, q,
+ *     k_new, v_new, outputs, importances, teacher distributions, gradients,
+ *     pooler weights, workspaces) must be 16-byte aligned, since the kernels
+ *     access them 16 bytes at a time; index arrays need their element's
+ *     alignment, and so do the per-query KL output, one row of the shift
+ *     penalty output and the two scalar gradients.  Every HIP or torch
+ *     allocation, and every whole-row slice of one, qualifies.  Otherwise the
+ *     call returns RECSA_E_INVALID.
  *   - Return value: RECSA_OK or a negative status.  Arguments are validated
  *     before anything is launched; on an error nothing is launched.
  *     RECSA_E_HIP reports a failed launch (hipGetLastError).

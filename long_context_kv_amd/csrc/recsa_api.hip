@@ -2,6 +2,7 @@
 // Nothing is launched when validation fails; no call allocates, frees or
 // synchronises, so every call can be captured into a HIP graph.
 #include <math.h>
+#include <stdint.h>
 
 #include "recsa_common.hpp"
 #include "recsa_kernels.hpp"
@@ -9,6 +10,14 @@
 using namespace recsa;
 
 namespace {
+
+// Arrays of float32 or bf16 values are read and written with 16-byte vector
+// accesses, so they must be 16-byte aligned (HIP and torch allocations are
+// 256-byte aligned, and so is every whole-row slice of them); index arrays
+// need their element's alignment.  NULL passes: presence is checked apart.
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool a8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+bool a4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool tree_ok(const recsa_tree* t, int* why) {
   *why = RECSA_E_INVALID;
@@ -24,9 +33,10 @@ bool tree_ok(const recsa_tree* t, int* why) {
   }
   if (t->L_cap > (int64_t{1} << 40)) return false;
   if (t->n_levels < recsa_levels_needed(t->L_cap, t->C, t->k)) return false;
-  if (!t->rope) return false;
+  if (!t->rope || !a16(t->rope)) return false;
   for (int l = 0; l < t->n_levels; ++l) {
     if (level_rows_host(t->L_cap, l) > 0 && (!t->K[l] || !t->V[l] || !t->Kr[l])) return false;
+    if (!a16(t->K[l]) || !a16(t->V[l]) || !a16(t->Kr[l])) return false;
   }
   return true;
 }
@@ -35,6 +45,7 @@ bool pooler_ok(const recsa_pooler* p, const recsa_tree* t) {
   if (!p) return false;
   if (p->d != t->d || p->hidden < 16 || p->hidden > 256 || p->hidden % 16 != 0) return false;
   if (!p->w || !p->W1 || !p->b1 || !p->W2) return false;
+  if (!a16(p->w) || !a16(p->W1) || !a16(p->b1) || !a16(p->W2)) return false;
   if (!isfinite(p->tau) || !isfinite(p->g) || !isfinite(p->eps) || p->eps < 0.f) return false;
   return true;
 }
@@ -91,7 +102,8 @@ int32_t recsa_levels_needed(int64_t L_cap, int32_t C, int32_t k) {
 }
 
 int recsa_init_rope(float* table, int32_t d, int32_t n_pos, double theta, void* stream) {
-  if (!table || d < 2 || d % 2 != 0 || n_pos < 1 || !(theta > 1.0)) return RECSA_E_INVALID;
+  if (!table || !a16(table) || d < 2 || d % 2 != 0 || n_pos < 1 || !(theta > 1.0))
+    return RECSA_E_INVALID;
   return hip_status(launch_rope_table(table, d, n_pos, theta, static_cast<hipStream_t>(stream)));
 }
 
@@ -116,6 +128,7 @@ int recsa_append_decode(const recsa_tree* tree, const recsa_pooler* pooler, cons
   int why;
   if (!tree_ok(tree, &why)) return why;
   if (!pooler_ok(pooler, tree) || !k_new || !v_new || !pos_dev) return RECSA_E_INVALID;
+  if (!a16(k_new) || !a16(v_new) || !a8(pos_dev)) return RECSA_E_INVALID;
   return hip_status(launch_append(*tree, *pooler, k_new, v_new, pos_dev, static_cast<hipStream_t>(stream)));
 }
 
@@ -126,6 +139,9 @@ int recsa_select(const recsa_tree* tree, const void* q, int32_t Hq, int32_t T, c
   if (!tree_ok(tree, &why)) return why;
   if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
   if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !ws) return RECSA_E_INVALID;
+  if (!a16(q) || !a8(pos_dev) || !a4(sel_idx) || !a4(sel_cnt) || !a16(importance_or_null) ||
+      !a16(ws))
+    return RECSA_E_INVALID;
   if (!queries_fit(tree, T)) return RECSA_E_INVALID;
   const WsLayout w = ws_layout(*tree, Hq, static_cast<int64_t>(tree->B) * T);
   if (ws_bytes < static_cast<size_t>(w.total)) return RECSA_E_WORKSPACE;
@@ -141,6 +157,8 @@ static int attn_common(const recsa_tree* tree, const void* q, int32_t Hq, int32_
   if (!tree_ok(tree, &why)) return why;
   if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
   if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !out || !ws) return RECSA_E_INVALID;
+  if (!a16(q) || !a8(pos_dev) || !a4(sel_idx) || !a4(sel_cnt) || !a16(out) || !a16(ws))
+    return RECSA_E_INVALID;
   if (!queries_fit(tree, T)) return RECSA_E_INVALID;
   const WsLayout w = ws_layout(*tree, Hq, static_cast<int64_t>(tree->B) * T);
   if (ws_bytes < static_cast<size_t>(w.total)) return RECSA_E_WORKSPACE;
@@ -169,6 +187,9 @@ int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler, const void*
   if (!pooler_ok(pooler, tree)) return RECSA_E_INVALID;
   if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
   if (!k_new || !v_new || !q || !pos_dev || !sel_idx || !sel_cnt || !out || !ws)
+    return RECSA_E_INVALID;
+  if (!a16(k_new) || !a16(v_new) || !a16(q) || !a8(pos_dev) || !a4(sel_idx) || !a4(sel_cnt) ||
+      !a16(out) || !a16(ws))
     return RECSA_E_INVALID;
   const WsLayout w = ws_layout(*tree, Hq, tree->B);
   if (ws_bytes < static_cast<size_t>(w.total)) return RECSA_E_WORKSPACE;
@@ -200,6 +221,9 @@ int recsa_distill_kl(const recsa_tree* tree, const void* q, int32_t Hq, int32_t 
   if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
   if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !importance || !kl_out || !ws)
     return RECSA_E_INVALID;
+  if (!a16(q) || !a8(pos_dev) || !a4(sel_idx) || !a4(sel_cnt) || !a16(importance) ||
+      !a4(kl_out) || !a16(teacher_or_null) || !a16(ws))
+    return RECSA_E_INVALID;
   if (!(theta > 1.0) || !queries_fit(tree, T)) return RECSA_E_INVALID;
   if (!distill_fits(tree)) return RECSA_E_UNSUPPORTED;
   if (ws_bytes < static_cast<size_t>(distill_ws_bytes(*tree, Hq, static_cast<int64_t>(tree->B) * T)))
@@ -224,7 +248,7 @@ int recsa_shift_penalty(const recsa_tree* tree, const recsa_pooler* pooler, int6
                         float* out, void* ws, size_t ws_bytes, void* stream) {
   int why;
   if (!tree_ok(tree, &why)) return why;
-  if (!pooler_ok(pooler, tree) || !out || !ws) return RECSA_E_INVALID;
+  if (!pooler_ok(pooler, tree) || !out || !ws || !a16(out) || !a16(ws)) return RECSA_E_INVALID;
   if (tok_end < 1 || tok_end > tree->L_cap) return RECSA_E_INVALID;
   if (!shift_fits(tree)) return RECSA_E_UNSUPPORTED;
   if (ws_bytes < static_cast<size_t>(shift_ws_bytes(*tree))) return RECSA_E_WORKSPACE;
@@ -254,6 +278,9 @@ int recsa_distill_key_grad(const recsa_tree* tree, const void* q, int32_t Hq, in
   if (!q || T < 1 || !pos_dev || !sel_idx || !sel_cnt || !importance || !teacher ||
       !select_ws || !dK_out || !ws)
     return RECSA_E_INVALID;
+  if (!a16(q) || !a8(pos_dev) || !a4(sel_idx) || !a4(sel_cnt) || !a16(importance) ||
+      !a16(teacher) || !a16(select_ws) || !a16(dK_out) || !a16(ws))
+    return RECSA_E_INVALID;
   if (!queries_fit(tree, T)) return RECSA_E_INVALID;
   const int64_t nq = static_cast<int64_t>(tree->B) * T;
   const WsLayout w = ws_layout(*tree, Hq, nq);
@@ -270,7 +297,8 @@ int recsa_distill_key_grad(const recsa_tree* tree, const void* q, int32_t Hq, in
 // ---- pooler backward
 
 static bool grad_ok(const recsa_pooler_grad* g) {
-  return g && g->w && g->W1 && g->b1 && g->W2 && g->tau && g->g;
+  return g && g->w && g->W1 && g->b1 && g->W2 && g->tau && g->g && a16(g->w) && a16(g->W1) &&
+         a16(g->b1) && a16(g->W2) && a4(g->tau) && a4(g->g);
 }
 
 size_t recsa_pooler_backward_workspace_bytes(const recsa_tree* tree, const recsa_pooler* pooler,
@@ -288,6 +316,7 @@ int recsa_pooler_backward(const recsa_tree* tree, const recsa_pooler* pooler, in
   int why;
   if (!tree_ok(tree, &why)) return why;
   if (!pooler_ok(pooler, tree) || !grad_ok(grad) || !ws) return RECSA_E_INVALID;
+  if (!a16(dK) || !a4(shift_sums) || !a16(ws)) return RECSA_E_INVALID;
   if (level < 1 || level >= tree->n_levels) return RECSA_E_INVALID;
   if (tok_end < 1 || tok_end > tree->L_cap || !isfinite(shift_weight)) return RECSA_E_INVALID;
   if (!shift_fits(tree)) return RECSA_E_UNSUPPORTED;

@@ -267,3 +267,26 @@ def test_key_grad_validates_without_launch():
     a = list(ok)
     a[2] = 24                                             # G = 3
     assert L.recsa_distill_key_grad(*a) == R.RECSA_E_UNSUPPORTED
+
+
+def test_misaligned_arrays_are_rejected_without_launch():
+    """Float and bf16 arrays must be 16-byte aligned, index arrays naturally
+    aligned; a misaligned pointer is RECSA_E_INVALID before any launch."""
+    L = R.lib()
+    b = ctypes.byref
+    t = _tree()
+    need = L.recsa_workspace_bytes(b(t), 32, 1)
+    ok = [b(t), 0x10, 32, 1, 0x10, 0x10, 0x10, None, 0x100, need, None]
+    for i, bad in ((1, 0x18), (4, 0x14), (5, 0x12), (6, 0x11), (8, 0x108)):
+        a = list(ok)
+        a[i] = bad
+        assert L.recsa_select(*a) == R.RECSA_E_INVALID, (i, bad)
+    a = list(ok)
+    a[7] = 0x24                                           # importance: 16-byte
+    assert L.recsa_select(*a) == R.RECSA_E_INVALID
+    mis = _tree()
+    mis.Kr[1] = 0x5008
+    assert L.recsa_workspace_bytes(b(mis), 32, 1) == 0
+    p = _pooler(W1=0x4004)
+    assert L.recsa_build_tree(b(t), b(p), 0, 16, None) == R.RECSA_E_INVALID
+    assert L.recsa_init_rope(0x3004, 128, 16, 1e6, None) == R.RECSA_E_INVALID
