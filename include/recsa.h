@@ -278,8 +278,8 @@ int recsa_shift_penalty(const recsa_tree* tree, const recsa_pooler* pooler,
                         int64_t tok_end, float* out, void* ws, size_t ws_bytes,
                         void* stream);
 
-/* Workspace bytes of recsa_distill_key_grad: one float32 coefficient per
- * scored candidate and query head, [B*T][Hkv][n_levels-1][Hq/Hkv][C*k]
+/* Workspace bytes of recsa_distill_key_grad: each query head's softmax
+ * figures at each level, four float32 per [B*T][Hkv][n_levels-1][Hq/Hkv]
  * (rounded up to 256 bytes), then float32 partial sums per chunk of 2048
  * queries, [B][Hkv][ceil(rows of level 1 / C)][ceil(T/2048)][C][d].  0 on
  * invalid arguments. */

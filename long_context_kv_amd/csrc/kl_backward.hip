@@ -12,12 +12,14 @@
 // as the forward scoring forms it).  Each key collects these terms over every
 // (query, head) whose list holds it as a non-current candidate.
 //
-// kgrad_coef_kernel   per (query, KV head, scored level): the coefficients
-//                     d KL / d s_h,e from the selection logits, pi and y.
+// kgrad_stats_kernel  per (query, KV head, scored level): each head's softmax
+//                     figures (max, 1/Z, sum_f r_f P_h,f) from the selection
+//                     logits, pi and y.
 // kgrad_accum_kernel  per (sequence, KV head, level, chunk of 2048 queries,
 //                     parent node w; XCD-contiguous): walks the chunk's queries in order, finds
-//                     w among each query's parents, and contracts coefficient
-//                     x rotated query for w's 16 children on the matrix cores.
+//                     w among each query's parents, forms their coefficients
+//                     for w's 16 children, and contracts coefficient x rotated
+//                     query on the matrix cores.
 // kgrad_finish_kernel per parent: the chunks in order, R(c)^T / sqrt(d), the
 //                     rows out.  Fixed orders: identical bits on every call.
 #include <math.h>
@@ -39,16 +41,17 @@ constexpr int kKgXcds = 8;         // XCDs the workgroups are dealt to
 
 }  // namespace
 
-// coef: [n_queries * Hkv][n_sel][G][C*k], like the selection logits.  Per
-// scored level, one pass keeps each head's running (max, sum exp, sum r exp)
-// for the thread's candidates, one block combine gives every head's softmax
-// and sum_f r_f P_h,f, and a second pass writes the coefficients.
+// stats: [n_queries * Hkv][n_sel][G] of {max, 1/Z, sum_f r_f P_h,f, 0}, the
+// softmax of each head's logits over a scored level's non-current candidates
+// and its r-weighted mean.  One pass keeps each head's running (max, sum exp,
+// sum r exp) for the thread's candidates; one block combine gives every
+// head's figures.  The accumulation forms the coefficients from these.
 template <int G>
-__global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
+__global__ void __launch_bounds__(kBlock) kgrad_stats_kernel(
     recsa_tree tr, int T, const int64_t* __restrict__ pos, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ cnt, const float* __restrict__ imp,
     const float* __restrict__ teacher, const float* __restrict__ logits,
-    float* __restrict__ coef) {
+    float4* __restrict__ stats) {
   constexpr int NW = kBlock / kWave;
   __shared__ float red[3 * G][NW];
   const int64_t qi = blockIdx.x;
@@ -67,7 +70,6 @@ __global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
     const float* yv = teacher + base;
     const float* pv = imp + base;
     const float* s = logits + base * G;
-    float* cf = coef + base * G;
     float mx[G], z[G], w[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -75,18 +77,21 @@ __global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
       z[h] = 0.f;
       w[h] = 0.f;
     }
+    // hardware exp2 and reciprocal (about 1 ulp each), as the accumulation's
+    // coefficient staging uses
+    constexpr float kLog2e = 1.44269504088896341f;
     for (int p = tid; p < n; p += kBlock) {
-      const float r = pv[p] > 0.f ? yv[p] / pv[p] : 0.f;
+      const float r = pv[p] > 0.f ? yv[p] * __builtin_amdgcn_rcpf(pv[p]) : 0.f;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float x = s[static_cast<int64_t>(h) * CK + p];
         if (x > mx[h]) {
-          const float sc = expf(mx[h] - x);
+          const float sc = __builtin_amdgcn_exp2f((mx[h] - x) * kLog2e);
           z[h] = z[h] * sc + 1.f;
           w[h] = w[h] * sc + r;
           mx[h] = x;
         } else {
-          const float e = expf(x - mx[h]);
+          const float e = __builtin_amdgcn_exp2f((x - mx[h]) * kLog2e);
           z[h] += e;
           w[h] += r * e;
         }
@@ -104,7 +109,7 @@ __global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
       float m = red[h][0];
 #pragma unroll
       for (int q = 1; q < NW; ++q) m = fmaxf(m, red[h][q]);
-      const float sc = mx[h] == -INFINITY ? 0.f : expf(mx[h] - m);
+      const float sc = mx[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mx[h] - m) * kLog2e);
       mx[h] = m;
       z[h] *= sc;
       w[h] *= sc;
@@ -118,27 +123,20 @@ __global__ void __launch_bounds__(kBlock) kgrad_coef_kernel(
       }
     }
     __syncthreads();
-    float inv[G], sr[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float zs = 0.f, ws = 0.f;
-#pragma unroll
-      for (int q = 0; q < NW; ++q) {
-        zs += red[G + h][q];
-        ws += red[2 * G + h][q];
-      }
-      inv[h] = 1.0f / zs;
-      sr[h] = ws * inv[h];                           // sum_f r_f P_h,f
-    }
-    __syncthreads();                                 // red is reused by the next level
-    for (int p = tid; p < n; p += kBlock) {
-      const float r = pv[p] > 0.f ? yv[p] / pv[p] : 0.f;
+    if (tid == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float P = expf(s[static_cast<int64_t>(h) * CK + p] - mx[h]) * inv[h];
-        cf[static_cast<int64_t>(h) * CK + p] = -(P / G) * (r - sr[h]);
+        float zs = 0.f, ws = 0.f;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+          zs += red[G + h][q];
+          ws += red[2 * G + h][q];
+        }
+        const float inv = 1.0f / zs;
+        stats[(slot * n_sel + (l - 1)) * G + h] = make_float4(mx[h], inv, ws * inv, 0.f);
       }
     }
+    __syncthreads();                                 // red is reused by the next level
   }
 }
 
@@ -154,8 +152,9 @@ template <int DT, int D, int G>
 __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
     recsa_tree tr, const void* qv, int Hq, int T, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
-    const float* __restrict__ coef, int level, int64_t n_par, int n_chunks,
-    float* __restrict__ part) {
+    const float* __restrict__ imp, const float* __restrict__ teacher,
+    const float* __restrict__ logits, const float4* __restrict__ stats, int level, int64_t n_par,
+    int n_chunks, float* __restrict__ part) {
   using Ty = typename Stor<DT>::T;
   constexpr int H2 = D / 2;
   constexpr int TPW = D / 64;                        // 16-column tiles per wave
@@ -264,25 +263,40 @@ __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
               make_float4(yo[e], yo[e + 1], yo[e + 2], yo[e + 3]);
         }
       }
-      // coefficients, four children per item (the row's 16 slots lie inside
-      // its C*k coefficients; slots past nv are zeroed)
+      // coefficients d KL / d s = -(P / G)(r - sum_f r_f P_f), four children
+      // per item, from the logits, pi, y and the head's softmax figures (the
+      // row's 16 slots lie inside its C*k entries; slots past nv are zeroed)
       for (int item = tid; item < KB * (kC / 4); item += kBlock) {
         const int row = item / (kC / 4), c0 = 4 * (item % (kC / 4));
         const int m = row / G, h = row % G;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        float cv[4] = {0.f, 0.f, 0.f, 0.f};
         if (m < mc) {
           const int nvm = m_nv[m0 + m];
           if (c0 < nvm) {
-            const int64_t slot = (q0 + m_qi[m0 + m]) * tr.Hkv + j;
-            v = *reinterpret_cast<const float4*>(
-                coef + ((slot * n_sel + (level - 1)) * G + h) * static_cast<int64_t>(CK) +
-                kC * m_rho[m0 + m] + c0);
-            if (c0 + 1 >= nvm) v.y = 0.f;
-            if (c0 + 2 >= nvm) v.z = 0.f;
-            if (c0 + 3 >= nvm) v.w = 0.f;
+            const int64_t lrow = ((q0 + m_qi[m0 + m]) * tr.Hkv + j) * n_sel + (level - 1);
+            const int64_t off = kC * m_rho[m0 + m] + c0;
+            const float4 st = stats[lrow * G + h];
+            const float4 s4 = *reinterpret_cast<const float4*>(
+                logits + (lrow * G + h) * static_cast<int64_t>(CK) + off);
+            const float4 y4 = *reinterpret_cast<const float4*>(teacher + lrow * CK + off);
+            const float4 p4 = *reinterpret_cast<const float4*>(imp + lrow * CK + off);
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+            const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
+            const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+            // hardware exp2 and reciprocal (about 1 ulp each): this staging
+            // runs once per (query, parent, head) on the accumulation's path
+            constexpr float kLog2e = 1.44269504088896341f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (c0 + e < nvm) {
+                const float r = pv[e] > 0.f ? yv[e] * __builtin_amdgcn_rcpf(pv[e]) : 0.f;
+                const float P = __builtin_amdgcn_exp2f((sv[e] - st.x) * kLog2e) * st.y;
+                cv[e] = -(P * (1.0f / G)) * (r - st.z);
+              }
+            }
           }
         }
-        *reinterpret_cast<float4*>(&cf[row][c0]) = v;
+        *reinterpret_cast<float4*>(&cf[row][c0]) = make_float4(cv[0], cv[1], cv[2], cv[3]);
       }
       __syncthreads();
       // A[child][kk] = cf[kk][child], B[kk][col] = qt[kk][col], kk = 4s + lane/16
@@ -341,11 +355,11 @@ __global__ void __launch_bounds__(kBlock) kgrad_finish_kernel(recsa_tree tr, int
 }
 
 // ------------------------------------------------------------ launchers
-// Workspace: the coefficients [n_queries*Hkv][n_sel][G][C*k], then the
-// chunk sums of the largest level, [B*Hkv][parents][chunks][16][d].
-static int64_t kgrad_coef_bytes(const recsa_tree& tr, int Hq, int64_t n_queries) {
+// Workspace: the softmax figures [n_queries*Hkv][n_sel][G] (float4), then
+// the chunk sums of the largest level, [B*Hkv][parents][chunks][16][d].
+static int64_t kgrad_stats_bytes(const recsa_tree& tr, int Hq, int64_t n_queries) {
   const int n_sel = tr.n_levels > 1 ? tr.n_levels - 1 : 1;
-  return align256(n_queries * tr.Hkv * n_sel * static_cast<int64_t>(Hq / tr.Hkv) * kC * tr.k * 4);
+  return align256(n_queries * tr.Hkv * n_sel * static_cast<int64_t>(Hq / tr.Hkv) * 16);
 }
 
 static int64_t kgrad_chunks(const recsa_tree& tr, int64_t n_queries) {
@@ -355,7 +369,7 @@ static int64_t kgrad_chunks(const recsa_tree& tr, int64_t n_queries) {
 
 int64_t kgrad_ws_bytes(const recsa_tree& tr, int Hq, int64_t n_queries) {
   const int64_t parents = (level_rows_host(tr.L_cap, 1) + kC - 1) / kC;   // level 1 is largest
-  return kgrad_coef_bytes(tr, Hq, n_queries) +
+  return kgrad_stats_bytes(tr, Hq, n_queries) +
          static_cast<int64_t>(tr.B) * tr.Hkv * parents * kgrad_chunks(tr, n_queries) * kC * tr.d * 4;
 }
 
@@ -371,12 +385,12 @@ static hipError_t kgrad_impl(const recsa_tree& tr, const void* q, int Hq, int T,
                              const int64_t* pos, const int32_t* sel, const int32_t* cnt,
                              const float* imp, const float* teacher, const float* logits,
                              float* dK, void* ws, hipStream_t s) {
-  float* coef = static_cast<float*>(ws);
+  float4* stats = static_cast<float4*>(ws);
   const int64_t nq = static_cast<int64_t>(tr.B) * T;
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + kgrad_coef_bytes(tr, Hq, nq));
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + kgrad_stats_bytes(tr, Hq, nq));
   const int n_chunks = static_cast<int>(kgrad_chunks(tr, nq));
-  kgrad_coef_kernel<G><<<dim3(static_cast<unsigned>(nq), tr.Hkv), kBlock, 0, s>>>(
-      tr, T, pos, sel, cnt, imp, teacher, logits, coef);
+  kgrad_stats_kernel<G><<<dim3(static_cast<unsigned>(nq), tr.Hkv), kBlock, 0, s>>>(
+      tr, T, pos, sel, cnt, imp, teacher, logits, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int64_t off = 0;
@@ -387,7 +401,7 @@ static hipError_t kgrad_impl(const recsa_tree& tr, const void* q, int Hq, int T,
       const int64_t n_wg = static_cast<int64_t>(parents) * n_chunks * tr.Hkv * tr.B;
       if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
       kgrad_accum_kernel<DT, D, G><<<dim3(static_cast<unsigned>(n_wg)), kBlock, 0, s>>>(
-          tr, q, Hq, T, pos, sel, cnt, coef, l, parents, n_chunks, part);
+          tr, q, Hq, T, pos, sel, cnt, imp, teacher, logits, stats, l, parents, n_chunks, part);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       dim3 gf(parents, tr.Hkv, tr.B);

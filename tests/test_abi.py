@@ -236,7 +236,7 @@ def test_pooler_backward_validates_without_launch():
 
 def test_key_grad_validates_without_launch():
     """recsa_distill_key_grad: workspace size from its documented layout
-    (coefficients, then the per-chunk partial sums of level 1), and bad
+    (softmax figures, then the per-chunk partial sums of level 1), and bad
     arguments rejected before any launch."""
     L = R.lib()
     b = ctypes.byref
@@ -244,9 +244,9 @@ def test_key_grad_validates_without_launch():
     al = lambda x: (x + 255) // 256 * 256
     nq = 5000
     need = L.recsa_distill_key_grad_workspace_bytes(b(t), 32, nq)
-    coef = al(nq * 8 * 3 * 4 * 16 * 64 * 4)
+    stats = al(nq * 8 * 3 * 4 * 16)
     parents, chunks = 2048 // 16, (nq + 2047) // 2048
-    assert need == coef + 8 * parents * chunks * 16 * 128 * 4
+    assert need == stats + 8 * parents * chunks * 16 * 128 * 4
     assert L.recsa_distill_key_grad_workspace_bytes(b(t), 30, nq) == 0     # Hq % Hkv
     assert L.recsa_distill_key_grad_workspace_bytes(b(t), 32, 0) == 0
     sws = L.recsa_workspace_bytes(b(t), 32, nq)
