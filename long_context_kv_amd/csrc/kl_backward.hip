@@ -16,10 +16,11 @@
 //                     figures (max, 1/Z, sum_f r_f P_h,f) from the selection
 //                     logits, pi and y.
 // kgrad_accum_kernel  per (sequence, KV head, level, chunk of 2048 queries,
-//                     parent node w; XCD-contiguous): walks the chunk's queries in order, finds
-//                     w among each query's parents, forms their coefficients
-//                     for w's 16 children, and contracts coefficient x rotated
-//                     query on the matrix cores.
+//                     parent node w; XCD-contiguous): walks the chunk's
+//                     queries in order, finds w among each query's parents,
+//                     forms their coefficients for w's 16 children, and
+//                     contracts coefficient x rotated query on the matrix
+//                     cores.
 // kgrad_finish_kernel per parent: the chunks in order, R(c)^T / sqrt(d), the
 //                     rows out.  Fixed orders: identical bits on every call.
 #include <math.h>
@@ -143,11 +144,12 @@ __global__ void __launch_bounds__(kBlock) kgrad_stats_kernel(
 // One workgroup per (parent node w of level l, chunk of kKgChunk queries) of
 // one (sequence, KV head): the sum over the chunk's queries, in order, for
 // w's children 16w .. 16w+15, before R(c)^T, into part[head][w][chunk][16][D].
-// Workgroups of one XCD take consecutive (chunk, parent) ids, so those running
-// together share one chunk's query rows in their L2.  Per batch of kKgMatch matched queries the
-// contraction coef[16 children][(m, h)] x q~[(m, h)][D] runs on the fp32
-// matrix cores (v_mfma_f32_16x16x4_f32, exact fp32 products, fp32
-// accumulation); wave wv owns the D/64 column tiles wv*D/64 ...
+// Workgroups of one XCD take consecutive (chunk, parent) ids, so those
+// running together share one chunk's query rows in their L2.  Per batch of
+// kKgMatch matched queries, the contraction
+// coef[16 children][(m, h)] x q~[(m, h)][D] runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32, exact fp32 products, fp32 accumulation); wave wv
+// owns the D/64 column tiles wv*D/64 ...
 template <int DT, int D, int G>
 __global__ void __launch_bounds__(kBlock) kgrad_accum_kernel(
     recsa_tree tr, const void* qv, int Hq, int T, const int64_t* __restrict__ pos,
