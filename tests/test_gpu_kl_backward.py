@@ -75,6 +75,27 @@ def test_key_grad_matches_oracle(dtype, d, tol):
                                tol) == (tree.Hkv, True)
 
 
+def test_key_grad_two_sequences_and_head_ratios():
+    """Two sequences (each with its own positions and chunk), G = 2 and
+    G = 1, k = 64 on 9000 tokens (level 1 scored from t = 1024 on)."""
+    _need_gpu()
+    L0, T, k, d = 9000, 10, 64, 64
+    tree, pool, pdict = TD._tree(2, 2, d, L0, k, "bf16", 92)
+    for G in (2, 1):
+        Hq = 2 * G
+        q = synth.to_storage(synth.normal((2, T, Hq, d), DEV, 92, G), "bf16")
+        pos = torch.stack([torch.tensor(TD.positions(L0, T, 92 + s)) for s in range(2)]).to(DEV)
+        sel, cnt, imp, dK = run_key_grad(tree, q, Hq, pos)
+        n, scored = compare_with_oracle(tree, pdict, q, pos, sel, cnt, imp, dK, range(tree.Hkv),
+                                        list_bar(k), strict=False)
+        assert n >= 2 * tree.Hkv - 1 and scored, (G, n)
+
+
+def list_bar(k):
+    """The bf16 bar for lists of up to 16 k candidates."""
+    return tolerance(2e-4, 16 * k)
+
+
 def tolerance(base, n_cand):
     """The bar for lists of up to n_cand candidates: the small cases' base
     (lists of at most 256) plus 4 n_cand 2^-24, the worst-case relative error
@@ -85,11 +106,13 @@ def tolerance(base, n_cand):
 
 
 def compare_with_oracle(tree, pdict, q, pos, sel, cnt, imp, dK, heads, tol, strict=True):
-    """The oracle's kl_key_grad summed over the queries of pos (one sequence),
-    per KV head in heads, against dK to the magnitude-scaled bar.  Every walk
+    """The oracle's kl_key_grad summed over the queries of pos (every
+    sequence), per sequence and KV head in heads, against dK to the
+    magnitude-scaled bar.  Every walk
     must match the oracle's selection; with strict=False a head whose walk
     differs (a near-tie swap) is skipped instead.  Returns the number of
-    heads compared and whether any of them had a scored term."""
+    (sequence, head) pairs compared and whether any of them had a scored
+    term."""
     compared, scored = 0, False
     k, d, dtype = tree.k, tree.d, tree.dtype
     Hq = q.shape[2]
@@ -99,42 +122,46 @@ def compare_with_oracle(tree, pdict, q, pos, sel, cnt, imp, dK, heads, tol, stri
     G = Hq // tree.Hkv
     rep = PY.WalkReport()
     P = PY.oracle_pooler(pdict)
-    n_tok = int(pos.max()) + 1
-    for j in heads:
-        K0 = PY.to64(tree.K[0][0, j, :n_tok])
-        V0 = PY.to64(tree.V[0][0, j, :n_tok])
-        K, _ = O.build_tree(K0, V0, 16, tree.n_levels, P, dtype)
-        ref = [np.zeros_like(dK[l][0, j]) for l in range(tree.n_levels - 1)]
-        mag = [np.zeros_like(dK[l][0, j]) for l in range(tree.n_levels - 1)]
-        for ti in range(T):
-            t = int(pos[0, ti])
-            D = O.n_levels_for(t, 16, k)
-            Kt = ([K[0][: t + 1]] + [K[l][: (t + 1) // 16 ** l] for l in range(1, len(K))])[: max(D, 1)]
-            qG = qn[0, ti, j * G:(j + 1) * G]
-            tr = O.walk(qG, t, Kt, 16, k, cos, sin, dtype)
-            same = PY.compare_walk(tr, sel[0, ti, j], cnt[0, ti, j], imp[0, ti, j], rep, 1e-5)
-            if not same and not strict:
-                break
-            assert same, (j, t, rep.notes)
-            g = O.kl_key_grad(qG, t, tr, K0[: t + 1], 16, TD.THETA, cos, sin, dtype)
-            m = O.kl_key_grad(qG, t, tr, K0[: t + 1], 16, TD.THETA, cos, sin, dtype, magnitude=True)
-            for lvl, (nodes, v) in g.items():
-                ref[lvl - 1][nodes] += v
-                mag[lvl - 1][nodes] += m[lvl][1]
-        else:
-            _check_head(tree, dK, j, ref, mag, tol)
-            compared += 1
-            scored |= any(m_.max() > 0 for m_ in mag)
+    for b in range(pos.shape[0]):
+        n_tok = int(pos[b].max()) + 1
+        for j in heads:
+            K0 = PY.to64(tree.K[0][b, j, :n_tok])
+            V0 = PY.to64(tree.V[0][b, j, :n_tok])
+            K, _ = O.build_tree(K0, V0, 16, tree.n_levels, P, dtype)
+            ref = [np.zeros_like(dK[l][b, j]) for l in range(tree.n_levels - 1)]
+            mag = [np.zeros_like(dK[l][b, j]) for l in range(tree.n_levels - 1)]
+            for ti in range(T):
+                t = int(pos[b, ti])
+                D = O.n_levels_for(t, 16, k)
+                Kt = ([K[0][: t + 1]] + [K[l][: (t + 1) // 16 ** l]
+                                         for l in range(1, len(K))])[: max(D, 1)]
+                qG = qn[b, ti, j * G:(j + 1) * G]
+                tr = O.walk(qG, t, Kt, 16, k, cos, sin, dtype)
+                same = PY.compare_walk(tr, sel[b, ti, j], cnt[b, ti, j], imp[b, ti, j], rep, 1e-5)
+                if not same and not strict:
+                    break
+                assert same, (b, j, t, rep.notes)
+                g = O.kl_key_grad(qG, t, tr, K0[: t + 1], 16, TD.THETA, cos, sin, dtype)
+                m = O.kl_key_grad(qG, t, tr, K0[: t + 1], 16, TD.THETA, cos, sin, dtype,
+                                  magnitude=True)
+                for lvl, (nodes, v) in g.items():
+                    ref[lvl - 1][nodes] += v
+                    mag[lvl - 1][nodes] += m[lvl][1]
+            else:
+                _check_head(tree, dK, b, j, ref, mag, tol)
+                compared += 1
+                scored |= any(m_.max() > 0 for m_ in mag)
     return compared, scored
 
 
-def _check_head(tree, dK, j, ref, mag, tol):
+def _check_head(tree, dK, b, j, ref, mag, tol):
     """Rows no query scores exactly 0, the rest within tol of their terms'
     summed magnitude."""
     for l in range(tree.n_levels - 1):
-        got = dK[l][0, j]
+        got = dK[l][b, j]
         assert np.all(np.isfinite(got)), l
         untouched = mag[l].max(axis=1) == 0
         assert np.all(got[untouched] == 0.0), l
         err = np.abs(got - ref[l])
-        assert np.all(err <= tol * mag[l] + 1e-30), (j, l + 1, float(np.max(err / (mag[l] + 1e-30))))
+        assert np.all(err <= tol * mag[l] + 1e-30), \
+            (b, j, l + 1, float(np.max(err / (mag[l] + 1e-30))))
