@@ -69,8 +69,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }  // namespace
 
 // ------------------------------------------------------------ teacher
-// Workgroup: 64/G consecutive queries of one (sequence, KV head), i.e. 64
-// rows r = G*(query - first) + h; wave w owns rows [16w, 16w + 16).
+// Workgroup: 128/G consecutive queries of one (sequence, KV head), i.e. 128
+// rows r = G*(query - first) + h; wave w owns the kTeacherSets sets of 16
+// rows starting at 32w.
 // Logits on the bf16 matrix cores at float32-level accuracy: every rotated
 // float32 operand x is split into x_hi = rnd(x) and x_lo = rnd(x - x_hi)
 // (bf16; |x - x_hi - x_lo| <= 2^-18 |x|), and each 32-dim block takes the
@@ -85,7 +86,8 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // Every key row is rotated at its absolute position and split once for the
 // whole call (teacher_keys_kernel); each tile of 64 keys is then staged into
 // LDS with 16-byte loads by all 256 threads.
-// lse: [B*T][Hkv][ng_cap][G] float32; entry (v, h) is written for every
+// lse: [B*T][Hkv][ng_cap][G] float32 group log-sum-exps in base-2 units
+// (log2 of the sum of 2^(logit log2 e)); entry (v, h) is written for every
 // level-1 group v <= t/16 of the row's query, never beyond.
 __device__ __forceinline__ void split_bf16x8(const float* v, uint4& hi, uint4& lo) {
   uint32_t h[4], l[4];
@@ -134,7 +136,7 @@ __global__ void __launch_bounds__(kBlock) teacher_keys_kernel(recsa_tree tr,
 // wave's kTeacherSets sets of 16 query columns: per group, the 16x16 logits of
 // each set on the matrix cores (split products lo.hi + hi.lo + hi.hi; each key
 // fragment read from LDS once for all sets), then per column the group's
-// log-sum-exp, stored in natural-log units.  MASK applies causality (keys
+// log-sum-exp, stored in base-2 units.  MASK applies causality (keys
 // after the column's position drop out); without it every key counts.
 template <bool MASK, int D, int G>
 __device__ __forceinline__ void teacher_tile_lse(const uint16_t (*khi)[D + 8],
@@ -145,7 +147,6 @@ __device__ __forceinline__ void teacher_tile_lse(const uint16_t (*khi)[D + 8],
                                                  float* const* lcol) {
   constexpr int KB = D / 32;
   constexpr int NS = kTeacherSets;
-  constexpr float kLn2 = 0.69314718055994531f;
 #pragma unroll
   for (int g = 0; g < kTeacherKeys / kC; ++g) {
     const int tg = tau0 + kC * g;   // first token of the level-1 group
@@ -190,7 +191,7 @@ __device__ __forceinline__ void teacher_tile_lse(const uint16_t (*khi)[D + 8],
       e += __shfl_xor(e, 16);
       e += __shfl_xor(e, 32);
       if (hh == 0 && t_col[u] >= 0 && (!MASK || m != -INFINITY))
-        lcol[u][static_cast<int64_t>(tg >> 4) * G] = (m + __builtin_amdgcn_logf(e)) * kLn2;
+        lcol[u][static_cast<int64_t>(tg >> 4) * G] = m + __builtin_amdgcn_logf(e);
     }
   }
 }
@@ -332,9 +333,10 @@ __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
   float* mass = dsm + ng_cap;
   float* red = mass + CK;
 
-  // softmax normaliser of each head, log Z_h = logsumexp over the groups:
-  // one pass of G-wide loads with a running (max, sum) per head, then one
-  // block exchange for all heads
+  // softmax normaliser of each head, log2 Z_h = log2-sum-exp2 over the
+  // groups (the group figures are in base-2 units, so every exponential and
+  // logarithm is one hardware instruction): one pass of G-wide loads with a
+  // running (max, sum) per head, then one block exchange for all heads
   float mx[G], sx[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -347,10 +349,10 @@ __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if (x[h] > mx[h]) {
-        sx[h] = sx[h] * expf(mx[h] - x[h]) + 1.0f;   // exp(-inf) = 0 on the first value
+        sx[h] = sx[h] * __builtin_amdgcn_exp2f(mx[h] - x[h]) + 1.0f;   // 2^-inf = 0 at first
         mx[h] = x[h];
       } else {
-        sx[h] += expf(x[h] - mx[h]);
+        sx[h] += __builtin_amdgcn_exp2f(x[h] - mx[h]);
       }
     }
   }
@@ -362,7 +364,8 @@ __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float wm = wave_max(mx[h]);
-      const float ws = wave_sum(mx[h] == -INFINITY ? 0.f : sx[h] * expf(mx[h] - wm));
+      const float ws =
+          wave_sum(mx[h] == -INFINITY ? 0.f : sx[h] * __builtin_amdgcn_exp2f(mx[h] - wm));
       if (lane == 0) {
         rm[4 * h + wid] = wm;
         rs[4 * h + wid] = ws;
@@ -377,8 +380,10 @@ __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < kBlock / kWave; ++w)
-        sum += rm[4 * h + w] == -INFINITY ? 0.f : rs[4 * h + w] * expf(rm[4 * h + w] - m);
-      lz[h] = m + logf(sum);
+        sum += rm[4 * h + w] == -INFINITY
+                   ? 0.f
+                   : rs[4 * h + w] * __builtin_amdgcn_exp2f(rm[4 * h + w] - m);
+      lz[h] = m + __builtin_amdgcn_logf(sum);
     }
   }
   for (int v = tid; v < ng; v += kBlock) {
@@ -386,7 +391,7 @@ __global__ void __launch_bounds__(kBlock) distill_kl_kernel(
     load_group<G>(L + static_cast<int64_t>(v) * G, x);
     float s = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) s += expf(x[h] - lz[h]);
+    for (int h = 0; h < G; ++h) s += __builtin_amdgcn_exp2f(x[h] - lz[h]);
     m1[v] = s * (1.0f / G);
   }
   __syncthreads();
