@@ -131,7 +131,7 @@ def positions(L0, T, seed):
     return sorted(fixed + rnd)
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 128)])
 def test_distill_kl_matches_oracle(dtype, d):
     """Eq. 6 terms of 40 queries x 2 KV heads (G = 4) on a 5000-token tree at
     k = 16: levels 1 and 2 scored for most positions, none below C*k = 256."""

@@ -59,7 +59,8 @@ def run_key_grad(tree, q, Hq, pos):
             [v.cpu().numpy().astype(np.float64) for v in outs[0][1]])
 
 
-@pytest.mark.parametrize("dtype,d,tol", [("f32", 64, 1e-4), ("bf16", 128, 2e-4)])
+@pytest.mark.parametrize("dtype,d,tol", [("f32", 64, 1e-4), ("f32", 128, 1e-4),
+                                         ("bf16", 128, 2e-4)])
 def test_key_grad_matches_oracle(dtype, d, tol):
     """20 queries on 2 KV heads (G = 4) of a 5000-token tree at k = 16 (levels
     1 and 2 scored), positions spread over the sequence."""
