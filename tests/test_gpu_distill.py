@@ -193,6 +193,8 @@ def _shift_oracle(tree, pdict, tok_end):
 
 @pytest.mark.parametrize("dtype,d,B,Hkv,L0,tok_end", [
     ("f32", 64, 1, 1, 4096, 4096),
+    ("f32", 128, 1, 1, 4096, 4096),
+    ("bf16", 64, 1, 2, 4200, 4200),
     ("bf16", 128, 2, 2, 8200, 8200),
     ("bf16", 128, 1, 2, 8200, 300),        # one complete level-1 tile, ragged
 ])

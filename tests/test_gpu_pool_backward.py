@@ -96,6 +96,8 @@ def compare(g, ref_mag, tol):
     ("f32", 64, 1, 1, 4096, 4096, (1, 2), 0.7, True),
     ("bf16", 128, 2, 2, 8200, 8200, (1, 2), 0.5, True),
     ("bf16", 128, 1, 2, 8200, 300, (1,), 1.0, False),     # 18 nodes: a ragged tile; penalty only
+    ("f32", 128, 1, 1, 4096, 4096, (1,), 0.3, True),
+    ("bf16", 64, 1, 2, 4200, 4200, (1, 2), 0.6, True),
 ])
 def test_pooler_backward_matches_oracle(dtype, d, B, Hkv, L0, tok_end, levels, lam, with_dk):
     _need_gpu()
