@@ -290,3 +290,48 @@ def test_misaligned_arrays_are_rejected_without_launch():
     p = _pooler(W1=0x4004)
     assert L.recsa_build_tree(b(t), b(p), 0, 16, None) == R.RECSA_E_INVALID
     assert L.recsa_init_rope(0x3004, 128, 16, 1e6, None) == R.RECSA_E_INVALID
+
+
+def test_misaligned_distillation_arrays_are_rejected_without_launch():
+    """The distillation calls apply the same alignment rule: 16 bytes for
+    float arrays, 4 for the per-query KL output and the scalar gradients."""
+    L = R.lib()
+    b = ctypes.byref
+    t = _tree(k=64, L_cap=32768, n_levels=4)
+    p = _pooler()
+    nq = 100
+    dneed = L.recsa_distill_workspace_bytes(b(t), 32, nq)
+    ok = [b(t), 0x10, 32, nq, 0x10, 0x10, 0x10, 0x10, 1e6, 0x10, None, 0x10, dneed, None]
+    for i, bad in ((1, 0x18), (7, 0x14), (11, 0x108)):
+        a = list(ok)
+        a[i] = bad
+        assert L.recsa_distill_kl(*a) == R.RECSA_E_INVALID, (i, bad)
+    a = list(ok)
+    a[10] = 0x24                                          # teacher output: 16-byte
+    assert L.recsa_distill_kl(*a) == R.RECSA_E_INVALID
+    kneed = L.recsa_distill_key_grad_workspace_bytes(b(t), 32, nq)
+    sws = L.recsa_workspace_bytes(b(t), 32, nq)
+    ok = [b(t), 0x10, 32, nq, 0x10, 0x10, 0x10, 0x10, 0x10, 0x10, sws, 0x10, 0x10, kneed, None]
+    for i, bad in ((7, 0x14), (8, 0x18), (9, 0x104), (11, 0x1c), (12, 0x108)):
+        a = list(ok)
+        a[i] = bad
+        assert L.recsa_distill_key_grad(*a) == R.RECSA_E_INVALID, (i, bad)
+    bneed = L.recsa_pooler_backward_workspace_bytes(b(t), b(p), 1)
+    g = R.PoolerGradC(0x10, 0x10, 0x10, 0x10, 0x14, 0x18)    # scalar gradients: 4-byte
+    ok = [b(t), b(p), 1, 4096, 0x10, 0x18, 0.5, b(g), 0x10, bneed, None]
+    for i, bad in ((4, 0x14), (5, 0x12), (8, 0x108)):
+        a = list(ok)
+        a[i] = bad
+        assert L.recsa_pooler_backward(*a) == R.RECSA_E_INVALID, (i, bad)
+    g_bad = R.PoolerGradC(0x10, 0x18, 0x10, 0x10, 0x14, 0x18)
+    a = list(ok)
+    a[7] = b(g_bad)
+    assert L.recsa_pooler_backward(*a) == R.RECSA_E_INVALID
+    # the decode step: q, the new rows, the output and the workspace
+    t2 = _tree()
+    need = L.recsa_workspace_bytes(b(t2), 32, 1)
+    ok = [b(t2), b(p), 0x10, 0x10, 0x10, 32, 0x10, 0x10, 0x10, 0x10, 0x100, need, None]
+    for i in (2, 3, 4, 9, 10):
+        a = list(ok)
+        a[i] = ok[i] + 8
+        assert L.recsa_decode(*a) == R.RECSA_E_INVALID, i
