@@ -249,6 +249,31 @@ def test_edge_positions_fp32():
         assert np.allclose(o2[0, 0], out[0, i], rtol=0, atol=1e-6 * np.abs(out[0, i]).max())
 
 
+@pytest.mark.parametrize("dtype,d,G", [("bf16", 64, 1), ("f32", 128, 2), ("bf16", 128, 1)])
+def test_head_ratios_prefill_and_decode_vs_oracle(dtype, d, G):
+    """G = 1 and G = 2 query heads per KV head (two KV heads, k = 16, 5000
+    tokens): every query of a T-query call and a few through the decode path,
+    selections and outputs against the oracle."""
+    _need_gpu()
+    L, Hkv, k = 5000, 2, 16
+    wl, tree, pool, pdict = _setup(1, Hkv, d, L, L, k, dtype, 21)
+    R.recsa_build_tree(tree, pool, 0, L)
+    Hq = Hkv * G
+    ts = [0, 17, 255, 256, 300, 1234, 4095, 4096, 4111, 4999]
+    pos = torch.tensor([ts], dtype=torch.int64, device=DEV)
+    q = synth.to_storage(synth.normal((1, len(ts), Hq, d), DEV, 21, 10 + G), dtype)
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    sel, cnt, imp, out = _run_select_attn(tree, q, Hq, pos, decode=False)
+    rep = _check_queries(tree, pdict, q, pos.cpu(), sel, cnt, imp, out, range(Hkv), 1e-5, tol,
+                         max_swaps=1)
+    assert rep.matched >= Hkv * len(ts) - 1, rep
+    for i in (0, 4, len(ts) - 1):
+        s2, c2, m2, o2 = _run_select_attn(tree, q[:, i:i + 1].contiguous(), Hq,
+                                          pos[:, i:i + 1].contiguous(), decode=True)
+        assert np.array_equal(s2[0, 0], sel[0, i]) and np.array_equal(c2[0, 0], cnt[0, i])
+        assert np.allclose(o2[0, 0], out[0, i], rtol=0, atol=1e-5 * np.abs(out[0, i]).max())
+
+
 def test_qwen_shape_bf16_decode_64k():
     """8 KV heads, 32 query heads, d=128, bf16, k=256 at L=65536: append the
     decode token at t=L, select, attend (decode path); every head vs oracle."""
@@ -354,7 +379,8 @@ def test_fused_decode_graph_replays_match_eager():
 
 
 @pytest.mark.parametrize("dtype,d,Hkv,G,B", [("bf16", 128, 8, 4, 1), ("f32", 64, 2, 4, 2),
-                                             ("bf16", 128, 4, 2, 3)])
+                                             ("bf16", 128, 4, 2, 3), ("bf16", 64, 2, 1, 2),
+                                             ("f32", 128, 2, 2, 1)])
 def test_fused_decode_matches_separate_calls(dtype, d, Hkv, G, B):
     """recsa_decode (append + select + attend in one launch) gives the same
     selection and output as recsa_append_decode + recsa_select +
