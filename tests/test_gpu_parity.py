@@ -115,7 +115,7 @@ def _check_rotated_keys(tree, heads, n_tokens):
             assert (diff > 0).mean() < 1e-3, (lvl, (diff > 0).mean())
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("f32", 128), ("bf16", 64)])
 def test_append_equals_build(dtype, d):
     """Appending tokens one at a time (completing nodes on the fly) gives
     exactly the tree a single build gives."""
