@@ -33,7 +33,7 @@ namespace recsa {
 
 namespace {
 
-constexpr int kTeacherSets = 2;    // 16-row query sets per teacher wave
+constexpr int kTeacherSets = 3;    // 16-row query sets per teacher wave
 constexpr int kTeacherRows = 16 * kTeacherSets * (kBlock / kWave);   // rows per workgroup
 constexpr int kTeacherKeys = 64;   // keys per tile: four level-1 groups
 
@@ -69,9 +69,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }  // namespace
 
 // ------------------------------------------------------------ teacher
-// Workgroup: 128/G consecutive queries of one (sequence, KV head), i.e. 128
-// rows r = G*(query - first) + h; wave w owns the kTeacherSets sets of 16
-// rows starting at 32w.
+// Workgroup: kTeacherRows/G consecutive queries of one (sequence, KV head),
+// i.e. kTeacherRows = 16 kTeacherSets x 4 rows r = G*(query - first) + h;
+// wave w owns the kTeacherSets sets of 16 rows starting at 16 kTeacherSets w.
 // Logits on the bf16 matrix cores at float32-level accuracy: every rotated
 // float32 operand x is split into x_hi = rnd(x) and x_lo = rnd(x - x_hi)
 // (bf16; |x - x_hi - x_lo| <= 2^-18 |x|), and each 32-dim block takes the
@@ -278,7 +278,8 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
   const float scale2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(D)));
   const int kk = tid >> 2, qq = tid & 3;     // the key row and quarter this thread loads
 
-  // the next tile's rows are fetched into registers while this one computes
+  // each tile's rows pass through registers into LDS (three row sets per
+  // wave leave no registers for fetching the next tile ahead)
   uint4 ph[DQ / 8], pl[DQ / 8];
   auto fetch = [&](int tau0) {
     const int tau = tau0 + kk;
@@ -294,17 +295,16 @@ __global__ void __launch_bounds__(kBlock) teacher_lse_kernel(recsa_tree tr, cons
     }
   };
   const int n_tiles = tmax / kTeacherKeys + 1;
-  fetch(0);
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int tau0 = tile * kTeacherKeys;
     __syncthreads();   // the previous tile is read
+    fetch(tau0);
 #pragma unroll
     for (int c = 0; c < DQ / 8; ++c) {
       *reinterpret_cast<uint4*>(&khi[kk][qq * DQ + 8 * c]) = ph[c];
       *reinterpret_cast<uint4*>(&klo[kk][qq * DQ + 8 * c]) = pl[c];
     }
     __syncthreads();
-    if (tile + 1 < n_tiles) fetch(tau0 + kTeacherKeys);
     // tiles wholly at or before every query of the block need no causal mask
     if (tau0 + kTeacherKeys - 1 <= tmin)
       teacher_tile_lse<false, D, G>(khi, klo, bhi, blo, tau0, tmax, t_col, col, hh, scale2, lcol);
