@@ -730,7 +730,7 @@ def cpu_baseline_distill(wl, tree, pdict, q, L):
     return {"value": round(scaled_ms, 1), "unit": "ms/layer-step", "cores": 1, "kind": "oracle",
             "sample": (f"KV head 0 of {heads}, one thread: oracle walk + Eq. 6 at 400 evenly "
                        f"spaced positions of {L}, scaled x{L} positions x{heads} heads "
-                       f"({total:.1f}s of CPU work; Eq. 7 not included)")}
+                       f"({total:.1f}s of CPU work; Eq. 7, the key gradient and the pooler backward not included)")}
 
 
 if __name__ == "__main__":
