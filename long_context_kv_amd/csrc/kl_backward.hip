@@ -81,20 +81,35 @@ __global__ void __launch_bounds__(kBlock) kgrad_stats_kernel(
     // hardware exp2 and reciprocal (about 1 ulp each), as the accumulation's
     // coefficient staging uses
     constexpr float kLog2e = 1.44269504088896341f;
-    for (int p = tid; p < n; p += kBlock) {
-      const float r = pv[p] > 0.f ? yv[p] * __builtin_amdgcn_rcpf(pv[p]) : 0.f;
+    // four candidates per thread per step, 16-byte loads (a level's row of
+    // C*k entries holds the reads past n; those lanes are skipped)
+    for (int p0 = 4 * tid; p0 < n; p0 += 4 * kBlock) {
+      const float4 y4 = *reinterpret_cast<const float4*>(yv + p0);
+      const float4 p4 = *reinterpret_cast<const float4*>(pv + p0);
+      const float ya[4] = {y4.x, y4.y, y4.z, y4.w};
+      const float pa[4] = {p4.x, p4.y, p4.z, p4.w};
+      float ra[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ra[e] = pa[e] > 0.f ? ya[e] * __builtin_amdgcn_rcpf(pa[e]) : 0.f;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float x = s[static_cast<int64_t>(h) * CK + p];
-        if (x > mx[h]) {
-          const float sc = __builtin_amdgcn_exp2f((mx[h] - x) * kLog2e);
-          z[h] = z[h] * sc + 1.f;
-          w[h] = w[h] * sc + r;
-          mx[h] = x;
-        } else {
-          const float e = __builtin_amdgcn_exp2f((x - mx[h]) * kLog2e);
-          z[h] += e;
-          w[h] += r * e;
+        const float4 s4 = *reinterpret_cast<const float4*>(s + static_cast<int64_t>(h) * CK + p0);
+        const float sa[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (p0 + e >= n) break;
+          const float x = sa[e], r = ra[e];
+          if (x > mx[h]) {
+            const float sc = __builtin_amdgcn_exp2f((mx[h] - x) * kLog2e);
+            z[h] = z[h] * sc + 1.f;
+            w[h] = w[h] * sc + r;
+            mx[h] = x;
+          } else {
+            const float ex = __builtin_amdgcn_exp2f((x - mx[h]) * kLog2e);
+            z[h] += ex;
+            w[h] += r * ex;
+          }
         }
       }
     }
