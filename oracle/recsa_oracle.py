@@ -271,6 +271,8 @@ class LevelTrace:
     scored: bool             # False when |A| <= k (everything selected)
     logits: np.ndarray | None = None       # [G, |A|-1] for the non-current entries
     importance: np.ndarray | None = None   # [|A|-1]
+    S_own: np.ndarray | None = None        # the walk's own top-k choice (== S unless
+                                           # a ``choose`` hook substituted another)
 
 
 @dataclass
@@ -330,13 +332,20 @@ def _topk_lowest_index(I, nodes, m):
 
 
 def walk(qG, t: int, K, C: int, k: int, cos=None, sin=None, dtype="f32",
-         exact=False, theta=1e6):
+         exact=False, theta=1e6, choose=None):
     """Top-down selection for one query at position t against one KV head's
     tree K (list of per-level key arrays; K[0] must hold rows 0..t).
 
     qG: [G, d] query heads sharing this KV head.  Returns a WalkTrace with the
     per-level lists A, selections S, logits and importances, the level-0 list
-    and the entry set E_t of Eq. 4 with one logit per head and entry."""
+    and the entry set E_t of Eq. 4 with one logit per head and entry.
+
+    choose: optional hook ``choose(level, others, I, S) -> S'`` called at
+    every scored level with the non-current candidates, their importances and
+    the walk's own selection; the walk continues with the returned set (a
+    caller comparing against another implementation uses it to follow that
+    implementation's choice at an accepted near-tie, so that one flipped
+    near-tie does not change every list below it)."""
     qG = np.asarray(qG, dtype=np.float64)
     G, d = qG.shape
     n_levels = len(K)
@@ -365,7 +374,10 @@ def walk(qG, t: int, K, C: int, k: int, cos=None, sin=None, dtype="f32",
             I = pi.mean(axis=0)
             keep = _topk_lowest_index(I, others, k - 1)
             S = np.sort(np.concatenate([others[keep], [cur]]))
-            tr.levels[lvl] = LevelTrace(lvl, A, S, True, s, I)
+            S_own = S
+            if choose is not None:
+                S = np.sort(np.asarray(choose(lvl, others, I, S), dtype=np.int64))
+            tr.levels[lvl] = LevelTrace(lvl, A, S, True, s, I, S_own)
             chosen = set(int(x) for x in S)
             for i, node in enumerate(others):
                 if int(node) not in chosen:
@@ -394,9 +406,10 @@ def attend(tr: WalkTrace, V):
     return (w @ rows) / w.sum(axis=1, keepdims=True)
 
 
-def decode_reference(qG, t, K, V, C, k, cos, sin, dtype, exact=False, theta=1e6):
+def decode_reference(qG, t, K, V, C, k, cos, sin, dtype, exact=False, theta=1e6,
+                     choose=None):
     """Walk plus attention for one query on one KV head."""
-    tr = walk(qG, t, K, C, k, cos, sin, dtype, exact, theta)
+    tr = walk(qG, t, K, C, k, cos, sin, dtype, exact, theta, choose)
     return attend(tr, V), tr
 
 

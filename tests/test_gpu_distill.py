@@ -84,19 +84,14 @@ def check_kl(tree, pdict, q, pos, sel, cnt, imp, kl, heads, y=None):
     for b in range(B):
         n_tok = int(pos[b].max()) + 1
         for j in heads:
-            K0 = PY.to64(tree.K[0][b, j, :n_tok])
-            V0 = PY.to64(tree.V[0][b, j, :n_tok])
-            K, _ = O.build_tree(K0, V0, 16, tree.n_levels, PY.oracle_pooler(pdict), tree.dtype)
+            K, V = PY.staged_tree(tree, pdict, b, j, n_tok)
+            K0 = K[0]
             for ti in range(T):
                 t = int(pos[b, ti])
-                D = O.n_levels_for(t, 16, tree.k)
-                Kt = ([K[0][: t + 1]] + [K[lvl][: (t + 1) // 16 ** lvl]
-                                         for lvl in range(1, len(K))])[: max(D, 1)]
                 qG = qn[b, ti, j * G:(j + 1) * G]
-                tr = O.walk(qG, t, Kt, 16, tree.k, cos, sin, tree.dtype)
-                if not PY.compare_walk(tr, sel[b, ti, j], cnt[b, ti, j], imp[b, ti, j], rep,
-                                       1e-5):
-                    continue
+                o = np.zeros((G, tree.d))
+                tr = PY.check_query(qG, t, K, V, sel[b, ti, j], cnt[b, ti, j], imp[b, ti, j], o,
+                                    rep, tree.dtype, tree.k, cos, sin, np.inf, tree.n_levels)
                 ref = O.distill_kl(qG, t, tr, K0[: t + 1], 16, THETA)
                 if y is not None:
                     yref = O.distill_targets(qG, t, tr, K0[: t + 1], 16, THETA)
@@ -118,7 +113,6 @@ def check_kl(tree, pdict, q, pos, sel, cnt, imp, kl, heads, y=None):
                         assert err <= KL_ATOL + KL_RTOL * abs(ref[lvl]), (b, t, j, lvl, g, ref[lvl])
                     else:
                         assert g == 0.0, (b, t, j, lvl, g)
-    assert rep.swapped <= 1, rep.notes
     return n_pairs, n_levels, worst
 
 
@@ -146,7 +140,7 @@ def test_distill_kl_matches_oracle(dtype, d):
     assert np.all(np.isfinite(kl))
     assert np.all(kl >= -1e-6)                         # a KL divergence
     n_pairs, n_lv, worst = check_kl(tree, pdict, q, pos.cpu(), sel, cnt, imp, kl, [0, 1], y)
-    assert n_pairs >= 2 * T - 1 and n_lv >= T, (n_pairs, n_lv)
+    assert n_pairs == 2 * T and n_lv >= T, (n_pairs, n_lv)
     # queries below C*k see every level whole: no term at all
     small = (pos.cpu().numpy()[0] < 16 * k)
     assert np.all(kl[0, small] == 0.0)
@@ -165,7 +159,7 @@ def test_distill_kl_two_sequences_and_head_ratios():
         pos = torch.stack([torch.tensor(positions(L0, T, 62 + s)) for s in range(2)]).to(DEV)
         sel, cnt, imp, kl = run_distill(tree, q, Hq, pos)
         n_pairs, n_lv, _ = check_kl(tree, pdict, q, pos.cpu(), sel, cnt, imp, kl, [0, 1])
-        assert n_pairs >= 4 * T - 1 and n_lv >= 2 * T
+        assert n_pairs == 4 * T and n_lv >= 2 * T
 
 
 def _shift_oracle(tree, pdict, tok_end):

@@ -75,9 +75,8 @@ def test_offloaded_level0_matches_device_resident():
     sel, cnt, imp, out = r_host
     idx = [0, T - 1]
     rep = TP._check_queries(host, pdict, q[:, idx], pos[:, idx].cpu(), sel[:, idx],
-                            cnt[:, idx], imp[:, idx], out[:, idx], [0, 1], 1e-5, 2e-3,
-                            max_swaps=1)
-    assert rep.matched >= 2 * len(idx) * 2 - 1
+                            cnt[:, idx], imp[:, idx], out[:, idx], [0, 1], 2e-3)
+    assert rep.compared == 2 * len(idx) * 2 and rep.imp_levels > 0, rep
 
     # one decode step at t = L0 + T (fused), then the same step as three calls
     t = L0 + T

@@ -583,6 +583,83 @@ def test_distill_kl_zero_for_zero_query_and_matches_relative_entropy():
             assert abs(v - scipy.stats.entropy(m / m.sum(), lt.importance)) < 1e-12
 
 
+def test_distill_targets_average_heads_then_renormalise():
+    """R15 by hand: head 0 with q = 0 spreads the teacher mass uniformly
+    over the t+1 tokens; head 1 puts all of it on one token tau* (its query
+    is the RoPE-rotated key of an outsized token).  Per candidate u of a
+    scored level (n_u tokens in its subtree, the current node dropped) the
+    head-mean mass is m_u = (n_u/(t+1) + [tau* under u]) / 2, and y is m
+    renormalised over the candidates.  Normalising each head first and then
+    averaging, or keeping the current node, would give other values."""
+    C, k, d, L, theta = 4, 3, 8, 300, 1e4
+    r = np.random.default_rng(76)
+    K0 = r.standard_normal((L, d))
+    t = L - 1
+    K, V, P = _tree(L, d, C, k, 77, "f32")
+    cos, sin = O.rope_table(d, C * k, theta)
+    # the candidate lists come from some walk; the teacher from the two heads
+    tr = O.walk(r.standard_normal((2, d)), t, K, C, k, cos, sin, "f32", theta=theta)
+    lowest = min(l for l, lt in tr.levels.items() if lt.scored)
+    lt0 = tr.levels[lowest]
+    u_star = int(lt0.A[len(lt0.A) // 2])            # a non-current candidate
+    tau_star = u_star * C ** lowest + 1
+    K0[tau_star] *= 30.0
+    q1 = 40.0 * O.rotate_exact(K0[tau_star], tau_star - t, theta)
+    qG = np.stack([np.zeros(d), q1])
+    a = O.teacher_attention(qG, t, K0, theta)
+    assert np.allclose(a[0], 1.0 / (t + 1)) and a[1, tau_star] == 1.0
+    y = O.distill_targets(qG, t, tr, K0, C, theta)
+    discriminating = 0
+    for lvl, lt in tr.levels.items():
+        if not lt.scored:
+            assert lvl not in y
+            continue
+        span = C ** lvl
+        nodes = lt.A[:-1]
+        n_u = np.array([min((u + 1) * span, t + 1) - u * span for u in nodes], dtype=np.float64)
+        hit = np.array([u * span <= tau_star < (u + 1) * span for u in nodes], dtype=np.float64)
+        m = 0.5 * (n_u / (t + 1) + hit)
+        assert np.allclose(y[lvl], m / m.sum(), rtol=0, atol=1e-15), lvl
+        if hit.any():
+            discriminating += 1
+            per_head_first = 0.5 * (n_u / n_u.sum() + hit)
+            assert np.abs(per_head_first - y[lvl]).max() > 1e-3
+    assert discriminating >= 1
+
+
+def test_pooler_sigma_is_one_scalar_over_children_and_dims():
+    """R8 reads sigma as one population standard deviation over all C x d
+    child entries.  Without the MLP (W2 = 0) and with g = 1 the key is the
+    attention-pooled child p, whose softmax logits tau w.(x_c - mu)/sigma
+    depend on sigma.  Rotating every child's deviation from mu by one
+    orthogonal matrix Q (and w with it) leaves a scalar over all entries
+    unchanged, so the key is Q-rotated exactly; a per-dimension or a
+    per-child deviation would not be invariant.  Scaling one dimension's
+    deviations by 3 changes the scalar sigma and hence the pooling weights."""
+    r = np.random.default_rng(78)
+    d, n = 8, 5
+    X = r.standard_normal((n, 16, d))
+    w = r.standard_normal(d)
+    Q, _ = np.linalg.qr(r.standard_normal((d, d)))
+    P = _pooler(d, d, 79, w=w, tau=2.0, g=1.0, W2=np.zeros((d, d)), eps=0.0)
+    Pq = _pooler(d, d, 79, w=Q @ w, tau=2.0, g=1.0, W2=np.zeros((d, d)), eps=0.0)
+    mu = X.mean(axis=1, keepdims=True)
+    Xq = mu + (X - mu) @ Q.T
+    k1 = O.pool_keys(X, P)
+    k2 = O.pool_keys(Xq, Pq)
+    assert np.allclose(k2 - mu[:, 0], (k1 - mu[:, 0]) @ Q.T, atol=1e-12)
+    # with a one-hot w, only dimension 0 enters the logits: stretching
+    # dimension 5's deviations changes sigma (a scalar over all entries) and
+    # therefore the weights, which a per-dimension sigma would not do
+    e0 = np.zeros(d)
+    e0[0] = 1.0
+    P0 = _pooler(d, d, 79, w=e0, tau=2.0, g=1.0, W2=np.zeros((d, d)), eps=0.0)
+    Xs = X.copy()
+    Xs[:, :, 5] = mu[:, :, 5] + 3.0 * (X[:, :, 5] - mu[:, :, 5])
+    ks, k0 = O.pool_keys(Xs, P0), O.pool_keys(X, P0)
+    assert np.abs(ks[:, 0] - k0[:, 0]).max() > 1e-3
+
+
 def test_shift_penalty_invariants():
     """Eq. 7: zero without the MLP term (W2 = 0); unchanged by scaling every
     child key by c > 0 (sigma and mu scale by c, m does not) up to eps, and
