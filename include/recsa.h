@@ -212,9 +212,16 @@ int recsa_attn_prefill(const recsa_tree* tree, const void* q, int32_t Hq,
  * ws: recsa_workspace_bytes(tree, Hq, B) bytes whose control block (the last
  * B*Hkv*2112 bytes: 528 32-bit words per (sequence, KV head)) is zero before
  * the first call -- a zero-filled workspace satisfies this -- and is left
- * zero by every call.  Should a group ever wait longer than its bounded
- * spin, word 1 of its block is set to nonzero and its output is NaN.  Calls
- * sharing one ws must not overlap. */
+ * zero by every call that succeeds.  Should a group ever wait longer than
+ * its bounded spin, word 1 of its block (the error word) is set to nonzero
+ * and its output is NaN; the rest of the block is then in an undefined
+ * state, and the caller must zero the whole control block before the next
+ * call with this ws.  Calls sharing one ws must not overlap.
+ * Precondition: the launch sizes each group's workgroups to fit the device
+ * with room to spare, assuming no other kernel occupies it; a kernel running
+ * concurrently on another stream can keep a group's workgroups from being
+ * placed, which then shows as the timeout above (NaN, error word set),
+ * never as a silently wrong result. */
 int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler,
                  const void* k_new, const void* v_new, const void* q, int32_t Hq,
                  const int64_t* pos_dev, int32_t* sel_idx, int32_t* sel_cnt,

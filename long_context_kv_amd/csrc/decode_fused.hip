@@ -301,12 +301,7 @@ __global__ void __launch_bounds__(kFusedThreads)
           wave_sync();
           query_frag_lds<D, G>(reinterpret_cast<const uint16_t*>(sm.at.qt[wid]), qf);
           const f32x4_t c = mfma_logits<D>(qf, kf);
-          const float scale = 1.0f / sqrtf(static_cast<float>(D));
-          if (lane < nvalid && lane < kC) {
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-              out_l[static_cast<int64_t>(g) * CK + p0 + lane] = c[g] * scale;
-          }
+          store_logit_tile<D, G>(c, out_l, CK, p0, nvalid);
         } else {
           KRows<DT, D> kr;               // key rows in flight during the rotation
           group_load_k<DT, D>(rows, 0, nvalid, kr);
@@ -357,6 +352,14 @@ __global__ void __launch_bounds__(kFusedThreads)
   }
   float* o = out + (static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G) * D;
   const float* pp_group = part + slot * kPartSlots * static_cast<int64_t>(G) * (D + kPartHead);
+  __syncthreads();
+  if (s_fail) {
+    // one of this workgroup's waits timed out: its selection and partial may
+    // be built on incomplete data, and the merge may never run (members on
+    // two XCDs count in two L2s), so it poisons the output itself; the error
+    // word is already set
+    for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
+  }
   if constexpr (XL) {
     // ---- the last workgroup to arrive merges (its arrival completes the
     // count, so every partial is in the L2); the others are done
@@ -377,7 +380,10 @@ __global__ void __launch_bounds__(kFusedThreads)
       const uint32_t mask = __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const bool split = __popc(mask) != 1;     // members on more than one XCD
       if (split) atomicOr(err, 2u);
-      s_bad = s_fail | l2_read(counter + 1) | (split ? 1u : 0u);
+      // any member's timed-out wait: in this L2 (word 3) or, device-wide, the
+      // sticky error word
+      s_bad = s_fail | l2_read(counter + 1) | (split ? 1u : 0u) |
+              __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (s_bad) {

@@ -133,4 +133,23 @@ __device__ __forceinline__ f32x4_t mfma_logits(const MFrag<D>& a, const MFrag<D>
   return c;
 }
 
+// Store the logits (times 1/sqrt(D)) of one tile whose A rows are the G
+// query heads (row g = head g) and whose B rows are list positions p0 ..
+// p0+15: head g is output row g, which lane 16*(g/4) + col holds as element
+// g%4 (the C layout above); positions at or past p0 + nvalid are not stored.
+template <int D, int G>
+__device__ __forceinline__ void store_logit_tile(const f32x4_t& c, float* out, int CK, int p0,
+                                                 int nvalid) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int col = lane & 15, rb = lane >> 4;
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  if (col < nvalid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * rb + i;
+      if (g < G) out[static_cast<int64_t>(g) * CK + p0 + col] = c[i] * scale;
+    }
+  }
+}
+
 }  // namespace recsa

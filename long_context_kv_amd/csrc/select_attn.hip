@@ -85,11 +85,7 @@ __global__ void __launch_bounds__(kBlock)
     wave_sync();
     query_frag_lds<D, G>(reinterpret_cast<const uint16_t*>(qt[wid]), qf);
     const f32x4_t c = mfma_logits<D>(qf, kf);
-    const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    if (lane < nvalid && lane < kC) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) out[static_cast<int64_t>(g) * CK + p0 + lane] = c[g] * scale;
-    }
+    store_logit_tile<D, G>(c, out, CK, p0, nvalid);
   } else {
     KRows<DT, D> kr;                       // key rows in flight during the rotation
     group_load_k<DT, D>(rows, 0, nvalid, kr);

@@ -167,6 +167,41 @@ def test_2m_layer_decode_and_prefill_sampled_vs_oracle():
     assert rep2.compared == len(idx) and rep2.imp_levels == 3 * len(idx), rep2
 
 
+def test_config5_4layers_2m_last_decode_step_sampled_vs_oracle():
+    """The 4-layer 2M-token configuration exactly as the benchmark runs it
+    (class Config5): all four layers resident, the full build and the
+    8192-query chunk of every layer, then 256 decode steps of the four layers
+    with fresh inputs.  The last step (token L + 8192 + 255) of the last
+    layer is checked on two KV heads against the oracle; its selection is
+    run again with importances (same bits), which are compared too."""
+    _need_gpu()
+    import bench
+    torch.cuda.empty_cache()
+    c = bench.Config5()
+    for ly in range(c.n_layers):
+        c.build(ly)
+    for ly in range(c.n_layers):
+        c.prefill(ly)
+    for s_ in range(c.steps):
+        c.decode(s_)
+    torch.cuda.synchronize()
+    ly = c.n_layers - 1
+    x = c.layers[ly]
+    tree, Hq = x["tree"], c.wl.Hq
+    assert torch.count_nonzero(R.decode_error_words(c.ws_dec, tree, Hq)).item() == 0
+    q, _, _, pos = x["dec"][c.steps - 1]
+    sel_d, cnt_d = c.sel_dec[ly]
+    out = c.out_dec[ly].cpu().numpy().astype(np.float64).reshape(1, 1, Hq, tree.d)
+    del c.ws_pre
+    torch.cuda.empty_cache()
+    sd, cd, idd = _select_with_importance(tree, q, Hq, 1, pos, sel_d, cnt_d)
+    print(f"config 5: layer {ly}, decode step {c.steps - 1} at t={int(pos[0])}: KV heads 2, 7",
+          flush=True)
+    rep = _check_queries(tree, x["pdict"], q, pos.view(1, 1).cpu(), sd, cd, idd, out, [2, 7],
+                         2e-3)
+    assert rep.compared == 2 and rep.imp_levels == 2 * 3, rep
+
+
 def test_distill_32k_bench_configuration_sampled_vs_oracle():
     """The distillation workload exactly as `bench.py --distill` runs it: a
     32768-token tree at k = 64, every position a query (selection with
