@@ -227,6 +227,25 @@ int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler,
                  const int64_t* pos_dev, int32_t* sel_idx, int32_t* sel_cnt,
                  float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* recsa_decode without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and launch as
+ * recsa_decode, except that the workspace is the library's own device array
+ * of 32 MiB (one per device, set up on the first call on that device and
+ * held until the process ends); the call allocates nothing.  Each call first
+ * zeroes the array's control block with a kernel, so no state carries over
+ * from an earlier call, including one that timed out.  Configurations whose
+ * recsa_workspace_bytes(tree, Hq, B) exceeds 32 MiB return
+ * RECSA_E_WORKSPACE (for example 8 sequences x 8 KV heads at G = 4, k = 256
+ * and 5 levels need 25 MiB; 16 x 8 do not fit).  Every call on one device
+ * shares that device's array: calls that overlap on one device (two streams,
+ * two threads) race and give undefined results.  A timed-out wait makes the
+ * output NaN, as in recsa_decode. */
+int recsa_decode_static(const recsa_tree* tree, const recsa_pooler* pooler,
+                        const void* k_new, const void* v_new, const void* q, int32_t Hq,
+                        const int64_t* pos_dev, int32_t* sel_idx, int32_t* sel_cnt,
+                        float* out, void* stream);
+
 /* ---- Pooler distillation losses (picx.dev Pooler Distillation, Eq. 6 and
  * Eq. 7).  Readings of their operands: the teacher is the dense causal
  * attention of the same G query heads at position t over the level-0 tokens

@@ -4,10 +4,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "recsa_common.hpp"
 #include "recsa_kernels.hpp"
 
 using namespace recsa;
+
+// Workspace of recsa_decode_static: one array per device, held until the
+// process ends.  Host code never uses this name as an address; it takes the
+// device address from hipGetSymbolAddress once per device.
+constexpr size_t kStaticScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -50,8 +58,9 @@ bool pooler_ok(const recsa_pooler* p, const recsa_tree* t) {
   return true;
 }
 
-// Query heads per KV head: 1, 2 or 4.  (8 is switched off: its fused-decode
-// variant runs out of registers and its one GPU run stalled.)
+// Query heads per KV head: 1, 2 or 4.  (8 is switched off: the one GPU run
+// of its fused decode failed, and no cause has been shown; its build needs
+// 256 VGPRs with a 76-byte spill and 119 KB of LDS per workgroup.)
 bool heads_ok(const recsa_tree* t, int32_t Hq) {
   if (Hq < 1 || Hq % t->Hkv != 0) return false;
   const int G = Hq / t->Hkv;
@@ -66,6 +75,36 @@ bool queries_fit(const recsa_tree* t, int32_t T) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RECSA_OK : RECSA_E_HIP; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Zero n 32-bit words (a kernel, not a memset node, so the call stays safe to
+// capture into a graph).
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
 
 }  // namespace
 
@@ -195,6 +234,36 @@ int recsa_decode(const recsa_tree* tree, const recsa_pooler* pooler, const void*
   if (ws_bytes < static_cast<size_t>(w.total)) return RECSA_E_WORKSPACE;
   const hipError_t e = launch_decode_fused(*tree, *pooler, k_new, v_new, q, Hq, pos_dev, sel_idx,
                                            sel_cnt, out, ws, w, static_cast<hipStream_t>(stream));
+  if (e == hipErrorLaunchOutOfResources) return RECSA_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
+int recsa_decode_static(const recsa_tree* tree, const recsa_pooler* pooler, const void* k_new,
+                        const void* v_new, const void* q, int32_t Hq, const int64_t* pos_dev,
+                        int32_t* sel_idx, int32_t* sel_cnt, float* out, void* stream) {
+  int why;
+  if (!tree_ok(tree, &why)) return why;
+  if (!pooler_ok(pooler, tree)) return RECSA_E_INVALID;
+  if (!heads_ok(tree, Hq)) return RECSA_E_UNSUPPORTED;
+  if (!k_new || !v_new || !q || !pos_dev || !sel_idx || !sel_cnt || !out) return RECSA_E_INVALID;
+  if (!a16(k_new) || !a16(v_new) || !a16(q) || !a8(pos_dev) || !a4(sel_idx) || !a4(sel_cnt) ||
+      !a16(out))
+    return RECSA_E_INVALID;
+  const WsLayout w = ws_layout(*tree, Hq, tree->B);
+  if (w.total > static_cast<int64_t>(kStaticScratchBytes)) return RECSA_E_WORKSPACE;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return RECSA_E_HIP;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the control block starts every call at zero (a call that timed out left
+  // it in an undefined state)
+  const int64_t n_ctl = (w.total - w.ctl_off) / 4;
+  zero_words_kernel<<<static_cast<unsigned>((n_ctl + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + w.ctl_off), n_ctl);
+  e = hipGetLastError();
+  if (e != hipSuccess) return RECSA_E_HIP;
+  e = launch_decode_fused(*tree, *pooler, k_new, v_new, q, Hq, pos_dev, sel_idx, sel_cnt, out, ws,
+                          w, s);
   if (e == hipErrorLaunchOutOfResources) return RECSA_E_UNSUPPORTED;
   return hip_status(e);
 }

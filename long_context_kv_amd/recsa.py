@@ -30,7 +30,8 @@ EXPORTS = (
     "recsa_status_string", "recsa_level_rows", "recsa_levels_needed",
     "recsa_init_rope", "recsa_workspace_bytes", "recsa_build_tree",
     "recsa_append_decode", "recsa_select", "recsa_attn_decode",
-    "recsa_attn_prefill", "recsa_decode", "recsa_distill_workspace_bytes",
+    "recsa_attn_prefill", "recsa_decode", "recsa_decode_static",
+    "recsa_distill_workspace_bytes",
     "recsa_distill_kl", "recsa_shift_workspace_bytes", "recsa_shift_penalty",
     "recsa_pooler_backward_workspace_bytes", "recsa_pooler_backward",
     "recsa_distill_key_grad_workspace_bytes", "recsa_distill_key_grad",
@@ -96,6 +97,7 @@ def lib():
             "recsa_attn_decode": (ctypes.c_int, [T, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "recsa_attn_prefill": (ctypes.c_int, [T, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "recsa_decode": (ctypes.c_int, [T, P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "recsa_decode_static": (ctypes.c_int, [T, P, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
             "recsa_distill_workspace_bytes": (sz, [T, i32, i64]),
             "recsa_distill_kl": (ctypes.c_int, [T, vp, i32, i32, vp, vp, vp, vp,
                                                  ctypes.c_double, vp, vp, vp, sz, vp]),
@@ -348,6 +350,14 @@ def recsa_decode(tree, pooler, k_new, v_new, q, Hq: int, pos_dev, sel_idx, sel_c
     _check("recsa_decode", lib().recsa_decode(
         ctypes.byref(tc), ctypes.byref(pc), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, _ptr(pos_dev),
         _ptr(sel_idx), _ptr(sel_cnt), _ptr(out), _ptr(ws), nb, _stream(stream)))
+
+
+def recsa_decode_static(tree, pooler, k_new, v_new, q, Hq: int, pos_dev, sel_idx, sel_cnt, out,
+                        stream=None):
+    tc, pc = _tc(tree), _pc(pooler)
+    _check("recsa_decode_static", lib().recsa_decode_static(
+        ctypes.byref(tc), ctypes.byref(pc), _ptr(k_new), _ptr(v_new), _ptr(q), Hq, _ptr(pos_dev),
+        _ptr(sel_idx), _ptr(sel_cnt), _ptr(out), _stream(stream)))
 
 
 def recsa_distill_workspace_bytes(tree, Hq: int, n_queries: int) -> int:

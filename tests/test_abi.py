@@ -335,3 +335,34 @@ def test_misaligned_distillation_arrays_are_rejected_without_launch():
         a = list(ok)
         a[i] = ok[i] + 8
         assert L.recsa_decode(*a) == R.RECSA_E_INVALID, i
+
+
+def test_static_decode_validation_and_scratch_limit():
+    """recsa_decode_static validates like recsa_decode (nothing is launched
+    on an error) and rejects configurations whose workspace exceeds its
+    32 MiB device array: 8 sequences x 8 KV heads at G = 4, k = 256 and 5
+    levels need 25 MiB and pass validation; 16 x 8 need 51 MiB."""
+    L = R.lib()
+    b = ctypes.byref
+    p = _pooler()
+    ok = [None, b(p), 0x10, 0x10, 0x10, 32, 0x10, 0x10, 0x10, 0x10, None]
+    t = _tree(B=8, L_cap=1 << 20, n_levels=5)
+    for lvl in range(5):
+        t.K[lvl], t.V[lvl], t.Kr[lvl] = 0x1000 * (lvl + 1), 0x2000 * (lvl + 1), 0x5000 * (lvl + 1)
+    need = L.recsa_workspace_bytes(b(t), 32, 8)
+    assert 24 << 20 < need <= 32 << 20
+    big = _tree(B=16, L_cap=1 << 20, n_levels=5)
+    for lvl in range(5):
+        big.K[lvl], big.V[lvl], big.Kr[lvl] = t.K[lvl], t.V[lvl], t.Kr[lvl]
+    assert L.recsa_workspace_bytes(b(big), 32, 16) > 32 << 20
+    a = list(ok)
+    a[0] = b(big)
+    assert L.recsa_decode_static(*a) == R.RECSA_E_WORKSPACE
+    for i, bad in ((2, 0x18), (3, 0x18), (4, 0x18), (6, 0x14), (9, 0x18), (6, None)):
+        a = list(ok)
+        a[0] = b(_tree())
+        a[i] = bad
+        assert L.recsa_decode_static(*a) == R.RECSA_E_INVALID, (i, bad)
+    a = list(ok)
+    a[0], a[5] = b(_tree()), 64                                   # G = 8: off
+    assert L.recsa_decode_static(*a) == R.RECSA_E_UNSUPPORTED
