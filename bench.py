@@ -117,7 +117,7 @@ class Work:
     """Device-resident state of one benchmark workload (see module doc)."""
 
 
-def setup_workload(name="524k", dev="cuda", level0_host=False, n_decode=1):
+def setup_workload(name="524k", dev="cuda", level0_host=False, n_decode=1, rotated_keys=True):
     """Build the inputs of a workload in HBM and return the step closures.
 
     Level-0 K/V of L tokens plus the prefill chunk's rows and the rows of
@@ -146,7 +146,8 @@ def setup_workload(name="524k", dev="cuda", level0_host=False, n_decode=1):
     w.pdict = synth.pooler_params(d, d, dev, wl.seed)
     w.pool = R.Pooler.from_dict(w.pdict, dev)
     w.tree = R.Tree.allocate(B, Hkv, d, L_cap, k=wl.k, dtype=wl.dtype, device=dev,
-                             level0=(K0, V0), theta=wl.theta, level0_host=level0_host)
+                             level0=(K0, V0), theta=wl.theta, level0_host=level0_host,
+                             rotated_keys=rotated_keys)
     tree = w.tree
     if level0_host:
         del K0, V0                              # level 0 now lives in pinned host memory
@@ -223,6 +224,9 @@ def main():
     ap.add_argument("--workload", default="524k")
     ap.add_argument("--decode-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rotated-keys", action="store_true",
+                    help="keep no rotated-key copy Kr (K/V-only tree, 1/15 overhead): the "
+                         "kernels rotate the key rows they read")
     ap.add_argument("--no-config5", action="store_true",
                     help="skip the 4-layer 2M-token configuration after the headline")
     ap.add_argument("--pmc-pass", action="store_true",
@@ -257,7 +261,7 @@ def main():
         bench_offload(args)
         return
     n_dec = max(args.decode_reps, args.warmup + args.steps)
-    w = setup_workload(args.workload, n_decode=n_dec)
+    w = setup_workload(args.workload, n_decode=n_dec, rotated_keys=not args.no_rotated_keys)
     wl, tree, pool, R = w.wl, w.tree, w.pool, w.R
     L, T, B, Hkv, Hq, d = w.L, w.T, wl.B, wl.Hkv, wl.Hq, wl.d
     t_dec = w.t_dec
@@ -426,7 +430,9 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: 1 layer, {Hkv} KV heads, {Hq} query heads, d={d}, "
-                               f"{wl.dtype}, L={L}, C=16, k={wl.k}; per step a prefill chunk "
+                               f"{wl.dtype}, L={L}, C=16, k={wl.k}"
+                               f"{'' if tree.Kr[0].numel() else ', no rotated-key copy'}; "
+                               f"per step a prefill chunk "
                                f"T={T} at [{L},{L + T}) then decode B={B} of a new token from "
                                f"t={t_dec} with fresh q/k/v",
                    "seq_len": L, "global_batch": B, "prefill_T": T},

@@ -80,17 +80,23 @@ extern "C" {
  *   in the storage dtype; level 0 is the ordinary KV cache (pre-RoPE keys).
  *   Only complete nodes are ever written: node i of level l covers tokens
  *   [i*C^l, (i+1)*C^l).
- * Kr[l]: the same layout; row i holds the key half of the split RoPE,
- *   rnd(R(i mod C) K[l][i]) (see the logit below), which depends on the row
- *   alone.  The library writes it for every row it writes (nodes built or
- *   appended, the appended token) and, in recsa_build_tree, for the level-0
- *   rows of the given token range; selection and attention read keys only
- *   from Kr.  The caller allocates it like K.
+ * Kr[l]: optional -- every level NULL, or every level with rows set (a mix
+ *   is RECSA_E_INVALID).  NULL: the tree is K and V only, and levels >= 1 add
+ *   1/15 of the KV cache (picx.dev Practical Implications: under 7%); the
+ *   kernels rotate each key row they read.  Set: a speed path that costs one
+ *   more array of K's size (the cache grows to 1.5x K+V), laid out like K,
+ *   whose row i holds the key half of the split RoPE, rnd(R(i mod C)
+ *   K[l][i]) (see the logit below), which depends on the row alone; the
+ *   library writes it for every row it writes (nodes built or appended, the
+ *   appended token) and, in recsa_build_tree, for the level-0 rows of the
+ *   given token range, and selection and attention then read keys from it.
+ *   Both forms give identical results (the in-kernel rotation uses the same
+ *   float32 rotation and rounding).
  * n_levels: levels allocated, >= recsa_levels_needed(L_cap, C, k) (so the
  *   list of the top level has at most k nodes for every position < L_cap);
  *   more levels do not change any result.
  * rope: float32 table [C*k][d/2][2] of (cos, sin), filled by recsa_init_rope.
- * Level 0 (K[0], V[0], Kr[0]) may be page-locked host memory that the device
+ * Level 0 (K[0], V[0] and Kr[0] if kept) may be page-locked host memory that the device
  * can address (hipHostMalloc; pass the address hipHostGetDevicePointer
  * returns): every call then reads and writes the level-0 rows it needs in
  * place over PCIe, with identical results, while levels >= 1 (1/15 of the
@@ -155,9 +161,9 @@ int recsa_init_rope(float* table, int32_t d, int32_t n_pos, double theta, void* 
 size_t recsa_workspace_bytes(const recsa_tree* tree, int32_t Hq, int64_t n_queries);
 
 /* Tree Construction (Eq. 1, Eq. 5): write the rotated keys Kr[0] of the
- * level-0 rows [tok_begin, tok_end), then (re)compute every complete node, at
- * every level >= 1, whose last token lies in [tok_begin, tok_end), with its
- * rotated key.  Level-0 rows [0, tok_end) must already be written.  Nodes are
+ * level-0 rows [tok_begin, tok_end) (when the tree keeps Kr), then
+ * (re)compute every complete node, at every level >= 1, whose last token lies
+ * in [tok_begin, tok_end), with its rotated key.  Level-0 rows [0, tok_end) must already be written.  Nodes are
  * computed level by level, each from the stored (rounded) children.
  * 0 <= tok_begin <= tok_end <= L_cap. */
 int recsa_build_tree(const recsa_tree* tree, const recsa_pooler* pooler,

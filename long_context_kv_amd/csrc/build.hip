@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(NT) build_level_kernel(recsa_tree tr, recsa_po
   const T* vc = static_cast<const T*>(tr.V[level - 1]) + (head * rows_up + first * kC) * D;
   T* ko = static_cast<T*>(tr.K[level]) + (head * rows + first) * D;
   T* vo = static_cast<T*>(tr.V[level]) + (head * rows + first) * D;
-  T* kro = static_cast<T*>(tr.Kr[level]) + (head * rows + first) * D;
+  T* kro = tr.Kr[level] ? static_cast<T*>(tr.Kr[level]) + (head * rows + first) * D : nullptr;
   pool_tile<DT, D, NODES, NT>(kc, vc, ko, vo, kro, static_cast<int>(first % kC), tr.rope,
                               n_valid, P, sm);
 }
@@ -112,8 +112,9 @@ __global__ void __launch_bounds__(kBlock) append_kernel(recsa_tree tr, recsa_poo
       kd[i] = ks[i];
       vd[i] = vs[i];
     }
-    rotate_key_row<DT, D>(ks, static_cast<T*>(tr.Kr[0]) + (head * tr.L_cap + t) * D,
-                          static_cast<int>(t % kC), tr.rope, threadIdx.x, kBlock);
+    if (tr.Kr[0])
+      rotate_key_row<DT, D>(ks, static_cast<T*>(tr.Kr[0]) + (head * tr.L_cap + t) * D,
+                            static_cast<int>(t % kC), tr.rope, threadIdx.x, kBlock);
   }
   int64_t span = 1;
   for (int l = 1; l < tr.n_levels; ++l) {
@@ -128,7 +129,7 @@ __global__ void __launch_bounds__(kBlock) append_kernel(recsa_tree tr, recsa_poo
     const T* vc = static_cast<const T*>(tr.V[l - 1]) + (head * rows_up + node * kC) * D;
     T* ko = static_cast<T*>(tr.K[l]) + (head * rows + node) * D;
     T* vo = static_cast<T*>(tr.V[l]) + (head * rows + node) * D;
-    T* kro = static_cast<T*>(tr.Kr[l]) + (head * rows + node) * D;
+    T* kro = tr.Kr[l] ? static_cast<T*>(tr.Kr[l]) + (head * rows + node) * D : nullptr;
     pool_tile<DT, D, 1, kBlock>(kc, vc, ko, vo, kro, static_cast<int>(node % kC), tr.rope, 1, P,
                                 sm);
     __syncthreads();
@@ -146,7 +147,7 @@ hipError_t launch_rope_table(float* table, int d, int n_pos, double theta, hipSt
 template <int DT, int D>
 static hipError_t build_impl(const recsa_tree& tr, const recsa_pooler& P, int64_t tb, int64_t te,
                              hipStream_t s) {
-  {
+  if (tr.Kr[0]) {                                     // the rotated-key copy, when kept
     constexpr int RPB = kBlock / (D / 16);            // rows per workgroup
     dim3 grid(static_cast<unsigned>((te - tb + RPB - 1) / RPB), tr.Hkv, tr.B);
     rotate_level0_kernel<DT, D><<<grid, kBlock, 0, s>>>(tr, tb, te);

@@ -250,8 +250,9 @@ __global__ void __launch_bounds__(kFusedThreads)
       kd[i] = k_t[i];
       vd[i] = v_t[i];
     }
-    rotate_key_row<DT, D>(k_t, static_cast<T*>(tr.Kr[0]) + (slot * tr.L_cap + t) * D,
-                          static_cast<int>(t % kC), tr.rope, tid, NT);
+    if (tr.Kr[0])
+      rotate_key_row<DT, D>(k_t, static_cast<T*>(tr.Kr[0]) + (slot * tr.L_cap + t) * D,
+                            static_cast<int>(t % kC), tr.rope, tid, NT);
     int64_t span = 1;
     for (int l = 1; l < tr.n_levels; ++l) {
       span *= kC;
@@ -265,7 +266,8 @@ __global__ void __launch_bounds__(kFusedThreads)
                               static_cast<const T*>(tr.V[l - 1]) + (slot * rows_up + node * kC) * D,
                               static_cast<T*>(tr.K[l]) + (slot * rows + node) * D,
                               static_cast<T*>(tr.V[l]) + (slot * rows + node) * D,
-                              static_cast<T*>(tr.Kr[l]) + (slot * rows + node) * D,
+                              tr.Kr[l] ? static_cast<T*>(tr.Kr[l]) + (slot * rows + node) * D
+                                       : nullptr,
                               static_cast<int>(node % kC), tr.rope, 1, P, sm.pl);
       __syncthreads();
     }
@@ -292,12 +294,15 @@ __global__ void __launch_bounds__(kFusedThreads)
       for (int gi = w + W * wid; gi < ng; gi += W * NW) {
         const int p0 = gi * kC;
         const int nvalid = min(kC, n - p0);
-        const T* rows = static_cast<const T*>(tr.Kr[l]) + (slot * rows_l + lv.node(p0)) * D;
+        const bool raw = tr.Kr[l] == nullptr;     // no rotated copy: rotate the rows here
+        const T* rows = static_cast<const T*>(raw ? tr.K[l] : tr.Kr[l]) +
+                        (slot * rows_l + lv.node(p0)) * D;
         const int phi = p_q - p0;        // = C (r_q - r) + c_q, r = p0 / C
         if constexpr (DT == RECSA_BF16) {
           MFrag<D> kf, qf;               // key rows in flight during the rotation
           load_key_frag<D>(rows, nvalid, kf);
           rotate_query<DT, D, G>(qs, sm.at.qt[wid], phi, tr.rope);
+          if (raw) rotate_key_frag<D>(kf, tr.rope);
           wave_sync();
           query_frag_lds<D, G>(reinterpret_cast<const uint16_t*>(sm.at.qt[wid]), qf);
           const f32x4_t c = mfma_logits<D>(qf, kf);
@@ -308,7 +313,7 @@ __global__ void __launch_bounds__(kFusedThreads)
           rotate_query<DT, D, G>(qs, sm.at.qt[wid], phi, tr.rope);
           wave_sync();
           float lg[G];
-          group_logits_from<DT, D, G>(kr, 0, nvalid, sm.at.qt[wid], tr.rope, lg);
+          group_logits_any<DT, D, G>(raw, kr, 0, nvalid, sm.at.qt[wid], tr.rope, lg);
           const int c = lane >> 2, s = lane & 3;
           if (c < nvalid) {
 #pragma unroll

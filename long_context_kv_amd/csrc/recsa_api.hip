@@ -42,8 +42,12 @@ bool tree_ok(const recsa_tree* t, int* why) {
   if (t->L_cap > (int64_t{1} << 40)) return false;
   if (t->n_levels < recsa_levels_needed(t->L_cap, t->C, t->k)) return false;
   if (!t->rope || !a16(t->rope)) return false;
+  // the rotated-key copy Kr is optional, but all or nothing
+  const bool has_kr = t->Kr[0] != nullptr;
   for (int l = 0; l < t->n_levels; ++l) {
-    if (level_rows_host(t->L_cap, l) > 0 && (!t->K[l] || !t->V[l] || !t->Kr[l])) return false;
+    if (level_rows_host(t->L_cap, l) > 0 &&
+        (!t->K[l] || !t->V[l] || (has_kr != (t->Kr[l] != nullptr))))
+      return false;
     if (!a16(t->K[l]) || !a16(t->V[l]) || !a16(t->Kr[l])) return false;
   }
   return true;

@@ -141,6 +141,19 @@ __device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int ro
   }
 }
 
+// group_logits_from on rows that are either the stored rotated keys Kr
+// (rot false) or raw keys rotated here (rot true: the tree keeps no Kr);
+// both give the same bits.
+template <int DT, int D, int G>
+__device__ __forceinline__ void group_logits_any(bool rot, const KRows<DT, D>& kr, int row_lo,
+                                                 int nvalid, const float* qt,
+                                                 const float* __restrict__ rope, float* lg) {
+  if (rot)
+    group_logits_from<DT, D, G, true>(kr, row_lo, nvalid, qt, rope, lg);
+  else
+    group_logits_from<DT, D, G, false>(kr, row_lo, nvalid, qt, rope, lg);
+}
+
 // Rotate the G query heads by phi and round (one wave): qt = rnd(R(phi) q),
 // the query half of the split RoPE.  Layout of qt: float [G][D] for fp32
 // storage; for bf16 storage the rounded values are packed two per 32-bit
@@ -781,6 +794,9 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
   }
   const int n_groups = eg.total();
   const int n_chunks = (n_groups + NG - 1) / NG;
+  // level-0 key rows: the stored rotated copy, or raw rows rotated here
+  const bool raw0 = tr.Kr[0] == nullptr;
+  const void* kbase0 = raw0 ? tr.K[0] : tr.Kr[0];
 #pragma unroll 1
   for (int ci = g_lo + wid * g_step; ci < n_chunks; ci += NW * g_step) {
     // ---- this lane's entry: row lane % 16 of group ci*NG + lane / 16
@@ -810,7 +826,7 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
         const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
         const int len = __builtin_amdgcn_readlane(lv.len, lead);
         const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
-        const T* krow0 = static_cast<const T*>(lane_ptr(static_cast<const T*>(tr.Kr[0]) +
+        const T* krow0 = static_cast<const T*>(lane_ptr(static_cast<const T*>(kbase0) +
                                                             (seq_head * rows_l + node) * D, lead));
         const int ovr = k_t ? len - 1 - p0 : -1;          // row of token t, if in this group
         group_load_k<DT, D>(krow0, 0, (ovr >= 0 && ovr < kC) ? ovr : nv, ka[gg]);
@@ -895,12 +911,12 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
         KRows<DT, D> kb;
         group_load_k<DT, D>(k_t - static_cast<int64_t>(ovr) * D, ovr, ovr + 1, kb);
         float a[G], b[G];
-        group_logits_from<DT, D, G>(ka[gg], 0, ovr, sm.qt[wid], tr.rope, a);
+        group_logits_any<DT, D, G>(raw0, ka[gg], 0, ovr, sm.qt[wid], tr.rope, a);
         group_logits_from<DT, D, G, true>(kb, ovr, ovr + 1, sm.qt[wid], tr.rope, b);
 #pragma unroll
         for (int g = 0; g < G; ++g) lgv[g] = (c == ovr) ? b[g] : a[g];
       } else {
-        group_logits_from<DT, D, G>(ka[gg], 0, nv, sm.qt[wid], tr.rope, lgv);
+        group_logits_any<DT, D, G>(raw0, ka[gg], 0, nv, sm.qt[wid], tr.rope, lgv);
       }
       if (s == 0) {
 #pragma unroll

@@ -122,6 +122,36 @@ __device__ __forceinline__ void rotate_frag(const uint16_t* __restrict__ qrow,
   }
 }
 
+// The key half of the split RoPE applied in registers to a B operand loaded
+// from raw (unrotated) key rows: lane l holds row l%16 of a 16-row group
+// aligned to a multiple of 16 nodes, so its in-group offset is l%16, and it
+// rotates its own 8 pairs per block pair by that offset and rounds --
+// rnd(R(c) K), the value the stored rotated rows Kr hold, bit for bit.
+template <int D>
+__device__ __forceinline__ void rotate_key_frag(MFrag<D>& f, const float* __restrict__ rope) {
+  constexpr int HKB = D / 64;
+  RopeFrag<D> r;
+  load_rope_frag<D>(threadIdx.x & 15, rope, r);
+#pragma unroll
+  for (int kb = 0; kb < HKB; ++kb) {
+    const uint32_t xa[4] = {f.w[kb].x, f.w[kb].y, f.w[kb].z, f.w[kb].w};
+    const uint32_t ya[4] = {f.w[kb + HKB].x, f.w[kb + HKB].y, f.w[kb + HKB].z, f.w[kb + HKB].w};
+    uint32_t xo[4], yo[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x0, y0, x1, y1;
+      rope_pair(__uint_as_float(xa[v] << 16), __uint_as_float(ya[v] << 16), r.cs[kb][v].x,
+                r.cs[kb][v].y, x0, y0);
+      rope_pair(__uint_as_float(xa[v] & 0xFFFF0000u), __uint_as_float(ya[v] & 0xFFFF0000u),
+                r.cs[kb][v].z, r.cs[kb][v].w, x1, y1);
+      xo[v] = pack_bf16x2(x0, x1);
+      yo[v] = pack_bf16x2(y0, y1);
+    }
+    f.w[kb] = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+    f.w[kb + HKB] = make_uint4(yo[0], yo[1], yo[2], yo[3]);
+  }
+}
+
 // C = A B^T over the D dims, k blocks in ascending order (unscaled).
 template <int D>
 __device__ __forceinline__ f32x4_t mfma_logits(const MFrag<D>& a, const MFrag<D>& b) {

@@ -242,7 +242,9 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
   }
   __syncthreads();
 
-  // ---- phase 5: rotated keys from the stored (rounded) node keys
+  // ---- phase 5: rotated keys from the stored (rounded) node keys, when the
+  // tree keeps them (kro null: not kept)
+  if (kro == nullptr) return;
   constexpr int H2 = D / 2;
   for (int item = threadIdx.x; item < NODES * H2; item += NT) {
     const int n = item / H2, jj = item % H2;

@@ -75,13 +75,16 @@ __global__ void __launch_bounds__(kBlock)
   const int p_q = lv.len - 1;
   const int nvalid = min(kC, n_others - p0);
   const int64_t rows_l = level_rows_dev(tr.L_cap, level);
-  const T_* rows = static_cast<const T_*>(tr.Kr[level]) + (qc.seq_head * rows_l + lv.node(p0)) * D;
+  const bool raw = tr.Kr[level] == nullptr;        // no rotated copy: rotate the key rows here
+  const T_* rows = static_cast<const T_*>(raw ? tr.K[level] : tr.Kr[level]) +
+                   (qc.seq_head * rows_l + lv.node(p0)) * D;
   const int phi = p_q - p0;                 // = C (r_q - r) + c_q, r = p0 / C
   float* out = ws_logits + (qc.slot * n_sel + (level - 1)) * static_cast<int64_t>(G) * CK;
   if constexpr (DT == RECSA_BF16) {
     MFrag<D> kf, qf;                       // key rows in flight during the rotation
     load_key_frag<D>(rows, nvalid, kf);
     rotate_query<DT, D, G>(qs, qt[wid], phi, tr.rope);
+    if (raw) rotate_key_frag<D>(kf, tr.rope);
     wave_sync();
     query_frag_lds<D, G>(reinterpret_cast<const uint16_t*>(qt[wid]), qf);
     const f32x4_t c = mfma_logits<D>(qf, kf);
@@ -92,7 +95,7 @@ __global__ void __launch_bounds__(kBlock)
     rotate_query<DT, D, G>(qs, qt[wid], phi, tr.rope);
     wave_sync();
     float lg[G];
-    group_logits_from<DT, D, G>(kr, 0, nvalid, qt[wid], tr.rope, lg);
+    group_logits_any<DT, D, G>(raw, kr, 0, nvalid, qt[wid], tr.rope, lg);
     const int c = lane >> 2, s = lane & 3;
     if (c < nvalid) {
 #pragma unroll
@@ -291,6 +294,7 @@ __global__ void __launch_bounds__(kBlock)
   const int64_t rows_l = level_rows_dev(tr.L_cap, level);
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const bool raw = tr.Kr[level] == nullptr;        // no rotated copy: rotate the key rows here
   const int n_tiles = *ba.n_tiles;
   for (int tl = blockIdx.x * NW + wid; tl < n_tiles; tl += gridDim.x * NW) {
     const uint4 tile = ba.tiles[tl];
@@ -298,8 +302,10 @@ __global__ void __launch_bounds__(kBlock)
     const int64_t sh = tile.z, u = tile.w;
     const int j = static_cast<int>(sh % tr.Hkv);
     MFrag<D> kf;
-    load_key_frag<D>(static_cast<const uint16_t*>(tr.Kr[level]) + (sh * rows_l + u * kC) * D,
+    load_key_frag<D>(static_cast<const uint16_t*>(raw ? tr.K[level] : tr.Kr[level]) +
+                         (sh * rows_l + u * kC) * D,
                      static_cast<int>(min<int64_t>(kC, rows_l - u * kC)), kf);
+    if (raw) rotate_key_frag<D>(kf, tr.rope);
     uint2 nxt = first + m < end ? ba.entries[first + m] : make_uint2(0u, 0u);
     for (int64_t e0 = first; e0 < end; e0 += kC) {
       const uint2 ent = nxt;                         // A row m: entry e0 + m

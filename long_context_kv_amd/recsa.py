@@ -168,7 +168,9 @@ class Tree:
 
     K[l], V[l]: [B, Hkv, floor(L_cap / 16^l), d] in the storage dtype; level 0
     is the KV cache itself (pre-RoPE keys).  Kr[l]: the same shape, the rotated
-    keys the library writes next to every key row.  rope: [C*k, d/2, 2]
+    keys the library writes next to every key row -- or, with
+    rotated_keys=False, empty tensors (passed as NULL: the kernels then rotate
+    the key rows they read, with the same bits).  rope: [C*k, d/2, 2]
     float32.  With level0_host, K[0], V[0] and Kr[0] are pinned host tensors
     that the kernels read and write in place over PCIe (level0_dptr holds
     their device addresses); levels >= 1 stay in device memory."""
@@ -188,23 +190,24 @@ class Tree:
 
     @staticmethod
     def allocate(B, Hkv, d, L_cap, k=256, C=16, dtype="bf16", n_levels=None,
-                 device="cuda", theta=1e6, level0=None, level0_host=False):
+                 device="cuda", theta=1e6, level0=None, level0_host=False,
+                 rotated_keys=True):
         n = n_levels or max(2, recsa_levels_needed(L_cap, C, k))
         tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
         K, V, Kr = [], [], []
         for lvl in range(n):
             rows = recsa_level_rows(L_cap, C, lvl)
+            kr_rows = rows if rotated_keys else 0
             if lvl == 0 and level0_host:
-                shape = (B, Hkv, rows, d)
-                pin = lambda: torch.zeros(shape, dtype=tdt, pin_memory=True)
-                Kr.append(pin())
-                K.append(pin())
-                V.append(pin())
+                pin = lambda r: torch.zeros((B, Hkv, r, d), dtype=tdt, pin_memory=True)
+                Kr.append(pin(kr_rows))
+                K.append(pin(rows))
+                V.append(pin(rows))
                 if level0 is not None:
                     K[0].copy_(level0[0])
                     V[0].copy_(level0[1])
                 continue
-            Kr.append(torch.zeros((B, Hkv, rows, d), dtype=tdt, device=device))
+            Kr.append(torch.zeros((B, Hkv, kr_rows, d), dtype=tdt, device=device))
             if lvl == 0 and level0 is not None:
                 K.append(level0[0])
                 V.append(level0[1])
@@ -215,7 +218,7 @@ class Tree:
         recsa_init_rope(rope, d, C * k, theta)
         dptr = None
         if level0_host:
-            dptr = tuple(host_device_pointer(x) for x in (K[0], V[0], Kr[0]))
+            dptr = tuple(host_device_pointer(x) if x.numel() else None for x in (K[0], V[0], Kr[0]))
         return Tree(B, Hkv, d, L_cap, k, C, dtype, n, K, V, Kr, rope, dptr)
 
     def c(self) -> TreeC:

@@ -366,3 +366,23 @@ def test_static_decode_validation_and_scratch_limit():
     a = list(ok)
     a[0], a[5] = b(_tree()), 64                                   # G = 8: off
     assert L.recsa_decode_static(*a) == R.RECSA_E_UNSUPPORTED
+
+
+def test_rotated_key_copy_is_all_or_nothing():
+    """Kr may be absent (every level NULL: the kernels rotate raw key rows),
+    but a tree with it at some levels and not at others is invalid."""
+    L = R.lib()
+    b = ctypes.byref
+    p = _pooler()
+    none = _tree()
+    for lvl in range(4):
+        none.Kr[lvl] = None
+    # validation passes (an empty token range launches nothing)
+    assert L.recsa_build_tree(b(none), b(p), 5, 5, None) == R.RECSA_OK
+    assert L.recsa_workspace_bytes(b(none), 32, 1) > 0
+    mixed = _tree()
+    mixed.Kr[2] = None
+    assert L.recsa_build_tree(b(mixed), b(p), 5, 5, None) == R.RECSA_E_INVALID
+    mixed0 = _tree()
+    mixed0.Kr[0] = None
+    assert L.recsa_workspace_bytes(b(mixed0), 32, 1) == 0

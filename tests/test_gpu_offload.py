@@ -38,7 +38,8 @@ def _pair(B, Hkv, d, L_cap, k, dtype, seed):
     host = R.Tree.allocate(B, Hkv, d, L_cap, k=k, dtype=dtype, device=DEV, level0=(K, V),
                            level0_host=True)
     assert host.K[0].device.type == "cpu" and host.K[0].is_pinned()
-    assert host.level0_dptr is not None and all(p != 0 for p in host.level0_dptr)
+    assert host.level0_dptr is not None and all(host.level0_dptr[:2])
+    assert (host.level0_dptr[2] is None) == (host.Kr[0].numel() == 0)
     return dev, host, R.Pooler.from_dict(pdict, DEV), pdict
 
 
