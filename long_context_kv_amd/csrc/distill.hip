@@ -89,21 +89,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // lse: [B*T][Hkv][ng_cap][G] float32 group log-sum-exps in base-2 units
 // (log2 of the sum of 2^(logit log2 e)); entry (v, h) is written for every
 // level-1 group v <= t/16 of the row's query, never beyond.
-__device__ __forceinline__ void split_bf16x8(const float* v, uint4& hi, uint4& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint16_t a = f32_to_bf16_bits(v[2 * i]), b = f32_to_bf16_bits(v[2 * i + 1]);
-    const float ar = v[2 * i] - bf16_bits_to_f32(a);          // exact in float32
-    const float br = v[2 * i + 1] - bf16_bits_to_f32(b);
-    h[i] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
-    l[i] = static_cast<uint32_t>(f32_to_bf16_bits(ar)) |
-           (static_cast<uint32_t>(f32_to_bf16_bits(br)) << 16);
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
 // Every level-0 key row rotated at its absolute position and split once:
 // ksplit[b][j][tau] = {hi[D], lo[D]} (bf16), each thread 8 RoPE pairs of one
 // row.  The key tiles of every query block are then plain 16-byte loads.

@@ -152,6 +152,23 @@ __device__ __forceinline__ void rotate_key_frag(MFrag<D>& f, const float* __rest
   }
 }
 
+// Split 8 float32 values into bf16 halves, hi = rnd(x) and lo = rnd(x - hi),
+// packed two per word: hi + lo holds x to about 2^-17 relative, so that
+// hi.hi + hi.lo + lo.hi on the matrix cores gives a float32-level product.
+__device__ __forceinline__ void split_bf16x8(const float* x, uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint16_t a = f32_to_bf16_bits(x[2 * v]), b = f32_to_bf16_bits(x[2 * v + 1]);
+    const float ra = x[2 * v] - bf16_bits_to_f32(a), rb = x[2 * v + 1] - bf16_bits_to_f32(b);
+    h[v] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+    l[v] = static_cast<uint32_t>(f32_to_bf16_bits(ra)) |
+           (static_cast<uint32_t>(f32_to_bf16_bits(rb)) << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
 // C = A B^T over the D dims, k blocks in ascending order (unscaled).
 template <int D>
 __device__ __forceinline__ f32x4_t mfma_logits(const MFrag<D>& a, const MFrag<D>& b) {

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "recsa_common.hpp"
+#include "recsa_mfma.hpp"
 
 namespace recsa {
 
@@ -17,12 +18,159 @@ namespace recsa {
 // With STATS set (the shift penalty of Eq. 7) nothing is stored: phases 4-5
 // are replaced by the tile's sums of sigma*m (D values) and of ||mu||^2,
 // written to stats[0 .. D]; vc, vo, ko and kro are not used.
+// Wave totals of 16 per-lane values at once: a reduce-scatter over the lane
+// bits (each step keeps half the values and adds the partner lane's other
+// half), so lane l ends with the total of value l % 16; then every lane reads
+// the 16 totals back.  About 60 instructions instead of 16 separate
+// reductions.
+__device__ __forceinline__ void wave_sum16(float (&v)[16]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float a[8];
+  {
+    const bool hi = lane & 1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float keep = hi ? v[2 * j + 1] : v[2 * j];
+      const float send = hi ? v[2 * j] : v[2 * j + 1];
+      a[j] = keep + dpp_movf<dpp::kXor1>(0.f, send);
+    }
+  }
+  float b[4];                           // value 4 j + 2 bit1 + bit0 of the lane
+  {
+    const bool hi = lane & 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float keep = hi ? a[2 * j + 1] : a[2 * j];
+      const float send = hi ? a[2 * j] : a[2 * j + 1];
+      b[j] = keep + dpp_movf<dpp::kXor2>(0.f, send);
+    }
+  }
+  float c2[2];
+  {
+    const bool hi = lane & 4;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float keep = hi ? b[2 * j + 1] : b[2 * j];
+      const float send = hi ? b[2 * j] : b[2 * j + 1];
+      c2[j] = keep + __shfl_xor(send, 4, kWave);
+    }
+  }
+  float t;
+  {
+    const bool hi = lane & 8;
+    const float keep = hi ? c2[1] : c2[0];
+    const float send = hi ? c2[0] : c2[1];
+    t = keep + __shfl_xor(send, 8, kWave);
+  }
+  t += __shfl_xor(t, 16, kWave);
+  t += __shfl_xor(t, 32, kWave);
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    v[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), c));
+}
+
 template <int DT, int D, int NODES>
 struct PoolSmem {
-  float feat[NODES][2 * D];
-  float hid[NODES][256];
-  float m[NODES][D];
+  // rows padded by 16 bytes, so the 16 rows of a matrix-core operand read
+  // from LDS fall in different banks
+  float feat[NODES][2 * D + 4];
+  float hid[NODES][256 + 4];
+  float m[NODES][D + 4];
 };
+// The pooler MLP of a tile on the float32 matrix cores (bf16 trees): hid =
+// SiLU(W1 feat + b1), then m = W2 hid, as [16 nodes] x [k] x [16 outputs]
+// tiles of v_mfma_f32_16x16x4_f32 (float32 products and sums, like the vector
+// path).  Per 16-wide k block, lane group h holds k = 16 kb + 4h .. 4h+3 of
+// its row as one float4 and instruction s takes element s of it, for A and B
+// alike.  Rows are nodes (rows at or past n_valid, or past NODES, read as 0;
+// their outputs are not stored); the waves take the output tiles in turn.  A
+// node's result does not depend on the tile's other rows, so a tile of one
+// node (decode append) gives the bits a full tile gives.  Ends with a
+// workgroup barrier.
+template <int D, int NODES, int NT>
+__device__ void pool_mlp_mfma(const recsa_pooler& P, int n_valid, float (*feat)[2 * D + 4],
+                              float (*hid)[256 + 4], float (*mo)[D + 4]) {
+  constexpr int NWAVES = NT / kWave;
+  constexpr int K1 = 2 * D;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  const int row = lane & 15, h = lane >> 4;
+  const bool arow = row < NODES && row < n_valid;
+  const int H = P.hidden;
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  // ---- layer 1: output tiles of 16 hidden units, two per wave at a time
+  // (two independent accumulation chains over the same A operand)
+  for (int t = wid; t < H / 16; t += 2 * NWAVES) {
+    const int t2 = t + NWAVES;
+    const bool two = t2 < H / 16;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+    const float* wrow = P.W1 + static_cast<int64_t>(16 * t + row) * K1 + 4 * h;
+    const float* wrow2 = two ? P.W1 + static_cast<int64_t>(16 * t2 + row) * K1 + 4 * h : wrow;
+#pragma unroll 4
+    for (int kb = 0; kb < K1 / 16; ++kb) {
+      const float4 b = *reinterpret_cast<const float4*>(wrow + 16 * kb);
+      const float4 b2 = *reinterpret_cast<const float4*>(wrow2 + 16 * kb);
+      const float4 a = arow ? *reinterpret_cast<const float4*>(&feat[row][16 * kb + 4 * h]) : zero4;
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b2.x, acc2, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b2.y, acc2, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b2.z, acc2, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b2.w, acc2, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q == 1 && !two) break;
+      const int hu = 16 * (q ? t2 : t) + row;      // this lane's hidden unit
+      const float bias = P.b1[hu];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 4 * h + i;
+        if (n < NODES) {
+          const float z = (q ? acc2[i] : acc[i]) + bias;
+          hid[n][hu] = z / (1.0f + __expf(-z));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // ---- layer 2: output tiles of 16 key dims (k = the hidden units), two
+  // per wave at a time
+  for (int t = wid; t < D / 16; t += 2 * NWAVES) {
+    const int t2 = t + NWAVES;
+    const bool two = t2 < D / 16;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+    const float* wrow = P.W2 + static_cast<int64_t>(16 * t + row) * H + 4 * h;
+    const float* wrow2 = two ? P.W2 + static_cast<int64_t>(16 * t2 + row) * H + 4 * h : wrow;
+#pragma unroll 4
+    for (int kb = 0; kb < H / 16; ++kb) {
+      const float4 b = *reinterpret_cast<const float4*>(wrow + 16 * kb);
+      const float4 b2 = *reinterpret_cast<const float4*>(wrow2 + 16 * kb);
+      const float4 a = arow ? *reinterpret_cast<const float4*>(&hid[row][16 * kb + 4 * h]) : zero4;
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b2.x, acc2, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b2.y, acc2, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b2.z, acc2, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b2.w, acc2, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q == 1 && !two) break;
+      const int j = 16 * (q ? t2 : t) + row;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 4 * h + i;
+        if (n < NODES) mo[n][j] = q ? acc2[i] : acc[i];
+      }
+    }
+  }
+  __syncthreads();
+}
+
 
 template <int DT, int D, int NODES, int NT, bool STATS = false>
 __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child K rows
@@ -115,8 +263,8 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
       for (int u = 0; u < DPL; ++u) s += w[u] * (x[c][u] - mu[u]);
       a[c] = s;
     }
-#pragma unroll
-    for (int c = 0; c < kC; ++c) a[c] = wave_sum(a[c]);
+    static_assert(kC == 16, "children per node");
+    wave_sum16(a);
     const float scale = P.tau / sigma;
     float amax = -INFINITY;
 #pragma unroll
@@ -152,6 +300,9 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
   }
   __syncthreads();
 
+  if constexpr (DT == RECSA_BF16) {
+    pool_mlp_mfma<D, NODES, NT>(P, n_valid, sm.feat, sm.hid, sm.m);
+  } else {
   // ---- phase 2: hid = SiLU(W1 feat + b1)
   // nodes per thread: 8 with 256 threads, 4 with 512 (one item per thread
   // for 16 nodes and 128 hidden units); the per-element sums run in the same
@@ -205,6 +356,7 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
     for (int q = 0; q < NPG; ++q) sm.m[g0 + q][j] = acc[q];
   }
   __syncthreads();
+  }
 
   if constexpr (STATS) {
     // sigma and ||mu||^2 of each node next to its m (feat is free after
