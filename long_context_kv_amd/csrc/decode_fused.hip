@@ -291,7 +291,11 @@ __global__ void __launch_bounds__(kFusedThreads)
       const int64_t rows_l = level_rows_dev(tr.L_cap, l);
       const int p_q = lv.len - 1;
       float* out_l = lg_slot + static_cast<int64_t>(l - 1) * G * CK;
-      for (int gi = w + W * wid; gi < ng; gi += W * NW) {
+      // at the first scored level workgroup 0 has spent the start appending,
+      // so the other W - 1 take its share of the groups
+      const bool skip0 = gen == 0 && W > 1;
+      const int wl = skip0 ? w - 1 : w, Wl = skip0 ? W - 1 : W;
+      for (int gi = wl + Wl * wid; wl >= 0 && gi < ng; gi += Wl * NW) {
         const int p0 = gi * kC;
         const int nvalid = min(kC, n - p0);
         const bool raw = tr.Kr[l] == nullptr;     // no rotated copy: rotate the rows here
