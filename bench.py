@@ -475,6 +475,16 @@ def main():
         "roofline": roof,
     }
 
+    # measured peaks of this device, for fractions beside the datasheet's
+    mp = measured_peaks()
+    result["measured_peaks"] = mp
+    result["fractions_of_measured_peaks"] = {
+        "decode_fused_of_copy": round(fused_gbs / mp["copy_GBs"], 4),
+        "build_of_copy": round(bb / build_s / 1e9 / mp["copy_GBs"], 4),
+        "prefill_scoring_of_gemm": round(sel_tflops / mp["bf16_gemm_TFLOPs"], 4),
+        "prefill_attention_of_gemm": round(att_flops / att_s / 1e12 / mp["bf16_gemm_TFLOPs"], 4),
+    }
+
     # ------------------------------------------------------- CPU baseline
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, tree, pdict, q_dec, q_pre, t_dec, L, T,
@@ -622,6 +632,42 @@ def bench_config5(args):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out
+
+
+def measured_peaks():
+    """This device's achievable rates, measured here: a 4 GiB device-to-device
+    copy (bytes read + written per second) and an 8192^3 bf16 matrix product
+    through torch (the vendor GEMM library), each the best of 10 timed
+    runs."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    best_copy = 1e9
+    for _ in range(10):
+        a, b = ev(), ev()
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best_copy = min(best_copy, a.elapsed_time(b) * 1e-3)
+    del src, dst
+    n = 8192
+    x = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    y = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    best_mm = 1e9
+    for _ in range(10):
+        a, b = ev(), ev()
+        a.record()
+        torch.matmul(x, y)
+        b.record()
+        torch.cuda.synchronize()
+        best_mm = min(best_mm, a.elapsed_time(b) * 1e-3)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"copy_GBs": round(2 * (4 << 30) / best_copy / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2 * n ** 3 / best_mm / 1e12, 1),
+            "how": "best of 10: 4 GiB device copy (read + write); 8192^3 bf16 torch.matmul"}
 
 
 def needle_recall_in_level0(w):
