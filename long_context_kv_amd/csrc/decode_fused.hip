@@ -348,10 +348,11 @@ __global__ void __launch_bounds__(kFusedThreads)
 
   // ---- unified softmax over this workgroup's interleaved entry groups
   const EntryGroups eg = entry_groups(t, tr, n_sel, s_sel, s_cnt);
-  // two-group chunks: fewer registers per wave (no spills), more chunks to
-  // spread over the group's waves
-  attn_groups<DT, D, G, NT, 2>(tr, t, slot, s_sel, s_cnt, eg, w, W, qs, lg_slot, s_bm, CK, k_t,
-                               v_t, sm.at);
+  // two-group level-0 chunks and four-group summary chunks (as many
+  // registers per wave, no spills): at the longest lists about one chunk
+  // per wave, so the group's loads go out in one round
+  attn_groups<DT, D, G, NT, 2, true>(tr, t, slot, s_sel, s_cnt, eg, w, W, qs, lg_slot, s_bm, CK,
+                                     k_t, v_t, sm.at);
   float* pp = part + (slot * kPartSlots + w) * static_cast<int64_t>(G) * (D + kPartHead);
   for (int e = tid; e < G * D; e += NT)
     pp[(e / D) * (D + kPartHead) + kPartHead + e % D] = sm.at.wacc[0][e / D][e % D];

@@ -761,29 +761,239 @@ __device__ __forceinline__ const void* lane_ptr(const void* p, int src_lane) {
   return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// One chunk of the entry set -- its 16-entry groups [gfirst, gend), at most
+// NG of them -- folded into this wave's softmax state (m, lsum, acc).  HAS0:
+// the chunk may hold level-0 groups, whose key rows are loaded and whose
+// logits are formed here; without it every group is a summary group of a
+// scored level (value rows and stored logits only).  Per chunk the level-0
+// key rows are issued first, then the value rows, so both are in flight
+// during the query rotations.  If k_t/v_t are given they replace the tree
+// rows of token t (decode append in the same launch).
+template <int DT, int D, int G, int NT, int NG, bool HAS0>
+__device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int64_t seq_head,
+                                           const int32_t* sel, const int32_t* cnt,
+                                           const EntryGroups& eg, int gfirst, int gend,
+                                           const float* qs, const float* __restrict__ lg_slot,
+                                           const uint32_t* __restrict__ bm_slot, int CK,
+                                           const typename Stor<DT>::T* k_t,
+                                           const typename Stor<DT>::T* v_t, bool raw0,
+                                           const void* kbase0, float (&m)[G], float (&lsum)[G],
+                                           float (&acc)[G][D / kC], AttnSmem<D, G, NT>& sm) {
+  using T = typename Stor<DT>::T;
+  constexpr int DPB = D / kC;                                      // dims per lane
+  constexpr int VWE = (DT == RECSA_BF16) ? DPB / 2 : DPB;          // value words per entry
+  constexpr int NE = NG * kC, EPL = NE / 4;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  const int c = lane >> 2, s = lane & 3;
+  const int top = tr.n_levels - 1;
+  const int bm_words = (CK + 31) / 32;
+  // ---- this lane's entry: row lane % 16 of group ci*NG + lane / 16
+  const int gi = gfirst + lane / kC;
+  const bool in_group = lane < NE && gi < gend;
+  int level = 0, local = 0;
+  if (in_group) eg.locate(gi, level, local);
+  const ListView lv = list_view(t, level, top, tr.k, sel, cnt);
+  const int p = local * kC + (lane % kC);
+  const int n_pos = level == 0 ? lv.len : lv.len - 1;
+  const bool valid = in_group && p < n_pos;
+  const int64_t rows_l = level_rows_dev(tr.L_cap, level);
+  const int64_t node = valid ? lv.node(p) : 0;
+  // per group (read from the group's first lane): level-0 groups get logits here
+  const int grp_nvalid = in_group ? min(kC, n_pos - local * kC) : 0;
+
+  // ---- level-0 key rows and query-rotation table rows of the chunk's
+  // groups (issued before the value rows, which are needed only last)
+  KRows<DT, D> ka[NG];
+  QRope<DT, D, G> rq[NG];
+  bool is0[NG];
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    const int lead = gg * kC;
+    is0[gg] = HAS0 &&
+              __builtin_amdgcn_readlane(static_cast<int>(in_group && level == 0), lead) != 0;
+    if (is0[gg]) {
+      const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
+      const int len = __builtin_amdgcn_readlane(lv.len, lead);
+      const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
+      const T* krow0 = static_cast<const T*>(lane_ptr(static_cast<const T*>(kbase0) +
+                                                          (seq_head * rows_l + node) * D, lead));
+      const int ovr = k_t ? len - 1 - p0 : -1;          // row of token t, if in this group
+      group_load_k<DT, D>(krow0, 0, (ovr >= 0 && ovr < kC) ? ovr : nv, ka[gg]);
+      const int p_q = len - 1;
+      load_query_rope<DT, D, G>(kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope, rq[gg]);
+    }
+  }
+  // ---- summary logits (levels >= 1: from scoring, minus the selected ones)
+  // (the loads do not wait for the selection bitmap: it masks afterwards)
+  float lg[G];
+  uint32_t sel_word = 0u;
+  const bool summ = valid && level >= 1;
+  {
+    const float* src = lg_slot + static_cast<int64_t>(level - 1) * G * CK + p;
+    if (summ) {
+      sel_word = bm_slot[(level - 1) * bm_words + (p >> 5)];
+#pragma unroll
+      for (int g = 0; g < G; ++g) lg[g] = src[static_cast<int64_t>(g) * CK];
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
+    }
+  }
+  // ---- value rows: a group's entries are 16 consecutive rows (children
+  // of one parent), one base address per group read from its first lane;
+  // this lane loads its DPB dims of rows c, c+4, c+8, c+12 of each group;
+  // token t's row may come from v_t
+  uint32_t vraw[EPL][VWE];
+  const T* vgrp = static_cast<const T*>(level_ptr(tr.V, level)) + (seq_head * rows_l + node) * D;
+  const int vcls = lane >> 4, vdim = (lane & 15) * DPB;
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    const int lead = gg * kC;
+    const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
+    const bool g0 =
+        HAS0 && __builtin_amdgcn_readlane(static_cast<int>(in_group && level == 0), lead) != 0;
+    const int len = __builtin_amdgcn_readlane(lv.len, lead);
+    const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
+    const int own_r = (g0 && k_t) ? len - 1 - p0 : -1;
+    const T* vb = static_cast<const T*>(lane_ptr(vgrp, lead)) + vdim;
+#pragma unroll
+    for (int rr = 0; rr < kC / 4; ++rr) {
+      const int r = 4 * rr + vcls;                       // row within the group
+      const int slot = gg * (kC / 4) + rr;               // this lane's entry slot
+      const T* vr = (own_r == r) ? v_t + vdim : vb + r * D;
+      if (r < nv) {
+        if constexpr (VWE == 4) {
+          const uint4 x = *reinterpret_cast<const uint4*>(vr);
+          vraw[slot][0] = x.x; vraw[slot][1] = x.y; vraw[slot][2] = x.z; vraw[slot][3] = x.w;
+        } else if constexpr (VWE == 2) {
+          const uint2 x = *reinterpret_cast<const uint2*>(vr);
+          vraw[slot][0] = x.x; vraw[slot][1] = x.y;
+        } else {
+#pragma unroll
+          for (int u = 0; u < VWE; u += 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(vr + u);
+            vraw[slot][u] = x.x; vraw[slot][u + 1] = x.y; vraw[slot][u + 2] = x.z; vraw[slot][u + 3] = x.w;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < VWE; ++u) vraw[slot][u] = 0u;
+      }
+    }
+  }
+  // ---- level-0 logits: split RoPE, one query rotation per group
+  bool any0 = false;
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    if (!is0[gg]) continue;
+    any0 = true;
+    const int lead = gg * kC;
+    const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
+    const int len = __builtin_amdgcn_readlane(lv.len, lead);
+    const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
+    const int ovr = k_t ? len - 1 - p0 : -1;
+    const bool split = ovr >= 0 && ovr < kC;
+    rotate_query_from<DT, D, G>(qs, sm.qt[wid], rq[gg]);
+    wave_sync();
+    float lgv[G];
+    if (split) {
+      // row t is not in Kr yet (appended in the same launch): rotate it here
+      KRows<DT, D> kb;
+      group_load_k<DT, D>(k_t - static_cast<int64_t>(ovr) * D, ovr, ovr + 1, kb);
+      float a[G], b[G];
+      group_logits_any<DT, D, G>(raw0, ka[gg], 0, ovr, sm.qt[wid], tr.rope, a);
+      group_logits_from<DT, D, G, true>(kb, ovr, ovr + 1, sm.qt[wid], tr.rope, b);
+#pragma unroll
+      for (int g = 0; g < G; ++g) lgv[g] = (c == ovr) ? b[g] : a[g];
+    } else {
+      group_logits_any<DT, D, G>(raw0, ka[gg], 0, nv, sm.qt[wid], tr.rope, lgv);
+    }
+    if (s == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) sm.ew[wid][lead + c][g] = (c < nv) ? lgv[g] : -INFINITY;
+    }
+    wave_sync();
+  }
+  if (summ && ((sel_word >> (p & 31)) & 1u)) {      // selected: not an entry of E
+#pragma unroll
+    for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
+  }
+  if (any0 && valid && level == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) lg[g] = sm.ew[wid][lane][g];
+  }
+  wave_sync();
+  // ---- online softmax over the chunk (entry per lane); sums stay per lane
+  float pr[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float mnew = fmaxf(m[g], wave_max(lg[g]));
+    if (mnew == -INFINITY) {
+      pr[g] = 0.f;
+      continue;
+    }
+    const float sc = (m[g] == -INFINITY) ? 0.f : __expf(m[g] - mnew);
+    pr[g] = (lg[g] == -INFINITY) ? 0.f : __expf(lg[g] - mnew);
+    lsum[g] = lsum[g] * sc + pr[g];
+#pragma unroll
+    for (int u = 0; u < DPB; ++u) acc[g][u] *= sc;
+    m[g] = mnew;
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) sm.ew[wid][lane][g] = pr[g];
+  wave_sync();
+  // ---- P V (this lane: its DPB dims of its entries); a chunk's groups past
+  // gend hold no entries (a short last chunk skips their work)
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    if (gfirst + gg >= gend) break;
+#pragma unroll
+    for (int rr = 0; rr < kC / 4; ++rr) {
+      const int slot = gg * (kC / 4) + rr;
+      const int e = gg * kC + 4 * rr + vcls;
+      float v[DPB];
+#pragma unroll
+      for (int u = 0; u < DPB; ++u) {
+        if constexpr (DT == RECSA_BF16) {
+          const uint32_t wv = vraw[slot][u / 2];
+          v[u] = __uint_as_float((u & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+        } else {
+          v[u] = __uint_as_float(vraw[slot][u]);
+        }
+      }
+      float wgt[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) wgt[g] = sm.ew[wid][e][g];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int u = 0; u < DPB; ++u) acc[g][u] += wgt[g] * v[u];
+      }
+    }
+  }
+  wave_sync();
+}
+
 // Process the entry chunks g_lo, g_lo + g_step, ... of one (query, KV head)
 // with the whole workgroup (its waves take every NW-th of those; no block
 // barrier inside the loop), then merge the waves: on return sm.res_m,
 // sm.res_l and sm.wacc[0] hold the workgroup's softmax state (valid after
-// the trailing __syncthreads).  Per chunk the level-0 key rows are issued
-// first, then the value rows, so both are in flight during the query
-// rotations.  If k_t/v_t are given they replace the tree rows of token t
-// (decode append in the same launch).
-template <int DT, int D, int G, int NT, int NG_MAX = 4>
+// the trailing __syncthreads).  Chunks of NG_MAX groups (at most 2 with
+// 8 value words per entry) run over the groups in order; with SPLIT the
+// level-0 groups (key and value rows) form chunks of that size and the
+// summary groups (value rows only) chunks of up to 4, which hold as many
+// registers, so that each wave's loads go out in fewer rounds.
+template <int DT, int D, int G, int NT, int NG_MAX = 4, bool SPLIT = false>
 __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, const int32_t* sel,
                             const int32_t* cnt, const EntryGroups& eg, int g_lo, int g_step,
                             const float* qs, const float* __restrict__ lg_slot,
                             const uint32_t* __restrict__ bm_slot, int CK,
                             const typename Stor<DT>::T* k_t, const typename Stor<DT>::T* v_t,
                             AttnSmem<D, G, NT>& sm) {
-  using T = typename Stor<DT>::T;
   using CS = ChunkShape<DT, D, NG_MAX>;
-  constexpr int DPB = CS::DPB, VWE = CS::VWE, NG = CS::NG, NE = CS::NE, EPL = CS::EPL;
+  constexpr int DPB = CS::DPB, NG = CS::NG;
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-  const int c = lane >> 2, s = lane & 3;
-  const int top = tr.n_levels - 1;
-  const int bm_words = (CK + 31) / 32;
   float m[G], lsum[G], acc[G][DPB];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -798,188 +1008,29 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
   const bool raw0 = tr.Kr[0] == nullptr;
   const void* kbase0 = raw0 ? tr.K[0] : tr.Kr[0];
 #pragma unroll 1
-  for (int ci = g_lo + wid * g_step; ci < n_chunks; ci += NW * g_step) {
-    // ---- this lane's entry: row lane % 16 of group ci*NG + lane / 16
-    const int gi = ci * NG + lane / kC;
-    const bool in_group = lane < NE && gi < n_groups;
-    int level = 0, local = 0;
-    if (in_group) eg.locate(gi, level, local);
-    const ListView lv = list_view(t, level, top, tr.k, sel, cnt);
-    const int p = local * kC + (lane % kC);
-    const int n_pos = level == 0 ? lv.len : lv.len - 1;
-    const bool valid = in_group && p < n_pos;
-    const int64_t rows_l = level_rows_dev(tr.L_cap, level);
-    const int64_t node = valid ? lv.node(p) : 0;
-    // per group (read from the group's first lane): level-0 groups get logits here
-    const int grp_nvalid = in_group ? min(kC, n_pos - local * kC) : 0;
-
-    // ---- level-0 key rows and query-rotation table rows of the chunk's
-    // groups (issued before the value rows, which are needed only last)
-    KRows<DT, D> ka[NG];
-    QRope<DT, D, G> rq[NG];
-    bool is0[NG];
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      const int lead = gg * kC;
-      is0[gg] = __builtin_amdgcn_readlane(static_cast<int>(in_group && level == 0), lead) != 0;
-      if (is0[gg]) {
-        const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
-        const int len = __builtin_amdgcn_readlane(lv.len, lead);
-        const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
-        const T* krow0 = static_cast<const T*>(lane_ptr(static_cast<const T*>(kbase0) +
-                                                            (seq_head * rows_l + node) * D, lead));
-        const int ovr = k_t ? len - 1 - p0 : -1;          // row of token t, if in this group
-        group_load_k<DT, D>(krow0, 0, (ovr >= 0 && ovr < kC) ? ovr : nv, ka[gg]);
-        const int p_q = len - 1;
-        load_query_rope<DT, D, G>(kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope, rq[gg]);
-      }
-    }
-    // ---- summary logits (levels >= 1: from scoring, minus the selected ones)
-    // (the loads do not wait for the selection bitmap: it masks afterwards)
-    float lg[G];
-    uint32_t sel_word = 0u;
-    const bool summ = valid && level >= 1;
-    {
-      const float* src = lg_slot + static_cast<int64_t>(level - 1) * G * CK + p;
-      if (summ) {
-        sel_word = bm_slot[(level - 1) * bm_words + (p >> 5)];
-#pragma unroll
-        for (int g = 0; g < G; ++g) lg[g] = src[static_cast<int64_t>(g) * CK];
+  for (int ci = g_lo + wid * g_step;; ci += NW * g_step) {
+    if constexpr (SPLIT) {
+      using CSS = ChunkShape<DT, D, 4>;
+      const int n0 = eg.first[1];                       // level-0 groups come first
+      const int c0 = (n0 + NG - 1) / NG;
+      if (ci >= c0 + (n_groups - n0 + CSS::NG - 1) / CSS::NG) break;
+      if (ci < c0) {
+        attn_chunk<DT, D, G, NT, NG, true>(tr, t, seq_head, sel, cnt, eg, ci * NG,
+                                           min(ci * NG + NG, n0), qs, lg_slot, bm_slot, CK, k_t,
+                                           v_t, raw0, kbase0, m, lsum, acc, sm);
       } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
+        const int g0 = n0 + (ci - c0) * CSS::NG;
+        attn_chunk<DT, D, G, NT, CSS::NG, false>(tr, t, seq_head, sel, cnt, eg, g0,
+                                                 min(g0 + CSS::NG, n_groups), qs, lg_slot,
+                                                 bm_slot, CK, k_t, v_t, raw0, kbase0, m, lsum,
+                                                 acc, sm);
       }
+    } else {
+      if (ci >= n_chunks) break;
+      attn_chunk<DT, D, G, NT, NG, true>(tr, t, seq_head, sel, cnt, eg, ci * NG,
+                                         min(ci * NG + NG, n_groups), qs, lg_slot, bm_slot, CK,
+                                         k_t, v_t, raw0, kbase0, m, lsum, acc, sm);
     }
-    // ---- value rows: a group's entries are 16 consecutive rows (children
-    // of one parent), one base address per group read from its first lane;
-    // this lane loads its DPB dims of rows c, c+4, c+8, c+12 of each group;
-    // token t's row may come from v_t
-    uint32_t vraw[EPL][VWE];
-    const T* vgrp = static_cast<const T*>(level_ptr(tr.V, level)) + (seq_head * rows_l + node) * D;
-    const int vcls = lane >> 4, vdim = (lane & 15) * DPB;
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      const int lead = gg * kC;
-      const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
-      const bool g0 = __builtin_amdgcn_readlane(static_cast<int>(in_group && level == 0), lead) != 0;
-      const int len = __builtin_amdgcn_readlane(lv.len, lead);
-      const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
-      const int own_r = (g0 && k_t) ? len - 1 - p0 : -1;
-      const T* vb = static_cast<const T*>(lane_ptr(vgrp, lead)) + vdim;
-#pragma unroll
-      for (int rr = 0; rr < kC / 4; ++rr) {
-        const int r = 4 * rr + vcls;                       // row within the group
-        const int slot = gg * (kC / 4) + rr;               // this lane's entry slot
-        const T* vr = (own_r == r) ? v_t + vdim : vb + r * D;
-        if (r < nv) {
-          if constexpr (VWE == 4) {
-            const uint4 x = *reinterpret_cast<const uint4*>(vr);
-            vraw[slot][0] = x.x; vraw[slot][1] = x.y; vraw[slot][2] = x.z; vraw[slot][3] = x.w;
-          } else if constexpr (VWE == 2) {
-            const uint2 x = *reinterpret_cast<const uint2*>(vr);
-            vraw[slot][0] = x.x; vraw[slot][1] = x.y;
-          } else {
-#pragma unroll
-            for (int u = 0; u < VWE; u += 4) {
-              const uint4 x = *reinterpret_cast<const uint4*>(vr + u);
-              vraw[slot][u] = x.x; vraw[slot][u + 1] = x.y; vraw[slot][u + 2] = x.z; vraw[slot][u + 3] = x.w;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int u = 0; u < VWE; ++u) vraw[slot][u] = 0u;
-        }
-      }
-    }
-    // ---- level-0 logits: split RoPE, one query rotation per group
-    bool any0 = false;
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      if (!is0[gg]) continue;
-      any0 = true;
-      const int lead = gg * kC;
-      const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
-      const int len = __builtin_amdgcn_readlane(lv.len, lead);
-      const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
-      const int ovr = k_t ? len - 1 - p0 : -1;
-      const bool split = ovr >= 0 && ovr < kC;
-      rotate_query_from<DT, D, G>(qs, sm.qt[wid], rq[gg]);
-      wave_sync();
-      float lgv[G];
-      if (split) {
-        // row t is not in Kr yet (appended in the same launch): rotate it here
-        KRows<DT, D> kb;
-        group_load_k<DT, D>(k_t - static_cast<int64_t>(ovr) * D, ovr, ovr + 1, kb);
-        float a[G], b[G];
-        group_logits_any<DT, D, G>(raw0, ka[gg], 0, ovr, sm.qt[wid], tr.rope, a);
-        group_logits_from<DT, D, G, true>(kb, ovr, ovr + 1, sm.qt[wid], tr.rope, b);
-#pragma unroll
-        for (int g = 0; g < G; ++g) lgv[g] = (c == ovr) ? b[g] : a[g];
-      } else {
-        group_logits_any<DT, D, G>(raw0, ka[gg], 0, nv, sm.qt[wid], tr.rope, lgv);
-      }
-      if (s == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) sm.ew[wid][lead + c][g] = (c < nv) ? lgv[g] : -INFINITY;
-      }
-      wave_sync();
-    }
-    if (summ && ((sel_word >> (p & 31)) & 1u)) {      // selected: not an entry of E
-#pragma unroll
-      for (int g = 0; g < G; ++g) lg[g] = -INFINITY;
-    }
-    if (any0 && valid && level == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) lg[g] = sm.ew[wid][lane][g];
-    }
-    wave_sync();
-    // ---- online softmax over the chunk (entry per lane); sums stay per lane
-    float pr[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mnew = fmaxf(m[g], wave_max(lg[g]));
-      if (mnew == -INFINITY) {
-        pr[g] = 0.f;
-        continue;
-      }
-      const float sc = (m[g] == -INFINITY) ? 0.f : __expf(m[g] - mnew);
-      pr[g] = (lg[g] == -INFINITY) ? 0.f : __expf(lg[g] - mnew);
-      lsum[g] = lsum[g] * sc + pr[g];
-#pragma unroll
-      for (int u = 0; u < DPB; ++u) acc[g][u] *= sc;
-      m[g] = mnew;
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) sm.ew[wid][lane][g] = pr[g];
-    wave_sync();
-    // ---- P V (this lane: its DPB dims of its entries)
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-#pragma unroll
-      for (int rr = 0; rr < kC / 4; ++rr) {
-        const int slot = gg * (kC / 4) + rr;
-        const int e = gg * kC + 4 * rr + vcls;
-        float v[DPB];
-#pragma unroll
-        for (int u = 0; u < DPB; ++u) {
-          if constexpr (DT == RECSA_BF16) {
-            const uint32_t wv = vraw[slot][u / 2];
-            v[u] = __uint_as_float((u & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
-          } else {
-            v[u] = __uint_as_float(vraw[slot][u]);
-          }
-        }
-        float wgt[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) wgt[g] = sm.ew[wid][e][g];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-          for (int u = 0; u < DPB; ++u) acc[g][u] += wgt[g] * v[u];
-        }
-      }
-    }
-    wave_sync();
   }
   // the four lane classes hold partial sums of the same dims: add them
   // (lanes 0..15 end with the totals)
