@@ -5,6 +5,7 @@
 #pragma once
 
 #include "recsa_common.hpp"
+#include "recsa_mfma.hpp"
 
 namespace recsa {
 
@@ -769,7 +770,7 @@ __device__ __forceinline__ const void* lane_ptr(const void* p, int src_lane) {
 // key rows are issued first, then the value rows, so both are in flight
 // during the query rotations.  If k_t/v_t are given they replace the tree
 // rows of token t (decode append in the same launch).
-template <int DT, int D, int G, int NT, int NG, bool HAS0>
+template <int DT, int D, int G, int NT, int NG, bool HAS0, bool MF = false>
 __device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int64_t seq_head,
                                            const int32_t* sel, const int32_t* cnt,
                                            const EntryGroups& eg, int gfirst, int gend,
@@ -803,7 +804,9 @@ __device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int6
 
   // ---- level-0 key rows and query-rotation table rows of the chunk's
   // groups (issued before the value rows, which are needed only last)
-  KRows<DT, D> ka[NG];
+  static_assert(!MF || DT == RECSA_BF16, "matrix-core logits take bf16 rows");
+  KRows<DT, D> ka[NG];                 // vector-unit logits: rows split over lane quads
+  MFrag<D> kf[NG];                     // matrix-core logits: the B operand (row = lane % 16)
   QRope<DT, D, G> rq[NG];
   bool is0[NG];
 #pragma unroll
@@ -818,7 +821,23 @@ __device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int6
       const T* krow0 = static_cast<const T*>(lane_ptr(static_cast<const T*>(kbase0) +
                                                           (seq_head * rows_l + node) * D, lead));
       const int ovr = k_t ? len - 1 - p0 : -1;          // row of token t, if in this group
-      group_load_k<DT, D>(krow0, 0, (ovr >= 0 && ovr < kC) ? ovr : nv, ka[gg]);
+      if constexpr (MF) {
+        // lane l loads row l % 16; token t's row comes raw from k_t (rotated
+        // before use), the group's last row when it is there
+        const int r = lane & 15, hq = lane >> 4;
+        const uint16_t* src = (r == ovr) ? reinterpret_cast<const uint16_t*>(k_t)
+                                         : reinterpret_cast<const uint16_t*>(krow0) + r * D;
+        if (r < nv) {
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb)
+            kf[gg].w[kb] = *reinterpret_cast<const uint4*>(src + 8 * hq + 32 * kb);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb) kf[gg].w[kb] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      } else {
+        group_load_k<DT, D>(krow0, 0, (ovr >= 0 && ovr < kC) ? ovr : nv, ka[gg]);
+      }
       const int p_q = len - 1;
       load_query_rope<DT, D, G>(kC * (p_q / kC - p0 / kC) + p_q % kC, tr.rope, rq[gg]);
     }
@@ -894,6 +913,25 @@ __device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int6
     const int ovr = k_t ? len - 1 - p0 : -1;
     const bool split = ovr >= 0 && ovr < kC;
     rotate_query_from<DT, D, G>(qs, sm.qt[wid], rq[gg]);
+    if constexpr (MF) {
+      // raw rows take the key half of the split RoPE here (every row without
+      // a rotated copy, else only token t's): the values Kr holds
+      if (raw0 || (split && (lane & 15) == ovr)) rotate_key_frag<D>(kf[gg], tr.rope);
+      wave_sync();
+      MFrag<D> qf;
+      query_frag_lds<D, G>(reinterpret_cast<const uint16_t*>(sm.qt[wid]), qf);
+      const f32x4_t acc4 = mfma_logits<D>(qf, kf[gg]);
+      // C layout: lane l holds heads 4 (l / 16) + i of entry l % 16
+      const int col = lane & 15, rb = lane >> 4;
+      const float scale = 1.0f / sqrtf(static_cast<float>(D));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * rb + i;
+        if (g < G) sm.ew[wid][lead + col][g] = (col < nv) ? acc4[i] * scale : -INFINITY;
+      }
+      wave_sync();
+      continue;
+    }
     wave_sync();
     float lgv[G];
     if (split) {
@@ -982,7 +1020,9 @@ __device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int6
 // 8 value words per entry) run over the groups in order; with SPLIT the
 // level-0 groups (key and value rows) form chunks of that size and the
 // summary groups (value rows only) chunks of up to 4, which hold as many
-// registers, so that each wave's loads go out in fewer rounds.
+// registers, so that each wave's loads go out in fewer rounds; there the
+// level-0 logits of bf16 rows are formed on the matrix cores (a group's 16
+// rows against the G rotated query heads, v_mfma_f32_16x16x32_bf16).
 template <int DT, int D, int G, int NT, int NG_MAX = 4, bool SPLIT = false>
 __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, const int32_t* sel,
                             const int32_t* cnt, const EntryGroups& eg, int g_lo, int g_step,
@@ -1015,9 +1055,9 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
       const int c0 = (n0 + NG - 1) / NG;
       if (ci >= c0 + (n_groups - n0 + CSS::NG - 1) / CSS::NG) break;
       if (ci < c0) {
-        attn_chunk<DT, D, G, NT, NG, true>(tr, t, seq_head, sel, cnt, eg, ci * NG,
-                                           min(ci * NG + NG, n0), qs, lg_slot, bm_slot, CK, k_t,
-                                           v_t, raw0, kbase0, m, lsum, acc, sm);
+        attn_chunk<DT, D, G, NT, NG, true, DT == RECSA_BF16>(
+            tr, t, seq_head, sel, cnt, eg, ci * NG, min(ci * NG + NG, n0), qs, lg_slot, bm_slot,
+            CK, k_t, v_t, raw0, kbase0, m, lsum, acc, sm);
       } else {
         const int g0 = n0 + (ci - c0) * CSS::NG;
         attn_chunk<DT, D, G, NT, CSS::NG, false>(tr, t, seq_head, sel, cnt, eg, g0,

@@ -132,6 +132,13 @@ inline float __builtin_amdgcn_fdot2_f32_bf16(cpusim_bf16x2, cpusim_bf16x2, float
   std::abort();
   return acc;
 }
+typedef __bf16 cpusim_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float cpusim_f32x4 __attribute__((ext_vector_type(4)));
+inline cpusim_f32x4 __builtin_amdgcn_mfma_f32_16x16x32_bf16(cpusim_bf16x8, cpusim_bf16x8,
+                                                            cpusim_f32x4 c, int, int, int) {
+  std::abort();
+  return c;
+}
 inline float __shfl_xor(float v, int, int = 64) { std::abort(); return v; }
 inline float __shfl(float v, int, int = 64) { std::abort(); return v; }
 inline uint32_t __shfl(uint32_t v, int, int = 64) { std::abort(); return v; }
