@@ -116,72 +116,72 @@ __device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uin
 }
 
 // Merge the W partial softmax states [W][G][kPartHead + D] (max, sum, -,
-// -, weighted values) of one group into the output [G][D].  Thread
-// (column c, subset q) owns the 4 output values 4c..4c+3 over the partials
-// w = q, q + NQ, ...: it issues those 16-byte loads first, the (max, sum)
-// pairs become per-partial weights while they land, and the NQ subsets'
-// sums meet in LDS.
+// -, weighted values) of one group into the output [G][D].  Thread (column
+// c, subset q) owns the 4 output values 4c..4c+3 over the partials w = q,
+// q + NQ, ...: it issues those loads (values and normaliser) first, while
+// the first W*G threads bring every partial's maximum into LDS; after one
+// barrier each thread forms its head's maximum, its partials' weights and
+// their share of the normaliser, and after a second the threads of subset
+// 0 add the NQ shares and write the output.
 template <int D, int G, int NT>
 __device__ void merge_partials_fused(const float* __restrict__ pp, int W, float* __restrict__ o) {
   constexpr int PS = D + kPartHead;                  // floats per query head of a partial
   constexpr int stride = G * PS;
   constexpr int NC = G * D / 4;                      // float4 columns of the output
-  static_assert(NT % NC == 0, "thread count");
+  static_assert(NT % NC == 0 && NT >= kFusedMaxW * kMaxG, "thread count");
   constexpr int NQ = NT / NC;                        // partial subsets
   constexpr int WQ = (kFusedMaxW + NQ - 1) / NQ;     // partials per thread
-  __shared__ float s_m[kFusedMaxW][kMaxG], s_l[kFusedMaxW][kMaxG];
-  __shared__ float s_f[kFusedMaxW][kMaxG], s_inv[kMaxG];
+  __shared__ float s_m[kMaxG][kFusedMaxW];
   __shared__ float4 s_acc[NQ][NC];
+  __shared__ float s_l[NQ][NC];
   const int tid = threadIdx.x;
   const int c = tid % NC, qs = tid / NC;
   const int ge = (4 * c) / D, dd = (4 * c) % D;
+  const float* ph = pp + ge * PS;                    // this head's state in partial 0
   float4 av[WQ];
+  float lw[WQ];
 #pragma unroll
   for (int i = 0; i < WQ; ++i) {
     const int w = qs + NQ * i;
-    av[i] = w < W ? *reinterpret_cast<const float4*>(pp + w * stride + ge * PS + kPartHead + dd)
+    av[i] = w < W ? *reinterpret_cast<const float4*>(ph + w * stride + kPartHead + dd)
                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    lw[i] = w < W ? ph[w * stride + 1] : 0.f;
   }
   if (tid < W * G) {
     const int w = tid / G, g = tid % G;
-    s_m[w][g] = pp[w * stride + g * PS];
-    s_l[w][g] = pp[w * stride + g * PS + 1];
+    s_m[g][w] = pp[w * stride + g * PS];
   }
   __syncthreads();
-  if (tid < W * G) {
-    const int w = tid / G, g = tid % G;
-    float M = -INFINITY;
-    for (int v = 0; v < W; ++v) M = fmaxf(M, s_m[v][g]);
-    s_f[w][g] = (s_m[w][g] == -INFINITY) ? 0.f : __expf(s_m[w][g] - M);
-  }
-  __syncthreads();
-  if (tid < G) {
-    float L = 0.f;
-    for (int v = 0; v < W; ++v) L += s_f[v][tid] * s_l[v][tid];
-    s_inv[tid] = 1.0f / L;
-  }
+  float M = -INFINITY;
+  for (int v = 0; v < W; ++v) M = fmaxf(M, s_m[ge][v]);
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
 #pragma unroll
   for (int i = 0; i < WQ; ++i) {
     const int w = qs + NQ * i;
     if (w < W) {
-      const float f = s_f[w][ge];
+      const float mv = s_m[ge][w];
+      const float f = (mv == -INFINITY) ? 0.f : __expf(mv - M);
       a.x += f * av[i].x;
       a.y += f * av[i].y;
       a.z += f * av[i].z;
       a.w += f * av[i].w;
+      L += f * lw[i];
     }
   }
   s_acc[qs][c] = a;
+  s_l[qs][c] = L;
   __syncthreads();
-  if (tid < NC) {
+  if (qs == 0) {
     float4 r = s_acc[0][c];
+    float l = s_l[0][c];
 #pragma unroll
     for (int q2 = 1; q2 < NQ; ++q2) {
       const float4 x = s_acc[q2][c];
       r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+      l += s_l[q2][c];
     }
-    const float inv = s_inv[ge];
+    const float inv = 1.0f / l;
     *reinterpret_cast<float4*>(o + 4 * c) = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
   }
 }
@@ -376,24 +376,31 @@ __global__ void __launch_bounds__(kFusedThreads)
     __shared__ uint32_t s_last;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // the group's status words, read by the merging thread as soon as it
+    // knows every member has arrived and first used after the merge, so
+    // their latency overlaps it
+    uint32_t st_mask = 0u, st_late = 0u, st_err = 0u;
     if (tid == 0) {
       const uint32_t before =
           __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       s_last = (before + 1 == (gen + 1) * static_cast<uint32_t>(W)) ? 1u : 0u;
-      if (s_last) __asm__ __volatile__("buffer_inv sc0" ::: "memory");
+      if (s_last) {
+        __asm__ __volatile__("buffer_inv sc0" ::: "memory");
+        st_mask = __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_late = l2_read(counter + 1);
+        st_err = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __syncthreads();
     if (!s_last) return;
     merge_partials_fused<D, G, NT>(pp_group, W, o);
     __shared__ uint32_t s_bad;
     if (tid == 0) {
-      const uint32_t mask = __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool split = __popc(mask) != 1;     // members on more than one XCD
+      const bool split = __popc(st_mask) != 1;  // members on more than one XCD
       if (split) atomicOr(err, 2u);
       // any member's timed-out wait: in this L2 (word 3) or, device-wide, the
       // sticky error word
-      s_bad = s_fail | l2_read(counter + 1) | (split ? 1u : 0u) |
-              __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_bad = s_fail | st_late | (split ? 1u : 0u) | st_err;
     }
     __syncthreads();
     if (s_bad) {
