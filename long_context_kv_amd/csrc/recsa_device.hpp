@@ -762,6 +762,19 @@ __device__ __forceinline__ const void* lane_ptr(const void* p, int src_lane) {
   return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// Sum of a value over the four 16-lane rows of the wave, in every lane:
+// (x[l & ~16] + x[l | 16]) from v_permlane16_swap, then the same across the
+// two 32-lane halves from v_permlane32_swap -- the additions of the
+// xor-16 / xor-32 butterfly, in the same order.
+__device__ __forceinline__ float row_sum4(float x) {
+  const uint32_t xb = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+  const float y = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const uint32_t yb = __float_as_uint(y);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
 // One chunk of the entry set -- its 16-entry groups [gfirst, gend), at most
 // NG of them -- folded into this wave's softmax state (m, lsum, acc).  HAS0:
 // the chunk may hold level-0 groups, whose key rows are loaded and whose
@@ -1072,17 +1085,14 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
                                          k_t, v_t, raw0, kbase0, m, lsum, acc, sm);
     }
   }
-  // the four lane classes hold partial sums of the same dims: add them
-  // (lanes 0..15 end with the totals)
+  // the four lane classes (16-lane rows) hold partial sums of the same dims:
+  // add them with the gfx950 lane swaps, which read lanes l & ~16 and l | 16,
+  // then l & 31 and (l & 31) + 32 (every lane ends with the totals)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int u = 0; u < DPB; ++u) {
-      float v = acc[g][u];
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      acc[g][u] = v;
-    }
+    for (int u = 0; u < DPB; ++u)
+      acc[g][u] = row_sum4(acc[g][u]);
   }
   SoftState<G, DPB> st;
 #pragma unroll

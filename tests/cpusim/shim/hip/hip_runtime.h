@@ -139,6 +139,15 @@ inline cpusim_f32x4 __builtin_amdgcn_mfma_f32_16x16x32_bf16(cpusim_bf16x8, cpusi
   std::abort();
   return c;
 }
+typedef uint32_t cpusim_u32x2 __attribute__((ext_vector_type(2)));
+inline cpusim_u32x2 __builtin_amdgcn_permlane16_swap(uint32_t a, uint32_t, bool, bool) {
+  std::abort();
+  return cpusim_u32x2{a, a};
+}
+inline cpusim_u32x2 __builtin_amdgcn_permlane32_swap(uint32_t a, uint32_t, bool, bool) {
+  std::abort();
+  return cpusim_u32x2{a, a};
+}
 inline float __shfl_xor(float v, int, int = 64) { std::abort(); return v; }
 inline float __shfl(float v, int, int = 64) { std::abort(); return v; }
 inline uint32_t __shfl(uint32_t v, int, int = 64) { std::abort(); return v; }
