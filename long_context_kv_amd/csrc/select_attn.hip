@@ -136,7 +136,12 @@ __global__ void __launch_bounds__(NT)
 
 // ------------------------------------------------------------- attention
 // Entry groups of one (query, KV head) dealt round-robin to n_split workgroups.
-template <int DT, int D, int G>
+// SPLIT (decode calls, a few queries over many workgroups): two-group
+// level-0 chunks with matrix-core logits and four-group summary chunks, the
+// shape of the fused decode.  Without it (prefill, many queries): chunks of
+// four groups in list order, logits on the vector units -- the faster form
+// when every CU holds many such workgroups.
+template <int DT, int D, int G, bool SPLIT>
 __global__ void __launch_bounds__(kBlock)
     attn_kernel(recsa_tree tr, const void* q, int Hq, int T, const int64_t* pos, int32_t* sel,
                 int32_t* cnt, float* out, const float* ws_logits, const uint32_t* ws_bitmap,
@@ -149,8 +154,9 @@ __global__ void __launch_bounds__(kBlock)
   const EntryGroups eg = entry_groups(qc.t, tr, n_sel, qc.sel, qc.cnt);
   const float* lg_slot = ws_logits + qc.slot * n_sel * static_cast<int64_t>(G) * CK;
   const uint32_t* bm_slot = ws_bitmap + qc.slot * n_sel * static_cast<int64_t>((CK + 31) / 32);
-  attn_groups<DT, D, G, kBlock>(tr, qc.t, qc.seq_head, qc.sel, qc.cnt, eg, qc.x, n_split, qs,
-                                lg_slot, bm_slot, CK, nullptr, nullptr, sm);
+  attn_groups<DT, D, G, kBlock, SPLIT ? 2 : 4, SPLIT>(tr, qc.t, qc.seq_head, qc.sel, qc.cnt, eg,
+                                                     qc.x, n_split, qs, lg_slot, bm_slot, CK,
+                                                     nullptr, nullptr, sm);
   if (n_split == 1) {
     float* o = out + (qc.qi * Hq + static_cast<int64_t>(qc.j) * G) * D;
     for (int e = threadIdx.x; e < G * D; e += kBlock) o[e] = sm.wacc[0][e / D][e % D] / sm.res_l[e / D];
@@ -412,9 +418,15 @@ static hipError_t attn_impl(const recsa_tree& tr, const void* q, int Hq, int T, 
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.part_off);
   const unsigned nq = static_cast<unsigned>(static_cast<int64_t>(tr.B) * T);
   const int n_split = decode ? w.n_split : 1;
-  attn_kernel<DT, D, G><<<dim3(static_cast<unsigned>(n_split) * nq, tr.Hkv), kBlock, 0, s>>>(
-      tr, q, Hq, T, pos, const_cast<int32_t*>(sel), const_cast<int32_t*>(cnt), out, logits, bitmap,
-      part, n_split, w.n_sel, w.CK);
+  const dim3 grid(static_cast<unsigned>(n_split) * nq, tr.Hkv);
+  if (decode)
+    attn_kernel<DT, D, G, true><<<grid, kBlock, 0, s>>>(
+        tr, q, Hq, T, pos, const_cast<int32_t*>(sel), const_cast<int32_t*>(cnt), out, logits,
+        bitmap, part, n_split, w.n_sel, w.CK);
+  else
+    attn_kernel<DT, D, G, false><<<grid, kBlock, 0, s>>>(
+        tr, q, Hq, T, pos, const_cast<int32_t*>(sel), const_cast<int32_t*>(cnt), out, logits,
+        bitmap, part, n_split, w.n_sel, w.CK);
   if (n_split > 1)
     combine_kernel<D, G><<<dim3(tr.Hkv, nq), kBlock, 0, s>>>(part, out, tr.Hkv, Hq, n_split);
   return hipGetLastError();
