@@ -72,10 +72,15 @@ __device__ __forceinline__ void wave_sum16(float (&v)[16]) {
 template <int DT, int D, int NODES>
 struct PoolSmem {
   // rows padded by 16 bytes, so the 16 rows of a matrix-core operand read
-  // from LDS fall in different banks
-  float feat[NODES][2 * D + 4];
+  // from LDS fall in different banks.  feat (the MLP input, 2D per node) is
+  // dead once the MLP's first layer has read it, so the MLP output m (D per
+  // node), and after it the stored node key, take the same rows: the tile
+  // needs 8 KB less LDS, and four tiles fit a CU instead of three.
+  union {
+    float feat[NODES][2 * D + 4];
+    float m[NODES][2 * D + 4];
+  };
   float hid[NODES][256 + 4];
-  float m[NODES][D + 4];
 };
 // The pooler MLP of a tile on the float32 matrix cores (bf16 trees): hid =
 // SiLU(W1 feat + b1), then m = W2 hid, as [16 nodes] x [k] x [16 outputs]
@@ -89,7 +94,7 @@ struct PoolSmem {
 // workgroup barrier.
 template <int D, int NODES, int NT>
 __device__ void pool_mlp_mfma(const recsa_pooler& P, int n_valid, float (*feat)[2 * D + 4],
-                              float (*hid)[256 + 4], float (*mo)[D + 4]) {
+                              float (*hid)[256 + 4], float (*mo)[2 * D + 4]) {
   constexpr int NWAVES = NT / kWave;
   constexpr int K1 = 2 * D;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
@@ -359,21 +364,21 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
   }
 
   if constexpr (STATS) {
-    // sigma and ||mu||^2 of each node next to its m (feat is free after
-    // phase 2), then per-dimension sums over the tile's nodes in node order
+    // sigma and ||mu||^2 of each node next to its m (hid is free once the
+    // MLP is done), then per-dimension sums over the tile's nodes in node order
 #pragma unroll
     for (int nw = 0; nw < NPW; ++nw) {
       const int n = wid * NPW + nw;
       if (n < NODES && lane == 0) {
-        sm.feat[n][0] = n < n_valid ? sig_r[nw] : 0.f;
-        sm.feat[n][1] = n < n_valid ? mu2_r[nw] : 0.f;
+        sm.hid[n][0] = n < n_valid ? sig_r[nw] : 0.f;
+        sm.hid[n][1] = n < n_valid ? mu2_r[nw] : 0.f;
       }
     }
     __syncthreads();
     for (int j = threadIdx.x; j <= D; j += NT) {
       float acc = 0.f;
       for (int n = 0; n < n_valid && n < NODES; ++n)
-        acc += j < D ? sm.feat[n][0] * sm.m[n][j] : sm.feat[n][1];
+        acc += j < D ? sm.hid[n][0] * sm.m[n][j] : sm.hid[n][1];
       stats[j] = acc;
     }
     return;
@@ -389,7 +394,8 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
       const float kv = mu_r[nw][u] + P.g * (p_r[nw][u] - mu_r[nw][u]) +
                        sig_r[nw] * sm.m[n][i0 + u];
       Stor<DT>::store(ko + static_cast<int64_t>(n) * D + i0 + u, kv);
-      sm.feat[n][i0 + u] = Stor<DT>::round(kv);      // the stored value, for phase 5
+      sm.m[n][i0 + u] = Stor<DT>::round(kv);         // the stored value, for phase 5
+                                                      // (over the m element just read)
     }
   }
   __syncthreads();
@@ -404,7 +410,7 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
     const int c = (c0 + n) % kC;
     const float* rp = rope + (c * H2 + jj) * 2;
     float xo, yo;
-    rope_pair(sm.feat[n][jj], sm.feat[n][jj + H2], rp[0], rp[1], xo, yo);
+    rope_pair(sm.m[n][jj], sm.m[n][jj + H2], rp[0], rp[1], xo, yo);
     Stor<DT>::store(kro + static_cast<int64_t>(n) * D + jj, xo);
     Stor<DT>::store(kro + static_cast<int64_t>(n) * D + jj + H2, yo);
   }
