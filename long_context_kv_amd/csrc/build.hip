@@ -52,8 +52,12 @@ __global__ void __launch_bounds__(NT) build_level_kernel(recsa_tree tr, recsa_po
   T* ko = static_cast<T*>(tr.K[level]) + (head * rows + first) * D;
   T* vo = static_cast<T*>(tr.V[level]) + (head * rows + first) * D;
   T* kro = tr.Kr[level] ? static_cast<T*>(tr.Kr[level]) + (head * rows + first) * D : nullptr;
+  // level 1 also writes its children's rotated rows Kr[0] (read here anyway)
+  T* krc = (level == 1 && tr.Kr[0])
+               ? static_cast<T*>(tr.Kr[0]) + (head * rows_up + first * kC) * D
+               : nullptr;
   pool_tile<DT, D, NODES, NT>(kc, vc, ko, vo, kro, static_cast<int>(first % kC), tr.rope,
-                              n_valid, P, sm);
+                              n_valid, P, sm, nullptr, krc);
 }
 
 // Rotated keys Kr[0] of the level-0 rows [tb, te): each thread rotates 8
@@ -147,12 +151,20 @@ hipError_t launch_rope_table(float* table, int d, int n_pos, double theta, hipSt
 template <int DT, int D>
 static hipError_t build_impl(const recsa_tree& tr, const recsa_pooler& P, int64_t tb, int64_t te,
                              hipStream_t s) {
-  if (tr.Kr[0]) {                                     // the rotated-key copy, when kept
-    constexpr int RPB = kBlock / (D / 16);            // rows per workgroup
-    dim3 grid(static_cast<unsigned>((te - tb + RPB - 1) / RPB), tr.Hkv, tr.B);
-    rotate_level0_kernel<DT, D><<<grid, kBlock, 0, s>>>(tr, tb, te);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (tr.Kr[0]) {
+    // the rotated-key copy of level 0, when kept: the level-1 pass writes the
+    // rows of the nodes it completes ([16 n_lo, 16 n_hi) covers [tb, 16 n_hi));
+    // this pass rotates the rest, the rows of a trailing incomplete node
+    const int64_t covered =
+        tr.n_levels > 1 ? std::min<int64_t>(te / kC, level_rows_host(tr.L_cap, 1)) * kC : tb;
+    const int64_t rb = std::max<int64_t>(tb, covered);
+    if (rb < te) {
+      constexpr int RPB = kBlock / (D / 16);            // rows per workgroup
+      dim3 grid(static_cast<unsigned>((te - rb + RPB - 1) / RPB), tr.Hkv, tr.B);
+      rotate_level0_kernel<DT, D><<<grid, kBlock, 0, s>>>(tr, rb, te);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   int64_t span = 1;
   for (int l = 1; l < tr.n_levels; ++l) {

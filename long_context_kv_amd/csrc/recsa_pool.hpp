@@ -186,7 +186,8 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
                           int c0,                   // index mod C of the tile's first node
                           const float* __restrict__ rope,
                           int n_valid, const recsa_pooler& P,
-                          PoolSmem<DT, D, NODES>& sm, float* __restrict__ stats = nullptr) {
+                          PoolSmem<DT, D, NODES>& sm, float* __restrict__ stats = nullptr,
+                          typename Stor<DT>::T* __restrict__ krc = nullptr) {
   using T = typename Stor<DT>::T;
   constexpr int DPL = D / kWave;                 // dims per lane (1 or 2)
   constexpr int NWAVES = NT / kWave;
@@ -224,6 +225,48 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
           vs[1] += tmp[1];
         } else {
           vs[0] += Stor<DT>::load(vr);
+        }
+      }
+    }
+    // the children's rotated key rows krc = rnd(R(c) K) (R13's key half; a
+    // node's children sit at in-group offsets 0..15), while the rows are in
+    // registers: dim j's RoPE partner j + D/2 is in lane l ^ 32 (same slot),
+    // which v_permlane32_swap exchanges; both lanes form the pair with
+    // rope_pair and keep their own member, so the bits equal the separate
+    // rotation pass's
+    if constexpr (!STATS) {
+      if (krc) {
+        constexpr int H2 = D / 2;
+        const int jl = (lane & 31) * DPL;          // this lane pair's first dim below D/2
+        const bool low = lane < 32;
+#pragma unroll 4
+        for (int c = 0; c < kC; ++c) {
+          float cs[2 * DPL];
+          if constexpr (DPL == 2) {
+            const float4 r = *reinterpret_cast<const float4*>(rope + (c * H2 + jl) * 2);
+            cs[0] = r.x; cs[1] = r.y; cs[2] = r.z; cs[3] = r.w;
+          } else {
+            const float2 r = *reinterpret_cast<const float2*>(rope + (c * H2 + jl) * 2);
+            cs[0] = r.x; cs[1] = r.y;
+          }
+          float o[DPL];
+#pragma unroll
+          for (int u = 0; u < DPL; ++u) {
+            const uint32_t xb = __float_as_uint(x[c][u]);
+            const auto pr = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+            float xo, yo;
+            rope_pair(__uint_as_float(pr[0]), __uint_as_float(pr[1]), cs[2 * u], cs[2 * u + 1], xo,
+                      yo);
+            o[u] = low ? xo : yo;
+          }
+          T* dst = krc + (static_cast<int64_t>(n) * kC + c) * D + i0;
+          if constexpr (DPL == 2 && DT == RECSA_BF16) {
+            *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(f32_to_bf16_bits(o[0])) |
+                                                (static_cast<uint32_t>(f32_to_bf16_bits(o[1])) << 16);
+          } else {
+#pragma unroll
+            for (int u = 0; u < DPL; ++u) Stor<DT>::store(dst + u, o[u]);
+          }
         }
       }
     }
