@@ -158,7 +158,7 @@ __device__ __forceinline__ void rotate_key_row(const typename Stor<DT>::T* src,
 namespace dpp {
 constexpr int kXor1 = 0xB1;                    // quad_perm [1,0,3,2]
 constexpr int kXor2 = 0x4E;                    // quad_perm [2,3,0,1]
-constexpr int kRor4 = 0x124, kRor8 = 0x128;    // row_ror:4, row_ror:8
+constexpr int kRor4 = 0x124, kRor8 = 0x128, kRor12 = 0x12C;   // row_ror:4, :8, :12
 constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;   // row_shr:n
 constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
 }  // namespace dpp
@@ -192,6 +192,19 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_movf<dpp::kBcast15, 0xA>(v, v));
   v = fmaxf(v, dpp_movf<dpp::kBcast31, 0xC>(v, v));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// Sum of a value over the four 16-lane rows of the wave, in every lane:
+// (x[l & ~16] + x[l | 16]) from v_permlane16_swap, then the same across the
+// two 32-lane halves from v_permlane32_swap -- the additions of the
+// xor-16 / xor-32 butterfly, in the same order.
+__device__ __forceinline__ float row_sum4(float x) {
+  const uint32_t xb = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+  const float y = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const uint32_t yb = __float_as_uint(y);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
 // Sum over each aligned quad of lanes (the result in all four lanes).

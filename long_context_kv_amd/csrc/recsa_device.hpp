@@ -762,19 +762,6 @@ __device__ __forceinline__ const void* lane_ptr(const void* p, int src_lane) {
   return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Sum of a value over the four 16-lane rows of the wave, in every lane:
-// (x[l & ~16] + x[l | 16]) from v_permlane16_swap, then the same across the
-// two 32-lane halves from v_permlane32_swap -- the additions of the
-// xor-16 / xor-32 butterfly, in the same order.
-__device__ __forceinline__ float row_sum4(float x) {
-  const uint32_t xb = __float_as_uint(x);
-  const auto p16 = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
-  const float y = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
-  const uint32_t yb = __float_as_uint(y);
-  const auto p32 = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
-  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
-}
-
 // One chunk of the entry set -- its 16-entry groups [gfirst, gend), at most
 // NG of them -- folded into this wave's softmax state (m, lsum, acc).  HAS0:
 // the chunk may hold level-0 groups, whose key rows are loaded and whose

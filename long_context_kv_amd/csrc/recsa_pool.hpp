@@ -22,7 +22,7 @@ namespace recsa {
 // bits (each step keeps half the values and adds the partner lane's other
 // half), so lane l ends with the total of value l % 16; then every lane reads
 // the 16 totals back.  About 60 instructions instead of 16 separate
-// reductions.
+// reductions; every exchange is a DPP move or a gfx950 lane swap (no LDS).
 __device__ __forceinline__ void wave_sum16(float (&v)[16]) {
   const int lane = threadIdx.x & (kWave - 1);
   float a[8];
@@ -47,23 +47,25 @@ __device__ __forceinline__ void wave_sum16(float (&v)[16]) {
   }
   float c2[2];
   {
+    // lane l ^ 4 within the 16-lane row: row_ror:12 reads lane l + 4 (the
+    // partner of the lanes with bit 2 clear), row_ror:4 lane l - 4
     const bool hi = lane & 4;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const float keep = hi ? b[2 * j + 1] : b[2 * j];
       const float send = hi ? b[2 * j] : b[2 * j + 1];
-      c2[j] = keep + __shfl_xor(send, 4, kWave);
+      const float up = dpp_movf<dpp::kRor12>(0.f, send), down = dpp_movf<dpp::kRor4>(0.f, send);
+      c2[j] = keep + (hi ? down : up);
     }
   }
   float t;
   {
-    const bool hi = lane & 8;
+    const bool hi = lane & 8;              // lane l ^ 8: row_ror:8 (its own inverse)
     const float keep = hi ? c2[1] : c2[0];
     const float send = hi ? c2[0] : c2[1];
-    t = keep + __shfl_xor(send, 8, kWave);
+    t = keep + dpp_movf<dpp::kRor8>(0.f, send);
   }
-  t += __shfl_xor(t, 16, kWave);
-  t += __shfl_xor(t, 32, kWave);
+  t = row_sum4(t);
 #pragma unroll
   for (int c = 0; c < 16; ++c)
     v[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), c));
