@@ -35,6 +35,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two float32 values rounded to bf16 (to nearest, ties to even, as
+// f32_to_bf16_bits) and packed, lo in bits 0-15: one v_cvt_pk_bf16_f32.
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_convertvector((f32x2_cvt_t){lo, hi}, bf16x2_cvt_t));
+}
+
 template <int DT>
 struct Stor;
 
@@ -107,8 +116,7 @@ __device__ __forceinline__ void store_vec8(typename Stor<DT>::T* p, const float*
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i + 1])) << 16);
+      w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);

@@ -106,8 +106,8 @@ __device__ __forceinline__ void group_logits_from(const KRows<DT, D>& kr, int ro
                       rp[4 * i + 1], x0, y0);
             rope_pair(__uint_as_float(kx[i] & 0xFFFF0000u), __uint_as_float(ky[i] & 0xFFFF0000u),
                       rp[4 * i + 2], rp[4 * i + 3], x1, y1);
-            kx[i] = f32_to_bf16_bits(x0) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
-            ky[i] = f32_to_bf16_bits(y0) | (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+            kx[i] = pack_bf16x2(x0, x1);
+            ky[i] = pack_bf16x2(y0, y1);
           }
         }
         const uint32_t* qw = reinterpret_cast<const uint32_t*>(qt);
@@ -212,9 +212,8 @@ __device__ __forceinline__ void rotate_query_from(const float* qs, float* qt,
       float x0, y0, x1, y1;
       rope_pair(qs[g * D + j], qs[g * D + j + H2], cs.x, cs.y, x0, y0);
       rope_pair(qs[g * D + j + 1], qs[g * D + j + 1 + H2], cs.z, cs.w, x1, y1);
-      qw[g * (D / 2) + j / 2] = f32_to_bf16_bits(x0) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
-      qw[g * (D / 2) + H2 / 2 + j / 2] =
-          f32_to_bf16_bits(y0) | (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+      qw[g * (D / 2) + j / 2] = pack_bf16x2(x0, x1);
+      qw[g * (D / 2) + H2 / 2 + j / 2] = pack_bf16x2(y0, y1);
     } else {
       const int g = idx / H2, j = idx % H2;
       float xo, yo;
@@ -238,9 +237,8 @@ __device__ __forceinline__ void rotate_query(const float* qs, float* qt, int phi
       float x0, y0, x1, y1;
       rope_pair(qs[g * D + j], qs[g * D + j + H2], rrow[2 * j], rrow[2 * j + 1], x0, y0);
       rope_pair(qs[g * D + j + 1], qs[g * D + j + 1 + H2], rrow[2 * j + 2], rrow[2 * j + 3], x1, y1);
-      qw[g * (D / 2) + j / 2] = f32_to_bf16_bits(x0) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
-      qw[g * (D / 2) + H2 / 2 + j / 2] =
-          f32_to_bf16_bits(y0) | (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+      qw[g * (D / 2) + j / 2] = pack_bf16x2(x0, x1);
+      qw[g * (D / 2) + H2 / 2 + j / 2] = pack_bf16x2(y0, y1);
     }
   } else {
     for (int idx = lane; idx < G * H2; idx += kWave) {

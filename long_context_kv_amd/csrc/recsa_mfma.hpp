@@ -30,11 +30,6 @@ struct MFrag {
   uint4 w[D / 32];
 };
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
-         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
-}
-
 // B operand: rows [0, nrows) of a group of 16 consecutive stored rows; the
 // other rows read as 0 (their logits are never stored).
 template <int D>
@@ -162,8 +157,7 @@ __device__ __forceinline__ void split_bf16x8(const float* x, uint4& hi, uint4& l
     const uint16_t a = f32_to_bf16_bits(x[2 * v]), b = f32_to_bf16_bits(x[2 * v + 1]);
     const float ra = x[2 * v] - bf16_bits_to_f32(a), rb = x[2 * v + 1] - bf16_bits_to_f32(b);
     h[v] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
-    l[v] = static_cast<uint32_t>(f32_to_bf16_bits(ra)) |
-           (static_cast<uint32_t>(f32_to_bf16_bits(rb)) << 16);
+    l[v] = pack_bf16x2(ra, rb);
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);

@@ -263,8 +263,7 @@ __device__ void pool_tile(const typename Stor<DT>::T* __restrict__ kc,  // child
           }
           T* dst = krc + (static_cast<int64_t>(n) * kC + c) * D + i0;
           if constexpr (DPL == 2 && DT == RECSA_BF16) {
-            *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(f32_to_bf16_bits(o[0])) |
-                                                (static_cast<uint32_t>(f32_to_bf16_bits(o[1])) << 16);
+            *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o[0], o[1]);
           } else {
 #pragma unroll
             for (int u = 0; u < DPL; ++u) Stor<DT>::store(dst + u, o[u]);
