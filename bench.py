@@ -17,7 +17,9 @@ steps between two device synchronisations; HIP events on the stream the
 kernels run on split each step into its prefill and decode parts.  Then the
 decode alone: >= 200 consecutive tokens, each with fresh inputs and captured
 as its own HIP graph, replayed back to back (warm caches) and again each
-after a 512 MB buffer is rewritten (last-level cache scrubbed); medians.
+after a 512 MB buffer is rewritten (last-level cache scrubbed), and the same
+tokens as direct launches (warm); medians.  `roofline` averages the fused
+decode launches of the timed steps.
 
 The 4-layer 2M-token configuration (full build of each layer, an 8192-query
 prefill chunk per layer, then 256 decode steps over the 4 layers with fresh
@@ -328,6 +330,19 @@ def main():
         return [a.elapsed_time(b) * 1e3 for a, b in xs]
     first_us = replay_all()                            # every token appended once more
     warm_us = replay_all()
+
+    def direct_all():
+        xs = []
+        for i in range(n_dec):
+            a, b = ev(), ev()
+            a.record()
+            decode(i)
+            b.record()
+            xs.append((a, b))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in xs]
+    direct_all()
+    direct_us = direct_all()                           # the same tokens as direct launches
     scrub = torch.zeros(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
     cold_us = replay_all(scrub)
     del scrub
@@ -385,17 +400,14 @@ def main():
     dec_ms_us = [x * 1e3 for x in dec_ms]
     dec_us = med(dec_ms) * 1e3
     pre_s = med(pre_ms) / 1e3
-    # every event-timed fused launch of this run (after a chunk, warm, scrubbed),
-    # the set a kernel trace of the same command averages over
-    all_us = dec_ms_us + first_us + warm_us + cold_us
-    avg_us = float(np.mean(all_us))
+    # the fused launches of the timed steps (each right after a prefill chunk)
+    avg_us = float(np.mean(dec_ms_us))
     fused_gbs = dec_bytes_mean / (avg_us * 1e-6) / 1e9
     traffic_b = measured_traffic(args.workload)
     roof = {
         "kernel": "decode_fused_kernel (recsa_decode: append + select + attention), "
-                  "mean of its %d event-timed launches: tokens from t=%d with fresh q/k/v, "
-                  "after each prefill chunk, as graph replays warm and after a cache scrub" %
-                  (len(all_us), t_dec),
+                  "mean of its %d event-timed launches in the timed steps: tokens from t=%d "
+                  "with fresh q/k/v, each right after a prefill chunk" % (len(dec_ms_us), t_dec),
         "bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
         "traffic": (round(traffic_b / (avg_us * 1e-6) / 1e9, 1) if traffic_b else None),
@@ -441,6 +453,9 @@ def main():
                        "each prefill chunk (the chunk's gathers leave the caches cold)",
         "decode_fresh_inputs_us_median_warm": round(med(warm_us), 2),
         "decode_fresh_inputs_us_median_scrubbed": round(med(cold_us), 2),
+        "decode_fresh_inputs_us_median_warm_direct": round(med(direct_us), 2),
+        "decode_fresh_note": "warm and scrubbed: each token its own HIP graph (torch.cuda.CUDAGraph "
+                             "replay); warm_direct: the same tokens as direct launches",
         "decode_fresh_inputs_us_p10_p90_warm": [round(sorted(warm_us)[len(warm_us) // 10], 2),
                                                 round(sorted(warm_us)[9 * len(warm_us) // 10], 2)],
         "decode_fresh_inputs_steps": n_dec,
