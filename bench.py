@@ -715,6 +715,7 @@ COPY_BYTES = 512 << 20
 FUSED_SOURCES = ("long_context_kv_amd/csrc/decode_fused.hip", "long_context_kv_amd/csrc/recsa_common.hpp",
                  "long_context_kv_amd/csrc/recsa_device.hpp", "long_context_kv_amd/csrc/recsa_mfma.hpp",
                  "long_context_kv_amd/csrc/recsa_pool.hpp", "long_context_kv_amd/csrc/recsa_kernels.hpp",
+                 "long_context_kv_amd/csrc/recsa_fused_ctl.hpp", "long_context_kv_amd/csrc/recsa_hw.hpp",
                  "include/recsa.h")
 
 

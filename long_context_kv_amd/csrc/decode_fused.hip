@@ -35,6 +35,7 @@
 
 #include "recsa_common.hpp"
 #include "recsa_device.hpp"
+#include "recsa_fused_ctl.hpp"
 #include "recsa_mfma.hpp"
 #include "recsa_kernels.hpp"
 #include "recsa_pool.hpp"
@@ -42,79 +43,6 @@
 namespace recsa {
 
 constexpr int kFusedThreads = 512;
-constexpr uint32_t kSpinLimit = 1u << 19;
-
-// Value of *p read by an atomic executed in the L2 (a plain or relaxed
-// workgroup-scope load may be served by this CU's L1).
-__device__ __forceinline__ uint32_t l2_read(uint32_t* p) {
-  uint32_t e = 0xFFFFFFFFu;
-  __hip_atomic_compare_exchange_strong(p, &e, 0xFFFFFFFFu, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-  return e;
-}
-
-// XCD-local barrier.  Every wave drains its own memory operations, so after
-// the workgroup barrier the workgroup's stores are in the XCD's L2; one
-// thread adds this arrival to the group's counter (an L2 atomic), waits for
-// `target` arrivals, and invalidates this CU's L1 so that later loads see
-// what the other workgroups wrote.
-__device__ __forceinline__ void group_barrier_xcd(uint32_t* counter, uint32_t target,
-                                                  uint32_t* err, uint32_t* s_fail) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    uint32_t spins = 0;
-    while (l2_read(counter) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        atomicOr(err, 1u);                       // for the host (device scope)
-        __hip_atomic_fetch_or(counter + 1, 1u, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_WORKGROUP);   // for the merge (this L2)
-        *s_fail = 1u;
-        break;
-      }
-    }
-    __asm__ __volatile__("buffer_inv sc0" ::: "memory");
-  }
-  __syncthreads();
-}
-
-// Device-wide barrier.  After the workgroup barrier one thread releases the
-// workgroup's stores to the device (one L2 write-back per workgroup), raises
-// this workgroup's flag to `gen`, waits for every flag of the group with
-// relaxed loads, and acquires once (one L2 invalidation per workgroup).
-__device__ __forceinline__ void group_barrier(uint32_t* flags, int w, int W, uint32_t gen,
-                                              uint32_t* err, uint32_t* s_fail) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    // an atomic read-modify-write is performed where every XCD sees it (a
-    // plain store could stay in this XCD's L2)
-    __hip_atomic_exchange(flags + 16 * w, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // every poll reads all W flags at once (one memory round trip)
-    uint32_t spins = 0;
-    while (true) {
-      uint32_t lo = 0xFFFFFFFFu;
-#pragma unroll
-      for (int i = 0; i < kFusedMaxW; ++i) {
-        if (i < W)
-          lo = min(lo, __hip_atomic_load(flags + 16 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      }
-      if (lo >= gen) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        atomicOr(err, 1u);
-        *s_fail = 1u;
-        break;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-}
-
 // Merge the W partial softmax states [W][G][kPartHead + D] (max, sum, -,
 // -, weighted values) of one group into the output [G][D].  Thread (column
 // c, subset q) owns the 4 output values 4c..4c+3 over the partials w = q,
@@ -220,25 +148,14 @@ __global__ void __launch_bounds__(kFusedThreads)
   int32_t* sel_q = sel + slot * n_sel * k;
   int32_t* cnt_q = cnt + slot * n_sel;
   float* lg_slot = ws_logits + slot * n_sel * static_cast<int64_t>(G) * CK;
-  uint32_t* ctl = ctl_words + slot * kCtlWords;
-  uint32_t* err = ctl + 1;
-  uint32_t* counter = ctl + 2;                       // arrivals (XCD-local barrier);
-                                                     // ctl[3]: a wait timed out (same L2)
-  uint32_t* flags = ctl + 16;                        // one flag line per member (device-wide)
+  const FusedCtl ctl = fused_ctl(ctl_words + slot * kCtlWords);
   const T* k_t = static_cast<const T*>(k_new) + slot * D;
   const T* v_t = static_cast<const T*>(v_new) + slot * D;
   if (tid == 0) {
     s_fail = 0u;
-    if constexpr (XL) {
-      // the local barrier needs every workgroup of the group on one XCD:
-      // record this one's XCD in the group's placement mask (flags[0], its
-      // own line; unused by this form's barriers).  The returned value keeps
-      // the atomic performed before this workgroup's first arrival.
-      const int xcc = __builtin_amdgcn_s_getreg(20 | (15 << 11)) & 0xF;   // hwreg XCC_ID
-      const uint32_t prev =
-          __hip_atomic_fetch_or(flags, 1u << xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev & 0x80000000u) s_fail = 1u;     // never set: keeps the result live
-    }
+    // the local barrier needs every workgroup of the group on one XCD:
+    // record this one's XCD in the group's placement mask
+    if constexpr (XL) ctl_mark_xcd(ctl, &s_fail);
   }
   load_query_rows<DT, D, G, NT>(q, static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G, qs);
 
@@ -329,9 +246,9 @@ __global__ void __launch_bounds__(kFusedThreads)
       }
       ++gen;
       if constexpr (XL)
-        group_barrier_xcd(counter, gen * static_cast<uint32_t>(W), err, &s_fail);
+        group_barrier_xcd(ctl.counter, gen * static_cast<uint32_t>(W), ctl.err, &s_fail);
       else
-        group_barrier(flags, w, W, gen, err, &s_fail);
+        group_barrier(ctl.flags, w, W, gen, ctl.err, &s_fail);
       if (CK <= 4096)
         wg_topk<G, NT, 4096>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1), s_bm + (l - 1) * bm_words,
                              nullptr, sm.tk);
@@ -376,61 +293,37 @@ __global__ void __launch_bounds__(kFusedThreads)
     __shared__ uint32_t s_last;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // the group's status words, read by the merging thread as soon as it
-    // knows every member has arrived and first used after the merge, so
+    // the group's status words are read by the merging thread as soon as
+    // it knows every member has arrived and first used after the merge, so
     // their latency overlaps it
-    uint32_t st_mask = 0u, st_late = 0u, st_err = 0u;
-    if (tid == 0) {
-      const uint32_t before =
-          __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      s_last = (before + 1 == (gen + 1) * static_cast<uint32_t>(W)) ? 1u : 0u;
-      if (s_last) {
-        __asm__ __volatile__("buffer_inv sc0" ::: "memory");
-        st_mask = __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        st_late = l2_read(counter + 1);
-        st_err = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    FusedStatus st;
+    if (tid == 0) s_last = xl_final_arrival(ctl, gen, W, st) ? 1u : 0u;
     __syncthreads();
     if (!s_last) return;
     merge_partials_fused<D, G, NT>(pp_group, W, o);
     __shared__ uint32_t s_bad;
-    if (tid == 0) {
-      const bool split = __popc(st_mask) != 1;  // members on more than one XCD
-      if (split) atomicOr(err, 2u);
-      // any member's timed-out wait: in this L2 (word 3) or, device-wide, the
-      // sticky error word
-      s_bad = s_fail | st_late | (split ? 1u : 0u) | st_err;
-    }
+    if (tid == 0) s_bad = xl_result_bad(ctl, st, s_fail) ? 1u : 0u;
     __syncthreads();
     if (s_bad) {
       for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
     }
-    // every workgroup has arrived for the last time: none reads the counter again
-    if (tid == 0) {
-      __hip_atomic_exchange(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_exchange(counter + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_exchange(flags, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid == 0) xl_reset(ctl);
   } else {
     // ---- WG 0 waits for every partial and merges them
     if (w != 0) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_exchange(flags + 16 * w, gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (tid == 0) dw_final_flag(ctl, w, gen);
       return;
     }
-    group_barrier(flags, w, W, gen + 1, err, &s_fail);
+    group_barrier(ctl.flags, w, W, gen + 1, ctl.err, &s_fail);
     merge_partials_fused<D, G, NT>(pp_group, W, o);
     __syncthreads();
-    if (s_fail || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    if (dw_result_bad(ctl, s_fail)) {
       for (int e = tid; e < G * D; e += NT) o[e] = __builtin_nanf("");
     }
     // every other workgroup has raised its final flag, so none reads them again
-    if (tid < W) __hip_atomic_exchange(flags + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    dw_reset(ctl, tid, W);
   }
 }
 

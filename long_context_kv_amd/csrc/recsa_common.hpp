@@ -17,6 +17,7 @@ constexpr int kMaxK = 512;         // largest selection depth k
 constexpr int kPartHead = 4;
 constexpr int kMaxCK = 8192;       // longest candidate list, C*k
 constexpr int kMaxG = 8;           // query heads per KV head
+constexpr int kFusedMaxW = 32;     // workgroups per (sequence, KV head), fused decode
 constexpr int kChunk = 256;        // list positions per attention/score chunk
 
 // Rows allocated at a level: floor(L_cap / 16^level).

@@ -29,7 +29,6 @@ constexpr int kDecodeSplits = 64;    // attention workgroups per (query, KV head
 // most workgroups per query along the query launch dimension (scoring:
 // C*k/64 <= 128 list blocks; decode attention: kDecodeSplits)
 constexpr int kQueryLaunchX = 128;
-constexpr int kFusedMaxW = 32;       // workgroups per (sequence, KV head), fused decode
 constexpr int kPartSlots = kDecodeSplits > kFusedMaxW ? kDecodeSplits : kFusedMaxW;
 constexpr int kCtlWords = 16 + 16 * kFusedMaxW;   // one 64-byte line per flag
 constexpr int kBucketTile = 64;                   // bucket entries per scoring tile

@@ -1,5 +1,6 @@
 // Host stand-in for <hip/hip_runtime.h>, for building the selection device
-// code (recsa_device.hpp) on the CPU under sanitizers: each GPU lane is a
+// code (recsa_device.hpp) and the fused decode's control protocol
+// (recsa_fused_ctl.hpp) on the CPU under sanitizers: each GPU lane is a
 // host thread, a workgroup is NT such threads, and the wave-level operations
 // (DPP moves, readlane) and barriers are emulated with std::barrier and a
 // per-wave exchange array.  Only what the top-k path uses is modelled
@@ -104,13 +105,30 @@ inline int __builtin_amdgcn_readfirstlane(int v) { return cpusim::exchange(v, 0,
 inline void __builtin_amdgcn_wave_barrier() {
   cpusim::blk->wave_bar[cpusim::wave_()]->arrive_and_wait();
 }
-#define __builtin_amdgcn_fence(order, scope) ((void)0)
+#define __builtin_amdgcn_fence(order, scope) __atomic_thread_fence(__ATOMIC_SEQ_CST)
+
+// HIP's scoped atomics, as sequentially consistent host atomics (the CPU
+// emulation checks the control protocol's logic, not the GPU memory model;
+// the scope argument is ignored)
+#ifndef __HIP_MEMORY_SCOPE_WORKGROUP
+#define __HIP_MEMORY_SCOPE_WORKGROUP 3
+#endif
+#ifndef __HIP_MEMORY_SCOPE_AGENT
+#define __HIP_MEMORY_SCOPE_AGENT 4
+#endif
+// (macros: host clang knows the __hip_atomic_* names as builtins)
+#define __hip_atomic_fetch_add(p, v, order, scope) __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST)
+#define __hip_atomic_fetch_or(p, v, order, scope) __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST)
+#define __hip_atomic_exchange(p, v, order, scope) __atomic_exchange_n(p, v, __ATOMIC_SEQ_CST)
+#define __hip_atomic_load(p, order, scope) __atomic_load_n(p, __ATOMIC_SEQ_CST)
+#define __hip_atomic_compare_exchange_strong(p, e, d, so, fo, scope) \
+  __atomic_compare_exchange_n(p, e, d, false, __ATOMIC_SEQ_CST, __ATOMIC_SEQ_CST)
 inline void __builtin_amdgcn_sched_barrier(int) {}
 inline void __builtin_amdgcn_s_sleep(int) {}
 inline void __builtin_amdgcn_s_waitcnt(int) {}
 
 inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_RELAXED); }
-inline uint32_t atomicOr(uint32_t* p, uint32_t v) { return __atomic_fetch_or(p, v, __ATOMIC_RELAXED); }
+inline uint32_t atomicOr(uint32_t* p, uint32_t v) { return __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST); }
 
 inline float __expf(float x) { return std::exp(x); }
 inline int __clz(int x) { return x == 0 ? 32 : __builtin_clz(static_cast<unsigned>(x)); }
