@@ -753,11 +753,16 @@ __device__ __forceinline__ const void* level_ptr(void* const (&arr)[RECSA_MAX_LE
   return r;
 }
 
-__device__ __forceinline__ const void* lane_ptr(const void* p, int src_lane) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(a), src_lane);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(a >> 32), src_lane);
-  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+// A 64-bit value of lane src_lane.  Row addresses are formed as a tree
+// array (a kernel argument) plus such an offset: the compiler then knows the
+// address is global memory and issues global loads; an address read whole
+// from another lane would be a generic one, whose flat loads also count
+// against the LDS wait counter and stall the LDS work behind them.
+__device__ __forceinline__ int64_t lane_i64(int64_t v, int src_lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), src_lane);
+  const uint32_t hi =
+      __builtin_amdgcn_readlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32), src_lane);
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // One chunk of the entry set -- its 16-entry groups [gfirst, gend), at most
@@ -816,23 +821,18 @@ __device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int6
       const int nv = __builtin_amdgcn_readlane(grp_nvalid, lead);
       const int len = __builtin_amdgcn_readlane(lv.len, lead);
       const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
-      const T* krow0 = static_cast<const T*>(lane_ptr(static_cast<const T*>(kbase0) +
-                                                          (seq_head * rows_l + node) * D, lead));
+      const T* krow0 = static_cast<const T*>(kbase0) + lane_i64((seq_head * rows_l + node) * D, lead);
       const int ovr = k_t ? len - 1 - p0 : -1;          // row of token t, if in this group
       if constexpr (MF) {
         // lane l loads row l % 16; token t's row comes raw from k_t (rotated
-        // before use), the group's last row when it is there
+        // before use), the group's last row when it is there; rows past the
+        // group's end re-read its last row (their logits are masked)
         const int r = lane & 15, hq = lane >> 4;
         const uint16_t* src = (r == ovr) ? reinterpret_cast<const uint16_t*>(k_t)
-                                         : reinterpret_cast<const uint16_t*>(krow0) + r * D;
-        if (r < nv) {
+                                         : reinterpret_cast<const uint16_t*>(krow0) + min(r, nv - 1) * D;
 #pragma unroll
-          for (int kb = 0; kb < D / 32; ++kb)
-            kf[gg].w[kb] = *reinterpret_cast<const uint4*>(src + 8 * hq + 32 * kb);
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < D / 32; ++kb) kf[gg].w[kb] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int kb = 0; kb < D / 32; ++kb)
+          kf[gg].w[kb] = *reinterpret_cast<const uint4*>(src + 8 * hq + 32 * kb);
       } else {
         group_load_k<DT, D>(krow0, 0, (ovr >= 0 && ovr < kC) ? ovr : nv, ka[gg]);
       }
@@ -857,11 +857,13 @@ __device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int6
     }
   }
   // ---- value rows: a group's entries are 16 consecutive rows (children
-  // of one parent), one base address per group read from its first lane;
+  // of one parent), one row offset per group read from its first lane;
   // this lane loads its DPB dims of rows c, c+4, c+8, c+12 of each group;
-  // token t's row may come from v_t
+  // token t's row may come from v_t.  Rows past the group's end (and every
+  // row of a group past the chunk's end, which reads the first level-0 row)
+  // re-read a valid row: their weights are 0.
   uint32_t vraw[EPL][VWE];
-  const T* vgrp = static_cast<const T*>(level_ptr(tr.V, level)) + (seq_head * rows_l + node) * D;
+  const int64_t voff = (seq_head * rows_l + node) * D;
   const int vcls = lane >> 4, vdim = (lane & 15) * DPB;
 #pragma unroll
   for (int gg = 0; gg < NG; ++gg) {
@@ -872,29 +874,26 @@ __device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int6
     const int len = __builtin_amdgcn_readlane(lv.len, lead);
     const int p0 = __builtin_amdgcn_readlane(local, lead) * kC;
     const int own_r = (g0 && k_t) ? len - 1 - p0 : -1;
-    const T* vb = static_cast<const T*>(lane_ptr(vgrp, lead)) + vdim;
+    const int glevel = __builtin_amdgcn_readlane(level, lead);
+    const T* vb = static_cast<const T*>(level_ptr(tr.V, glevel)) + lane_i64(voff, lead) + vdim;
+    const int rlast = max(nv, 1) - 1;
 #pragma unroll
     for (int rr = 0; rr < kC / 4; ++rr) {
       const int r = 4 * rr + vcls;                       // row within the group
       const int slot = gg * (kC / 4) + rr;               // this lane's entry slot
-      const T* vr = (own_r == r) ? v_t + vdim : vb + r * D;
-      if (r < nv) {
-        if constexpr (VWE == 4) {
-          const uint4 x = *reinterpret_cast<const uint4*>(vr);
-          vraw[slot][0] = x.x; vraw[slot][1] = x.y; vraw[slot][2] = x.z; vraw[slot][3] = x.w;
-        } else if constexpr (VWE == 2) {
-          const uint2 x = *reinterpret_cast<const uint2*>(vr);
-          vraw[slot][0] = x.x; vraw[slot][1] = x.y;
-        } else {
-#pragma unroll
-          for (int u = 0; u < VWE; u += 4) {
-            const uint4 x = *reinterpret_cast<const uint4*>(vr + u);
-            vraw[slot][u] = x.x; vraw[slot][u + 1] = x.y; vraw[slot][u + 2] = x.z; vraw[slot][u + 3] = x.w;
-          }
-        }
+      const T* vr = (own_r == r) ? v_t + vdim : vb + min(r, rlast) * D;
+      if constexpr (VWE == 4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(vr);
+        vraw[slot][0] = x.x; vraw[slot][1] = x.y; vraw[slot][2] = x.z; vraw[slot][3] = x.w;
+      } else if constexpr (VWE == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(vr);
+        vraw[slot][0] = x.x; vraw[slot][1] = x.y;
       } else {
 #pragma unroll
-        for (int u = 0; u < VWE; ++u) vraw[slot][u] = 0u;
+        for (int u = 0; u < VWE; u += 4) {
+          const uint4 x = *reinterpret_cast<const uint4*>(vr + u);
+          vraw[slot][u] = x.x; vraw[slot][u + 1] = x.y; vraw[slot][u + 2] = x.z; vraw[slot][u + 3] = x.w;
+        }
       }
     }
   }

@@ -302,7 +302,17 @@ __global__ void __launch_bounds__(kBlock)
   const uint16_t* qb = static_cast<const uint16_t*>(q);
   const bool raw = tr.Kr[level] == nullptr;        // no rotated copy: rotate the key rows here
   const int n_tiles = *ba.n_tiles;
-  for (int tl = blockIdx.x * NW + wid; tl < n_tiles; tl += gridDim.x * NW) {
+  // XCD-aware order: the device deals workgroups to its 8 XCDs round-robin,
+  // so XCD x = blockIdx % 8 walks the x-th eighth of the tile array in order;
+  // the tiles sit region by region (256 queries of one KV head each), so an
+  // XCD's concurrent tiles share few queries' rows, which its L2 keeps
+  constexpr int kXcd = 8;
+  const int x = static_cast<int>(blockIdx.x % kXcd);
+  const int nbx = static_cast<int>(gridDim.x / kXcd);
+  const int per = (n_tiles + kXcd - 1) / kXcd;
+  const int t_end = min(n_tiles, (x + 1) * per);
+  for (int tl = x * per + static_cast<int>(blockIdx.x / kXcd) * NW + wid; tl < t_end;
+       tl += nbx * NW) {
     const uint4 tile = ba.tiles[tl];
     const int64_t first = tile.x, end = first + tile.y;
     const int64_t sh = tile.z, u = tile.w;
@@ -383,8 +393,10 @@ static hipError_t select_impl(const recsa_tree& tr, const void* q, int Hq, int T
           bucket_file_kernel<<<dim3(nblk, tr.Hkv), kBlock, 0, s>>>(tr, T, pos, sel, cnt, l,
                                                                   w.n_sel, ba);
           const int64_t wgs = (w.bk_max_tiles + kBlock / kWave - 1) / (kBlock / kWave);
-          bucket_score_kernel<D, G><<<static_cast<unsigned>(std::min<int64_t>(wgs, 8192)), kBlock,
-                                      0, s>>>(tr, q, Hq, logits, l, w.n_sel, w.CK, ba);
+          // a multiple of 8 workgroups (the tile walk splits them by XCD)
+          const int64_t nwg = std::min<int64_t>((wgs + 7) / 8 * 8, 8192);
+          bucket_score_kernel<D, G><<<static_cast<unsigned>(nwg), kBlock, 0, s>>>(
+              tr, q, Hq, logits, l, w.n_sel, w.CK, ba);
           scored = true;
         }
       }
