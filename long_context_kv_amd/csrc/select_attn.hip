@@ -148,13 +148,21 @@ __global__ void __launch_bounds__(kBlock)
                 float* part, int n_split, int n_sel, int CK) {
   __shared__ float qs[G * D];
   __shared__ AttnSmem<D, G, kBlock> sm;
+  // this query's selections S^(l) [n_sel][k] and counts [n_sel], staged in
+  // LDS once: every chunk maps its entries to nodes through them, and from
+  // global memory that would be two dependent round trips per chunk
+  extern __shared__ int32_t s_dyn[];
   const QueryCtx qc = query_ctx(tr, T, pos, sel, cnt, n_sel, n_split);
+  int32_t* s_sel = s_dyn;
+  int32_t* s_cnt = s_dyn + n_sel * tr.k;
+  for (int i = threadIdx.x; i < n_sel * tr.k; i += kBlock) s_sel[i] = qc.sel[i];
+  if (threadIdx.x < n_sel) s_cnt[threadIdx.x] = qc.cnt[threadIdx.x];
   load_query_rows<DT, D, G, kBlock>(q, qc.qi * Hq + static_cast<int64_t>(qc.j) * G, qs);
   __syncthreads();
-  const EntryGroups eg = entry_groups(qc.t, tr, n_sel, qc.sel, qc.cnt);
+  const EntryGroups eg = entry_groups(qc.t, tr, n_sel, s_sel, s_cnt);
   const float* lg_slot = ws_logits + qc.slot * n_sel * static_cast<int64_t>(G) * CK;
   const uint32_t* bm_slot = ws_bitmap + qc.slot * n_sel * static_cast<int64_t>((CK + 31) / 32);
-  attn_groups<DT, D, G, kBlock, SPLIT ? 2 : 4, SPLIT>(tr, qc.t, qc.seq_head, qc.sel, qc.cnt, eg,
+  attn_groups<DT, D, G, kBlock, SPLIT ? 2 : 4, SPLIT>(tr, qc.t, qc.seq_head, s_sel, s_cnt, eg,
                                                      qc.x, n_split, qs, lg_slot, bm_slot, CK,
                                                      nullptr, nullptr, sm);
   if (n_split == 1) {
@@ -431,12 +439,13 @@ static hipError_t attn_impl(const recsa_tree& tr, const void* q, int Hq, int T, 
   const unsigned nq = static_cast<unsigned>(static_cast<int64_t>(tr.B) * T);
   const int n_split = decode ? w.n_split : 1;
   const dim3 grid(static_cast<unsigned>(n_split) * nq, tr.Hkv);
+  const size_t sel_lds = static_cast<size_t>(w.n_sel) * (tr.k + 1) * sizeof(int32_t);
   if (decode)
-    attn_kernel<DT, D, G, true><<<grid, kBlock, 0, s>>>(
+    attn_kernel<DT, D, G, true><<<grid, kBlock, sel_lds, s>>>(
         tr, q, Hq, T, pos, const_cast<int32_t*>(sel), const_cast<int32_t*>(cnt), out, logits,
         bitmap, part, n_split, w.n_sel, w.CK);
   else
-    attn_kernel<DT, D, G, false><<<grid, kBlock, 0, s>>>(
+    attn_kernel<DT, D, G, false><<<grid, kBlock, sel_lds, s>>>(
         tr, q, Hq, T, pos, const_cast<int32_t*>(sel), const_cast<int32_t*>(cnt), out, logits,
         bitmap, part, n_split, w.n_sel, w.CK);
   if (n_split > 1)
