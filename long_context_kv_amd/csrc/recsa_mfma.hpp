@@ -94,11 +94,16 @@ __device__ __forceinline__ void rotate_frag(const uint16_t* __restrict__ qrow,
                                             const RopeFrag<D>& r, MFrag<D>& f) {
   constexpr int H2 = D / 2, HKB = D / 64;
   const int h = (threadIdx.x & (kWave - 1)) >> 4;
+  // every load of the row first (one memory round trip), then the rotations
+  uint4 xws[HKB], yws[HKB];
 #pragma unroll
   for (int kb = 0; kb < HKB; ++kb) {
-    const int j0 = 32 * kb + 8 * h;
-    const uint4 xw = *reinterpret_cast<const uint4*>(qrow + j0);
-    const uint4 yw = *reinterpret_cast<const uint4*>(qrow + H2 + j0);
+    xws[kb] = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * h);
+    yws[kb] = *reinterpret_cast<const uint4*>(qrow + H2 + 32 * kb + 8 * h);
+  }
+#pragma unroll
+  for (int kb = 0; kb < HKB; ++kb) {
+    const uint4 xw = xws[kb], yw = yws[kb];
     const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w};
     const uint32_t ya[4] = {yw.x, yw.y, yw.z, yw.w};
     uint32_t xo[4], yo[4];
