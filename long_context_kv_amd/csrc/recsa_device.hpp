@@ -193,8 +193,8 @@ __device__ __forceinline__ void load_query_rope(int phi, const float* __restrict
   }
 }
 
-// The rotation itself from preloaded table entries (same result as
-// rotate_query).
+// The rotation itself from preloaded table entries: rnd(R(phi) q) of the
+// G query heads into qt (LDS).
 template <int DT, int D, int G>
 __device__ __forceinline__ void rotate_query_from(const float* qs, float* qt,
                                                   const QRope<DT, D, G>& r) {
@@ -223,34 +223,6 @@ __device__ __forceinline__ void rotate_query_from(const float* qs, float* qt,
     }
   }
 }
-
-template <int DT, int D, int G>
-__device__ __forceinline__ void rotate_query(const float* qs, float* qt, int phi,
-                                             const float* __restrict__ rope) {
-  constexpr int H2 = D / 2;
-  const int lane = threadIdx.x & (kWave - 1);
-  const float* rrow = rope + static_cast<int64_t>(phi) * H2 * 2;
-  if constexpr (DT == RECSA_BF16) {
-    uint32_t* qw = reinterpret_cast<uint32_t*>(qt);
-    for (int idx = lane; idx < G * H2 / 2; idx += kWave) {
-      const int g = idx / (H2 / 2), j = 2 * (idx % (H2 / 2));
-      float x0, y0, x1, y1;
-      rope_pair(qs[g * D + j], qs[g * D + j + H2], rrow[2 * j], rrow[2 * j + 1], x0, y0);
-      rope_pair(qs[g * D + j + 1], qs[g * D + j + 1 + H2], rrow[2 * j + 2], rrow[2 * j + 3], x1, y1);
-      qw[g * (D / 2) + j / 2] = pack_bf16x2(x0, x1);
-      qw[g * (D / 2) + H2 / 2 + j / 2] = pack_bf16x2(y0, y1);
-    }
-  } else {
-    for (int idx = lane; idx < G * H2; idx += kWave) {
-      const int g = idx / H2, j = idx % H2;
-      float xo, yo;
-      rope_pair(qs[g * D + j], qs[g * D + j + H2], rrow[2 * j], rrow[2 * j + 1], xo, yo);
-      qt[g * D + j] = xo;
-      qt[g * D + j + H2] = yo;
-    }
-  }
-}
-
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -85,7 +85,7 @@ __device__ __forceinline__ void load_rope_frag(int phi, const float* __restrict_
 }
 
 // A operand row of this lane: the bf16 query row qrow rotated with the
-// table entries in r and rounded, rnd(R(phi) q) -- the values rotate_query
+// table entries in r and rounded, rnd(R(phi) q) -- the values rotate_query_from
 // produces.  The block pairs (kb, kb + D/64) hold dims j and j + D/2, the
 // two members of a RoPE pair, so each lane rotates its own 8 pairs per
 // block pair.

@@ -81,9 +81,13 @@ __global__ void __launch_bounds__(kBlock)
   const int phi = p_q - p0;                 // = C (r_q - r) + c_q, r = p0 / C
   float* out = ws_logits + (qc.slot * n_sel + (level - 1)) * static_cast<int64_t>(G) * CK;
   if constexpr (DT == RECSA_BF16) {
-    MFrag<D> kf, qf;                       // key rows in flight during the rotation
+    // the table row first (the rotation waits only for it), then the key
+    // rows, in flight during the rotation
+    MFrag<D> kf, qf;
+    QRope<DT, D, G> rq;
+    load_query_rope<DT, D, G>(phi, tr.rope, rq);
     load_key_frag<D>(rows, nvalid, kf);
-    rotate_query<DT, D, G>(qs, qt[wid], phi, tr.rope);
+    rotate_query_from<DT, D, G>(qs, qt[wid], rq);
     if (raw) rotate_key_frag<D>(kf, tr.rope);
     wave_sync();
     query_frag_lds<D, G>(reinterpret_cast<const uint16_t*>(qt[wid]), qf);
@@ -91,8 +95,10 @@ __global__ void __launch_bounds__(kBlock)
     store_logit_tile<D, G>(c, out, CK, p0, nvalid);
   } else {
     KRows<DT, D> kr;                       // key rows in flight during the rotation
+    QRope<DT, D, G> rq;
+    load_query_rope<DT, D, G>(phi, tr.rope, rq);
     group_load_k<DT, D>(rows, 0, nvalid, kr);
-    rotate_query<DT, D, G>(qs, qt[wid], phi, tr.rope);
+    rotate_query_from<DT, D, G>(qs, qt[wid], rq);
     wave_sync();
     float lg[G];
     group_logits_any<DT, D, G>(raw, kr, 0, nvalid, qt[wid], tr.rope, lg);
