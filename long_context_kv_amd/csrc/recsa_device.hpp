@@ -332,12 +332,13 @@ constexpr int kHistBits = 11;
 constexpr int kHistBins = 1 << kHistBits;
 
 constexpr int kSmallBin = 64;
+constexpr float kLog2e = 1.44269504088896341f;
 
 struct TopkSmem {
   int hist[kHistBins];
   uint32_t small_key[kSmallBin];
   int small_pos[kSmallBin];
-  uint32_t small_take[kMaxCK / 32];
+  int small_rank[kSmallBin];   // keys of the boundary bin ranked above each
   int s_nsmall;
   float redg[kMaxG][16];      // per wave: softmax max of each head
   float reds[kMaxG][16];      // per wave: softmax normaliser of each head
@@ -361,10 +362,10 @@ struct TopkSmem {
 // lower node index, the list being in ascending node order).
 // CKM: the list-size class (C*k <= CKM), so thread i owns PPT = CKM/NT
 // positions; PPT divides C, so each thread's vector loads stay in its row.
-template <int G, int NT, int CKM = 4096>
-__device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
-                        int32_t* out_sel, int32_t* out_cnt, uint32_t* bm, float* imp,
-                        TopkSmem& sm) {
+template <int G, int NT, int CKM>
+__device__ void wg_topk_cls(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
+                            int32_t* out_sel, int32_t* out_cnt, uint32_t* bm, float* imp,
+                            TopkSmem& sm) {
   static_assert(CKM <= kMaxCK && kC % (CKM / NT) == 0, "list-size class");
   constexpr int PPT = CKM / NT;
   const int tid = threadIdx.x;
@@ -376,7 +377,7 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   // the first radix pass's bins and the small-bin state start at zero
   // (ordered before their first use by the exchanges below)
   for (int b = tid; b < kHistBins; b += NT) sm.hist[b] = 0;
-  for (int wd = tid; wd < CKM / 32; wd += NT) sm.small_take[wd] = 0u;
+  for (int b = tid; b < kSmallBin; b += NT) sm.small_rank[b] = 0;
   if (tid == 0) sm.s_nsmall = 0;
   // ---- all logits first (one memory round trip), then per-head max and
   // normaliser with one block exchange for all heads
@@ -416,10 +417,15 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       float m = sm.redg[g][0];
 #pragma unroll
       for (int w = 1; w < NW; ++w) m = fmaxf(m, sm.redg[g][w]);
+      // exp(x - m) = 2^(x log2 e - m log2 e): one multiply-add and v_exp_f32
+      // per entry; positions past the list hold -inf and give 0 (m is a
+      // real logit, the list being non-empty); the rounding of m log2 e
+      // scales every entry of the head alike and cancels in the normaliser
+      const float nml = -m * kLog2e;
       float z = 0.f;
 #pragma unroll
       for (int i = 0; i < PPT; ++i) {
-        e[g][i] = (p0 + i < n) ? __expf(e[g][i] - m) : 0.f;
+        e[g][i] = __builtin_amdgcn_exp2f(fmaf(e[g][i], kLog2e, nml));
         z += e[g][i];
       }
       Z[g] = wave_sum(z);
@@ -429,24 +435,26 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       for (int g = 0; g < G; ++g) sm.reds[g][wid] = Z[g];
     }
     __syncthreads();
+    // each head's weight 1/(G Z_g) (1/G is a power of two, so exact)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float z = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) z += sm.reds[g][w];
-      const float inv = 1.0f / z;
+      Z[g] = (1.0f / z) * (1.0f / G);
+    }
 #pragma unroll
-      for (int i = 0; i < PPT; ++i) e[g][i] *= inv;
+    for (int i = 0; i < PPT; ++i) {
+      float s = e[0][i] * Z[0];
+#pragma unroll
+      for (int g = 1; g < G; ++g) s = fmaf(e[g][i], Z[g], s);
+      I[i] = s;
     }
   }
   uint32_t key[PPT];
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
-    float s = 0.f;
-#pragma unroll
-    for (int g = 0; g < G; ++g) s += e[g][i];
-    I[i] = s * (1.0f / G);
     key[i] = __float_as_uint(I[i]);
     if (p0 + i < n) {
       kmin = min(kmin, key[i]);
@@ -462,6 +470,8 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   uint32_t prefix = 0, pmask = 0;
   int need = need0;
   bool whole_bin = false, small = false;
+  uint32_t small_m = 0u;          // my positions in the ranked boundary bin
+  int small_at = 0;               // the bin slot of the first of them
   if (need0 > 0) {
     // the keys' range: the passes start at the highest bit where they differ,
     // so the first pass's bins resolve the keys finely (coarse bins would
@@ -538,28 +548,43 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       if (whole_bin) break;
       if (lo > 0 && in_bin <= kSmallBin) {
         // few keys left in the boundary bin: rank them exactly (key
-        // descending, then list position ascending) in one wave
+        // descending, then list position ascending).  Each wave reserves
+        // slots for its bin keys with one LDS atomic (a wave prefix sum
+        // places its lanes' keys), then every wave ranks all bin keys (key
+        // q sits in lane q) against a stride of them and adds its counts
 #pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-          if (p0 + i < n && (key[i] & pmask) == prefix) {
-            const int at = atomicAdd(&sm.s_nsmall, 1);
-            sm.small_key[at] = key[i];
-            sm.small_pos[at] = p0 + i;
+        for (int i = 0; i < PPT; ++i)
+          small_m |= (p0 + i < n && (key[i] & pmask) == prefix) ? (1u << i) : 0u;
+        const int c_in = __popc(small_m);
+        const int c_inc = wave_incl_scan(c_in);
+        const int c_wave = __builtin_amdgcn_readlane(c_inc, kWave - 1);
+        if (c_wave > 0) {
+          int wbase = 0;
+          if (lane == kWave - 1) wbase = atomicAdd(&sm.s_nsmall, c_wave);
+          small_at = __builtin_amdgcn_readlane(wbase, kWave - 1) + c_inc - c_in;
+          int at = small_at;
+#pragma unroll
+          for (int i = 0; i < PPT; ++i) {
+            if ((small_m >> i) & 1u) {
+              sm.small_key[at] = key[i];
+              sm.small_pos[at] = p0 + i;
+              ++at;
+            }
           }
         }
         __syncthreads();
-        if (tid < kWave) {                           // wave 0; candidate q2 sits in lane q2
+        {
           const int m = __builtin_amdgcn_readfirstlane(sm.s_nsmall);
-          const uint32_t ki = tid < m ? sm.small_key[tid] : 0u;
-          const int pi = tid < m ? sm.small_pos[tid] : 0;
+          const uint32_t ki = lane < m ? sm.small_key[lane] : 0u;
+          const int pi = lane < m ? sm.small_pos[lane] : 0;
           int rank = 0;
-          for (int q2 = 0; q2 < m; ++q2) {
+          for (int q2 = __builtin_amdgcn_readfirstlane(wid); q2 < m; q2 += NW) {
             const uint32_t kq = static_cast<uint32_t>(
                 __builtin_amdgcn_readlane(static_cast<int>(ki), q2));
             const int pq = __builtin_amdgcn_readlane(pi, q2);
             rank += (kq > ki || (kq == ki && pq < pi)) ? 1 : 0;
           }
-          if (tid < m && rank < need) atomicOr(&sm.small_take[pi >> 5], 1u << (pi & 31));
+          if (lane < m && rank > 0) atomicAdd(&sm.small_rank[lane], rank);
         }
         __syncthreads();
         small = true;
@@ -588,7 +613,16 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
       (small || whole_bin) ? 0 : block_scan_excl_fresh<NT>(__popc(eqm), sm.redi, &tot);
   uint32_t inm;
   if (small) {
-    inm = (sm.small_take[p0 >> 5] >> (p0 & 31)) & eqm;
+    // my bin keys sit at slots small_at, small_at + 1, ... in position order
+    inm = 0u;
+    int at = small_at;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      if ((small_m >> i) & 1u) {
+        inm |= (sm.small_rank[at] < need) ? (1u << i) : 0u;
+        ++at;
+      }
+    }
   } else if (whole_bin) {
     inm = eqm;
   } else {
@@ -603,10 +637,15 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   }
   const uint32_t takem = gtm | inm;
   int slot = block_scan_excl_fresh<NT>(__popc(takem), sm.redt, &tot);
-#pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    if ((takem >> i) & 1u) {
-      if (slot < k - 1) out_sel[slot] = static_cast<int32_t>(lv.node(p0 + i));
+  if (takem) {
+    // a thread's positions lie in one 16-position group (PPT divides C), so
+    // one parent lookup serves them all; only the kept ones are visited
+    const int64_t node0 = lv.node(p0);
+    uint32_t tm = takem;
+    while (tm) {
+      const int i = __builtin_ctz(tm);
+      tm &= tm - 1u;
+      if (slot < k - 1) out_sel[slot] = static_cast<int32_t>(node0 + i);
       ++slot;
     }
   }
@@ -616,14 +655,45 @@ __device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, con
   uint32_t bits = takem << (p0 & 31);
   // PPT consecutive positions per thread: 32/PPT threads share one word
   constexpr int LPW = 32 / PPT;
-  static_assert(LPW <= 4, "bit words are merged within quads");
+  static_assert(LPW <= 8, "bit words are merged within 8-lane groups");
   if constexpr (LPW >= 2) bits |= static_cast<uint32_t>(dpp_mov<dpp::kXor1>(0, static_cast<int>(bits)));
   if constexpr (LPW >= 4) bits |= static_cast<uint32_t>(dpp_mov<dpp::kXor2>(0, static_cast<int>(bits)));
+  // the quads' words: row_ror:12 brings lane l + 4 to lane l, so the writing
+  // lane (l % 8 == 0) takes the other quad of its 8-lane group
+  if constexpr (LPW >= 8) bits |= static_cast<uint32_t>(dpp_mov<dpp::kRor12>(0, static_cast<int>(bits)));
   if ((tid % LPW) == 0 && p0 < CK) bm[p0 / 32] = bits;
   if (tid == 0) {
     out_sel[k - 1] = static_cast<int32_t>(lv.cur);
     *out_cnt = k;
   }
+}
+
+// The selection for a list of n + 1 candidates.  With 256 threads (many
+// lists at once, as in a prefill chunk, where the vector units bound it),
+// lists of at most half the class's positions take the half-size class, so
+// each thread ranks half as many positions and none runs the per-position
+// steps on positions past the list's end; the output words past the half
+// class's reach are cleared as the full class would clear them.  The choice
+// depends on n and the thread count alone, so every caller with the same
+// thread count ranks a list with the same arithmetic.  512-thread callers
+// (decode) keep one class: a second inlined copy would double the fused
+// decode's code.
+template <int G, int NT, int CKM = 4096>
+__device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
+                        int32_t* out_sel, int32_t* out_cnt, uint32_t* bm, float* imp,
+                        TopkSmem& sm) {
+  constexpr int HALF = CKM / 2;
+  if constexpr (NT == 256 && CKM / NT >= 8) {
+    if (n <= HALF) {
+      wg_topk_cls<G, NT, HALF>(lgs, n, k, CK, lv, out_sel, out_cnt, bm, imp, sm);
+      if (imp)
+        for (int p = HALF + static_cast<int>(threadIdx.x); p < CK; p += NT) imp[p] = 0.f;
+      for (int wd = HALF / 32 + static_cast<int>(threadIdx.x); wd < (CK + 31) / 32; wd += NT)
+        bm[wd] = 0u;
+      return;
+    }
+  }
+  wg_topk_cls<G, NT, CKM>(lgs, n, k, CK, lv, out_sel, out_cnt, bm, imp, sm);
 }
 
 // Fill the selection of a level whose list has at most k candidates (all kept).

@@ -131,6 +131,7 @@ inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_R
 inline uint32_t atomicOr(uint32_t* p, uint32_t v) { return __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST); }
 
 inline float __expf(float x) { return std::exp(x); }
+inline float __builtin_amdgcn_exp2f(float x) { return std::exp2(x); }
 inline int __clz(int x) { return x == 0 ? 32 : __builtin_clz(static_cast<unsigned>(x)); }
 inline int __popc(unsigned x) { return __builtin_popcount(x); }
 inline float __uint_as_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
