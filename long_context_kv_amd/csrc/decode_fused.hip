@@ -154,8 +154,9 @@ __global__ void __launch_bounds__(kFusedThreads)
   if (tid == 0) {
     s_fail = 0u;
     // the local barrier needs every workgroup of the group on one XCD:
-    // record this one's XCD in the group's placement mask
-    if constexpr (XL) ctl_mark_xcd(ctl, &s_fail);
+    // record this one's XCD in the group's placement mask (no wait for the
+    // atomic: its round trip overlaps the query loads)
+    if constexpr (XL) ctl_mark_xcd_post(ctl);
   }
   load_query_rows<DT, D, G, NT>(q, static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G, qs);
 

@@ -42,12 +42,21 @@ __device__ __forceinline__ uint32_t l2_read(uint32_t* p) {
 }
 
 // Thread 0, XCD-local form: record this workgroup's XCD in the group's
-// placement mask (device scope).  The returned value keeps the atomic
-// performed before this workgroup's first arrival.
+// placement mask (device scope).  ctl_mark_xcd waits for the returned value;
+// ctl_mark_xcd_post does not: it is performed before this workgroup's first
+// arrival all the same, since the arrival first waits for every memory
+// operation of the arriving wave (s_waitcnt 0), so other loads can be in
+// flight with it (the fused decode issues its query loads right behind it).
+__device__ __forceinline__ uint32_t ctl_mark_xcd_issue(const FusedCtl& c) {
+  return __hip_atomic_fetch_or(c.flags, 1u << xcc_id(), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ctl_mark_xcd_post(const FusedCtl& c) {
+  (void)ctl_mark_xcd_issue(c);
+}
 __device__ __forceinline__ void ctl_mark_xcd(const FusedCtl& c, uint32_t* s_fail) {
-  const uint32_t prev = __hip_atomic_fetch_or(c.flags, 1u << xcc_id(), __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-  if (prev & 0x80000000u) *s_fail = 1u;     // never set: keeps the result live
+  const uint32_t prev = ctl_mark_xcd_issue(c);
+  if (prev & 0x80000000u) *s_fail = 1u;     // never set: waits for the result
 }
 
 // XCD-local barrier.  Every wave drains its own memory operations, so after
