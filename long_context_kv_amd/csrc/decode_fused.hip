@@ -114,7 +114,10 @@ __device__ void merge_partials_fused(const float* __restrict__ pp, int W, float*
   }
 }
 
-template <int DT, int D, int G, bool XL>
+// CKM: the top-k's list-size class (C*k <= CKM); each class is its own
+// kernel, so the one top-k it holds is inlined and the kernel makes no calls
+// (no private stack for the dispatch to set up).
+template <int DT, int D, int G, bool XL, int CKM>
 __global__ void __launch_bounds__(kFusedThreads)
     decode_fused_kernel(recsa_tree tr, recsa_pooler P, const void* k_new, const void* v_new,
                         const void* q, int Hq, const int64_t* pos, int32_t* sel, int32_t* cnt,
@@ -128,7 +131,7 @@ __global__ void __launch_bounds__(kFusedThreads)
   // stride list_view reads the parent selection with (k <= kMaxK)
   __shared__ int32_t s_sel[kMaxSel * kMaxK];
   __shared__ int32_t s_cnt[kMaxSel + 1];
-  __shared__ uint32_t s_bm[kMaxSel * (kMaxCK / 32)];
+  __shared__ uint32_t s_bm[kMaxSel * (CKM / 32)];
   __shared__ uint32_t s_fail;
   __shared__ float qs[G * D];
   __shared__ union Smem {
@@ -256,12 +259,8 @@ __global__ void __launch_bounds__(kFusedThreads)
         group_barrier_xcd(ctl.counter, gen * static_cast<uint32_t>(W), ctl.err, &s_fail);
       else
         group_barrier(ctl.flags, w, W, gen, ctl.err, &s_fail);
-      if (CK <= 4096)
-        wg_topk<G, NT, 4096>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1), s_bm + (l - 1) * bm_words,
-                             nullptr, sm.tk);
-      else
-        wg_topk<G, NT, kMaxCK>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1),
-                               s_bm + (l - 1) * bm_words, nullptr, sm.tk);
+      wg_topk<G, NT, CKM>(out_l, n, k, CK, lv, ls, s_cnt + (l - 1), s_bm + (l - 1) * bm_words,
+                          nullptr, sm.tk);
     }
     __syncthreads();
     if (w == 0) {                      // API outputs
@@ -347,7 +346,7 @@ struct FusedGeom {
 // Device facts, cached per device: CUs, co-resident workgroups per CU for
 // both forms of the kernel, and the XCD count when the device is known to
 // hand out workgroups to its XCDs round-robin (gfx950: 32 CUs per XCD).
-template <int DT, int D, int G>
+template <int DT, int D, int G, int CKM>
 static FusedGeom fused_geom(const recsa_tree& tr) {
   static int cached_dev = -1, cus = 0, per_cu_xl = 0, per_cu = 0, n_xcd = 0;
   int dev = 0;
@@ -357,10 +356,10 @@ static FusedGeom fused_geom(const recsa_tree& tr) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return g;
     cus = prop.multiProcessorCount;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fused_kernel<DT, D, G, false>,
-                                                     kFusedThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_xl, decode_fused_kernel<DT, D, G, true>,
-                                                     kFusedThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, decode_fused_kernel<DT, D, G, false, CKM>, kFusedThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu_xl, decode_fused_kernel<DT, D, G, true, CKM>, kFusedThreads, 0) != hipSuccess)
       return g;
     n_xcd = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && cus % 32 == 0) ? cus / 32 : 0;
     const char* env = std::getenv("RECSA_FUSED_XCD_LOCAL");
@@ -385,12 +384,12 @@ static FusedGeom fused_geom(const recsa_tree& tr) {
   return g;
 }
 
-template <int DT, int D, int G>
-static hipError_t fused_impl(const recsa_tree& tr, const recsa_pooler& P, const void* k_new,
-                             const void* v_new, const void* q, int Hq, const int64_t* pos,
-                             int32_t* sel, int32_t* cnt, float* out, void* ws, const WsLayout& w,
-                             hipStream_t s) {
-  const FusedGeom g = fused_geom<DT, D, G>(tr);
+template <int DT, int D, int G, int CKM>
+static hipError_t fused_launch(const recsa_tree& tr, const recsa_pooler& P, const void* k_new,
+                               const void* v_new, const void* q, int Hq, const int64_t* pos,
+                               int32_t* sel, int32_t* cnt, float* out, void* ws,
+                               const WsLayout& w, hipStream_t s) {
+  const FusedGeom g = fused_geom<DT, D, G, CKM>(tr);
   if (g.W < 1) return hipErrorLaunchOutOfResources;
   char* base = static_cast<char*>(ws);
   const dim3 grid(static_cast<unsigned>(g.W) * static_cast<unsigned>(g.S));
@@ -398,14 +397,24 @@ static hipError_t fused_impl(const recsa_tree& tr, const recsa_pooler& P, const 
   float* part = reinterpret_cast<float*>(base + w.part_off);
   uint32_t* ctl = reinterpret_cast<uint32_t*>(base + w.ctl_off);
   if (g.xl)
-    decode_fused_kernel<DT, D, G, true><<<grid, kFusedThreads, 0, s>>>(
+    decode_fused_kernel<DT, D, G, true, CKM><<<grid, kFusedThreads, 0, s>>>(
         tr, P, k_new, v_new, q, Hq, pos, sel, cnt, out, lg, part, ctl, g.W, g.S, g.n_xcd, w.n_sel,
         w.CK);
   else
-    decode_fused_kernel<DT, D, G, false><<<grid, kFusedThreads, 0, s>>>(
+    decode_fused_kernel<DT, D, G, false, CKM><<<grid, kFusedThreads, 0, s>>>(
         tr, P, k_new, v_new, q, Hq, pos, sel, cnt, out, lg, part, ctl, g.W, g.S, g.n_xcd, w.n_sel,
         w.CK);
   return hipGetLastError();
+}
+
+template <int DT, int D, int G>
+static hipError_t fused_impl(const recsa_tree& tr, const recsa_pooler& P, const void* k_new,
+                             const void* v_new, const void* q, int Hq, const int64_t* pos,
+                             int32_t* sel, int32_t* cnt, float* out, void* ws, const WsLayout& w,
+                             hipStream_t s) {
+  if (w.CK <= 4096)
+    return fused_launch<DT, D, G, 4096>(tr, P, k_new, v_new, q, Hq, pos, sel, cnt, out, ws, w, s);
+  return fused_launch<DT, D, G, kMaxCK>(tr, P, k_new, v_new, q, Hq, pos, sel, cnt, out, ws, w, s);
 }
 
 hipError_t launch_decode_fused(const recsa_tree& tr, const recsa_pooler& P, const void* k_new,

@@ -363,7 +363,7 @@ struct TopkSmem {
 // CKM: the list-size class (C*k <= CKM), so thread i owns PPT = CKM/NT
 // positions; PPT divides C, so each thread's vector loads stay in its row.
 template <int G, int NT, int CKM>
-__device__ void wg_topk_cls(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
+__device__ __attribute__((always_inline)) void wg_topk_cls(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
                             int32_t* out_sel, int32_t* out_cnt, uint32_t* bm, float* imp,
                             TopkSmem& sm) {
   static_assert(CKM <= kMaxCK && kC % (CKM / NT) == 0, "list-size class");
@@ -679,7 +679,7 @@ __device__ void wg_topk_cls(const float* __restrict__ lgs, int n, int k, int CK,
 // (decode) keep one class: a second inlined copy would double the fused
 // decode's code.
 template <int G, int NT, int CKM = 4096>
-__device__ void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
+__device__ __attribute__((always_inline)) void wg_topk(const float* __restrict__ lgs, int n, int k, int CK, const ListView& lv,
                         int32_t* out_sel, int32_t* out_cnt, uint32_t* bm, float* imp,
                         TopkSmem& sm) {
   constexpr int HALF = CKM / 2;
