@@ -274,18 +274,14 @@ __global__ void __launch_bounds__(kFusedThreads)
   // two-group level-0 chunks and four-group summary chunks (as many
   // registers per wave, no spills): at the longest lists about one chunk
   // per wave, so the group's loads go out in one round
-  attn_groups<DT, D, G, NT, 2, true>(tr, t, slot, s_sel, s_cnt, eg, w, W, qs, lg_slot, s_bm, CK,
-                                     k_t, v_t, sm.at);
+  // (the waves' merge writes this workgroup's partial state straight out)
   float* pp = part + (slot * kPartSlots + w) * static_cast<int64_t>(G) * (D + kPartHead);
-  for (int e = tid; e < G * D; e += NT)
-    pp[(e / D) * (D + kPartHead) + kPartHead + e % D] = sm.at.wacc[0][e / D][e % D];
-  if (tid < G) {
-    pp[tid * (D + kPartHead)] = sm.at.res_m[tid];
-    pp[tid * (D + kPartHead) + 1] = sm.at.res_l[tid];
-  }
+  attn_groups<DT, D, G, NT, 2, true>(tr, t, slot, s_sel, s_cnt, eg, w, W, qs, lg_slot, s_bm, CK,
+                                     k_t, v_t, sm.at, pp);
   float* o = out + (static_cast<int64_t>(b) * Hq + static_cast<int64_t>(j) * G) * D;
   const float* pp_group = part + slot * kPartSlots * static_cast<int64_t>(G) * (D + kPartHead);
-  __syncthreads();
+  // s_fail is only written inside the waits, each of which ends with a
+  // workgroup barrier, so every thread reads its final value here
   if (s_fail) {
     // one of this workgroup's waits timed out: its selection and partial may
     // be built on incomplete data, and the merge may never run (members on

@@ -1055,7 +1055,9 @@ __device__ __forceinline__ void attn_chunk(const recsa_tree& tr, int64_t t, int6
 // with the whole workgroup (its waves take every NW-th of those; no block
 // barrier inside the loop), then merge the waves: on return sm.res_m,
 // sm.res_l and sm.wacc[0] hold the workgroup's softmax state (valid after
-// the trailing __syncthreads).  Chunks of NG_MAX groups (at most 2 with
+// the trailing __syncthreads), or, given part_out, the merge writes that
+// state there as a partial [G][kPartHead + D] (max, sum, -, -, d values per
+// query head) and returns without the barrier.  Chunks of NG_MAX groups (at most 2 with
 // 8 value words per entry) run over the groups in order; with SPLIT the
 // level-0 groups (key and value rows) form chunks of that size and the
 // summary groups (value rows only) chunks of up to 4, which hold as many
@@ -1068,7 +1070,7 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
                             const float* qs, const float* __restrict__ lg_slot,
                             const uint32_t* __restrict__ bm_slot, int CK,
                             const typename Stor<DT>::T* k_t, const typename Stor<DT>::T* v_t,
-                            AttnSmem<D, G, NT>& sm) {
+                            AttnSmem<D, G, NT>& sm, float* __restrict__ part_out = nullptr) {
   using CS = ChunkShape<DT, D, NG_MAX>;
   constexpr int DPB = CS::DPB, NG = CS::NG;
   constexpr int NW = NT / kWave;
@@ -1152,8 +1154,13 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
       for (int w = 0; w < NW; ++w)
         if (sm.wm[w][g] != -INFINITY) l += __expf(sm.wm[w][g] - M) * sm.wl[w][g];
     }
-    sm.res_m[g] = M;
-    sm.res_l[g] = l;
+    if (part_out) {
+      part_out[g * (D + kPartHead)] = M;
+      part_out[g * (D + kPartHead) + 1] = l;
+    } else {
+      sm.res_m[g] = M;
+      sm.res_l[g] = l;
+    }
   }
   // each (g, d) is read and then overwritten by exactly one thread
   for (int e = threadIdx.x; e < G * D; e += NT) {
@@ -1169,9 +1176,12 @@ __device__ void attn_groups(const recsa_tree& tr, int64_t t, int64_t seq_head, c
         if (mw != -INFINITY) a += __expf(mw - M) * sm.wacc[w][g][dd];
       }
     }
-    sm.wacc[0][g][dd] = a;
+    if (part_out)
+      part_out[g * (D + kPartHead) + kPartHead + dd] = a;
+    else
+      sm.wacc[0][g][dd] = a;
   }
-  __syncthreads();
+  if (!part_out) __syncthreads();
 }
 
 // Merge n_split partial softmax states [n_split][G][D+2] = (m, l, acc[D])
